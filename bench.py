@@ -1,0 +1,231 @@
+"""Benchmark: one FSDP FULL_SHARD rank's fused optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over the rank's shard: the fp32 mean
+of the N incoming gradient slices, AdamW on the shard, and the bf16 cast into
+the all-gather slot -- one fsdp_mt_step launch over every local shard.  The
+shard layout is planned once, before timing, as FSDP does at wrap time.
+Inputs are synthetic and already resident in HBM when timing starts.
+
+Default workload: the 7B model's rank shard at N=8 (291 Shard(0) shards,
+842,301,952 local params, 8 bf16 gradient slices, fp32 master/m/v, bf16 out).
+
+Prints ONE JSON line: params/s as ``value``, HBM GB/s, the roofline fraction
+of the fused kernel against the 8 TB/s HBM3E peak (kernel time from HIP events
+on the launch stream), and the CPU oracle timed on a bounded sample of the
+same workload on this host's cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+METRIC = "sharded AdamW step params/s + HBM GB/s (% peak), 7B rank shard at N=8"
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["rank_step_amd/csrc/rank_step.hip"]
+WORKLOAD_BY_NAME = {"llama7b_full_n8": 4, "llama7b_block_n8": 3, "mlp128m_flat_n4": 2,
+                    "tiny_mlp_flat_n4": 1, "llama70b_full_n32": 5}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_per_param(w, bf16_out):
+    """Algorithmic HBM bytes per parameter of the fused pass: N slices read,
+    fp32 master/m/v read and written, the bf16 copy written.  The reduced
+    gradient never leaves registers."""
+    slice_b = 2 if w.slice_dtype == "bf16" else 4
+    return w.n_slices * slice_b + 12 + 12 + (2 if bf16_out else 0)
+
+
+def measured_traffic(workload, launches_numel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash() or d.get("total_numel") != launches_numel:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(st, t, seconds_hint=15.0):
+    """The oracle (float64 NumPy), as it stands, on a bounded sample of the
+    workload: the rank's first shards, split across this host's cores with a
+    thread pool (NumPy releases the GIL inside its array loops)."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import step as O
+
+    w = st.w
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    # the first shards in registration order, up to ~16M params
+    n = 0
+    names = []
+    for (off, length, held, _), p in zip(st.segments, w.params):
+        if n + length > 16_500_000 and n > 0:
+            break
+        n += length
+        names.append(p.name)
+    p = st.master[:n].double().cpu().numpy()
+    m = st.exp_avg[:n].double().cpu().numpy()
+    v = st.exp_avg_sq[:n].double().cpu().numpy()
+    if w.slice_dtype == "bf16":
+        raw = st.slices[:, :n].view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        raw = st.slices[:, :n].cpu().numpy()
+    bounds = np.linspace(0, n, cores + 1).astype(np.int64)
+
+    def work(i):
+        a, b = bounds[i], bounds[i + 1]
+        sl = O.widen_bf16_bits(raw[:, a:b]) if w.slice_dtype == "bf16" else O.widen_f32(raw[:, a:b])
+        O.rank_step(p[a:b], m[a:b], v[a:b], sl, b - a, t, w.hparams)
+        return b - a
+
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        t0 = time.perf_counter()
+        done = sum(ex.map(work, range(cores)))
+        dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "sample": f"one step of the oracle (float64) on the first {len(names)} shard(s) of the "
+                      f"rank ({', '.join(names)}): {done:,} params x {w.n_slices} "
+                      f"{w.slice_dtype} slices, {dt:.2f} s wall on {cores} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_full_n8", choices=sorted(WORKLOAD_BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle timing (e.g. under a profiler)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the step, run torch copies of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(each rank's step is independent: see the sharding section of DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(args.warmup):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                          "ms_per_copy": ms, "gb_s": 8 * n / ms / 1e6}), flush=True)
+        return
+
+    from rank_step_amd.state import RankState
+    from rank_step_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[WORKLOAD_BY_NAME[args.workload]]
+    bf16_out = w.bf16_out
+    st = RankState(w, 0, dev, bf16_out=bf16_out)
+    st.load_grads(1)
+    st.make_plan(stream)
+    info = st.plan.info()
+    total = st.total
+    bpp = bytes_per_param(w, bf16_out)
+
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        st.step(t, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        t += 1
+        st.step(t, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    sec = ms / 1e3
+    params_s = total / sec
+    gbs = bpp * total / sec / 1e9
+
+    traffic = measured_traffic(w.name, total)
+    out = {
+        "metric": METRIC,
+        "value": params_s,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "layout": "shard0" if w.mode == "shard0" else "flat",
+            "world_size": w.world_size,
+            "rank": 0,
+            "local_params": total,
+            "shards": info["n_tensors"],
+            "grad_slices": f"{w.n_slices} x {w.slice_dtype}",
+            "state": "fp32 master + exp_avg + exp_avg_sq" if w.has_master else "fp32 param + exp_avg + exp_avg_sq",
+            "bf16_out": bf16_out,
+            "bytes_per_param": bpp,
+            "launch": {"workgroups": info["n_blocks"], "chunks": info["n_chunks"],
+                       "chunk_numel": info["chunk_numel"]},
+        },
+        "hbm_gb_s": gbs,
+        "hbm_frac_of_peak": gbs / HBM_PEAK_GBS,
+        "host_wall_s_timed": wall,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(st, t + 1)
+    st.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+/*
+ * fsdp_step.h -- C ABI of librank_step.so: one data-parallel rank's share of an
+ * FSDP FULL_SHARD (ZeRO-3) training step on an AMD Instinct MI355X (gfx950).
+ *
+ * The rank's work between the backward reduce-scatter and the next forward
+ * all-gather, as the pages describe it:
+ *   1. fsdp_shard_layout      where the rank's 1/N shard of each parameter lies
+ *   2. fsdp_reduce_grad_shard the fp32 mean of the N gradient slices of that shard
+ *   3. fsdp_adamw_shard_step  decoupled-weight-decay AdamW on the shard only
+ *   4. fsdp_cast_unshard_bf16 the updated shard cast to bf16, into the buffer the
+ *                             next all-gather reads
+ * plus a multi-tensor plan (fsdp_mt_*) that runs 2+3+4 fused, in one pass over
+ * memory, for many per-parameter shards in a single kernel launch.
+ *
+ * Page citations use the pages' titles:
+ *   [FSDP ch.18]   "PyTorch 训练框架内核深度解析 -- 第18章 FSDP：ZeRO 风格的参数分片"
+ *   [ZeRO post]    NCCL ZeRO / FSDP state sharding (blog.cptz.space)
+ *   [FSDP2 doc]    "PyTorch FSDP2 后端特性介绍" (MindSpeed-LLM docs)
+ *   [titan FSDP2]  torchtitan FSDP2 / HSDP / meta-init article (gsyq.cn)
+ *
+ * Conventions for every call:
+ *   - Return value: FSDP_OK (0) or a negative FSDP_E_* code; on error
+ *     fsdp_last_error() gives a message (thread-local, valid until the next
+ *     failing call on the same thread).  Nothing aborts, nothing throws.
+ *   - All arguments are checked on the host before any device work is queued.
+ *   - Device pointers are plain HIP device addresses on the current device.
+ *     The caller owns every buffer; the library never allocates or frees them.
+ *   - Work is queued on the caller's stream (NULL = the null stream) and is
+ *     asynchronous; no call synchronises the host except fsdp_mt_plan_create.
+ *   - Sizes and offsets are in elements unless a name says bytes.
+ *   - Padding: positions [valid, shard_numel) of every buffer the call writes
+ *     are set to +0.0 (all-zero bits); inputs are never read there.  NaN and
+ *     Inf in inputs are not errors: they propagate per IEEE 754.
+ *   - Floating point: fp32 with IEEE-correct division and square root, no
+ *     flush of denormals.  Results are deterministic run to run (no atomics).
+ */
+#ifndef FSDP_STEP_H
+#define FSDP_STEP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t; /* the HIP stream handle type */
+
+enum {
+    FSDP_OK = 0,
+    FSDP_E_ARG = -1,      /* null pointer, negative size, value out of range */
+    FSDP_E_DTYPE = -2,    /* unknown dtype, or mixed dtypes in one flat unit */
+    FSDP_E_ALIGN = -3,    /* pointer not aligned to its element size */
+    FSDP_E_ALIAS = -4,    /* a written buffer overlaps another buffer of the call */
+    FSDP_E_HIP = -5,      /* a HIP runtime call or kernel launch failed */
+    FSDP_E_CAPACITY = -6, /* a size exceeds what the call supports */
+    FSDP_E_STATE = -7     /* plan used on a device other than the one it was made on */
+};
+
+typedef enum { FSDP_DT_F32 = 0, FSDP_DT_BF16 = 1 } fsdp_dtype;
+typedef enum { FSDP_LAYOUT_FLAT = 0, FSDP_LAYOUT_SHARD0 = 1 } fsdp_layout_mode;
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* fsdp_last_error(void);
+
+/* ------------------------------------------------------------------ layout */
+
+/* One original parameter: total element count, size of dim 0 (a 0-d tensor
+ * is numel=1, dim0=1; numel must be a multiple of dim0 when numel > 0), and
+ * its dtype (fsdp_dtype). */
+typedef struct {
+    int64_t numel;
+    int64_t dim0;
+    int32_t dtype;
+    int32_t reserved; /* must be 0 */
+} fsdp_tensor_shape;
+
+/* Where one parameter's data lies on one rank.
+ *   shard_numel    length of the local buffer holding it (FLAT: the rank's
+ *                  whole flat shard S; SHARD0: ceil(dim0/N) rows)
+ *   valid          leading elements of that buffer that are real data; the
+ *                  rest, [valid, shard_numel), is zero padding
+ *   global_offset  offset of the parameter in the unpadded concatenation of
+ *                  all parameters in the order given
+ *   view_offset    where its local piece starts in the rank's local storage
+ *                  (FLAT: in the flat shard; SHARD0: in the concatenation of
+ *                  the rank's shards in the order given)
+ *   view_numel     elements of the parameter the rank holds (may be 0)
+ *   tensor_offset  index, in the flattened parameter, of the first one held
+ * For an empty FLAT view, with lo = max(global_offset, rank*S):
+ * view_offset = min(lo - rank*S, S), tensor_offset = min(lo - global_offset, numel). */
+typedef struct {
+    int64_t shard_numel, valid, global_offset, view_offset, view_numel, tensor_offset;
+} fsdp_shard_view;
+
+/* Per-rank totals.  logical_numel: sum of numel; physical_numel: padded
+ * element count over all N ranks; shard_numel / pad_numel: this rank's local
+ * elements and the padding among them; bytes_param: local parameter bytes in
+ * the parameters' dtypes; bytes_grad: the fp32 reduced-gradient shard;
+ * bytes_optim: exp_avg + exp_avg_sq (fp32); bytes_master: fp32 master copy
+ * (0 when has_master is 0).  All per rank, padding included. */
+typedef struct {
+    int64_t logical_numel, physical_numel, shard_numel, pad_numel;
+    int64_t bytes_param, bytes_grad, bytes_optim, bytes_master;
+} fsdp_layout_summary;
+
+/* Shard layout of `rank` among `world_size` ranks.  Host only: no device
+ * work, deterministic, thread-safe.
+ *
+ * FSDP_LAYOUT_FLAT -- [FSDP ch.18] §18.12 FlatParameter: the parameters are
+ *   flattened and concatenated in the order given into one vector of P
+ *   elements, which must share one dtype (else FSDP_E_DTYPE); [ZeRO post]
+ *   section "FlatParameter 与 Padding": it is padded at its end to
+ *   N*ceil(P/N) and rank r owns [r*S, r*S+S), S = ceil(P/N); the rank's view
+ *   of a parameter may be empty.
+ * FSDP_LAYOUT_SHARD0 -- [FSDP2 doc] section "DTensor", [titan FSDP2] §2.3:
+ *   each parameter is sharded on its own along dim 0, (d0, ...) ->
+ *   (d0/N, ...); when N does not divide d0, every rank gets ceil(d0/N) rows
+ *   and the trailing ranks' missing rows are padding.
+ * Byte totals follow [ZeRO post] tables "Canonical ZeRO 状态公式" /
+ * "实测状态因子" (stage 3: P/N params, P/N grads, 2P/N optimizer state per
+ * rank) and [titan FSDP2] §2.3 (master + moments = 12 bytes per parameter).
+ *
+ * views_out: caller array of n_tensors records (may be NULL if n_tensors is
+ * 0); summary_out may be NULL.  n_tensors may be 0.  Errors: FSDP_E_ARG for
+ * a bad mode, world_size < 1, rank outside [0, world_size), negative sizes,
+ * numel not a multiple of dim0, nonzero reserved, or int64 overflow;
+ * FSDP_E_DTYPE as above.  Outputs are untouched on error. */
+int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t rank,
+                          const fsdp_tensor_shape* tensors, int32_t n_tensors,
+                          int32_t has_master, fsdp_shard_view* views_out,
+                          fsdp_layout_summary* summary_out);
+
+/* ------------------------------------------------------------------ step */
+
+/* AdamW hyperparameters.  step is the 1-based count of this update.
+ * Required: all finite, lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps >= 0,
+ * weight_decay >= 0, step >= 1 (else FSDP_E_ARG).  Derived scalars
+ * (1 - lr*wd, lr/(1 - beta1^step), 1/sqrt(1 - beta2^step)) are computed on
+ * the host in double and rounded to fp32. */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step;
+} fsdp_adamw_hparams;
+
+/* Reduce the N gradient slices of a shard to their fp32 mean:
+ *   grad_shard_out[k] = (x_0[k] + x_1[k] + ... + x_{N-1}[k]) / N,  k < valid
+ *   grad_shard_out[k] = +0,                                        k >= valid
+ * with x_q[k] = grad_slices[q*slice_stride + k] widened exactly to fp32, the
+ * sum taken in fp32 in the order q = 0..N-1 and one correctly rounded
+ * division by N.  This is the arithmetic a rank does in a reduce-scatter with
+ * reduce_dtype=float32: [FSDP ch.18] §18.3 / §18.6, [ZeRO post] "ZeRO-2
+ * 方向：Gradient Sharding", [FSDP2 doc] "混合精度"; the mean (not the sum)
+ * per [ZeRO post] "Optimizer Step 的所有权" (replicas step with averaged
+ * gradients).
+ *   grad_shard_out  device fp32 [shard_numel], written
+ *   grad_slices     device [n_slices][slice_stride] of slice_dtype, read in
+ *                   [0, valid) of each slice only
+ *   n_slices        N >= 1 (1 = already reduced: a copy); at most 1024
+ *   slice_stride    elements between slices, >= shard_numel when N > 1
+ * The output must not overlap the slices (FSDP_E_ALIAS).  shard_numel = 0 is
+ * a no-op. */
+int32_t fsdp_reduce_grad_shard(float* grad_shard_out, const void* grad_slices,
+                               int32_t slice_dtype, int64_t slice_stride,
+                               int32_t n_slices, int64_t shard_numel, int64_t valid,
+                               hipStream_t stream);
+
+/* One decoupled-weight-decay AdamW step on the local shard only, in place
+ * ([FSDP ch.18] §18.21, [ZeRO post] "FSDP Sharded Optimizer", [FSDP2 doc]
+ * "工作原理": each rank updates its own 1/N with its 1/N gradient and state,
+ * with no communication).  The optimizer is torch.optim.AdamW
+ * ([FSDP ch.18] §18.43); with t = hp->step, for k < valid:
+ *   p1 = p*(1 - lr*wd);  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*g*g
+ *   p  = p1 - (lr/(1-b1^t)) * m / (sqrt(v)/sqrt(1-b2^t) + eps)
+ * and p = m = v = +0 for k >= valid.
+ *   param_fp32, exp_avg, exp_avg_sq  device fp32 [shard_numel], read/written
+ *   grad_shard                       device fp32 [shard_numel], read in [0, valid)
+ * The three state buffers must be pairwise disjoint and not overlap the
+ * gradient (FSDP_E_ALIAS).  shard_numel = 0 is a no-op. */
+int32_t fsdp_adamw_shard_step(float* param_fp32, float* exp_avg, float* exp_avg_sq,
+                              const float* grad_shard, int64_t shard_numel, int64_t valid,
+                              const fsdp_adamw_hparams* hp, hipStream_t stream);
+
+/* Cast the updated fp32 shard to bf16 into this rank's slot of the next
+ * all-gather's input ([FSDP ch.18] §18.6: bf16 on the wire, fp32 master;
+ * §18.10: the low-precision cast runs before the all-gather).
+ *   out[k] = RNE_bf16(param_fp32[k]) for k < valid, 0x0000 for k >= valid
+ * Round to nearest, ties to even; overflow gives +-Inf; NaN gives the quiet
+ * NaN 0x7FC0 with the input's sign.
+ *   unshard_bf16_out  device bf16 [shard_numel] (e.g. offset rank*S of a
+ *                     packed [N*S] all-gather buffer), written
+ *   param_fp32        device fp32 [shard_numel], read in [0, valid)
+ * The two must not overlap (FSDP_E_ALIAS).  shard_numel = 0 is a no-op. */
+int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const float* param_fp32,
+                               int64_t shard_numel, int64_t valid, hipStream_t stream);
+
+/* ------------------------------------------------------------------ multi-tensor */
+
+/* One local shard in a multi-tensor plan.  The plan runs, per element and in
+ * one pass over memory: the reduce of fsdp_reduce_grad_shard, the update of
+ * fsdp_adamw_shard_step and the cast of fsdp_cast_unshard_bf16 -- with
+ * bit-identical results to calling the three in that order.
+ *   param_fp32, exp_avg, exp_avg_sq  device fp32 [shard_numel], read/written
+ *   grad_slices, slice_stride        as in fsdp_reduce_grad_shard
+ *   unshard_bf16_out                 device bf16 [shard_numel] or NULL (no cast)
+ *   grad_shard_out                   device fp32 [shard_numel] or NULL (the
+ *                                    reduced gradient is not stored) */
+typedef struct {
+    float* param_fp32;
+    float* exp_avg;
+    float* exp_avg_sq;
+    const void* grad_slices;
+    int64_t slice_stride;
+    uint16_t* unshard_bf16_out;
+    float* grad_shard_out;
+    int64_t shard_numel;
+    int64_t valid;
+} fsdp_mt_tensor;
+
+typedef struct fsdp_mt_plan fsdp_mt_plan; /* opaque */
+
+typedef struct {
+    int64_t n_tensors;   /* shards in the plan */
+    int64_t n_chunks;    /* entries of the chunk-descriptor table */
+    int64_t n_blocks;    /* workgroups of one fsdp_mt_step launch */
+    int64_t total_numel; /* sum of shard_numel */
+    int64_t total_valid; /* sum of valid */
+    int64_t chunk_numel; /* elements per chunk (the last of a shard may be shorter) */
+    int32_t n_slices;
+    int32_t slice_dtype;
+} fsdp_mt_plan_info;
+
+/* Build a plan over n_tensors shards sharing N = n_slices and slice_dtype
+ * (the multi-tensor "fused optimizer" batching of [FSDP ch.18] §18.12 and
+ * §18.43: many parameters per launch instead of one by one).  Copies the
+ * records, checks them as the single-shard calls would (no written buffer
+ * may overlap any other buffer of any shard in the plan; read-only slices
+ * may overlap each other), builds the chunk-descriptor table and uploads it
+ * to device memory the plan owns on the current device.  Synchronises
+ * `stream` once.  The caller keeps every referenced buffer alive and in
+ * place while the plan exists.  n_tensors may be 0 (an empty plan).
+ * Errors: as the single-shard calls; FSDP_E_HIP if the upload fails. */
+int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tensors,
+                            int32_t n_tensors, int32_t n_slices, int32_t slice_dtype,
+                            hipStream_t stream);
+
+/* One step over every shard of the plan: exactly one kernel launch on
+ * `stream` (none for an empty plan), no host synchronisation.  The plan must
+ * be used on the device it was made on (FSDP_E_STATE).  Two steps of one
+ * plan on different streams without ordering between them race. */
+int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, hipStream_t stream);
+
+/* Sizes of a plan (host only). */
+int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info_out);
+
+/* Free a plan's device tables; waits for device work that may still read
+ * them.  NULL is a no-op. */
+int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSDP_STEP_H */

@@ -1,0 +1,247 @@
+"""ctypes binding of librank_step.so (C ABI in include/fsdp_step.h).
+
+Argument marshalling only: every function here converts its Python arguments
+(torch tensors, ints, dicts) to the C types of the entry point of the same
+name, calls it, and raises ``FsdpError`` on a nonzero status.  No arithmetic of
+the step happens here.  The library is loaded on first use and a missing
+library is an error -- there is no fallback.
+
+Pointer arguments accept a torch tensor (its ``data_ptr()``), a raw address
+(int) or None (NULL).  Stream arguments accept a ``torch.cuda.Stream``, a raw
+``hipStream_t`` (int) or None, which means torch's current stream on the
+current device so that the work is ordered with torch's own.
+"""
+
+import ctypes
+import os
+import threading
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librank_step.so")
+_lib = None
+_lock = threading.Lock()
+
+FSDP_OK = 0
+ERRORS = {-1: "FSDP_E_ARG", -2: "FSDP_E_DTYPE", -3: "FSDP_E_ALIGN", -4: "FSDP_E_ALIAS",
+          -5: "FSDP_E_HIP", -6: "FSDP_E_CAPACITY", -7: "FSDP_E_STATE"}
+DTYPES = {"f32": 0, "bf16": 1}
+LAYOUTS = {"flat": 0, "shard0": 1}
+
+# Every function the header declares; the CPU tests check each is exported.
+EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
+           "fsdp_adamw_shard_step", "fsdp_cast_unshard_bf16", "fsdp_mt_plan_create",
+           "fsdp_mt_step", "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy")
+
+
+class FsdpError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+
+
+class TensorShape(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("dim0", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class ShardView(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("shard_numel", "valid", "global_offset",
+                                              "view_offset", "view_numel", "tensor_offset")]
+
+
+class LayoutSummary(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("logical_numel", "physical_numel", "shard_numel",
+                                              "pad_numel", "bytes_param", "bytes_grad",
+                                              "bytes_optim", "bytes_master")]
+
+
+class AdamWHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("step", ctypes.c_int64)]
+
+
+class MtTensor(ctypes.Structure):
+    _fields_ = [("param_fp32", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("grad_slices", ctypes.c_void_p),
+                ("slice_stride", ctypes.c_int64), ("unshard_bf16_out", ctypes.c_void_p),
+                ("grad_shard_out", ctypes.c_void_p), ("shard_numel", ctypes.c_int64),
+                ("valid", ctypes.c_int64)]
+
+
+class MtPlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("n_tensors", "n_chunks", "n_blocks", "total_numel",
+                                              "total_valid", "chunk_numel")] + [
+        ("n_slices", ctypes.c_int32), ("slice_dtype", ctypes.c_int32)]
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
+                               "(python -m rank_step_amd.build or __graft_entry__.build())")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.fsdp_last_error.restype = ctypes.c_char_p
+        L.fsdp_last_error.argtypes = []
+        sig = {
+            "fsdp_shard_layout": [i32, i32, i32, ctypes.POINTER(TensorShape), i32, i32,
+                                  ctypes.POINTER(ShardView), ctypes.POINTER(LayoutSummary)],
+            "fsdp_reduce_grad_shard": [vp, vp, i32, i64, i32, i64, i64, vp],
+            "fsdp_adamw_shard_step": [vp, vp, vp, vp, i64, i64, ctypes.POINTER(AdamWHparams), vp],
+            "fsdp_cast_unshard_bf16": [vp, vp, i64, i64, vp],
+            "fsdp_mt_plan_create": [ctypes.POINTER(vp), ctypes.POINTER(MtTensor), i32, i32, i32, vp],
+            "fsdp_mt_step": [vp, ctypes.POINTER(AdamWHparams), vp],
+            "fsdp_mt_plan_get_info": [vp, ctypes.POINTER(MtPlanInfo)],
+            "fsdp_mt_plan_destroy": [vp],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = i32
+        _lib = L
+        return L
+
+
+def _check(code):
+    if code != FSDP_OK:
+        msg = lib().fsdp_last_error().decode(errors="replace")
+        raise FsdpError(code, msg)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _dtype(d):
+    return DTYPES[d] if isinstance(d, str) else int(d)
+
+
+def _hparams(hp, step):
+    return AdamWHparams(float(hp["lr"]), float(hp["beta1"]), float(hp["beta2"]),
+                        float(hp["eps"]), float(hp["weight_decay"]), int(step))
+
+
+# ---------------------------------------------------------------- entry points
+
+def fsdp_shard_layout(mode, world_size, rank, shapes, has_master):
+    """``shapes``: (numel, dim0, dtype) triples.  Returns (views, summary) as
+    lists/dicts of ints, fields named as in the header."""
+    n = len(shapes)
+    arr = (TensorShape * max(n, 1))()
+    for i, (numel, dim0, dt) in enumerate(shapes):
+        arr[i] = TensorShape(int(numel), int(dim0), _dtype(dt), 0)
+    views = (ShardView * max(n, 1))()
+    summ = LayoutSummary()
+    m = LAYOUTS[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().fsdp_shard_layout(m, int(world_size), int(rank), arr, n, int(bool(has_master)),
+                                   views, ctypes.byref(summ)))
+    vs = [{f: getattr(views[i], f) for f, _ in ShardView._fields_} for i in range(n)]
+    return vs, {f: getattr(summ, f) for f, _ in LayoutSummary._fields_}
+
+
+def fsdp_reduce_grad_shard(grad_shard_out, grad_slices, slice_dtype, slice_stride, n_slices,
+                           shard_numel, valid, stream=None):
+    _check(lib().fsdp_reduce_grad_shard(_ptr(grad_shard_out), _ptr(grad_slices),
+                                        _dtype(slice_dtype), int(slice_stride), int(n_slices),
+                                        int(shard_numel), int(valid), _stream(stream)))
+
+
+def fsdp_adamw_shard_step(param_fp32, exp_avg, exp_avg_sq, grad_shard, shard_numel, valid, hp,
+                          step, stream=None):
+    h = _hparams(hp, step)
+    _check(lib().fsdp_adamw_shard_step(_ptr(param_fp32), _ptr(exp_avg), _ptr(exp_avg_sq),
+                                       _ptr(grad_shard), int(shard_numel), int(valid),
+                                       ctypes.byref(h), _stream(stream)))
+
+
+def fsdp_cast_unshard_bf16(unshard_bf16_out, param_fp32, shard_numel, valid, stream=None):
+    _check(lib().fsdp_cast_unshard_bf16(_ptr(unshard_bf16_out), _ptr(param_fp32),
+                                        int(shard_numel), int(valid), _stream(stream)))
+
+
+def fsdp_mt_plan_create(tensors, n_slices, slice_dtype, stream=None):
+    """``tensors``: dicts with the fsdp_mt_tensor fields.  Returns an opaque
+    handle (int) to pass to fsdp_mt_step / fsdp_mt_plan_destroy."""
+    n = len(tensors)
+    arr = (MtTensor * max(n, 1))()
+    for i, t in enumerate(tensors):
+        arr[i] = MtTensor(_ptr(t["param_fp32"]), _ptr(t["exp_avg"]), _ptr(t["exp_avg_sq"]),
+                          _ptr(t.get("grad_slices")), int(t.get("slice_stride", 0)),
+                          _ptr(t.get("unshard_bf16_out")), _ptr(t.get("grad_shard_out")),
+                          int(t["shard_numel"]), int(t["valid"]))
+    h = ctypes.c_void_p()
+    _check(lib().fsdp_mt_plan_create(ctypes.byref(h), arr, n, int(n_slices), _dtype(slice_dtype),
+                                     _stream(stream)))
+    return h.value
+
+
+def fsdp_mt_step(plan, hp, step, stream=None):
+    h = _hparams(hp, step)
+    _check(lib().fsdp_mt_step(plan, ctypes.byref(h), _stream(stream)))
+
+
+def fsdp_mt_plan_get_info(plan):
+    info = MtPlanInfo()
+    _check(lib().fsdp_mt_plan_get_info(plan, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in MtPlanInfo._fields_}
+
+
+def fsdp_mt_plan_destroy(plan):
+    _check(lib().fsdp_mt_plan_destroy(plan))
+
+
+class MtPlan:
+    """Owns one fsdp_mt_plan handle (and keeps the Python objects whose
+    buffers it references alive)."""
+
+    def __init__(self, tensors, n_slices, slice_dtype, stream=None):
+        self._keep = tensors
+        self.handle = fsdp_mt_plan_create(tensors, n_slices, slice_dtype, stream)
+
+    def step(self, hp, step, stream=None):
+        fsdp_mt_step(self.handle, hp, step, stream)
+
+    def info(self):
+        return fsdp_mt_plan_get_info(self.handle)
+
+    def close(self):
+        if self.handle is not None:
+            fsdp_mt_plan_destroy(self.handle)
+            self.handle = None
+            self._keep = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,32 @@
+// Internal helpers shared by the host sources of librank_step.so.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "fsdp_step.h"
+
+namespace fsdp {
+
+// Records `code` with a printf-style message as this thread's last error and
+// returns `code`.
+int32_t fail(int32_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int32_t ok();
+
+// Overflow-checked int64 arithmetic; return false on overflow.
+bool mul_i64(int64_t a, int64_t b, int64_t* out);
+bool add_i64(int64_t a, int64_t b, int64_t* out);
+
+// A byte range [lo, hi) of one buffer named `what`, written or read-only.
+struct Range {
+    uintptr_t lo, hi;
+    bool written;
+    int32_t owner;  // tensor index inside a plan, or 0
+    const char* what;
+};
+
+// FSDP_E_ALIAS if a written range overlaps any other range (read-only ranges
+// may overlap each other); empty ranges never overlap.
+int32_t check_aliases(std::vector<Range>& ranges);
+
+}  // namespace fsdp

@@ -1,0 +1,142 @@
+// fsdp_shard_layout: the integer shard arithmetic of one rank (host only).
+//
+// FLAT mode follows the FlatParameter of the FSDP chapter (yangyitao.com,
+// ch. 18), §18.12: the unit's parameters are flattened and concatenated in
+// registration order into one vector that is sharded once, and they must
+// share a dtype.  The tail padding to N * ceil(P / N) and the possibly empty
+// per-rank views of the original parameters are from the ZeRO state sharding
+// post (blog.cptz.space), section "FlatParameter 与 Padding".
+//
+// SHARD0 mode follows FSDP2's per-parameter Shard(0) (MindSpeed-LLM FSDP2 doc,
+// section "DTensor"; torchtitan FSDP2 article, §2.3): each parameter is split
+// along dim 0 on its own.  When N does not divide dim 0 every rank still gets
+// ceil(dim0 / N) rows and the rows past the end are padding.
+
+#include <cstdint>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+using fsdp::fail;
+
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+int64_t clamp(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+int64_t dtype_size(int32_t dt) { return dt == FSDP_DT_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t rank,
+                                     const fsdp_tensor_shape* tensors, int32_t n_tensors,
+                                     int32_t has_master, fsdp_shard_view* views_out,
+                                     fsdp_layout_summary* summary_out) {
+    if (mode != FSDP_LAYOUT_FLAT && mode != FSDP_LAYOUT_SHARD0)
+        return fail(FSDP_E_ARG, "fsdp_shard_layout: unknown mode %d", mode);
+    if (world_size < 1) return fail(FSDP_E_ARG, "fsdp_shard_layout: world_size %d < 1", world_size);
+    if (rank < 0 || rank >= world_size)
+        return fail(FSDP_E_ARG, "fsdp_shard_layout: rank %d outside [0, %d)", rank, world_size);
+    if (n_tensors < 0) return fail(FSDP_E_ARG, "fsdp_shard_layout: n_tensors %d < 0", n_tensors);
+    if (n_tensors > 0 && (tensors == nullptr || views_out == nullptr))
+        return fail(FSDP_E_ARG, "fsdp_shard_layout: null tensors or views_out");
+
+    // Validate every shape before writing anything.
+    int64_t logical = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        const fsdp_tensor_shape& t = tensors[i];
+        if (t.reserved != 0) return fail(FSDP_E_ARG, "tensor %d: reserved field must be 0", i);
+        if (t.dtype != FSDP_DT_F32 && t.dtype != FSDP_DT_BF16)
+            return fail(FSDP_E_DTYPE, "tensor %d: unknown dtype %d", i, t.dtype);
+        if (t.numel < 0 || t.dim0 < 0)
+            return fail(FSDP_E_ARG, "tensor %d: negative numel or dim0", i);
+        if (t.numel > 0 && (t.dim0 < 1 || t.numel % t.dim0 != 0))
+            return fail(FSDP_E_ARG, "tensor %d: numel %lld is not a multiple of dim0 %lld", i,
+                        (long long)t.numel, (long long)t.dim0);
+        if (mode == FSDP_LAYOUT_FLAT && t.dtype != tensors[0].dtype)
+            return fail(FSDP_E_DTYPE, "FLAT unit mixes dtypes (tensor %d vs tensor 0)", i);
+        if (!fsdp::add_i64(logical, t.numel, &logical))
+            return fail(FSDP_E_ARG, "total element count overflows int64");
+    }
+
+    const int64_t N = world_size;
+    const int64_t r = rank;
+    std::vector<fsdp_shard_view> views(static_cast<size_t>(n_tensors));
+    fsdp_layout_summary s{};
+    s.logical_numel = logical;
+
+    if (mode == FSDP_LAYOUT_FLAT) {
+        const int64_t S = ceil_div(logical, N);
+        int64_t phys;
+        if (!fsdp::mul_i64(S, N, &phys)) return fail(FSDP_E_ARG, "padded size overflows int64");
+        const int64_t shard_lo = r * S;
+        const int64_t valid = clamp(logical - shard_lo, 0, S);
+        int64_t off = 0;
+        for (int32_t i = 0; i < n_tensors; ++i) {
+            const int64_t n = tensors[i].numel;
+            const int64_t lo = max64(off, shard_lo);
+            const int64_t hi = min64(off + n, shard_lo + S);
+            fsdp_shard_view& v = views[i];
+            v.shard_numel = S;
+            v.valid = valid;
+            v.global_offset = off;
+            if (hi > lo) {
+                v.view_offset = lo - shard_lo;
+                v.view_numel = hi - lo;
+                v.tensor_offset = lo - off;
+            } else {
+                v.view_offset = min64(lo - shard_lo, S);
+                v.view_numel = 0;
+                v.tensor_offset = min64(lo - off, n);
+            }
+            off += n;
+        }
+        const int64_t esize = n_tensors > 0 ? dtype_size(tensors[0].dtype) : 4;
+        s.physical_numel = phys;
+        s.shard_numel = S;
+        s.pad_numel = S - valid;
+        s.bytes_param = S * esize;
+    } else {
+        int64_t off = 0, packed = 0, phys = 0, bytes_param = 0, pad = 0;
+        for (int32_t i = 0; i < n_tensors; ++i) {
+            const fsdp_tensor_shape& t = tensors[i];
+            int64_t sn = 0, valid = 0, toff = 0;
+            if (t.numel > 0) {
+                const int64_t row = t.numel / t.dim0;
+                const int64_t c = ceil_div(t.dim0, N);
+                const int64_t rows = clamp(t.dim0 - r * c, 0, c);
+                if (!fsdp::mul_i64(c, row, &sn)) return fail(FSDP_E_ARG, "shard size overflows");
+                valid = rows * row;
+                toff = min64(r * c, t.dim0) * row;
+            }
+            fsdp_shard_view& v = views[i];
+            v.shard_numel = sn;
+            v.valid = valid;
+            v.global_offset = off;
+            v.view_offset = packed;
+            v.view_numel = valid;
+            v.tensor_offset = toff;
+            int64_t sn_all, b;
+            if (!fsdp::mul_i64(sn, N, &sn_all) || !fsdp::add_i64(phys, sn_all, &phys) ||
+                !fsdp::add_i64(packed, sn, &packed) ||
+                !fsdp::mul_i64(sn, dtype_size(t.dtype), &b) ||
+                !fsdp::add_i64(bytes_param, b, &bytes_param))
+                return fail(FSDP_E_ARG, "layout sizes overflow int64");
+            off += t.numel;
+            pad += sn - valid;
+        }
+        s.physical_numel = phys;
+        s.shard_numel = packed;
+        s.pad_numel = pad;
+        s.bytes_param = bytes_param;
+    }
+    if (!fsdp::mul_i64(s.shard_numel, 8, &s.bytes_optim))
+        return fail(FSDP_E_ARG, "byte counts overflow int64");
+    s.bytes_grad = s.shard_numel * 4;
+    s.bytes_master = has_master ? s.shard_numel * 4 : 0;
+    for (int32_t i = 0; i < n_tensors; ++i) views_out[i] = views[i];
+    if (summary_out) *summary_out = s;
+    return FSDP_OK;
+}

@@ -1,0 +1,904 @@
+// HIP kernels and device entry points of librank_step.so (gfx950 / MI355X).
+//
+// One FSDP FULL_SHARD rank's step after the backward reduce-scatter and before
+// the next forward all-gather: the fp32 mean of the N gradient slices of the
+// rank's shard, decoupled-weight-decay AdamW on that shard only, and the bf16
+// cast of the updated shard into the all-gather input slot.  The arithmetic
+// and its sources are stated at each device function below and in the header.
+//
+// The path is bound by HBM bandwidth (about half a flop per byte), so there is
+// no matrix-core work: every kernel is a streaming pass.  Each thread moves 8
+// consecutive elements per access -- one 16-byte load of bf16, two 16-byte
+// loads of fp32 -- and a 256-thread workgroup (four wave64s) covers 2048
+// elements per iteration.  Every load of an iteration is issued before its
+// first use; gradient slices and the bf16 copy are touched once and use
+// non-temporal accesses.  Shards whose buffers are not 16-byte aligned take an
+// element-by-element path with the same arithmetic (bit-identical results).
+//
+// The multi-tensor launch reads a host-built chunk-descriptor table: each
+// workgroup stages its run of chunk entries and the shard descriptors they
+// point to in LDS, then streams through the chunks.
+//
+// Floating point: fp32, FMA only where written (built with -ffp-contract=off),
+// IEEE-correct division and square root, denormals kept.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+
+using fsdp::fail;
+
+namespace {
+
+constexpr int kBlock = 256;             // threads per workgroup: four wave64s
+constexpr int kGroup = 8;               // elements per thread access
+constexpr int kTile = kBlock * kGroup;  // elements per workgroup iteration
+constexpr int kMaxSlices = 1024;
+constexpr int kChunksPerBlock = 4;      // chunk entries staged per workgroup
+constexpr int64_t kTargetBlocks = 4096; // ~16 workgroups per CU on 256 CUs
+constexpr int64_t kMinChunk = kTile;
+constexpr int64_t kMaxChunk = 32 * kTile;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One shard as the kernels see it.  Copied to LDS as 8-byte words.
+struct TensorDesc {
+    float* param;
+    float* m;
+    float* v;
+    const void* slices;
+    uint16_t* out_bf16;  // null: no cast
+    float* grad_out;     // null: reduced gradient not stored
+    int64_t slice_stride;
+    int64_t shard_numel;
+    int64_t valid;
+    int64_t vec_ok;      // every buffer 16-byte aligned, slice stride a multiple of 16 bytes
+};
+constexpr int kDescWords = sizeof(TensorDesc) / 8;
+static_assert(sizeof(TensorDesc) % 8 == 0, "descriptor is copied as 8-byte words");
+
+// One entry of the chunk-descriptor table: elements [begin, begin+count) of a shard.
+struct ChunkDesc {
+    int64_t begin;
+    int32_t tensor;
+    int32_t count;
+};
+static_assert(sizeof(ChunkDesc) == 16, "chunk entries are 16 bytes");
+
+// fp32 scalars of one step, derived on the host in double.
+struct StepConsts {
+    float decay;         // 1 - lr*wd
+    float beta1, omb1;   // beta1, 1 - beta1
+    float beta2, omb2;   // beta2, 1 - beta2
+    float step_size;     // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+    float eps;
+    float inv_n;         // 1/N, used when N is a power of two (then x*(1/N) == x/N exactly)
+    float n_f;           // N as fp32, the divisor otherwise
+    int32_t n;           // N
+    int32_t n_pow2;
+};
+
+// ---------------------------------------------------------------- device math
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest with ties to even; the carry out of the low
+// half rounds up, overflow reaches the infinity pattern; NaN becomes the quiet
+// NaN 0x7fc0 with the input's sign.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t qnan = ((u >> 16) & 0x8000u) | 0x7fc0u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? qnan : rounded;
+}
+
+// Mean of the slices: the fp32 sum in slice order, then one division by N.
+__device__ __forceinline__ float finish_mean(float s, const StepConsts& c) {
+    if (c.n == 1) return s;
+    return c.n_pow2 ? s * c.inv_n : s / c.n_f;
+}
+
+// Decoupled-weight-decay AdamW on one element, as torch.optim.AdamW does it:
+// decay the old parameter by (1 - lr*wd), update both moments, bias-correct
+// them, and step by lr * mhat / (sqrt(vhat) + eps).
+__device__ __forceinline__ void adamw(float& p, float& m, float& v, float g, const StepConsts& c) {
+    const float p1 = p * c.decay;
+    const float mn = __builtin_fmaf(c.beta1, m, c.omb1 * g);
+    const float gg = g * g;
+    const float vn = __builtin_fmaf(c.beta2, v, c.omb2 * gg);
+    const float den = __builtin_fmaf(sqrtf(vn), c.inv_sqrt_bc2, c.eps);
+    const float pn = __builtin_fmaf(-c.step_size, mn / den, p1);
+    p = pn;
+    m = mn;
+    v = vn;
+}
+
+// Every buffer is device global memory: address it as such so the compiler
+// emits global (not flat) loads and stores.
+template <typename T>
+using global_ptr = __attribute__((address_space(1))) T*;
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) {
+    return __builtin_nontemporal_load((const global_ptr<T>)p);
+}
+template <typename T>
+__device__ __forceinline__ void st_nt(T* p, T x) {
+    __builtin_nontemporal_store(x, (global_ptr<T>)p);
+}
+template <typename T>
+__device__ __forceinline__ T ld(const T* p) { return *(const global_ptr<T>)p; }
+template <typename T>
+__device__ __forceinline__ void st(T* p, T x) { *(global_ptr<T>)p = x; }
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// ---------------------------------------------------------------- 8-element groups
+
+// Raw slice data of one group, loaded before any arithmetic.
+template <int NS, bool BF16>
+struct SliceRegs {
+    static constexpr int kWords = BF16 ? 1 : 2;  // 16-byte vectors per slice
+    u32x4 w[NS > 0 ? NS : 1][kWords];
+};
+
+template <int NS, bool BF16>
+__device__ __forceinline__ void load_slices(SliceRegs<NS, BF16>& r, const void* slices,
+                                            int64_t stride, int64_t e) {
+    static_assert(NS > 0, "compile-time slice count");
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        if constexpr (BF16) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(
+                static_cast<const uint16_t*>(slices) + q * stride + e);
+            r.w[q][0] = ld_nt(p);
+        } else {
+            const u32x4* p = reinterpret_cast<const u32x4*>(
+                static_cast<const float*>(slices) + q * stride + e);
+            r.w[q][0] = ld_nt(p);
+            r.w[q][1] = ld_nt(p + 1);
+        }
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void widen(const u32x4* w, float x[kGroup]) {
+    if constexpr (BF16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf16_lo(w[0][j]);
+            x[2 * j + 1] = bf16_hi(w[0][j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = __uint_as_float(w[0][j]);
+            x[4 + j] = __uint_as_float(w[1][j]);
+        }
+    }
+}
+
+template <int NS, bool BF16>
+__device__ __forceinline__ void reduce_regs(const SliceRegs<NS, BF16>& r, float g[kGroup],
+                                            const StepConsts& c) {
+    widen<BF16>(r.w[0], g);
+#pragma unroll
+    for (int q = 1; q < NS; ++q) {
+        float x[kGroup];
+        widen<BF16>(r.w[q], x);
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) g[j] = g[j] + x[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) g[j] = finish_mean(g[j], c);
+}
+
+// Runtime slice count: load and accumulate slice by slice.
+template <bool BF16>
+__device__ __forceinline__ void reduce_runtime(const void* slices, int64_t stride, int64_t e,
+                                               float g[kGroup], const StepConsts& c) {
+    u32x4 w[2];
+    auto load = [&](int q) {
+        if constexpr (BF16) {
+            w[0] = ld_nt(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(slices) +
+                                                        q * stride + e));
+        } else {
+            const u32x4* p =
+                reinterpret_cast<const u32x4*>(static_cast<const float*>(slices) + q * stride + e);
+            w[0] = ld_nt(p);
+            w[1] = ld_nt(p + 1);
+        }
+    };
+    load(0);
+    widen<BF16>(w, g);
+    for (int q = 1; q < c.n; ++q) {
+        load(q);
+        float x[kGroup];
+        widen<BF16>(w, x);
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) g[j] = g[j] + x[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) g[j] = finish_mean(g[j], c);
+}
+
+struct StateRegs {
+    f32x4 p[2], m[2], v[2];
+};
+
+__device__ __forceinline__ void load_state(StateRegs& s, const TensorDesc& T, int64_t e) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(T.param + e);
+    const f32x4* m = reinterpret_cast<const f32x4*>(T.m + e);
+    const f32x4* v = reinterpret_cast<const f32x4*>(T.v + e);
+    s.p[0] = ld_nt(p);
+    s.p[1] = ld_nt(p + 1);
+    s.m[0] = ld_nt(m);
+    s.m[1] = ld_nt(m + 1);
+    s.v[0] = ld_nt(v);
+    s.v[1] = ld_nt(v + 1);
+}
+
+// AdamW on a group and the stores of its results.
+__device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup],
+                                             const TensorDesc& T, int64_t e, const StepConsts& c) {
+    uint32_t b[kGroup];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float p = s.p[h][j], m = s.m[h][j], v = s.v[h][j];
+            adamw(p, m, v, g[4 * h + j], c);
+            s.p[h][j] = p;
+            s.m[h][j] = m;
+            s.v[h][j] = v;
+            b[4 * h + j] = bf16_rne(p);
+        }
+    }
+    f32x4* p = reinterpret_cast<f32x4*>(T.param + e);
+    f32x4* m = reinterpret_cast<f32x4*>(T.m + e);
+    f32x4* v = reinterpret_cast<f32x4*>(T.v + e);
+    st_nt(p, s.p[0]);
+    st_nt(p + 1, s.p[1]);
+    st_nt(m, s.m[0]);
+    st_nt(m + 1, s.m[1]);
+    st_nt(v, s.v[0]);
+    st_nt(v + 1, s.v[1]);
+    if (T.out_bf16) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = b[2 * j] | (b[2 * j + 1] << 16);
+        st_nt(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
+    }
+    if (T.grad_out) {
+        f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
+        st_nt(go, f32x4{g[0], g[1], g[2], g[3]});
+        st_nt(go + 1, f32x4{g[4], g[5], g[6], g[7]});
+    }
+}
+
+// ---------------------------------------------------------------- single elements
+
+template <bool BF16>
+__device__ __forceinline__ float slice_elem(const void* slices, int64_t i) {
+    if constexpr (BF16) {
+        return __uint_as_float(static_cast<uint32_t>(ld(static_cast<const uint16_t*>(slices) + i)) << 16);
+    } else {
+        return ld(static_cast<const float*>(slices) + i);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float reduce_elem(const TensorDesc& T, int64_t k, const StepConsts& c) {
+    float s = slice_elem<BF16>(T.slices, k);
+    for (int q = 1; q < c.n; ++q) s = s + slice_elem<BF16>(T.slices, q * T.slice_stride + k);
+    return finish_mean(s, c);
+}
+
+// The whole fused step on element k (any alignment); +0 everywhere in the pad.
+template <bool BF16>
+__device__ __forceinline__ void fused_elem(const TensorDesc& T, int64_t k, const StepConsts& c) {
+    if (k < T.valid) {
+        const float g = reduce_elem<BF16>(T, k, c);
+        float p = ld(T.param + k), m = ld(T.m + k), v = ld(T.v + k);
+        adamw(p, m, v, g, c);
+        st(T.param + k, p);
+        st(T.m + k, m);
+        st(T.v + k, v);
+        if (T.out_bf16) st(T.out_bf16 + k, static_cast<uint16_t>(bf16_rne(p)));
+        if (T.grad_out) st(T.grad_out + k, g);
+    } else {
+        st(T.param + k, 0.0f);
+        st(T.m + k, 0.0f);
+        st(T.v + k, 0.0f);
+        if (T.out_bf16) st(T.out_bf16 + k, uint16_t(0));
+        if (T.grad_out) st(T.grad_out + k, 0.0f);
+    }
+}
+
+// ---------------------------------------------------------------- ranges of a shard
+
+// The fused step on elements [begin, end) of shard T.  `begin` is a multiple
+// of kGroup.  Whole groups below `valid` take the vector path; the rest (the
+// partial group at `valid`, the padding, misaligned shards) go element by element.
+template <int NS, bool BF16, int UNROLL>
+__device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, int64_t end,
+                                            const StepConsts& c) {
+    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
+    vend = std::max(vend, begin);
+    const int64_t g1 = vend / kGroup;
+    int64_t g = begin / kGroup + threadIdx.x;
+    if constexpr (NS > 0) {
+        for (; g + (UNROLL - 1) * kBlock < g1; g += UNROLL * kBlock) {
+            SliceRegs<NS, BF16> sr[UNROLL];
+            StateRegs st[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t e = (g + u * kBlock) * kGroup;
+                load_slices<NS, BF16>(sr[u], T.slices, T.slice_stride, e);
+                load_state(st[u], T, e);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                float gr[kGroup];
+                reduce_regs<NS, BF16>(sr[u], gr, c);
+                update_store(st[u], gr, T, (g + u * kBlock) * kGroup, c);
+            }
+        }
+        for (; g < g1; g += kBlock) {
+            SliceRegs<NS, BF16> sr;
+            StateRegs st;
+            const int64_t e = g * kGroup;
+            load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
+            load_state(st, T, e);
+            float gr[kGroup];
+            reduce_regs<NS, BF16>(sr, gr, c);
+            update_store(st, gr, T, e, c);
+        }
+    } else {
+        for (; g < g1; g += kBlock) {
+            const int64_t e = g * kGroup;
+            StateRegs st;
+            load_state(st, T, e);
+            float gr[kGroup];
+            reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
+            update_store(st, gr, T, e, c);
+        }
+    }
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) fused_elem<BF16>(T, k, c);
+}
+
+// Reduce only: grad_out = mean of the slices on [begin, end).
+template <int NS, bool BF16>
+__device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin, int64_t end,
+                                             const StepConsts& c) {
+    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
+    vend = std::max(vend, begin);
+    const int64_t g1 = vend / kGroup;
+    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
+        const int64_t e = g * kGroup;
+        float gr[kGroup];
+        if constexpr (NS > 0) {
+            SliceRegs<NS, BF16> sr;
+            load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
+            reduce_regs<NS, BF16>(sr, gr, c);
+        } else {
+            reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
+        }
+        f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
+        st_nt(go, f32x4{gr[0], gr[1], gr[2], gr[3]});
+        st_nt(go + 1, f32x4{gr[4], gr[5], gr[6], gr[7]});
+    }
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
+        st(T.grad_out + k, k < T.valid ? reduce_elem<BF16>(T, k, c) : 0.0f);
+}
+
+// Cast only: out_bf16 = RNE(param) on [begin, end).
+__device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, int64_t end) {
+    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
+    vend = std::max(vend, begin);
+    const int64_t g1 = vend / kGroup;
+    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
+        const int64_t e = g * kGroup;
+        const f32x4* p = reinterpret_cast<const f32x4*>(T.param + e);
+        const f32x4 a = ld_nt(p), b = ld_nt(p + 1);
+        u32x4 o;
+        o[0] = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
+        o[1] = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
+        o[2] = bf16_rne(b[0]) | (bf16_rne(b[1]) << 16);
+        o[3] = bf16_rne(b[2]) | (bf16_rne(b[3]) << 16);
+        st_nt(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
+    }
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
+        st(T.out_bf16 + k, k < T.valid ? static_cast<uint16_t>(bf16_rne(ld(T.param + k))) : uint16_t(0));
+}
+
+// ---------------------------------------------------------------- kernels
+
+// Multi-tensor fused step.  Workgroup b owns chunk entries
+// [b*cpb, min((b+1)*cpb, n_chunks)); it stages them and the shard descriptors
+// they name in LDS, then runs the chunks in order.
+template <int NS, bool BF16, int UNROLL>
+__global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
+                                                         const ChunkDesc* __restrict__ chunks,
+                                                         int64_t n_chunks, int32_t cpb,
+                                                         StepConsts c) {
+    __shared__ ChunkDesc s_chunk[kChunksPerBlock];
+    __shared__ TensorDesc s_desc[kChunksPerBlock];
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * cpb;
+    const int cnt = static_cast<int>(std::min<int64_t>(cpb, n_chunks - first));
+    if (static_cast<int>(threadIdx.x) < cnt) s_chunk[threadIdx.x] = chunks[first + threadIdx.x];
+    __syncthreads();
+    for (int w = threadIdx.x; w < cnt * kDescWords; w += kBlock) {
+        const int i = w / kDescWords, j = w % kDescWords;
+        reinterpret_cast<uint64_t*>(&s_desc[i])[j] =
+            reinterpret_cast<const uint64_t*>(&tensors[s_chunk[i].tensor])[j];
+    }
+    __syncthreads();
+    for (int i = 0; i < cnt; ++i) {
+        TensorDesc T;
+#pragma unroll
+        for (int j = 0; j < kDescWords; ++j)
+            reinterpret_cast<uint64_t*>(&T)[j] =
+                uniform64(reinterpret_cast<const uint64_t*>(&s_desc[i])[j]);
+        const int64_t begin = static_cast<int64_t>(uniform64(s_chunk[i].begin));
+        const int64_t count = __builtin_amdgcn_readfirstlane(s_chunk[i].count);
+        fused_range<NS, BF16, UNROLL>(T, begin, begin + count, c);
+    }
+}
+
+// Single-shard kernels: workgroup b covers elements [b*chunk, (b+1)*chunk).
+template <int NS, bool BF16, int UNROLL>
+__global__ __launch_bounds__(kBlock) void fused_single_kernel(TensorDesc T, int64_t chunk,
+                                                              StepConsts c) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+    fused_range<NS, BF16, UNROLL>(T, begin, std::min(begin + chunk, T.shard_numel), c);
+}
+
+template <int NS, bool BF16>
+__global__ __launch_bounds__(kBlock) void reduce_single_kernel(TensorDesc T, int64_t chunk,
+                                                               StepConsts c) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+    reduce_range<NS, BF16>(T, begin, std::min(begin + chunk, T.shard_numel), c);
+}
+
+__global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T, int64_t chunk) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+    cast_range(T, begin, std::min(begin + chunk, T.shard_numel));
+}
+
+// ---------------------------------------------------------------- kernel selection
+
+constexpr int kUnroll = 1;
+
+using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts);
+using FusedKernel = void (*)(TensorDesc, int64_t, StepConsts);
+using ReduceKernel = void (*)(TensorDesc, int64_t, StepConsts);
+
+template <bool BF16>
+MtKernel pick_mt(int n) {
+    switch (n) {
+        case 1: return mt_step_kernel<1, BF16, kUnroll>;
+        case 2: return mt_step_kernel<2, BF16, kUnroll>;
+        case 4: return mt_step_kernel<4, BF16, kUnroll>;
+        case 8: return mt_step_kernel<8, BF16, kUnroll>;
+        default: return mt_step_kernel<0, BF16, 1>;
+    }
+}
+
+template <bool BF16>
+ReduceKernel pick_reduce(int n) {
+    switch (n) {
+        case 1: return reduce_single_kernel<1, BF16>;
+        case 2: return reduce_single_kernel<2, BF16>;
+        case 4: return reduce_single_kernel<4, BF16>;
+        case 8: return reduce_single_kernel<8, BF16>;
+        default: return reduce_single_kernel<0, BF16>;
+    }
+}
+
+// ---------------------------------------------------------------- host helpers
+
+int64_t dtype_bytes(int32_t dt) { return dt == FSDP_DT_F32 ? 4 : 2; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t check_hparams(const fsdp_adamw_hparams* hp) {
+    if (!hp) return fail(FSDP_E_ARG, "null hyperparameters");
+    const double xs[5] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+    for (double x : xs)
+        if (!std::isfinite(x)) return fail(FSDP_E_ARG, "hyperparameters must be finite");
+    if (hp->lr < 0) return fail(FSDP_E_ARG, "lr %g < 0", hp->lr);
+    if (hp->beta1 < 0 || hp->beta1 >= 1) return fail(FSDP_E_ARG, "beta1 %g outside [0, 1)", hp->beta1);
+    if (hp->beta2 < 0 || hp->beta2 >= 1) return fail(FSDP_E_ARG, "beta2 %g outside [0, 1)", hp->beta2);
+    if (hp->eps < 0) return fail(FSDP_E_ARG, "eps %g < 0", hp->eps);
+    if (hp->weight_decay < 0) return fail(FSDP_E_ARG, "weight_decay %g < 0", hp->weight_decay);
+    if (hp->step < 1) return fail(FSDP_E_ARG, "step %lld < 1", static_cast<long long>(hp->step));
+    return FSDP_OK;
+}
+
+StepConsts make_consts(const fsdp_adamw_hparams* hp, int32_t n) {
+    StepConsts c{};
+    if (hp) {
+        const double t = static_cast<double>(hp->step);
+        const double bc1 = 1.0 - std::pow(hp->beta1, t);
+        const double bc2 = 1.0 - std::pow(hp->beta2, t);
+        c.decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
+        c.beta1 = static_cast<float>(hp->beta1);
+        c.omb1 = static_cast<float>(1.0 - hp->beta1);
+        c.beta2 = static_cast<float>(hp->beta2);
+        c.omb2 = static_cast<float>(1.0 - hp->beta2);
+        c.step_size = static_cast<float>(hp->lr / bc1);
+        c.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+        c.eps = static_cast<float>(hp->eps);
+    }
+    c.n = n;
+    c.n_pow2 = (n & (n - 1)) == 0;
+    c.inv_n = static_cast<float>(1.0 / n);
+    c.n_f = static_cast<float>(n);
+    return c;
+}
+
+bool vec_ok(const TensorDesc& T, int32_t slice_dtype, int32_t n_slices) {
+    if (!aligned(T.param, 16) || !aligned(T.m, 16) || !aligned(T.v, 16)) return false;
+    if (T.slices && !aligned(T.slices, 16)) return false;
+    if (n_slices > 1 && (T.slice_stride * dtype_bytes(slice_dtype)) % 16 != 0) return false;
+    if (T.out_bf16 && !aligned(T.out_bf16, 16)) return false;
+    if (T.grad_out && !aligned(T.grad_out, 16)) return false;
+    return true;
+}
+
+int64_t single_chunk(int64_t S) {
+    int64_t per = (S + kTargetBlocks - 1) / kTargetBlocks;
+    per = (per + kTile - 1) / kTile * kTile;
+    return std::min(std::max(per, kMinChunk), kMaxChunk);
+}
+
+int64_t blocks_for(int64_t S, int64_t chunk) { return (S + chunk - 1) / chunk; }
+
+constexpr int64_t kMaxGrid = 0x7fffffff;  // workgroups in one launch
+
+int32_t check_grid(int64_t blocks, const char* who) {
+    if (blocks > kMaxGrid)
+        return fail(FSDP_E_CAPACITY, "%s: %lld workgroups exceed one launch", who,
+                    static_cast<long long>(blocks));
+    return FSDP_OK;
+}
+
+int32_t launch_status(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FSDP_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return FSDP_OK;
+}
+
+// Checks shared by the slice-reading calls.
+int32_t check_slices(const void* slices, int32_t slice_dtype, int64_t slice_stride,
+                     int32_t n_slices, int64_t S, int64_t valid, const char* who) {
+    if (slice_dtype != FSDP_DT_F32 && slice_dtype != FSDP_DT_BF16)
+        return fail(FSDP_E_DTYPE, "%s: unknown slice dtype %d", who, slice_dtype);
+    if (n_slices < 1 || n_slices > kMaxSlices)
+        return fail(FSDP_E_ARG, "%s: n_slices %d outside [1, %d]", who, n_slices, kMaxSlices);
+    if (n_slices > 1 && slice_stride < S)
+        return fail(FSDP_E_ARG, "%s: slice_stride %lld < shard_numel %lld", who,
+                    static_cast<long long>(slice_stride), static_cast<long long>(S));
+    if (valid > 0 && !slices) return fail(FSDP_E_ARG, "%s: null grad_slices", who);
+    if (slices && !aligned(slices, dtype_bytes(slice_dtype)))
+        return fail(FSDP_E_ALIGN, "%s: grad_slices not aligned to its element size", who);
+    int64_t span;
+    if (n_slices > 1 && (!fsdp::mul_i64(n_slices - 1, slice_stride, &span) ||
+                         !fsdp::add_i64(span, S, &span) ||
+                         !fsdp::mul_i64(span, dtype_bytes(slice_dtype), &span)))
+        return fail(FSDP_E_ARG, "%s: slice extent overflows int64", who);
+    return FSDP_OK;
+}
+
+int32_t check_sizes(int64_t S, int64_t valid, const char* who) {
+    if (S < 0 || valid < 0 || valid > S)
+        return fail(FSDP_E_ARG, "%s: need 0 <= valid (%lld) <= shard_numel (%lld)", who,
+                    static_cast<long long>(valid), static_cast<long long>(S));
+    if (S > (int64_t(1) << 60)) return fail(FSDP_E_ARG, "%s: shard_numel too large", who);
+    return FSDP_OK;
+}
+
+fsdp::Range range_of(const void* p, int64_t elems, int64_t esize, bool written, int32_t owner,
+                     const char* what) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return fsdp::Range{lo, p ? lo + static_cast<uintptr_t>(elems * esize) : lo, written, owner, what};
+}
+
+void add_slice_ranges(std::vector<fsdp::Range>& rs, const void* slices, int32_t dt,
+                      int64_t stride, int32_t n, int64_t valid, int32_t owner) {
+    if (!slices || valid == 0) return;
+    const int64_t es = dtype_bytes(dt);
+    for (int32_t q = 0; q < n; ++q)
+        rs.push_back(range_of(static_cast<const char*>(slices) + q * stride * es, valid, es, false,
+                              owner, "grad_slices"));
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+struct fsdp_mt_plan {
+    int device = -1;
+    int32_t n_slices = 1;
+    int32_t slice_dtype = FSDP_DT_F32;
+    int32_t cpb = kChunksPerBlock;
+    int64_t n_tensors = 0, n_chunks = 0, n_blocks = 0, total_numel = 0, total_valid = 0;
+    int64_t chunk_numel = 0;
+    TensorDesc* d_tensors = nullptr;
+    ChunkDesc* d_chunks = nullptr;
+};
+
+extern "C" int32_t fsdp_reduce_grad_shard(float* grad_shard_out, const void* grad_slices,
+                                          int32_t slice_dtype, int64_t slice_stride,
+                                          int32_t n_slices, int64_t shard_numel, int64_t valid,
+                                          hipStream_t stream) {
+    const char* who = "fsdp_reduce_grad_shard";
+    int32_t st;
+    if ((st = check_sizes(shard_numel, valid, who)) != FSDP_OK) return st;
+    if ((st = check_slices(grad_slices, slice_dtype, slice_stride, n_slices, shard_numel, valid,
+                           who)) != FSDP_OK)
+        return st;
+    if (shard_numel == 0) return FSDP_OK;
+    if (!grad_shard_out) return fail(FSDP_E_ARG, "%s: null grad_shard_out", who);
+    if (!aligned(grad_shard_out, 4)) return fail(FSDP_E_ALIGN, "%s: grad_shard_out misaligned", who);
+    std::vector<fsdp::Range> rs{range_of(grad_shard_out, shard_numel, 4, true, 0, "grad_shard_out")};
+    add_slice_ranges(rs, grad_slices, slice_dtype, slice_stride, n_slices, valid, 0);
+    if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
+
+    TensorDesc T{};
+    T.slices = grad_slices;
+    T.grad_out = grad_shard_out;
+    T.slice_stride = slice_stride;
+    T.shard_numel = shard_numel;
+    T.valid = valid;
+    T.vec_ok = aligned(grad_shard_out, 16) && (!grad_slices || aligned(grad_slices, 16)) &&
+               (n_slices == 1 || (slice_stride * dtype_bytes(slice_dtype)) % 16 == 0);
+    const StepConsts c = make_consts(nullptr, n_slices);
+    const int64_t chunk = single_chunk(shard_numel);
+    if ((st = check_grid(blocks_for(shard_numel, chunk), who)) != FSDP_OK) return st;
+    const ReduceKernel k = slice_dtype == FSDP_DT_BF16 ? pick_reduce<true>(n_slices)
+                                                       : pick_reduce<false>(n_slices);
+    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(blocks_for(shard_numel, chunk))),
+                       dim3(kBlock), 0, stream, T, chunk, c);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_adamw_shard_step(float* param_fp32, float* exp_avg, float* exp_avg_sq,
+                                         const float* grad_shard, int64_t shard_numel,
+                                         int64_t valid, const fsdp_adamw_hparams* hp,
+                                         hipStream_t stream) {
+    const char* who = "fsdp_adamw_shard_step";
+    int32_t st;
+    if ((st = check_sizes(shard_numel, valid, who)) != FSDP_OK) return st;
+    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    if (shard_numel == 0) return FSDP_OK;
+    if (!param_fp32 || !exp_avg || !exp_avg_sq)
+        return fail(FSDP_E_ARG, "%s: null param / exp_avg / exp_avg_sq", who);
+    if (valid > 0 && !grad_shard) return fail(FSDP_E_ARG, "%s: null grad_shard", who);
+    if (!aligned(param_fp32, 4) || !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) ||
+        !aligned(grad_shard, 4))
+        return fail(FSDP_E_ALIGN, "%s: fp32 buffer not 4-byte aligned", who);
+    std::vector<fsdp::Range> rs{range_of(param_fp32, shard_numel, 4, true, 0, "param"),
+                                range_of(exp_avg, shard_numel, 4, true, 0, "exp_avg"),
+                                range_of(exp_avg_sq, shard_numel, 4, true, 0, "exp_avg_sq")};
+    add_slice_ranges(rs, grad_shard, FSDP_DT_F32, shard_numel, 1, valid, 0);
+    if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
+
+    TensorDesc T{};
+    T.param = param_fp32;
+    T.m = exp_avg;
+    T.v = exp_avg_sq;
+    T.slices = grad_shard;
+    T.slice_stride = shard_numel;
+    T.shard_numel = shard_numel;
+    T.valid = valid;
+    T.vec_ok = vec_ok(T, FSDP_DT_F32, 1);
+    const StepConsts c = make_consts(hp, 1);
+    const int64_t chunk = single_chunk(shard_numel);
+    if ((st = check_grid(blocks_for(shard_numel, chunk), who)) != FSDP_OK) return st;
+    hipLaunchKernelGGL((fused_single_kernel<1, false, kUnroll>),
+                       dim3(static_cast<uint32_t>(blocks_for(shard_numel, chunk))), dim3(kBlock), 0,
+                       stream, T, chunk, c);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const float* param_fp32,
+                                          int64_t shard_numel, int64_t valid, hipStream_t stream) {
+    const char* who = "fsdp_cast_unshard_bf16";
+    int32_t st;
+    if ((st = check_sizes(shard_numel, valid, who)) != FSDP_OK) return st;
+    if (shard_numel == 0) return FSDP_OK;
+    if (!unshard_bf16_out) return fail(FSDP_E_ARG, "%s: null unshard_bf16_out", who);
+    if (valid > 0 && !param_fp32) return fail(FSDP_E_ARG, "%s: null param_fp32", who);
+    if (!aligned(unshard_bf16_out, 2) || !aligned(param_fp32, 4))
+        return fail(FSDP_E_ALIGN, "%s: buffer not aligned to its element size", who);
+    std::vector<fsdp::Range> rs{range_of(unshard_bf16_out, shard_numel, 2, true, 0, "unshard_bf16_out")};
+    if (valid > 0) rs.push_back(range_of(param_fp32, valid, 4, false, 0, "param"));
+    if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
+
+    TensorDesc T{};
+    T.param = const_cast<float*>(param_fp32);
+    T.out_bf16 = unshard_bf16_out;
+    T.shard_numel = shard_numel;
+    T.valid = valid;
+    T.vec_ok = aligned(unshard_bf16_out, 16) && aligned(param_fp32, 16);
+    const int64_t chunk = single_chunk(shard_numel);
+    if ((st = check_grid(blocks_for(shard_numel, chunk), who)) != FSDP_OK) return st;
+    hipLaunchKernelGGL(cast_single_kernel, dim3(static_cast<uint32_t>(blocks_for(shard_numel, chunk))),
+                       dim3(kBlock), 0, stream, T, chunk);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tensors,
+                                       int32_t n_tensors, int32_t n_slices, int32_t slice_dtype,
+                                       hipStream_t stream) {
+    const char* who = "fsdp_mt_plan_create";
+    if (!plan_out) return fail(FSDP_E_ARG, "%s: null plan_out", who);
+    *plan_out = nullptr;
+    if (n_tensors < 0) return fail(FSDP_E_ARG, "%s: n_tensors %d < 0", who, n_tensors);
+    if (n_tensors > 0 && !tensors) return fail(FSDP_E_ARG, "%s: null tensors", who);
+    if (slice_dtype != FSDP_DT_F32 && slice_dtype != FSDP_DT_BF16)
+        return fail(FSDP_E_DTYPE, "%s: unknown slice dtype %d", who, slice_dtype);
+    if (n_slices < 1 || n_slices > kMaxSlices)
+        return fail(FSDP_E_ARG, "%s: n_slices %d outside [1, %d]", who, n_slices, kMaxSlices);
+
+    std::vector<TensorDesc> descs;
+    descs.reserve(static_cast<size_t>(n_tensors));
+    std::vector<fsdp::Range> rs;
+    int64_t total = 0, total_valid = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        const fsdp_mt_tensor& t = tensors[i];
+        char tag[64];
+        snprintf(tag, sizeof tag, "%s: shard %d", who, i);
+        int32_t st;
+        if ((st = check_sizes(t.shard_numel, t.valid, tag)) != FSDP_OK) return st;
+        if ((st = check_slices(t.grad_slices, slice_dtype, t.slice_stride, n_slices, t.shard_numel,
+                               t.valid, tag)) != FSDP_OK)
+            return st;
+        if (t.shard_numel > 0 && (!t.param_fp32 || !t.exp_avg || !t.exp_avg_sq))
+            return fail(FSDP_E_ARG, "%s: null param / exp_avg / exp_avg_sq", tag);
+        if (!aligned(t.param_fp32, 4) || !aligned(t.exp_avg, 4) || !aligned(t.exp_avg_sq, 4) ||
+            !aligned(t.grad_shard_out, 4) || !aligned(t.unshard_bf16_out, 2))
+            return fail(FSDP_E_ALIGN, "%s: buffer not aligned to its element size", tag);
+        if (!fsdp::add_i64(total, t.shard_numel, &total))
+            return fail(FSDP_E_ARG, "%s: total size overflows", who);
+        total_valid += t.valid;
+        if (t.shard_numel == 0) continue;
+        rs.push_back(range_of(t.param_fp32, t.shard_numel, 4, true, i, "param"));
+        rs.push_back(range_of(t.exp_avg, t.shard_numel, 4, true, i, "exp_avg"));
+        rs.push_back(range_of(t.exp_avg_sq, t.shard_numel, 4, true, i, "exp_avg_sq"));
+        if (t.unshard_bf16_out)
+            rs.push_back(range_of(t.unshard_bf16_out, t.shard_numel, 2, true, i, "unshard_bf16_out"));
+        if (t.grad_shard_out)
+            rs.push_back(range_of(t.grad_shard_out, t.shard_numel, 4, true, i, "grad_shard_out"));
+        add_slice_ranges(rs, t.grad_slices, slice_dtype, t.slice_stride, n_slices, t.valid, i);
+        TensorDesc d{};
+        d.param = t.param_fp32;
+        d.m = t.exp_avg;
+        d.v = t.exp_avg_sq;
+        d.slices = t.grad_slices;
+        d.out_bf16 = t.unshard_bf16_out;
+        d.grad_out = t.grad_shard_out;
+        d.slice_stride = t.slice_stride;
+        d.shard_numel = t.shard_numel;
+        d.valid = t.valid;
+        d.vec_ok = vec_ok(d, slice_dtype, n_slices);
+        descs.push_back(d);
+    }
+    {
+        const int32_t st = fsdp::check_aliases(rs);
+        if (st != FSDP_OK) return st;
+    }
+
+    // Chunk size: enough workgroups to fill the chip, chunks a whole number of
+    // workgroup tiles so every chunk but a shard's last starts group-aligned.
+    int64_t chunk = (total + kTargetBlocks * kChunksPerBlock - 1) / (kTargetBlocks * kChunksPerBlock);
+    chunk = (chunk + kTile - 1) / kTile * kTile;
+    chunk = std::min(std::max(chunk, kMinChunk), kMaxChunk);
+    std::vector<ChunkDesc> chunks;
+    for (size_t i = 0; i < descs.size(); ++i) {
+        for (int64_t b = 0; b < descs[i].shard_numel; b += chunk) {
+            ChunkDesc cd{};
+            cd.begin = b;
+            cd.tensor = static_cast<int32_t>(i);
+            cd.count = static_cast<int32_t>(std::min(chunk, descs[i].shard_numel - b));
+            chunks.push_back(cd);
+        }
+    }
+
+    {
+        const int64_t blocks = (static_cast<int64_t>(chunks.size()) + kChunksPerBlock - 1) / kChunksPerBlock;
+        const int32_t st = check_grid(blocks, who);
+        if (st != FSDP_OK) return st;
+    }
+    fsdp_mt_plan* plan = new (std::nothrow) fsdp_mt_plan();
+    if (!plan) return fail(FSDP_E_ARG, "%s: out of host memory", who);
+    plan->n_slices = n_slices;
+    plan->slice_dtype = slice_dtype;
+    plan->n_tensors = n_tensors;
+    plan->n_chunks = static_cast<int64_t>(chunks.size());
+    plan->n_blocks = (plan->n_chunks + plan->cpb - 1) / plan->cpb;
+    plan->total_numel = total;
+    plan->total_valid = total_valid;
+    plan->chunk_numel = chunk;
+    hipError_t e = hipGetDevice(&plan->device);
+    if (e == hipSuccess && !chunks.empty()) {
+        e = hipMalloc(reinterpret_cast<void**>(&plan->d_tensors), descs.size() * sizeof(TensorDesc));
+        if (e == hipSuccess)
+            e = hipMalloc(reinterpret_cast<void**>(&plan->d_chunks), chunks.size() * sizeof(ChunkDesc));
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(plan->d_tensors, descs.data(), descs.size() * sizeof(TensorDesc),
+                               hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(plan->d_chunks, chunks.data(), chunks.size() * sizeof(ChunkDesc),
+                               hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    }
+    if (e != hipSuccess) {
+        fsdp_mt_plan_destroy(plan);
+        return fail(FSDP_E_HIP, "%s: %s", who, hipGetErrorString(e));
+    }
+    *plan_out = plan;
+    return FSDP_OK;
+}
+
+extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                hipStream_t stream) {
+    const char* who = "fsdp_mt_step";
+    if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
+    int32_t st;
+    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FSDP_E_HIP, "%s: %s", who, hipGetErrorString(e));
+    if (dev != plan->device)
+        return fail(FSDP_E_STATE, "%s: plan made on device %d used on device %d", who, plan->device,
+                    dev);
+    if (plan->n_chunks == 0) return FSDP_OK;
+    const StepConsts c = make_consts(hp, plan->n_slices);
+    const MtKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_mt<true>(plan->n_slices)
+                                                         : pick_mt<false>(plan->n_slices);
+    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), 0, stream,
+                       plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb, c);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info) {
+    if (!plan || !info) return fail(FSDP_E_ARG, "fsdp_mt_plan_get_info: null argument");
+    info->n_tensors = plan->n_tensors;
+    info->n_chunks = plan->n_chunks;
+    info->n_blocks = plan->n_blocks;
+    info->total_numel = plan->total_numel;
+    info->total_valid = plan->total_valid;
+    info->chunk_numel = plan->chunk_numel;
+    info->n_slices = plan->n_slices;
+    info->slice_dtype = plan->slice_dtype;
+    return FSDP_OK;
+}
+
+extern "C" int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan) {
+    if (!plan) return FSDP_OK;
+    hipError_t e = hipSuccess;
+    if (plan->d_tensors || plan->d_chunks) {
+        e = hipDeviceSynchronize();
+        if (plan->d_tensors) (void)hipFree(plan->d_tensors);
+        if (plan->d_chunks) (void)hipFree(plan->d_chunks);
+    }
+    delete plan;
+    if (e != hipSuccess) return fail(FSDP_E_HIP, "fsdp_mt_plan_destroy: %s", hipGetErrorString(e));
+    return FSDP_OK;
+}

@@ -1,0 +1,100 @@
+"""One rank's optimizer state of a workload, resident in HBM, and its plan.
+
+Sizes come from the library's own ``fsdp_shard_layout``; torch only allocates
+the buffers.  Layout of the buffers (all on one device):
+
+* ``master``, ``exp_avg``, ``exp_avg_sq``: fp32 ``[S_total]``, the rank's
+  local shards of every parameter packed in registration order (FLAT: the one
+  flat shard), each shard at its ``view_offset``;
+* ``slices``: ``[N, S_total]`` in the slice dtype -- slice q is the q-th
+  incoming gradient buffer of this rank's shard, i.e. the rank's chunk of rank
+  q's full gradient -- so the slice stride of every shard is ``S_total``;
+* ``ag``: bf16 all-gather input.  With ``ag_full`` it is the packed
+  ``[N * S_total]`` buffer of the next all-gather and this rank writes the
+  slot at ``rank * S_total``; otherwise only this rank's slot is allocated.
+"""
+
+import torch
+
+from . import binding
+from .workloads import grad_slices, init_master, init_seed, shapes_of
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class RankState:
+    def __init__(self, w, rank, device, bf16_out=True, grad_out=False, ag_full=False,
+                 garbage_pad=False):
+        self.w = w
+        self.rank = rank
+        self.device = device
+        views, summ = binding.fsdp_shard_layout(w.mode, w.world_size, rank, shapes_of(w),
+                                                w.has_master)
+        self.views = views
+        self.summary = summ
+        total = summ["shard_numel"]
+        self.total = total
+        if w.mode == "flat":
+            # one flat shard; is_norm does not apply to a flat unit
+            segs = [(0, total, views[0]["valid"] if views else 0, False)] if total else []
+        else:
+            segs = [(v["view_offset"], v["shard_numel"], v["valid"], p.is_norm)
+                    for v, p in zip(views, w.params) if v["shard_numel"] > 0]
+        self.segments = segs
+        f32 = dict(dtype=torch.float32, device=device)
+        self.master = init_master(total, segs, init_seed(w.cfg, rank), device,
+                                  garbage_pad=garbage_pad)
+        self.exp_avg = torch.zeros(total, **f32)
+        self.exp_avg_sq = torch.zeros(total, **f32)
+        if garbage_pad:
+            for off, length, held, _ in segs:
+                self.exp_avg[off + held:off + length] = float("nan")
+                self.exp_avg_sq[off + held:off + length] = float("inf")
+        self.slices = torch.empty((w.n_slices, total), dtype=_DT[w.slice_dtype], device=device)
+        self.ag = None
+        self.ag_slot = None
+        if bf16_out:
+            n_ag = total * w.world_size if ag_full else total
+            self.ag = torch.zeros(n_ag, dtype=torch.bfloat16, device=device)
+            self.ag_slot = self.ag[rank * total:(rank + 1) * total] if ag_full else self.ag
+        self.grad_out = torch.empty(total, **f32) if grad_out else None
+        self.plan = None
+
+    def load_grads(self, step):
+        """Fill the slice buffer with step ``step``'s seeded gradients."""
+        grad_slices(self.w, self.total, step, self.rank, self.device, out=self.slices)
+
+    def mt_tensors(self):
+        es = self.slices.element_size()
+        base = {
+            "param": self.master.data_ptr(), "m": self.exp_avg.data_ptr(),
+            "v": self.exp_avg_sq.data_ptr(), "s": self.slices.data_ptr(),
+            "ag": self.ag_slot.data_ptr() if self.ag_slot is not None else None,
+            "g": self.grad_out.data_ptr() if self.grad_out is not None else None,
+        }
+        out = []
+        for off, length, held, _ in self.segments:
+            out.append({
+                "param_fp32": base["param"] + 4 * off,
+                "exp_avg": base["m"] + 4 * off,
+                "exp_avg_sq": base["v"] + 4 * off,
+                "grad_slices": base["s"] + es * off,
+                "slice_stride": self.total,
+                "unshard_bf16_out": None if base["ag"] is None else base["ag"] + 2 * off,
+                "grad_shard_out": None if base["g"] is None else base["g"] + 4 * off,
+                "shard_numel": length,
+                "valid": held,
+            })
+        return out
+
+    def make_plan(self, stream=None):
+        self.plan = binding.MtPlan(self.mt_tensors(), self.w.n_slices, self.w.slice_dtype, stream)
+        return self.plan
+
+    def step(self, t, stream=None):
+        self.plan.step(self.w.hparams, t, stream)
+
+    def close(self):
+        if self.plan is not None:
+            self.plan.close()
+            self.plan = None

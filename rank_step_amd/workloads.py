@@ -161,28 +161,34 @@ def init_master(total, segments, seed, device, garbage_pad=False):
     return x
 
 
-def grad_slices(w, total, step, rank, device, n_slices=None, stride=None):
+def grad_slices(w, total, step, rank, device, n_slices=None, stride=None, out=None):
     """Gradient slices of one rank: a ``[n_slices, stride]`` tensor in the
     workload's slice dtype, of which the first ``total`` columns are drawn.
 
-    Columns beyond ``total`` (a wider stride) hold NaN garbage that the step
-    must never read.  Pad positions inside ``total`` hold random values that
-    the step must ignore as well.
+    ``out`` (optional) is filled in place instead of allocating.  Columns
+    beyond ``total`` (a wider stride) hold NaN garbage that the step must
+    never read; pad positions inside ``total`` hold random values that the
+    step must ignore as well.
     """
     n = w.n_slices if n_slices is None else n_slices
     stride = total if stride is None else stride
     dt = torch.float32 if w.slice_dtype == "f32" else torch.bfloat16
-    out = torch.full((n, stride), float("nan"), dtype=dt, device=device)
+    if out is None:
+        out = torch.full((n, stride), float("nan"), dtype=dt, device=device)
+    else:
+        assert out.shape[0] == n and out.shape[1] >= total and out.dtype == dt
     for q in range(n):
         s = slice_seed(w.cfg, step, rank, q)
         x = torch.randn(total, generator=_gen(device, s), device=device,
-                        dtype=torch.float32) * w.grad_sigma
+                        dtype=torch.float32)
+        x.mul_(w.grad_sigma)
         if w.zero_frac > 0.0 or w.outlier_frac > 0.0:
             u = torch.rand(total, generator=_gen(device, s + 50), device=device)
             if w.zero_frac > 0.0:
-                x = torch.where(u < w.zero_frac, torch.zeros_like(x), x)
+                x.masked_fill_(u < w.zero_frac, 0.0)
             if w.outlier_frac > 0.0:
                 x = torch.where(u < w.outlier_frac, x * w.outlier_scale, x)
-        out[q, :total] = x.to(dt)
+            del u
+        out[q, :total].copy_(x)
         del x
     return out

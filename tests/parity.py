@@ -1,0 +1,104 @@
+"""Comparison helpers for the GPU parity tests (test-side only).
+
+The fp32 criterion is the mixed one: for each fp32 output x,
+
+    |x_gpu - x_ref| <= TOL * max(|x_ref|, s_x)
+
+where s_x is the magnitude of the terms that form x, so that cancellation
+(a result much smaller than its terms) is judged against the terms' size:
+
+    s_G = mean_q |x_q|                               reduced gradient
+    s_m = beta1*|m| + (1-beta1)*s_G                  first moment
+    s_v = beta2*v + (1-beta2)*s_G^2                  second moment
+    s_p = |p|*(1-lr*wd) + lr*(s_m/bc1)/(sqrt(vhat)+eps)   parameter
+
+The inputs of the oracle are the GPU's own state before the step, widened
+exactly (per-step resynchronisation), so one step's rounding is judged.
+bf16: bit-exact to RNE of the GPU's own fp32 result, and within 1 ulp of RNE
+of the oracle's result wherever the fp32 error allowance is below half a bf16
+ulp of the value.
+"""
+
+import numpy as np
+import torch
+
+from oracle import step as O
+
+TOL = 2e-6
+
+
+def f64(t):
+    return t.detach().to("cpu").numpy().astype(np.float64)
+
+
+def bf16_bits(t):
+    return t.detach().to("cpu").view(torch.int16).numpy().view(np.uint16)
+
+
+def widen_slices(t, dtype):
+    """[N, n] device slices -> float64 host array, exactly."""
+    if dtype == "bf16":
+        return O.widen_bf16_bits(bf16_bits(t))
+    return t.detach().to("cpu").numpy().astype(np.float64)
+
+
+def floors(p, m, v, sl, ref, hp, t):
+    lr, b1, b2, eps, wd = hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"]
+    sG = np.mean(np.abs(sl), axis=0) if sl.shape[0] else np.zeros(0)
+    s_m = b1 * np.abs(m) + (1 - b1) * sG
+    s_v = b2 * v + (1 - b2) * sG * sG
+    bc1 = 1 - b1 ** t
+    bc2 = 1 - b2 ** t
+    vhat = ref["v"] / bc2
+    s_p = np.abs(p) * (1 - lr * wd) + lr * (s_m / bc1) / (np.sqrt(vhat) + eps)
+    return {"g": sG, "m": s_m, "v": s_v, "p": s_p}
+
+
+def assert_close(name, got, ref, floor, tol=TOL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bad_nan = np.isnan(got) != np.isnan(ref)
+    assert not bad_nan.any(), f"{name}: NaN mismatch at {np.flatnonzero(bad_nan)[:5]}"
+    ok = ~np.isnan(ref)
+    err = np.abs(got[ok] - ref[ok])
+    lim = tol * np.maximum(np.abs(ref[ok]), floor[ok])
+    bad = err > lim
+    if bad.any():
+        i = np.flatnonzero(ok)[np.flatnonzero(bad)[:5]]
+        raise AssertionError(f"{name}: {bad.sum()} of {ok.sum()} elements beyond tolerance; "
+                             f"first at {i.tolist()}: got {got[i].tolist()} ref {ref[i].tolist()} "
+                             f"floor {floor[i].tolist()}")
+    # plain relative error where the result is not a cancellation
+    big = np.abs(ref[ok]) >= 1e-3 * floor[ok]
+    rel = err[big] / np.maximum(np.abs(ref[ok][big]), 1e-300)
+    return float(rel.max()) if rel.size else 0.0
+
+
+def check_bf16(name, got_bits, gpu_p, ref_p, floor_p, tol=TOL):
+    """bf16 output: exact RNE of the GPU's fp32 value; <= 1 ulp from RNE(oracle)."""
+    own = O.bf16_rne(np.asarray(gpu_p, dtype=np.float64))
+    mism = got_bits != own
+    assert not mism.any(), (f"{name}: bf16 differs from RNE of its own fp32 at "
+                            f"{np.flatnonzero(mism)[:5].tolist()}")
+    ref_bits = O.bf16_rne(np.asarray(ref_p, dtype=np.float64))
+    fin = ~np.isnan(np.asarray(ref_p))
+    a = got_bits.astype(np.int32)
+    b = ref_bits.astype(np.int32)
+    # signed-magnitude -> monotone integers
+    a = np.where(a & 0x8000, -(a & 0x7FFF), a)
+    b = np.where(b & 0x8000, -(b & 0x7FFF), b)
+    half_ulp = np.abs(np.asarray(ref_p, dtype=np.float64)) * 2.0 ** -9
+    judged = fin & (tol * np.maximum(np.abs(ref_p), floor_p) < half_ulp)
+    far = judged & (np.abs(a - b) > 1)
+    assert not far.any(), f"{name}: bf16 more than 1 ulp from RNE(oracle) at {np.flatnonzero(far)[:5]}"
+    return int((a != b).sum())
+
+
+def check_pad_zero(name, arr, valid):
+    a = np.asarray(arr)
+    tail = a[valid:]
+    if tail.dtype == np.uint16:
+        assert np.all(tail == 0), f"{name}: pad not zero"
+    else:
+        assert np.all(tail.view(np.uint32 if tail.dtype == np.float32 else np.uint64) == 0), \
+            f"{name}: pad not +0"

@@ -1,0 +1,259 @@
+"""GPU parity of each entry point against the oracle, on small ragged shards.
+
+Every call goes through the C ABI (rank_step_amd.binding).  Sizes span
+several 2048-element workgroup tiles and a ragged tail; the cases cover empty
+shards, all-padding shards (valid = 0), partial groups, misaligned buffers
+(element-by-element path), slice strides wider than the shard, N that is not
+a power of two, NaN/Inf inputs, guard words around every buffer, and the
+bit-identity of the fused multi-tensor step with the chain of three calls.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import step as O
+from rank_step_amd import binding as B
+from rank_step_amd.workloads import HPARAMS
+from tests import parity as PR
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(HPARAMS)
+GUARD = 64
+CANARY_F32 = -7.0e33
+
+
+class Buf:
+    """A device buffer with guard words on both sides; ``t`` is the payload view.
+
+    ``offset`` shifts the payload by whole elements (1 breaks 16-byte alignment).
+    """
+
+    def __init__(self, n, dtype, device, fill=float("nan"), offset=0):
+        self.n = n
+        self.offset = offset
+        self.full = torch.empty(n + 2 * GUARD + offset, dtype=dtype, device=device)
+        self.full.fill_(CANARY_F32 if dtype == torch.float32 else 1.5)
+        self.t = self.full[GUARD + offset:GUARD + offset + n]
+        self.t.fill_(fill)
+        self._canary = None
+
+    def seal(self):
+        self._canary = torch.cat([self.full[:GUARD + self.offset], self.full[GUARD + self.offset + self.n:]]).clone()
+
+    def check_guards(self, name):
+        now = torch.cat([self.full[:GUARD + self.offset], self.full[GUARD + self.offset + self.n:]])
+        assert torch.equal(now.view(torch.int16 if now.dtype == torch.bfloat16 else torch.int32),
+                           self._canary.view(torch.int16 if now.dtype == torch.bfloat16 else torch.int32)), \
+            f"{name}: guard words overwritten"
+
+
+class Shard:
+    def __init__(self, S, valid, N, sdt, device, seed, offset=0, stride_extra=0, bf16=True,
+                 gout=True):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        f32 = torch.float32
+        self.S, self.valid, self.N, self.sdt = S, valid, N, sdt
+        self.p = Buf(S, f32, device, fill=1.0e30, offset=offset)
+        self.m = Buf(S, f32, device, fill=float("nan"), offset=offset)
+        self.v = Buf(S, f32, device, fill=float("inf"), offset=offset)
+        if valid:
+            self.p.t[:valid] = torch.randn(valid, generator=g, device=device) * 0.02
+            self.m.t[:valid] = torch.randn(valid, generator=g, device=device) * 1e-3
+            self.v.t[:valid] = torch.randn(valid, generator=g, device=device).square() * 1e-6
+        self.stride = S + stride_extra
+        sd = torch.float32 if sdt == "f32" else torch.bfloat16
+        self.sl = Buf(N * self.stride, sd, device, fill=float("nan"), offset=offset)
+        x = torch.randn(N, S, generator=g, device=device) * 1e-2
+        self.sl.t.view(N, self.stride)[:, :S] = x.to(sd)
+        if valid < S:
+            self.sl.t.view(N, self.stride)[:, valid:S] = float("nan")   # pad garbage
+        self.out = Buf(S, torch.bfloat16, device, fill=1.5, offset=offset) if bf16 else None
+        self.gout = Buf(S, f32, device, fill=float("nan"), offset=offset) if gout else None
+        for b in self.bufs():
+            b.seal()
+
+    def bufs(self):
+        return [b for b in (self.p, self.m, self.v, self.sl, self.out, self.gout) if b is not None]
+
+    def snapshot(self):
+        return (PR.f64(self.p.t), PR.f64(self.m.t), PR.f64(self.v.t),
+                PR.widen_slices(self.sl.t.view(self.N, self.stride)[:, :self.S], self.sdt))
+
+    def mt(self):
+        return {"param_fp32": self.p.t, "exp_avg": self.m.t, "exp_avg_sq": self.v.t,
+                "grad_slices": self.sl.t, "slice_stride": self.stride,
+                "unshard_bf16_out": self.out.t if self.out else None,
+                "grad_shard_out": self.gout.t if self.gout else None,
+                "shard_numel": self.S, "valid": self.valid}
+
+    def check(self, name, snap, t, check_g=True):
+        p0, m0, v0, sl = snap
+        ref = O.rank_step(p0, m0, v0, sl, self.valid, t, HP)
+        va = self.valid
+        fl = PR.floors(p0[:va], m0[:va], v0[:va], sl[:, :va], {k: r[:va] for k, r in ref.items()}, HP, t)
+        gp = self.p.t.cpu().numpy()
+        PR.assert_close(f"{name} p", gp[:va], ref["p"][:va], fl["p"])
+        PR.assert_close(f"{name} m", self.m.t.cpu().numpy()[:va], ref["m"][:va], fl["m"])
+        PR.assert_close(f"{name} v", self.v.t.cpu().numpy()[:va], ref["v"][:va], fl["v"])
+        for b, nm in ((self.p, "p"), (self.m, "m"), (self.v, "v")):
+            PR.check_pad_zero(f"{name} {nm}", b.t.cpu().numpy(), va)
+        if self.out is not None:
+            bits = PR.bf16_bits(self.out.t)
+            PR.check_bf16(f"{name} bf16", bits[:va], gp[:va], ref["p"][:va], fl["p"])
+            PR.check_pad_zero(f"{name} bf16", bits, va)
+        if self.gout is not None and check_g:
+            gg = self.gout.t.cpu().numpy()
+            PR.assert_close(f"{name} g", gg[:va], ref["g"][:va], fl["g"])
+            PR.check_pad_zero(f"{name} g", gg, va)
+        for b in self.bufs():
+            b.check_guards(name)
+
+
+SPECS = [  # (S, valid, offset, stride_extra)
+    (0, 0, 0, 0),
+    (1, 1, 0, 0),
+    (7, 0, 0, 0),
+    (8, 8, 0, 0),
+    (2048 * 5 + 1237, 2048 * 5 + 1230, 0, 0),     # several tiles + ragged tail, partial pad
+    (16384, 16384, 0, 40),                         # wider slice stride
+    (9001, 8999, 1, 0),                            # misaligned: element path
+    (4096, 3, 0, 0),                               # nearly all padding
+    (70001, 70001, 0, 0),
+]
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 8, 16])
+def test_mt_step_parity(gpu, N, sdt):
+    shards = [Shard(S, va, N, sdt, gpu, seed=100 * N + i, offset=o, stride_extra=x,
+                    bf16=(i % 3 != 1), gout=(i % 2 == 0))
+              for i, (S, va, o, x) in enumerate(SPECS)]
+    plan = B.MtPlan([s.mt() for s in shards], N, sdt)
+    info = plan.info()
+    assert info["n_tensors"] == len(SPECS) and info["total_numel"] == sum(s[0] for s in SPECS)
+    for t in (1, 2, 3):
+        # fresh gradients each step; the state carries over (per-step resync)
+        for i, s in enumerate(shards):
+            g = torch.Generator(device=gpu)
+            g.manual_seed(7 * t + i)
+            x = torch.randn(N, s.S, generator=g, device=gpu) * 1e-2
+            s.sl.t.view(N, s.stride)[:, :s.valid] = x[:, :s.valid].to(s.sl.t.dtype)
+        snaps = [s.snapshot() for s in shards]
+        plan.step(HP, t)
+        torch.cuda.synchronize()
+        for i, (s, snap) in enumerate(zip(shards, snaps)):
+            s.check(f"N={N} {sdt} shard {i} t={t}", snap, t)
+    plan.close()
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 3, 4, 8])
+def test_single_calls_parity(gpu, N, sdt):
+    for i, (S, va, o, x) in enumerate(SPECS):
+        s = Shard(S, va, N, sdt, gpu, seed=1000 + i, offset=o, stride_extra=x)
+        snap = s.snapshot()
+        B.fsdp_reduce_grad_shard(s.gout.t, s.sl.t, sdt, s.stride, N, S, va)
+        B.fsdp_adamw_shard_step(s.p.t, s.m.t, s.v.t, s.gout.t, S, va, HP, 1)
+        B.fsdp_cast_unshard_bf16(s.out.t, s.p.t, S, va)
+        torch.cuda.synchronize()
+        s.check(f"single N={N} {sdt} case {i}", snap, 1)
+
+
+@pytest.mark.parametrize("sdt,N", [("bf16", 8), ("f32", 4), ("f32", 3), ("bf16", 1)])
+def test_fused_equals_chain_bitwise(gpu, sdt, N):
+    a = [Shard(S, va, N, sdt, gpu, seed=5000 + i, offset=o, stride_extra=x)
+         for i, (S, va, o, x) in enumerate(SPECS)]
+    b = [Shard(S, va, N, sdt, gpu, seed=5000 + i, offset=o, stride_extra=x)
+         for i, (S, va, o, x) in enumerate(SPECS)]
+    plan = B.MtPlan([s.mt() for s in a], N, sdt)
+    for t in (1, 2):
+        plan.step(HP, t)
+        for s in b:
+            B.fsdp_reduce_grad_shard(s.gout.t, s.sl.t, sdt, s.stride, N, s.S, s.valid)
+            B.fsdp_adamw_shard_step(s.p.t, s.m.t, s.v.t, s.gout.t, s.S, s.valid, HP, t)
+            B.fsdp_cast_unshard_bf16(s.out.t, s.p.t, s.S, s.valid)
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(a, b)):
+            for nm in ("p", "m", "v", "gout"):
+                bx, by = getattr(x, nm).t, getattr(y, nm).t
+                assert torch.equal(bx.view(torch.int32), by.view(torch.int32)), (i, nm, t)
+            assert torch.equal(x.out.t.view(torch.int16), y.out.t.view(torch.int16)), (i, t)
+    plan.close()
+
+
+def test_deterministic_and_resumable(gpu):
+    N, sdt = 8, "bf16"
+    runs = []
+    for _ in range(2):
+        s = [Shard(S, va, N, sdt, gpu, seed=77 + i, offset=o, stride_extra=x)
+             for i, (S, va, o, x) in enumerate(SPECS)]
+        plan = B.MtPlan([x.mt() for x in s], N, sdt)
+        for t in (1, 2, 3):
+            plan.step(HP, t)
+        torch.cuda.synchronize()
+        runs.append([(x.p.t.clone(), x.m.t.clone(), x.v.t.clone(), x.out.t.clone()) for x in s])
+        plan.close()
+    for ra, rb in zip(*runs):
+        for ta, tb in zip(ra, rb):
+            assert torch.equal(ta.view(torch.int16), tb.view(torch.int16))
+    # checkpoint after step 1, reload into fresh buffers, continue: identical to uninterrupted
+    s = [Shard(S, va, N, sdt, gpu, seed=77 + i, offset=o, stride_extra=x)
+         for i, (S, va, o, x) in enumerate(SPECS)]
+    plan = B.MtPlan([x.mt() for x in s], N, sdt)
+    plan.step(HP, 1)
+    torch.cuda.synchronize()
+    ckpt = [(x.p.t.clone(), x.m.t.clone(), x.v.t.clone()) for x in s]
+    plan.close()
+    r = [Shard(S, va, N, sdt, gpu, seed=77 + i, offset=o, stride_extra=x)
+         for i, (S, va, o, x) in enumerate(SPECS)]
+    for x, (p, m, v) in zip(r, ckpt):
+        x.p.t.copy_(p), x.m.t.copy_(m), x.v.t.copy_(v)
+    plan = B.MtPlan([x.mt() for x in r], N, sdt)
+    plan.step(HP, 2)
+    plan.step(HP, 3)
+    torch.cuda.synchronize()
+    for x, (p, m, v, o) in zip(r, runs[0]):
+        for ta, tb in ((x.p.t, p), (x.m.t, m), (x.v.t, v), (x.out.t, o)):
+            assert torch.equal(ta.view(torch.int16), tb.view(torch.int16))
+    plan.close()
+
+
+def test_nan_inf_propagate(gpu):
+    N, sdt, S = 4, "f32", 4096
+    s = Shard(S, S, N, sdt, gpu, seed=9)
+    s.sl.t.view(N, S)[1, 100] = float("nan")
+    s.sl.t.view(N, S)[2, 200] = float("inf")
+    s.sl.t.view(N, S)[0, 300] = float("inf")
+    s.sl.t.view(N, S)[3, 300] = float("-inf")
+    snap = s.snapshot()
+    plan = B.MtPlan([s.mt()], N, sdt)
+    plan.step(HP, 1)
+    torch.cuda.synchronize()
+    s.check("nan/inf", snap, 1)
+    p = s.p.t.cpu().numpy()
+    assert np.isnan(p[[100, 200, 300]]).all() and np.isfinite(np.delete(p, [100, 200, 300])).all()
+    bits = PR.bf16_bits(s.out.t)
+    assert all((bits[i] & 0x7FFF) == 0x7FC0 for i in (100, 200, 300))
+    plan.close()
+
+
+def test_cast_rounding_classes(gpu):
+    # every bf16 top half x the rounding-relevant low halves, plus random patterns
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xC000, 0xFFFF], dtype=np.uint32)
+    rng = np.random.default_rng(1)
+    bits = np.concatenate([(hi[:, None] | lows[None, :]).ravel(),
+                           rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)])
+    n = bits.size
+    x = torch.from_numpy(bits.view(np.int32).copy()).to(gpu).view(torch.float32)
+    out = torch.full((n,), 12345, dtype=torch.int16, device=gpu)
+    B.fsdp_cast_unshard_bf16(out, x, n, n)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    f = bits.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        ref = O.bf16_rne(f)
+    assert np.array_equal(got, ref)

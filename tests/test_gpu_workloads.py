@@ -1,0 +1,180 @@
+"""GPU parity on the five synthetic workloads, in the launch configuration the
+benchmark times (one multi-tensor plan over the rank's packed shards).
+
+* tiny MLP, FLAT, N=4: every rank, every element, 3 steps, per-step resync and
+  a free-running double-precision trajectory beside it; the other ranks' slots
+  of the packed all-gather buffer stay untouched.
+* 128 MiB MLP, FLAT, N=4 (rank 0): every element, 10 steps.
+* Llama-7B block, Shard(0), N=8: every element of steps 1-2, a sample after.
+* 7B rank shard (291 shards) and 70B rank shard (723 shards): full size, a
+  sample of elements (random plus the first and last elements of every shard)
+  that the oracle computes one by one from the GPU's state before each step.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import layout as OL
+from oracle import step as O
+from rank_step_amd.state import RankState
+from rank_step_amd.workloads import WORKLOADS, shapes_of
+from tests import parity as PR
+
+pytestmark = pytest.mark.gpu
+
+
+def _layout_matches_oracle(st):
+    w = st.w
+    ref_v, ref_s = OL.layout(OL.FLAT if w.mode == "flat" else OL.SHARD0, w.world_size, st.rank,
+                             shapes_of(w), w.has_master)
+    assert st.views == [v.__dict__ for v in ref_v]
+    assert st.summary == ref_s.__dict__
+
+
+def _check_full(st, snap, t, name, check_g=False):
+    p0, m0, v0, sl = snap
+    hp = st.w.hparams
+    gp = st.master.cpu().numpy()
+    gm = st.exp_avg.cpu().numpy()
+    gv = st.exp_avg_sq.cpu().numpy()
+    bits = PR.bf16_bits(st.ag_slot) if st.ag_slot is not None else None
+    worst = 0.0
+    for off, length, held, _ in st.segments:
+        a, b = off, off + held
+        ref = O.rank_step(p0[a:b], m0[a:b], v0[a:b], sl[:, a:b], held, t, hp)
+        fl = PR.floors(p0[a:b], m0[a:b], v0[a:b], sl[:, a:b], ref, hp, t)
+        worst = max(worst, PR.assert_close(f"{name} p", gp[a:b], ref["p"], fl["p"]))
+        PR.assert_close(f"{name} m", gm[a:b], ref["m"], fl["m"])
+        PR.assert_close(f"{name} v", gv[a:b], ref["v"], fl["v"])
+        for arr, nm in ((gp, "p"), (gm, "m"), (gv, "v")):
+            PR.check_pad_zero(f"{name} {nm}", arr[a:off + length], held)
+        if bits is not None:
+            PR.check_bf16(f"{name} bf16", bits[a:b], gp[a:b], ref["p"], fl["p"])
+            PR.check_pad_zero(f"{name} bf16", bits[a:off + length], held)
+        if check_g:
+            gg = st.grad_out.cpu().numpy()
+            PR.assert_close(f"{name} g", gg[a:b], ref["g"], fl["g"])
+    return worst
+
+
+def _snapshot(st):
+    return (PR.f64(st.master), PR.f64(st.exp_avg), PR.f64(st.exp_avg_sq),
+            PR.widen_slices(st.slices, st.w.slice_dtype))
+
+
+def test_tiny_mlp_every_rank(gpu):
+    w = WORKLOADS[1]
+    for r in range(w.world_size):
+        st = RankState(w, r, gpu, bf16_out=True, grad_out=True, ag_full=True)
+        _layout_matches_oracle(st)
+        assert st.total == 147_520 and len(st.segments) == 1
+        st.make_plan()
+        free = None
+        for t in range(1, w.steps + 1):
+            st.load_grads(t)
+            snap = _snapshot(st)
+            if free is None:
+                free = snap[:3]
+            st.step(t)
+            torch.cuda.synchronize()
+            _check_full(st, snap, t, f"tiny rank {r} t={t}", check_g=True)
+            # free-running double trajectory from the initial state
+            ref = O.rank_step(*free, snap[3], st.total, t, w.hparams)
+            free = (ref["p"], ref["m"], ref["v"])
+            fl = PR.floors(*free, snap[3], ref, w.hparams, t)
+            PR.assert_close(f"tiny rank {r} free p t={t}", st.master.cpu().numpy(), ref["p"], fl["p"])
+            PR.assert_close(f"tiny rank {r} free m t={t}", st.exp_avg.cpu().numpy(), ref["m"], fl["m"])
+            PR.assert_close(f"tiny rank {r} free v t={t}", st.exp_avg_sq.cpu().numpy(), ref["v"], fl["v"])
+        # the other ranks' slots of the packed all-gather buffer are untouched (zeros)
+        ag = PR.bf16_bits(st.ag)
+        S = st.total
+        mask = np.ones(ag.size, dtype=bool)
+        mask[r * S:(r + 1) * S] = False
+        assert np.all(ag[mask] == 0)
+        st.close()
+
+
+def test_mlp128m_rank0(gpu):
+    w = WORKLOADS[2]
+    st = RankState(w, 0, gpu, bf16_out=True)
+    _layout_matches_oracle(st)
+    assert st.total == 8_388_608
+    st.make_plan()
+    for t in range(1, w.steps + 1):
+        st.load_grads(t)
+        snap = _snapshot(st)
+        assert (snap[3] == 0).mean() > 0.09          # 10% exact zeros per slice
+        st.step(t)
+        torch.cuda.synchronize()
+        _check_full(st, snap, t, f"mlp128m t={t}")
+    st.close()
+
+
+def _sample_idx(st, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = [rng.integers(0, st.total, n)]
+    for off, length, held, _ in st.segments:
+        idx.append(np.arange(off, off + min(16, length)))
+        idx.append(np.arange(off + max(0, length - 16), off + length))
+    return np.unique(np.concatenate(idx))
+
+
+def _check_sampled(st, idx_t, before, t, name):
+    """Oracle on the sampled elements, from the GPU's state before the step.
+    (These workloads have no padding: every sampled element is valid.)"""
+    p0, m0, v0, sl = before
+    hp = st.w.hparams
+    assert st.summary["pad_numel"] == 0
+    ref = O.rank_step(p0, m0, v0, sl, p0.size, t, hp)
+    fl = PR.floors(p0, m0, v0, sl, ref, hp, t)
+    gp = PR.f64(st.master[idx_t])
+    PR.assert_close(f"{name} p", gp, ref["p"], fl["p"])
+    PR.assert_close(f"{name} m", PR.f64(st.exp_avg[idx_t]), ref["m"], fl["m"])
+    PR.assert_close(f"{name} v", PR.f64(st.exp_avg_sq[idx_t]), ref["v"], fl["v"])
+    if st.ag_slot is not None:
+        PR.check_bf16(f"{name} bf16", PR.bf16_bits(st.ag_slot[idx_t]), gp, ref["p"], fl["p"])
+
+
+def _run_sampled(cfg, gpu, n_sample, full_steps=()):
+    w = WORKLOADS[cfg]
+    st = RankState(w, 0, gpu, bf16_out=True)
+    _layout_matches_oracle(st)
+    st.make_plan()
+    info = st.plan.info()
+    assert info["n_tensors"] == len(st.segments)
+    idx = _sample_idx(st, n_sample, cfg)
+    idx_t = torch.from_numpy(idx).to(gpu)
+    for t in range(1, w.steps + 1):
+        st.load_grads(t)
+        if t in full_steps:
+            snap = _snapshot(st)
+        before = (PR.f64(st.master[idx_t]), PR.f64(st.exp_avg[idx_t]), PR.f64(st.exp_avg_sq[idx_t]),
+                  PR.widen_slices(st.slices[:, idx_t], w.slice_dtype))
+        st.step(t)
+        torch.cuda.synchronize()
+        _check_sampled(st, idx_t, before, t, f"cfg{cfg} t={t} sampled")
+        if t in full_steps:
+            _check_full(st, snap, t, f"cfg{cfg} t={t}")
+            del snap
+    st.close()
+    return st
+
+
+def test_llama7b_block(gpu):
+    st = _run_sampled(3, gpu, 1 << 20, full_steps=(1, 2))
+    assert st.total == 25_297_920
+
+
+def test_llama7b_full_rank_shard(gpu):
+    st = _run_sampled(4, gpu, 1 << 20)
+    assert st.total == 842_301_952 and len(st.segments) == 291
+    del st
+    torch.cuda.empty_cache()
+
+
+def test_llama70b_rank_shard(gpu):
+    st = _run_sampled(5, gpu, 1 << 20)
+    assert st.total == 2_204_803_328 and len(st.segments) == 723
+    del st
+    torch.cuda.empty_cache()
