@@ -61,10 +61,12 @@ def measured_traffic(workload, launches_numel):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(st, t, seconds_hint=15.0):
+def cpu_baseline(st, t, min_seconds=10.0):
     """The oracle (float64 NumPy), as it stands, on a bounded sample of the
-    workload: the rank's first shards, split across this host's cores with a
-    thread pool (NumPy releases the GIL inside its array loops)."""
+    workload: the rank's first shard(s), about 16M params, split across this
+    host's cores with a thread pool (NumPy releases the GIL inside its array
+    loops).  Consecutive steps run on the sample until at least
+    ``min_seconds`` of wall time have passed."""
     import numpy as np
     import torch
     from concurrent.futures import ThreadPoolExecutor
@@ -73,7 +75,6 @@ def cpu_baseline(st, t, seconds_hint=15.0):
 
     w = st.w
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    # the first shards in registration order, up to ~16M params
     n = 0
     names = []
     for (off, length, held, _), p in zip(st.segments, w.params):
@@ -89,21 +90,29 @@ def cpu_baseline(st, t, seconds_hint=15.0):
     else:
         raw = st.slices[:, :n].cpu().numpy()
     bounds = np.linspace(0, n, cores + 1).astype(np.int64)
+    state = [(p[a:b], m[a:b], v[a:b]) for a, b in zip(bounds[:-1], bounds[1:])]
 
-    def work(i):
+    def work(i, step):
         a, b = bounds[i], bounds[i + 1]
         sl = O.widen_bf16_bits(raw[:, a:b]) if w.slice_dtype == "bf16" else O.widen_f32(raw[:, a:b])
-        O.rank_step(p[a:b], m[a:b], v[a:b], sl, b - a, t, w.hparams)
+        r = O.rank_step(*state[i], sl, b - a, step, w.hparams)
+        state[i] = (r["p"], r["m"], r["v"])
         return b - a
 
+    done = 0
+    steps = 0
     with ThreadPoolExecutor(max_workers=cores) as ex:
         t0 = time.perf_counter()
-        done = sum(ex.map(work, range(cores)))
-        dt = time.perf_counter() - t0
+        while True:
+            done += sum(ex.map(lambda i: work(i, t + steps), range(cores)))
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
     return {"value": done / dt, "unit": "params/s", "cores": cores, "kind": "oracle",
-            "sample": f"one step of the oracle (float64) on the first {len(names)} shard(s) of the "
-                      f"rank ({', '.join(names)}): {done:,} params x {w.n_slices} "
-                      f"{w.slice_dtype} slices, {dt:.2f} s wall on {cores} threads"}
+            "sample": f"{steps} consecutive steps of the float64 oracle on the rank's first "
+                      f"{len(names)} shard(s) ({', '.join(names)}: {n:,} params, {w.n_slices} "
+                      f"{w.slice_dtype} gradient slices each), {dt:.1f} s wall on {cores} threads"}
 
 
 def main():

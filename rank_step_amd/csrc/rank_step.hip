@@ -37,14 +37,38 @@ using fsdp::fail;
 
 namespace {
 
+// Launch-shape tunables (build-time; the defaults are the measured best on MI355X).
+#ifndef RS_CHUNKS_PER_BLOCK
+#define RS_CHUNKS_PER_BLOCK 4
+#endif
+#ifndef RS_TARGET_BLOCKS
+#define RS_TARGET_BLOCKS 4096
+#endif
+#ifndef RS_MAX_CHUNK_TILES
+#define RS_MAX_CHUNK_TILES 32
+#endif
+#ifndef RS_UNROLL
+#define RS_UNROLL 1
+#endif
+// Non-temporal hints: 1 = nt on the access class, 0 = ordinary access.
+#ifndef RS_NT_SLICES
+#define RS_NT_SLICES 1
+#endif
+#ifndef RS_NT_STATE
+#define RS_NT_STATE 1
+#endif
+#ifndef RS_NT_OUT
+#define RS_NT_OUT 1
+#endif
+
 constexpr int kBlock = 256;             // threads per workgroup: four wave64s
 constexpr int kGroup = 8;               // elements per thread access
 constexpr int kTile = kBlock * kGroup;  // elements per workgroup iteration
 constexpr int kMaxSlices = 1024;
-constexpr int kChunksPerBlock = 4;      // chunk entries staged per workgroup
-constexpr int64_t kTargetBlocks = 4096; // ~16 workgroups per CU on 256 CUs
+constexpr int kChunksPerBlock = RS_CHUNKS_PER_BLOCK;  // chunk entries staged per workgroup
+constexpr int64_t kTargetBlocks = RS_TARGET_BLOCKS;   // workgroups a plan aims for
 constexpr int64_t kMinChunk = kTile;
-constexpr int64_t kMaxChunk = 32 * kTile;
+constexpr int64_t kMaxChunk = RS_MAX_CHUNK_TILES * kTile;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -129,17 +153,25 @@ template <typename T>
 using global_ptr = __attribute__((address_space(1))) T*;
 
 template <typename T>
-__device__ __forceinline__ T ld_nt(const T* p) {
-    return __builtin_nontemporal_load((const global_ptr<T>)p);
-}
-template <typename T>
-__device__ __forceinline__ void st_nt(T* p, T x) {
-    __builtin_nontemporal_store(x, (global_ptr<T>)p);
-}
-template <typename T>
 __device__ __forceinline__ T ld(const T* p) { return *(const global_ptr<T>)p; }
 template <typename T>
 __device__ __forceinline__ void st(T* p, T x) { *(global_ptr<T>)p = x; }
+
+// Streaming accesses; NT selects the non-temporal form.
+template <bool NT, typename T>
+__device__ __forceinline__ T ld_s(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load((const global_ptr<T>)p);
+    else return ld(p);
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void st_s(T* p, T x) {
+    if constexpr (NT) __builtin_nontemporal_store(x, (global_ptr<T>)p);
+    else st(p, x);
+}
+template <typename T> __device__ __forceinline__ T ld_slice(const T* p) { return ld_s<RS_NT_SLICES>(p); }
+template <typename T> __device__ __forceinline__ T ld_state(const T* p) { return ld_s<RS_NT_STATE>(p); }
+template <typename T> __device__ __forceinline__ void st_state(T* p, T x) { st_s<RS_NT_STATE>(p, x); }
+template <typename T> __device__ __forceinline__ void st_out(T* p, T x) { st_s<RS_NT_OUT>(p, x); }
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
@@ -165,12 +197,12 @@ __device__ __forceinline__ void load_slices(SliceRegs<NS, BF16>& r, const void* 
         if constexpr (BF16) {
             const u32x4* p = reinterpret_cast<const u32x4*>(
                 static_cast<const uint16_t*>(slices) + q * stride + e);
-            r.w[q][0] = ld_nt(p);
+            r.w[q][0] = ld_slice(p);
         } else {
             const u32x4* p = reinterpret_cast<const u32x4*>(
                 static_cast<const float*>(slices) + q * stride + e);
-            r.w[q][0] = ld_nt(p);
-            r.w[q][1] = ld_nt(p + 1);
+            r.w[q][0] = ld_slice(p);
+            r.w[q][1] = ld_slice(p + 1);
         }
     }
 }
@@ -214,13 +246,13 @@ __device__ __forceinline__ void reduce_runtime(const void* slices, int64_t strid
     u32x4 w[2];
     auto load = [&](int q) {
         if constexpr (BF16) {
-            w[0] = ld_nt(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(slices) +
-                                                        q * stride + e));
+            w[0] = ld_slice(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(slices) +
+                                                           q * stride + e));
         } else {
             const u32x4* p =
                 reinterpret_cast<const u32x4*>(static_cast<const float*>(slices) + q * stride + e);
-            w[0] = ld_nt(p);
-            w[1] = ld_nt(p + 1);
+            w[0] = ld_slice(p);
+            w[1] = ld_slice(p + 1);
         }
     };
     load(0);
@@ -244,12 +276,12 @@ __device__ __forceinline__ void load_state(StateRegs& s, const TensorDesc& T, in
     const f32x4* p = reinterpret_cast<const f32x4*>(T.param + e);
     const f32x4* m = reinterpret_cast<const f32x4*>(T.m + e);
     const f32x4* v = reinterpret_cast<const f32x4*>(T.v + e);
-    s.p[0] = ld_nt(p);
-    s.p[1] = ld_nt(p + 1);
-    s.m[0] = ld_nt(m);
-    s.m[1] = ld_nt(m + 1);
-    s.v[0] = ld_nt(v);
-    s.v[1] = ld_nt(v + 1);
+    s.p[0] = ld_state(p);
+    s.p[1] = ld_state(p + 1);
+    s.m[0] = ld_state(m);
+    s.m[1] = ld_state(m + 1);
+    s.v[0] = ld_state(v);
+    s.v[1] = ld_state(v + 1);
 }
 
 // AdamW on a group and the stores of its results.
@@ -271,22 +303,22 @@ __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup]
     f32x4* p = reinterpret_cast<f32x4*>(T.param + e);
     f32x4* m = reinterpret_cast<f32x4*>(T.m + e);
     f32x4* v = reinterpret_cast<f32x4*>(T.v + e);
-    st_nt(p, s.p[0]);
-    st_nt(p + 1, s.p[1]);
-    st_nt(m, s.m[0]);
-    st_nt(m + 1, s.m[1]);
-    st_nt(v, s.v[0]);
-    st_nt(v + 1, s.v[1]);
+    st_state(p, s.p[0]);
+    st_state(p + 1, s.p[1]);
+    st_state(m, s.m[0]);
+    st_state(m + 1, s.m[1]);
+    st_state(v, s.v[0]);
+    st_state(v + 1, s.v[1]);
     if (T.out_bf16) {
         u32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = b[2 * j] | (b[2 * j + 1] << 16);
-        st_nt(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
+        st_out(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
     }
     if (T.grad_out) {
         f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
-        st_nt(go, f32x4{g[0], g[1], g[2], g[3]});
-        st_nt(go + 1, f32x4{g[4], g[5], g[6], g[7]});
+        st_out(go, f32x4{g[0], g[1], g[2], g[3]});
+        st_out(go + 1, f32x4{g[4], g[5], g[6], g[7]});
     }
 }
 
@@ -399,8 +431,8 @@ __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin,
             reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
         }
         f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
-        st_nt(go, f32x4{gr[0], gr[1], gr[2], gr[3]});
-        st_nt(go + 1, f32x4{gr[4], gr[5], gr[6], gr[7]});
+        st_out(go, f32x4{gr[0], gr[1], gr[2], gr[3]});
+        st_out(go + 1, f32x4{gr[4], gr[5], gr[6], gr[7]});
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.grad_out + k, k < T.valid ? reduce_elem<BF16>(T, k, c) : 0.0f);
@@ -414,13 +446,13 @@ __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, i
     for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
         const int64_t e = g * kGroup;
         const f32x4* p = reinterpret_cast<const f32x4*>(T.param + e);
-        const f32x4 a = ld_nt(p), b = ld_nt(p + 1);
+        const f32x4 a = ld_state(p), b = ld_state(p + 1);
         u32x4 o;
         o[0] = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
         o[1] = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
         o[2] = bf16_rne(b[0]) | (bf16_rne(b[1]) << 16);
         o[3] = bf16_rne(b[2]) | (bf16_rne(b[3]) << 16);
-        st_nt(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
+        st_out(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.out_bf16 + k, k < T.valid ? static_cast<uint16_t>(bf16_rne(ld(T.param + k))) : uint16_t(0));
@@ -482,7 +514,7 @@ __global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T, int64
 
 // ---------------------------------------------------------------- kernel selection
 
-constexpr int kUnroll = 1;
+constexpr int kUnroll = RS_UNROLL;
 
 using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts);
 using FusedKernel = void (*)(TensorDesc, int64_t, StepConsts);

@@ -54,12 +54,28 @@ def floors(p, m, v, sl, ref, hp, t):
     return {"g": sG, "m": s_m, "v": s_v, "p": s_p}
 
 
+def free_floors(prev, sl, ref, hp, t):
+    """Floors for a free-running comparison: the term magnitudes carried along
+    the whole trajectory, so that slack allowed at an earlier step (e.g. an
+    element whose mean gradient cancelled to about eps) is still allowed.
+    ``prev`` holds the previous step's floors (initially |p0|, |m0|, v0)."""
+    lr, b1, b2, eps, wd = hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"]
+    sG = np.mean(np.abs(sl), axis=0)
+    s_m = b1 * prev["m"] + (1 - b1) * sG
+    s_v = b2 * prev["v"] + (1 - b2) * sG * sG
+    vhat = ref["v"] / (1 - b2 ** t)
+    s_p = prev["p"] * (1 - lr * wd) + lr * (s_m / (1 - b1 ** t)) / (np.sqrt(vhat) + eps)
+    return {"g": sG, "m": s_m, "v": s_v, "p": s_p}
+
+
 def assert_close(name, got, ref, floor, tol=TOL):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     bad_nan = np.isnan(got) != np.isnan(ref)
     assert not bad_nan.any(), f"{name}: NaN mismatch at {np.flatnonzero(bad_nan)[:5]}"
-    ok = ~np.isnan(ref)
+    inf = np.isinf(ref)
+    assert np.array_equal(got[inf], ref[inf]), f"{name}: infinity mismatch"
+    ok = ~np.isnan(ref) & ~inf
     err = np.abs(got[ok] - ref[ok])
     lim = tol * np.maximum(np.abs(ref[ok]), floor[ok])
     bad = err > lim

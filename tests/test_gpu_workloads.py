@@ -76,13 +76,14 @@ def test_tiny_mlp_every_rank(gpu):
             snap = _snapshot(st)
             if free is None:
                 free = snap[:3]
+                ffl = {"p": np.abs(free[0]), "m": np.abs(free[1]), "v": free[2]}
             st.step(t)
             torch.cuda.synchronize()
             _check_full(st, snap, t, f"tiny rank {r} t={t}", check_g=True)
             # free-running double trajectory from the initial state
             ref = O.rank_step(*free, snap[3], st.total, t, w.hparams)
             free = (ref["p"], ref["m"], ref["v"])
-            fl = PR.floors(*free, snap[3], ref, w.hparams, t)
+            ffl = fl = PR.free_floors(ffl, snap[3], ref, w.hparams, t)
             PR.assert_close(f"tiny rank {r} free p t={t}", st.master.cpu().numpy(), ref["p"], fl["p"])
             PR.assert_close(f"tiny rank {r} free m t={t}", st.exp_avg.cpu().numpy(), ref["m"], fl["m"])
             PR.assert_close(f"tiny rank {r} free v t={t}", st.exp_avg_sq.cpu().numpy(), ref["v"], fl["v"])
@@ -101,13 +102,24 @@ def test_mlp128m_rank0(gpu):
     _layout_matches_oracle(st)
     assert st.total == 8_388_608
     st.make_plan()
+    free = None
     for t in range(1, w.steps + 1):
         st.load_grads(t)
         snap = _snapshot(st)
         assert (snap[3] == 0).mean() > 0.09          # 10% exact zeros per slice
+        if free is None:
+            free = snap[:3]
+            ffl = {"p": np.abs(free[0]), "m": np.abs(free[1]), "v": free[2]}
         st.step(t)
         torch.cuda.synchronize()
         _check_full(st, snap, t, f"mlp128m t={t}")
+        ref = O.rank_step(*free, snap[3], st.total, t, w.hparams)
+        free = (ref["p"], ref["m"], ref["v"])
+        ffl = PR.free_floors(ffl, snap[3], ref, w.hparams, t)
+        PR.assert_close(f"mlp128m free p t={t}", st.master.cpu().numpy(), ref["p"], ffl["p"])
+        PR.assert_close(f"mlp128m free m t={t}", st.exp_avg.cpu().numpy(), ref["m"], ffl["m"])
+        PR.assert_close(f"mlp128m free v t={t}", st.exp_avg_sq.cpu().numpy(), ref["v"], ffl["v"])
+        del snap, ref
     st.close()
 
 
