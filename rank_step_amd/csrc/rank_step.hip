@@ -37,15 +37,15 @@ using fsdp::fail;
 
 namespace {
 
-// Launch-shape tunables (build-time; the defaults are the measured best on MI355X).
+// Build-time tunables.  The defaults are the fastest measured on MI355X for
+// the 7B rank shard (one 2048-element tile per workgroup, chunk entries and
+// shard descriptors read with scalar loads, non-temporal slice loads and bf16
+// stores, ordinary cached state accesses); other values exist for measurement.
+#ifndef RS_CHUNK_TILES
+#define RS_CHUNK_TILES 1        // 2048-element tiles per chunk-table entry
+#endif
 #ifndef RS_CHUNKS_PER_BLOCK
-#define RS_CHUNKS_PER_BLOCK 4
-#endif
-#ifndef RS_TARGET_BLOCKS
-#define RS_TARGET_BLOCKS 4096
-#endif
-#ifndef RS_MAX_CHUNK_TILES
-#define RS_MAX_CHUNK_TILES 32
+#define RS_CHUNKS_PER_BLOCK 1   // chunk-table entries per workgroup
 #endif
 #ifndef RS_UNROLL
 #define RS_UNROLL 1
@@ -54,21 +54,31 @@ namespace {
 #ifndef RS_NT_SLICES
 #define RS_NT_SLICES 1
 #endif
-#ifndef RS_NT_STATE
-#define RS_NT_STATE 1
-#endif
 #ifndef RS_NT_OUT
 #define RS_NT_OUT 1
+#endif
+#ifndef RS_NT_STATE_LD
+#define RS_NT_STATE_LD 0
+#endif
+#ifndef RS_NT_STATE_ST
+#define RS_NT_STATE_ST 0
+#endif
+// 1: stage the workgroup's chunk entries and shard descriptors in LDS;
+// 0: read them with scalar loads straight from the device tables.
+#ifndef RS_DESC_LDS
+#define RS_DESC_LDS 0
+#endif
+// 1: map workgroup ids so that each XCD walks a contiguous run of chunks.
+#ifndef RS_XCD_REMAP
+#define RS_XCD_REMAP 0
 #endif
 
 constexpr int kBlock = 256;             // threads per workgroup: four wave64s
 constexpr int kGroup = 8;               // elements per thread access
 constexpr int kTile = kBlock * kGroup;  // elements per workgroup iteration
 constexpr int kMaxSlices = 1024;
-constexpr int kChunksPerBlock = RS_CHUNKS_PER_BLOCK;  // chunk entries staged per workgroup
-constexpr int64_t kTargetBlocks = RS_TARGET_BLOCKS;   // workgroups a plan aims for
-constexpr int64_t kMinChunk = kTile;
-constexpr int64_t kMaxChunk = RS_MAX_CHUNK_TILES * kTile;
+constexpr int kChunksPerBlock = RS_CHUNKS_PER_BLOCK;
+constexpr int64_t kChunk = int64_t(RS_CHUNK_TILES) * kTile;  // elements per chunk entry
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -169,8 +179,8 @@ __device__ __forceinline__ void st_s(T* p, T x) {
     else st(p, x);
 }
 template <typename T> __device__ __forceinline__ T ld_slice(const T* p) { return ld_s<RS_NT_SLICES>(p); }
-template <typename T> __device__ __forceinline__ T ld_state(const T* p) { return ld_s<RS_NT_STATE>(p); }
-template <typename T> __device__ __forceinline__ void st_state(T* p, T x) { st_s<RS_NT_STATE>(p, x); }
+template <typename T> __device__ __forceinline__ T ld_state(const T* p) { return ld_s<RS_NT_STATE_LD>(p); }
+template <typename T> __device__ __forceinline__ void st_state(T* p, T x) { st_s<RS_NT_STATE_ST>(p, x); }
 template <typename T> __device__ __forceinline__ void st_out(T* p, T x) { st_s<RS_NT_OUT>(p, x); }
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
@@ -460,35 +470,59 @@ __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, i
 
 // ---------------------------------------------------------------- kernels
 
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).
+// With the remap on, the logical index of workgroup b is chosen so that every
+// XCD walks one contiguous run of logical indices.
+__device__ __forceinline__ int64_t logical_block() {
+    const int64_t b = blockIdx.x;
+    if constexpr (RS_XCD_REMAP) {
+        const int64_t nb = gridDim.x, q = nb / 8, r = nb % 8;
+        const int64_t x = b % 8, k = b / 8;
+        return x * q + std::min<int64_t>(x, r) + k;
+    }
+    return b;
+}
+
 // Multi-tensor fused step.  Workgroup b owns chunk entries
-// [b*cpb, min((b+1)*cpb, n_chunks)); it stages them and the shard descriptors
-// they name in LDS, then runs the chunks in order.
+// [b*cpb, min((b+1)*cpb, n_chunks)) of the chunk-descriptor table and runs
+// them in order; each entry names a shard and an element range of it.
 template <int NS, bool BF16, int UNROLL>
 __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
                                                          const ChunkDesc* __restrict__ chunks,
                                                          int64_t n_chunks, int32_t cpb,
                                                          StepConsts c) {
-    __shared__ ChunkDesc s_chunk[kChunksPerBlock];
-    __shared__ TensorDesc s_desc[kChunksPerBlock];
-    const int64_t first = static_cast<int64_t>(blockIdx.x) * cpb;
+    const int64_t first = logical_block() * cpb;
     const int cnt = static_cast<int>(std::min<int64_t>(cpb, n_chunks - first));
-    if (static_cast<int>(threadIdx.x) < cnt) s_chunk[threadIdx.x] = chunks[first + threadIdx.x];
-    __syncthreads();
-    for (int w = threadIdx.x; w < cnt * kDescWords; w += kBlock) {
-        const int i = w / kDescWords, j = w % kDescWords;
-        reinterpret_cast<uint64_t*>(&s_desc[i])[j] =
-            reinterpret_cast<const uint64_t*>(&tensors[s_chunk[i].tensor])[j];
-    }
-    __syncthreads();
-    for (int i = 0; i < cnt; ++i) {
-        TensorDesc T;
+    if constexpr (RS_DESC_LDS) {
+        // Stage this workgroup's run of the table, and the descriptors of the
+        // shards it names, in LDS with one parallel copy.
+        __shared__ ChunkDesc s_chunk[kChunksPerBlock];
+        __shared__ TensorDesc s_desc[kChunksPerBlock];
+        if (static_cast<int>(threadIdx.x) < cnt) s_chunk[threadIdx.x] = chunks[first + threadIdx.x];
+        __syncthreads();
+        for (int w = threadIdx.x; w < cnt * kDescWords; w += kBlock) {
+            const int i = w / kDescWords, j = w % kDescWords;
+            reinterpret_cast<uint64_t*>(&s_desc[i])[j] =
+                reinterpret_cast<const uint64_t*>(&tensors[s_chunk[i].tensor])[j];
+        }
+        __syncthreads();
+        for (int i = 0; i < cnt; ++i) {
+            TensorDesc T;
 #pragma unroll
-        for (int j = 0; j < kDescWords; ++j)
-            reinterpret_cast<uint64_t*>(&T)[j] =
-                uniform64(reinterpret_cast<const uint64_t*>(&s_desc[i])[j]);
-        const int64_t begin = static_cast<int64_t>(uniform64(s_chunk[i].begin));
-        const int64_t count = __builtin_amdgcn_readfirstlane(s_chunk[i].count);
-        fused_range<NS, BF16, UNROLL>(T, begin, begin + count, c);
+            for (int j = 0; j < kDescWords; ++j)
+                reinterpret_cast<uint64_t*>(&T)[j] =
+                    uniform64(reinterpret_cast<const uint64_t*>(&s_desc[i])[j]);
+            const int64_t begin = static_cast<int64_t>(uniform64(s_chunk[i].begin));
+            const int64_t count = __builtin_amdgcn_readfirstlane(s_chunk[i].count);
+            fused_range<NS, BF16, UNROLL>(T, begin, begin + count, c);
+        }
+    } else {
+        // Uniform addresses: the entries and descriptors arrive by scalar loads.
+        for (int i = 0; i < cnt; ++i) {
+            const ChunkDesc cd = chunks[first + i];
+            const TensorDesc T = tensors[cd.tensor];
+            fused_range<NS, BF16, UNROLL>(T, cd.begin, cd.begin + cd.count, c);
+        }
     }
 }
 
@@ -592,11 +626,7 @@ bool vec_ok(const TensorDesc& T, int32_t slice_dtype, int32_t n_slices) {
     return true;
 }
 
-int64_t single_chunk(int64_t S) {
-    int64_t per = (S + kTargetBlocks - 1) / kTargetBlocks;
-    per = (per + kTile - 1) / kTile * kTile;
-    return std::min(std::max(per, kMinChunk), kMaxChunk);
-}
+int64_t single_chunk(int64_t) { return kChunk; }
 
 int64_t blocks_for(int64_t S, int64_t chunk) { return (S + chunk - 1) / chunk; }
 
@@ -836,11 +866,9 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
         if (st != FSDP_OK) return st;
     }
 
-    // Chunk size: enough workgroups to fill the chip, chunks a whole number of
-    // workgroup tiles so every chunk but a shard's last starts group-aligned.
-    int64_t chunk = (total + kTargetBlocks * kChunksPerBlock - 1) / (kTargetBlocks * kChunksPerBlock);
-    chunk = (chunk + kTile - 1) / kTile * kTile;
-    chunk = std::min(std::max(chunk, kMinChunk), kMaxChunk);
+    // Every chunk but a shard's last is kChunk elements, so every chunk starts
+    // group-aligned; short-lived single-tile workgroups stream best on MI355X.
+    const int64_t chunk = kChunk;
     std::vector<ChunkDesc> chunks;
     for (size_t i = 0; i < descs.size(); ++i) {
         for (int64_t b = 0; b < descs[i].shard_numel; b += chunk) {
