@@ -115,6 +115,44 @@ def cpu_baseline(st, t, min_seconds=10.0):
                       f"{w.slice_dtype} gradient slices each), {dt:.1f} s wall on {cores} threads"}
 
 
+def clipped_step(st, stream, args, t0):
+    """Time the clipped step on the same state: reduce + sum of squares
+    (pass 1), the clip coefficient, AdamW + cast from the scaled gradient
+    (pass 2).  Bytes per param: 2N+4 in pass 1, 4+24+2 in pass 2."""
+    import torch
+    from rank_step_amd import binding as B
+
+    w = st.w
+    plan = B.MtPlan(st.mt_tensors(with_grad_out=True), w.n_slices, w.slice_dtype, stream)
+    sq = torch.zeros(1, dtype=torch.float64, device=st.device)
+    coef = torch.zeros(1, dtype=torch.float32, device=st.device)
+
+    def one(t):
+        plan.reduce_sqnorm(sq, stream)
+        B.fsdp_clip_coef(coef, None, sq, 1, args.clip, stream)
+        plan.step_clipped(w.hparams, t, coef, stream)
+
+    t = t0
+    for _ in range(args.warmup):
+        t += 1
+        one(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        t += 1
+        one(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    plan.close()
+    slice_b = 2 if w.slice_dtype == "bf16" else 4
+    bpp = w.n_slices * slice_b + 4 + 4 + 24 + (2 if w.bf16_out else 0)
+    return {"ms_per_step": ms, "params_per_s": st.total / (ms / 1e3), "bytes_per_param": bpp,
+            "hbm_gb_s": bpp * st.total / (ms / 1e3) / 1e9, "max_norm": args.clip,
+            "coef": float(coef.item()), "launches": 4}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +161,10 @@ def main():
     ap.add_argument("--workload", default="llama7b_full_n8", choices=sorted(WORKLOAD_BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle timing (e.g. under a profiler)")
+    ap.add_argument("--clip", type=float, default=1.0, metavar="MAX_NORM",
+                    help="also time the clipped step (global grad-norm clipping) with this max_norm")
+    ap.add_argument("--no-clip", dest="clip", action="store_const", const=None,
+                    help="do not time the clipped step")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the step, run torch copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -164,9 +206,9 @@ def main():
 
     w = WORKLOADS[WORKLOAD_BY_NAME[args.workload]]
     bf16_out = w.bf16_out
-    st = RankState(w, 0, dev, bf16_out=bf16_out)
+    st = RankState(w, 0, dev, bf16_out=bf16_out, grad_out=args.clip is not None)
     st.load_grads(1)
-    st.make_plan(stream)
+    st.make_plan(stream, with_grad_out=False)
     info = st.plan.info()
     total = st.total
     bpp = bytes_per_param(w, bf16_out)
@@ -230,6 +272,8 @@ def main():
             "traffic": traffic,
         },
     }
+    if args.clip is not None:
+        out["clipped_step"] = clipped_step(st, stream, args, t)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, t + 1)
     st.close()

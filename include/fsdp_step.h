@@ -24,7 +24,8 @@
  *     failing call on the same thread).  Nothing aborts, nothing throws.
  *   - All arguments are checked on the host before any device work is queued.
  *   - Device pointers are plain HIP device addresses on the current device.
- *     The caller owns every buffer; the library never allocates or frees them.
+ *     The caller owns every buffer it passes; the library never allocates or
+ *     frees them (a plan allocates only its own tables, see fsdp_mt_plan_create).
  *   - Work is queued on the caller's stream (NULL = the null stream) and is
  *     asynchronous; no call synchronises the host except fsdp_mt_plan_create.
  *   - Sizes and offsets are in elements unless a name says bytes.
@@ -236,7 +237,9 @@ typedef struct {
  * records, checks them as the single-shard calls would (no written buffer
  * may overlap any other buffer of any shard in the plan; read-only slices
  * may overlap each other), builds the chunk-descriptor table and uploads it
- * to device memory the plan owns on the current device.  Synchronises
+ * to device memory the plan owns on the current device.  When every
+ * non-empty shard has a grad_shard_out the plan also owns one fp64 partial
+ * sum per workgroup for fsdp_mt_reduce_sqnorm.  Synchronises
  * `stream` once.  The caller keeps every referenced buffer alive and in
  * place while the plan exists.  n_tensors may be 0 (an empty plan).
  * Errors: as the single-shard calls; FSDP_E_HIP if the upload fails. */
@@ -249,6 +252,48 @@ int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tenso
  * be used on the device it was made on (FSDP_E_STATE).  Two steps of one
  * plan on different streams without ordering between them race. */
 int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, hipStream_t stream);
+
+/* ------------------------------------------------------------------ clipping */
+
+/* Global gradient-norm clipping across the ranks' shards, [FSDP ch.18] §18.18:
+ * each rank takes the sum of squares of its own reduced gradient shard, an
+ * all-reduce sums those over the ranks, the square root is the global norm,
+ * and every rank scales its own shard by one coefficient.  The page names
+ * clip_grad_norm_(max_norm, norm_type=2.0); its formula is taken as torch's:
+ * coef = min(1, max_norm / (norm + 1e-6)), g <- g * coef.  A clipped step is
+ * two passes over memory (the update needs the global norm first):
+ *   fsdp_mt_reduce_sqnorm  slices -> grad_shard_out, and the rank's sum of squares
+ *   (all-reduce of the per-rank sums: outside this library)
+ *   fsdp_clip_coef         per-rank sums -> norm and coefficient, on the device
+ *   fsdp_mt_step_clipped   AdamW + cast from grad_shard_out * coef
+ * No host synchronisation anywhere in the sequence. */
+
+/* Pass 1 over every shard of `plan`: write the reduced gradient (as
+ * fsdp_reduce_grad_shard) to each shard's grad_shard_out and the rank's sum
+ * of its squares to sqnorm_out (device, one fp64).  Squares are exact in fp64
+ * and summed in fp64 in a fixed order, so the result is deterministic.  Every
+ * non-empty shard of the plan must have a grad_shard_out (else FSDP_E_ARG).
+ * Uses the plan's own per-workgroup partial-sum buffer: two calls on one plan
+ * must not overlap.  An empty plan writes 0. */
+int32_t fsdp_mt_reduce_sqnorm(fsdp_mt_plan* plan, double* sqnorm_out, hipStream_t stream);
+
+/* Global norm and clip coefficient from n_ranks per-rank sums of squares
+ * (device fp64 [n_ranks], summed in index order -- the all-reduce's result
+ * when n_ranks is 1, or the ranks' own sums when one device holds them all):
+ *   norm = sqrt(sum), coef = min(1, max_norm / (norm + 1e-6))
+ * coef_out: device fp32 [1]; norm_out: device fp64 [1] or NULL.  A NaN norm
+ * gives a NaN coefficient; an infinite norm gives 0.  max_norm must be finite
+ * and >= 0, 1 <= n_ranks <= 2^20; outputs must not overlap the input. */
+int32_t fsdp_clip_coef(float* coef_out, double* norm_out, const double* sqnorms,
+                       int32_t n_ranks, double max_norm, hipStream_t stream);
+
+/* Pass 2: AdamW and the bf16 cast on every shard of `plan`, from the reduced
+ * gradient that fsdp_mt_reduce_sqnorm stored, multiplied in fp32 by
+ * *grad_scale (device fp32, e.g. fsdp_clip_coef's output).  With a scale of
+ * exactly 1 the results are bit-identical to fsdp_mt_step's.  The gradient
+ * buffers are read, not written.  One kernel launch. */
+int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                             const float* grad_scale, hipStream_t stream);
 
 /* Sizes of a plan (host only). */
 int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info_out);

@@ -14,6 +14,8 @@ backward reduce-scatter and the next forward all-gather):
 * ``oracle.step``    -- the fp32 mean of the N incoming gradient slices, the
   decoupled-weight-decay AdamW update on the shard only, and the
   round-to-nearest-even bf16 cast of the updated shard.  float64 throughout.
+* ``oracle.clip``    -- global gradient-norm clipping across the ranks'
+  shards (squared norms summed over ranks, one coefficient for all).
 
 Sources (the pages this follows; cited by page title and section):
 
@@ -31,4 +33,4 @@ force; none is "parity unpinned" except where the function's docstring says
 so.
 """
 
-from . import layout, step  # noqa: F401
+from . import clip, layout, step  # noqa: F401

@@ -152,14 +152,16 @@ def bf16_bits_to_f64(u16):
 # the whole rank step on one shard buffer
 
 
-def rank_step(p, m, v, slices_f64, valid, t, hp):
+def rank_step(p, m, v, slices_f64, valid, t, hp, grad_scale=None):
     """One rank step on one shard buffer of length S = len(p).
 
     ``slices_f64`` is ``[N, >=valid]`` (already widened); only the first
     ``valid`` columns are read.  ``hp`` holds lr, beta1, beta2, eps,
-    weight_decay.  Returns dict with g, p, m, v (float64, length S) and bf16
-    (uint16 bits of RNE(p'), length S).  Positions >= valid are +0 in every
-    output, whatever the inputs hold there.
+    weight_decay.  ``grad_scale`` (optional) multiplies the reduced gradient
+    before the update: the clip coefficient of ``oracle.clip``.  Returns dict
+    with g (the reduced gradient, unscaled), p, m, v (float64, length S) and
+    bf16 (uint16 bits of RNE(p'), length S).  Positions >= valid are +0 in
+    every output, whatever the inputs hold there.
     """
     S = len(p)
     g = np.zeros(S, dtype=np.float64)
@@ -169,7 +171,8 @@ def rank_step(p, m, v, slices_f64, valid, t, hp):
     if valid > 0:
         sl = np.asarray(slices_f64, dtype=np.float64)[:, :valid]
         g[:valid] = reduce_mean(sl)
-        pv, mv, vv = adamw(p[:valid], m[:valid], v[:valid], g[:valid], t,
+        gu = g[:valid] if grad_scale is None else g[:valid] * grad_scale
+        pv, mv, vv = adamw(p[:valid], m[:valid], v[:valid], gu, t,
                            hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
                            hp["weight_decay"])
         p_out[:valid], m_out[:valid], v_out[:valid] = pv, mv, vv

@@ -29,7 +29,8 @@ LAYOUTS = {"flat": 0, "shard0": 1}
 # Every function the header declares; the CPU tests check each is exported.
 EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
            "fsdp_adamw_shard_step", "fsdp_cast_unshard_bf16", "fsdp_mt_plan_create",
-           "fsdp_mt_step", "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy")
+           "fsdp_mt_step", "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy",
+           "fsdp_mt_reduce_sqnorm", "fsdp_clip_coef", "fsdp_mt_step_clipped")
 
 
 class FsdpError(RuntimeError):
@@ -104,6 +105,9 @@ def lib():
             "fsdp_mt_step": [vp, ctypes.POINTER(AdamWHparams), vp],
             "fsdp_mt_plan_get_info": [vp, ctypes.POINTER(MtPlanInfo)],
             "fsdp_mt_plan_destroy": [vp],
+            "fsdp_mt_reduce_sqnorm": [vp, vp, vp],
+            "fsdp_clip_coef": [vp, vp, vp, i32, ctypes.c_double, vp],
+            "fsdp_mt_step_clipped": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -214,6 +218,20 @@ def fsdp_mt_plan_destroy(plan):
     _check(lib().fsdp_mt_plan_destroy(plan))
 
 
+def fsdp_mt_reduce_sqnorm(plan, sqnorm_out, stream=None):
+    _check(lib().fsdp_mt_reduce_sqnorm(plan, _ptr(sqnorm_out), _stream(stream)))
+
+
+def fsdp_clip_coef(coef_out, norm_out, sqnorms, n_ranks, max_norm, stream=None):
+    _check(lib().fsdp_clip_coef(_ptr(coef_out), _ptr(norm_out), _ptr(sqnorms), int(n_ranks),
+                                float(max_norm), _stream(stream)))
+
+
+def fsdp_mt_step_clipped(plan, hp, step, grad_scale, stream=None):
+    h = _hparams(hp, step)
+    _check(lib().fsdp_mt_step_clipped(plan, ctypes.byref(h), _ptr(grad_scale), _stream(stream)))
+
+
 class MtPlan:
     """Owns one fsdp_mt_plan handle (and keeps the Python objects whose
     buffers it references alive)."""
@@ -227,6 +245,12 @@ class MtPlan:
 
     def info(self):
         return fsdp_mt_plan_get_info(self.handle)
+
+    def reduce_sqnorm(self, sqnorm_out, stream=None):
+        fsdp_mt_reduce_sqnorm(self.handle, sqnorm_out, stream)
+
+    def step_clipped(self, hp, step, grad_scale, stream=None):
+        fsdp_mt_step_clipped(self.handle, hp, step, grad_scale, stream)
 
     def close(self):
         if self.handle is not None:

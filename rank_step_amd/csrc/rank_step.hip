@@ -294,7 +294,9 @@ __device__ __forceinline__ void load_state(StateRegs& s, const TensorDesc& T, in
     s.v[1] = ld_state(v + 1);
 }
 
-// AdamW on a group and the stores of its results.
+// AdamW on a group and the stores of its results.  WRITE_G: also store the
+// reduced gradient when the shard has a grad_shard_out.
+template <bool WRITE_G = true>
 __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup],
                                              const TensorDesc& T, int64_t e, const StepConsts& c) {
     uint32_t b[kGroup];
@@ -325,7 +327,7 @@ __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup]
         for (int j = 0; j < 4; ++j) o[j] = b[2 * j] | (b[2 * j + 1] << 16);
         st_out(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
     }
-    if (T.grad_out) {
+    if (WRITE_G && T.grad_out) {
         f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
         st_out(go, f32x4{g[0], g[1], g[2], g[3]});
         st_out(go + 1, f32x4{g[4], g[5], g[6], g[7]});
@@ -368,6 +370,26 @@ __device__ __forceinline__ void fused_elem(const TensorDesc& T, int64_t k, const
         st(T.v + k, 0.0f);
         if (T.out_bf16) st(T.out_bf16 + k, uint16_t(0));
         if (T.grad_out) st(T.grad_out + k, 0.0f);
+    }
+}
+
+// AdamW on element k from the stored reduced gradient times `scale` (the clip
+// coefficient); +0 everywhere in the pad.  The gradient buffer is not written.
+__device__ __forceinline__ void scaled_elem(const TensorDesc& T, int64_t k, float scale,
+                                            const StepConsts& c) {
+    if (k < T.valid) {
+        const float g = ld(T.grad_out + k) * scale;
+        float p = ld(T.param + k), m = ld(T.m + k), v = ld(T.v + k);
+        adamw(p, m, v, g, c);
+        st(T.param + k, p);
+        st(T.m + k, m);
+        st(T.v + k, v);
+        if (T.out_bf16) st(T.out_bf16 + k, static_cast<uint16_t>(bf16_rne(p)));
+    } else {
+        st(T.param + k, 0.0f);
+        st(T.m + k, 0.0f);
+        st(T.v + k, 0.0f);
+        if (T.out_bf16) st(T.out_bf16 + k, uint16_t(0));
     }
 }
 
@@ -448,6 +470,62 @@ __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin,
         st(T.grad_out + k, k < T.valid ? reduce_elem<BF16>(T, k, c) : 0.0f);
 }
 
+// Reduce into grad_out on [begin, end) and return this thread's sum of the
+// squares of the reduced values, in fp64 (each fp32 square is exact in fp64).
+template <int NS, bool BF16>
+__device__ __forceinline__ double reduce_sq_range(const TensorDesc& T, int64_t begin, int64_t end,
+                                                  const StepConsts& c) {
+    double acc = 0.0;
+    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
+    vend = std::max(vend, begin);
+    const int64_t g1 = vend / kGroup;
+    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
+        const int64_t e = g * kGroup;
+        float gr[kGroup];
+        if constexpr (NS > 0) {
+            SliceRegs<NS, BF16> sr;
+            load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
+            reduce_regs<NS, BF16>(sr, gr, c);
+        } else {
+            reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
+        }
+        f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
+        st_out(go, f32x4{gr[0], gr[1], gr[2], gr[3]});
+        st_out(go + 1, f32x4{gr[4], gr[5], gr[6], gr[7]});
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) acc += static_cast<double>(gr[j]) * static_cast<double>(gr[j]);
+    }
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) {
+        const float gk = k < T.valid ? reduce_elem<BF16>(T, k, c) : 0.0f;
+        st(T.grad_out + k, gk);
+        acc += static_cast<double>(gk) * static_cast<double>(gk);
+    }
+    return acc;
+}
+
+// AdamW + cast on [begin, end) from the stored reduced gradient times `scale`.
+__device__ __forceinline__ void scaled_range(const TensorDesc& T, int64_t begin, int64_t end,
+                                             float scale, const StepConsts& c) {
+    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
+    vend = std::max(vend, begin);
+    const int64_t g1 = vend / kGroup;
+    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
+        const int64_t e = g * kGroup;
+        const f32x4* gp = reinterpret_cast<const f32x4*>(T.grad_out + e);
+        const f32x4 a = ld_slice(gp), b = ld_slice(gp + 1);
+        StateRegs st;
+        load_state(st, T, e);
+        float gr[kGroup];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gr[j] = a[j] * scale;
+            gr[4 + j] = b[j] * scale;
+        }
+        update_store<false>(st, gr, T, e, c);
+    }
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) scaled_elem(T, k, scale, c);
+}
+
 // Cast only: out_bf16 = RNE(param) on [begin, end).
 __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, int64_t end) {
     int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
@@ -483,14 +561,13 @@ __device__ __forceinline__ int64_t logical_block() {
     return b;
 }
 
-// Multi-tensor fused step.  Workgroup b owns chunk entries
-// [b*cpb, min((b+1)*cpb, n_chunks)) of the chunk-descriptor table and runs
-// them in order; each entry names a shard and an element range of it.
-template <int NS, bool BF16, int UNROLL>
-__global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
-                                                         const ChunkDesc* __restrict__ chunks,
-                                                         int64_t n_chunks, int32_t cpb,
-                                                         StepConsts c) {
+// Runs f(T, begin, end) for each chunk entry of this workgroup:
+// entries [b*cpb, min((b+1)*cpb, n_chunks)) of the chunk-descriptor table,
+// each naming a shard and an element range of it.
+template <typename F>
+__device__ __forceinline__ void for_my_chunks(const TensorDesc* __restrict__ tensors,
+                                              const ChunkDesc* __restrict__ chunks,
+                                              int64_t n_chunks, int32_t cpb, F&& f) {
     const int64_t first = logical_block() * cpb;
     const int cnt = static_cast<int>(std::min<int64_t>(cpb, n_chunks - first));
     if constexpr (RS_DESC_LDS) {
@@ -514,16 +591,107 @@ __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __res
                     uniform64(reinterpret_cast<const uint64_t*>(&s_desc[i])[j]);
             const int64_t begin = static_cast<int64_t>(uniform64(s_chunk[i].begin));
             const int64_t count = __builtin_amdgcn_readfirstlane(s_chunk[i].count);
-            fused_range<NS, BF16, UNROLL>(T, begin, begin + count, c);
+            f(T, begin, begin + count);
         }
     } else {
         // Uniform addresses: the entries and descriptors arrive by scalar loads.
         for (int i = 0; i < cnt; ++i) {
             const ChunkDesc cd = chunks[first + i];
             const TensorDesc T = tensors[cd.tensor];
-            fused_range<NS, BF16, UNROLL>(T, cd.begin, cd.begin + cd.count, c);
+            f(T, cd.begin, cd.begin + cd.count);
         }
     }
+}
+
+// Sum of a value over the workgroup in a fixed order (lanes by xor-shuffle
+// steps, then the four waves in index order); the result is valid in thread 0.
+__device__ __forceinline__ double block_sum(double x) {
+    __shared__ double s_wave[kBlock / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    const int wave = threadIdx.x / 64;
+    if ((threadIdx.x & 63) == 0) s_wave[wave] = x;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0)
+        for (int w = 0; w < kBlock / 64; ++w) t += s_wave[w];
+    return t;
+}
+
+// Multi-tensor fused step: reduce, AdamW and cast for every chunk.
+template <int NS, bool BF16, int UNROLL>
+__global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
+                                                         const ChunkDesc* __restrict__ chunks,
+                                                         int64_t n_chunks, int32_t cpb,
+                                                         StepConsts c) {
+    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e) {
+        fused_range<NS, BF16, UNROLL>(T, b, e, c);
+    });
+}
+
+// Pass 1 of a clipped step: reduce into grad_shard_out and write this
+// workgroup's sum of squares to partials[logical block].
+template <int NS, bool BF16>
+__global__ __launch_bounds__(kBlock) void mt_reduce_sq_kernel(const TensorDesc* __restrict__ tensors,
+                                                              const ChunkDesc* __restrict__ chunks,
+                                                              int64_t n_chunks, int32_t cpb,
+                                                              StepConsts c, double* partials) {
+    double acc = 0.0;
+    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e) {
+        acc += reduce_sq_range<NS, BF16>(T, b, e, c);
+    });
+    const double total = block_sum(acc);
+    if (threadIdx.x == 0) st(partials + logical_block(), total);
+}
+
+// Pass 2 of a clipped step: AdamW and cast from grad_shard_out times *scale.
+__global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc* __restrict__ tensors,
+                                                                const ChunkDesc* __restrict__ chunks,
+                                                                int64_t n_chunks, int32_t cpb,
+                                                                StepConsts c, const float* scale) {
+    const float k = *scale;
+    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e) {
+        scaled_range(T, b, e, k, c);
+    });
+}
+
+constexpr int kSumBlocks = 1024;        // workgroups of the first summation stage
+
+// Workgroup b sums partials[b*per, min(n, (b+1)*per)) into out[b]: thread t
+// adds the elements t, t+256, ... of the range (coalesced, several loads in
+// flight), then the workgroup sum.  The order is fixed, so the sum is too.
+__global__ __launch_bounds__(kBlock) void sum_partials_kernel(const double* partials, int64_t n,
+                                                              int64_t per, double* out) {
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t hi = std::min(n, lo + per);
+    double acc = 0.0;
+    int64_t i = lo + threadIdx.x;
+    for (; i + 3 * kBlock < hi; i += 4 * kBlock) {
+        const double a = ld(partials + i), b = ld(partials + i + kBlock);
+        const double c = ld(partials + i + 2 * kBlock), d = ld(partials + i + 3 * kBlock);
+        acc += a;
+        acc += b;
+        acc += c;
+        acc += d;
+    }
+    for (; i < hi; i += kBlock) acc += ld(partials + i);
+    const double total = block_sum(acc);
+    if (threadIdx.x == 0) st(out + blockIdx.x, total);
+}
+
+// Clip coefficient from the ranks' squared norms (their all-reduce sum, taken
+// here in index order): norm = sqrt(sum), coef = min(1, max_norm/(norm+1e-6)),
+// NaN kept.  One thread.
+__global__ void clip_coef_kernel(float* coef_out, double* norm_out, const double* sq, int32_t n,
+                                 double max_norm) {
+    if (threadIdx.x != 0) return;
+    double total = 0.0;
+    for (int32_t i = 0; i < n; ++i) total += ld(sq + i);
+    const double norm = sqrt(total);
+    double coef = max_norm / (norm + 1e-6);
+    if (coef > 1.0) coef = 1.0;
+    st(coef_out, static_cast<float>(coef));
+    if (norm_out) st(norm_out, norm);
 }
 
 // Single-shard kernels: workgroup b covers elements [b*chunk, (b+1)*chunk).
@@ -562,6 +730,20 @@ MtKernel pick_mt(int n) {
         case 4: return mt_step_kernel<4, BF16, kUnroll>;
         case 8: return mt_step_kernel<8, BF16, kUnroll>;
         default: return mt_step_kernel<0, BF16, 1>;
+    }
+}
+
+using ReduceSqKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts,
+                                double*);
+
+template <bool BF16>
+ReduceSqKernel pick_reduce_sq(int n) {
+    switch (n) {
+        case 1: return mt_reduce_sq_kernel<1, BF16>;
+        case 2: return mt_reduce_sq_kernel<2, BF16>;
+        case 4: return mt_reduce_sq_kernel<4, BF16>;
+        case 8: return mt_reduce_sq_kernel<8, BF16>;
+        default: return mt_reduce_sq_kernel<0, BF16>;
     }
 }
 
@@ -700,9 +882,28 @@ struct fsdp_mt_plan {
     int32_t cpb = kChunksPerBlock;
     int64_t n_tensors = 0, n_chunks = 0, n_blocks = 0, total_numel = 0, total_valid = 0;
     int64_t chunk_numel = 0;
+    bool all_grad_out = false;       // every non-empty shard stores its reduced gradient
     TensorDesc* d_tensors = nullptr;
     ChunkDesc* d_chunks = nullptr;
+    double* d_partials = nullptr;    // clipped steps: one sum of squares per workgroup,
+                                     // then kSumBlocks second-stage sums
 };
+
+namespace {
+
+// The plan exists and belongs to the current device.
+int32_t check_plan_device(const fsdp_mt_plan* plan, const char* who) {
+    if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FSDP_E_HIP, "%s: %s", who, hipGetErrorString(e));
+    if (dev != plan->device)
+        return fail(FSDP_E_STATE, "%s: plan made on device %d used on device %d", who, plan->device,
+                    dev);
+    return FSDP_OK;
+}
+
+}  // namespace
 
 extern "C" int32_t fsdp_reduce_grad_shard(float* grad_shard_out, const void* grad_slices,
                                           int32_t slice_dtype, int64_t slice_stride,
@@ -820,6 +1021,7 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
 
     std::vector<TensorDesc> descs;
     descs.reserve(static_cast<size_t>(n_tensors));
+    bool all_grad_out = true;
     std::vector<fsdp::Range> rs;
     int64_t total = 0, total_valid = 0;
     for (int32_t i = 0; i < n_tensors; ++i) {
@@ -840,6 +1042,7 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
             return fail(FSDP_E_ARG, "%s: total size overflows", who);
         total_valid += t.valid;
         if (t.shard_numel == 0) continue;
+        if (!t.grad_shard_out) all_grad_out = false;
         rs.push_back(range_of(t.param_fp32, t.shard_numel, 4, true, i, "param"));
         rs.push_back(range_of(t.exp_avg, t.shard_numel, 4, true, i, "exp_avg"));
         rs.push_back(range_of(t.exp_avg_sq, t.shard_numel, 4, true, i, "exp_avg_sq"));
@@ -895,11 +1098,15 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
     plan->total_numel = total;
     plan->total_valid = total_valid;
     plan->chunk_numel = chunk;
+    plan->all_grad_out = all_grad_out;
     hipError_t e = hipGetDevice(&plan->device);
     if (e == hipSuccess && !chunks.empty()) {
         e = hipMalloc(reinterpret_cast<void**>(&plan->d_tensors), descs.size() * sizeof(TensorDesc));
         if (e == hipSuccess)
             e = hipMalloc(reinterpret_cast<void**>(&plan->d_chunks), chunks.size() * sizeof(ChunkDesc));
+        if (e == hipSuccess && all_grad_out)
+            e = hipMalloc(reinterpret_cast<void**>(&plan->d_partials),
+                          static_cast<size_t>(plan->n_blocks + kSumBlocks) * sizeof(double));
         if (e == hipSuccess)
             e = hipMemcpyAsync(plan->d_tensors, descs.data(), descs.size() * sizeof(TensorDesc),
                                hipMemcpyHostToDevice, stream);
@@ -922,18 +1129,92 @@ extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
     if ((st = check_hparams(hp)) != FSDP_OK) return st;
-    int dev = -1;
-    const hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(FSDP_E_HIP, "%s: %s", who, hipGetErrorString(e));
-    if (dev != plan->device)
-        return fail(FSDP_E_STATE, "%s: plan made on device %d used on device %d", who, plan->device,
-                    dev);
+    if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
     const MtKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_mt<true>(plan->n_slices)
                                                          : pick_mt<false>(plan->n_slices);
     hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), 0, stream,
                        plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb, c);
+    return launch_status(who);
+}
+
+
+extern "C" int32_t fsdp_mt_reduce_sqnorm(fsdp_mt_plan* plan, double* sqnorm_out,
+                                         hipStream_t stream) {
+    const char* who = "fsdp_mt_reduce_sqnorm";
+    if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
+    if (!sqnorm_out) return fail(FSDP_E_ARG, "%s: null sqnorm_out", who);
+    if (!aligned(sqnorm_out, 8)) return fail(FSDP_E_ALIGN, "%s: sqnorm_out not 8-byte aligned", who);
+    if (!plan->all_grad_out)
+        return fail(FSDP_E_ARG, "%s: every shard of the plan needs a grad_shard_out", who);
+    int32_t st;
+    if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    if (plan->n_chunks > 0) {
+        const StepConsts c = make_consts(nullptr, plan->n_slices);
+        const ReduceSqKernel k = plan->slice_dtype == FSDP_DT_BF16
+                                     ? pick_reduce_sq<true>(plan->n_slices)
+                                     : pick_reduce_sq<false>(plan->n_slices);
+        hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), 0, stream,
+                           plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb, c,
+                           plan->d_partials);
+        if ((st = launch_status(who)) != FSDP_OK) return st;
+    }
+    if (plan->n_chunks == 0) {
+        // nothing to sum: one workgroup over an empty range writes 0
+        hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
+                           static_cast<const double*>(nullptr), int64_t(0), int64_t(0), sqnorm_out);
+        return launch_status(who);
+    }
+    // two fixed-order stages: n_blocks partials -> up to kSumBlocks -> one
+    const int64_t n = plan->n_blocks;
+    const int64_t per = (n + kSumBlocks - 1) / kSumBlocks;
+    const int64_t stage = (n + per - 1) / per;
+    double* second = plan->d_partials + n;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(static_cast<uint32_t>(stage)), dim3(kBlock), 0,
+                       stream, static_cast<const double*>(plan->d_partials), n, per, second);
+    if ((st = launch_status(who)) != FSDP_OK) return st;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
+                       static_cast<const double*>(second), stage, stage, sqnorm_out);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_clip_coef(float* coef_out, double* norm_out, const double* sqnorms,
+                                  int32_t n_ranks, double max_norm, hipStream_t stream) {
+    const char* who = "fsdp_clip_coef";
+    if (!coef_out || !sqnorms) return fail(FSDP_E_ARG, "%s: null coef_out or sqnorms", who);
+    if (n_ranks < 1 || n_ranks > (1 << 20))
+        return fail(FSDP_E_ARG, "%s: n_ranks %d outside [1, 2^20]", who, n_ranks);
+    if (!std::isfinite(max_norm) || max_norm < 0)
+        return fail(FSDP_E_ARG, "%s: max_norm must be finite and >= 0", who);
+    if (!aligned(coef_out, 4) || !aligned(sqnorms, 8) || !aligned(norm_out, 8))
+        return fail(FSDP_E_ALIGN, "%s: buffer not aligned to its element size", who);
+    std::vector<fsdp::Range> rs{range_of(coef_out, 1, 4, true, 0, "coef_out"),
+                                range_of(sqnorms, n_ranks, 8, false, 0, "sqnorms")};
+    if (norm_out) rs.push_back(range_of(norm_out, 1, 8, true, 0, "norm_out"));
+    int32_t st;
+    if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
+    hipLaunchKernelGGL(clip_coef_kernel, dim3(1), dim3(64), 0, stream, coef_out, norm_out, sqnorms,
+                       n_ranks, max_norm);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                        const float* grad_scale, hipStream_t stream) {
+    const char* who = "fsdp_mt_step_clipped";
+    if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
+    int32_t st;
+    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    if (!grad_scale) return fail(FSDP_E_ARG, "%s: null grad_scale", who);
+    if (!aligned(grad_scale, 4)) return fail(FSDP_E_ALIGN, "%s: grad_scale misaligned", who);
+    if (!plan->all_grad_out)
+        return fail(FSDP_E_ARG, "%s: every shard of the plan needs a grad_shard_out", who);
+    if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    if (plan->n_chunks == 0) return FSDP_OK;
+    const StepConsts c = make_consts(hp, plan->n_slices);
+    hipLaunchKernelGGL(mt_scaled_step_kernel, dim3(static_cast<uint32_t>(plan->n_blocks)),
+                       dim3(kBlock), 0, stream, plan->d_tensors, plan->d_chunks, plan->n_chunks,
+                       plan->cpb, c, grad_scale);
     return launch_status(who);
 }
 
@@ -953,10 +1234,11 @@ extern "C" int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_
 extern "C" int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan) {
     if (!plan) return FSDP_OK;
     hipError_t e = hipSuccess;
-    if (plan->d_tensors || plan->d_chunks) {
+    if (plan->d_tensors || plan->d_chunks || plan->d_partials) {
         e = hipDeviceSynchronize();
         if (plan->d_tensors) (void)hipFree(plan->d_tensors);
         if (plan->d_chunks) (void)hipFree(plan->d_chunks);
+        if (plan->d_partials) (void)hipFree(plan->d_partials);
     }
     delete plan;
     if (e != hipSuccess) return fail(FSDP_E_HIP, "fsdp_mt_plan_destroy: %s", hipGetErrorString(e));

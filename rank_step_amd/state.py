@@ -64,13 +64,13 @@ class RankState:
         """Fill the slice buffer with step ``step``'s seeded gradients."""
         grad_slices(self.w, self.total, step, self.rank, self.device, out=self.slices)
 
-    def mt_tensors(self):
+    def mt_tensors(self, with_grad_out=True):
         es = self.slices.element_size()
         base = {
             "param": self.master.data_ptr(), "m": self.exp_avg.data_ptr(),
             "v": self.exp_avg_sq.data_ptr(), "s": self.slices.data_ptr(),
             "ag": self.ag_slot.data_ptr() if self.ag_slot is not None else None,
-            "g": self.grad_out.data_ptr() if self.grad_out is not None else None,
+            "g": self.grad_out.data_ptr() if (self.grad_out is not None and with_grad_out) else None,
         }
         out = []
         for off, length, held, _ in self.segments:
@@ -87,8 +87,9 @@ class RankState:
             })
         return out
 
-    def make_plan(self, stream=None):
-        self.plan = binding.MtPlan(self.mt_tensors(), self.w.n_slices, self.w.slice_dtype, stream)
+    def make_plan(self, stream=None, with_grad_out=True):
+        self.plan = binding.MtPlan(self.mt_tensors(with_grad_out), self.w.n_slices,
+                                   self.w.slice_dtype, stream)
         return self.plan
 
     def step(self, t, stream=None):

@@ -208,3 +208,18 @@ def test_mt_step_and_destroy_null():
     assert B.lib().fsdp_mt_step(None, None, None) == -1
     assert B.lib().fsdp_mt_plan_destroy(None) == 0
     assert B.lib().fsdp_mt_plan_get_info(None, None) == -1
+
+
+def test_clip_argument_checks():
+    f = B.fsdp_clip_coef
+    assert _err(f, None, None, A, 1, 1.0, stream=0) == "ARG"
+    assert _err(f, Bp, None, None, 1, 1.0, stream=0) == "ARG"
+    assert _err(f, Bp, None, A, 0, 1.0, stream=0) == "ARG"
+    assert _err(f, Bp, None, A, 4, float("nan"), stream=0) == "ARG"
+    assert _err(f, Bp, None, A, 4, -1.0, stream=0) == "ARG"
+    assert _err(f, Bp + 2, None, A, 4, 1.0, stream=0) == "ALIGN"
+    assert _err(f, Bp, C + 4, A, 4, 1.0, stream=0) == "ALIGN"
+    assert _err(f, A + 8, None, A, 4, 1.0, stream=0) == "ALIAS"     # coef inside the sums
+    assert _err(f, Bp, Bp, A, 4, 1.0, stream=0) == "ALIAS"          # both outputs at one address
+    assert B.lib().fsdp_mt_reduce_sqnorm(None, A, None) == -1
+    assert B.lib().fsdp_mt_step_clipped(None, None, A, None) == -1
