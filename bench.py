@@ -153,6 +153,45 @@ def clipped_step(st, stream, args, t0):
             "coef": float(coef.item()), "launches": 4}
 
 
+def fp8_step(st, stream, args, t0):
+    """Time the step with an fp8 all-gather copy instead of the bf16 one:
+    the fused step with per-tensor amax (2N+24 B/param), then the cast with
+    per-tensor scales (4+1 B/param)."""
+    import torch
+    from rank_step_amd import binding as B
+
+    w = st.w
+    plan = B.MtPlan(st.mt_tensors(with_grad_out=False, with_bf16=False, with_fp8=True), w.n_slices,
+                    w.slice_dtype, stream)
+    n = len(st.segments)
+    amax = torch.zeros(n, dtype=torch.float32, device=st.device)
+    scale = torch.zeros(n, dtype=torch.float32, device=st.device)
+
+    def one(t):
+        plan.step_amax(w.hparams, t, amax, stream)
+        plan.cast_fp8(amax, 1, scale, stream)
+
+    t = t0
+    for _ in range(args.warmup):
+        t += 1
+        one(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        t += 1
+        one(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    plan.close()
+    slice_b = 2 if w.slice_dtype == "bf16" else 4
+    bpp = w.n_slices * slice_b + 24 + 4 + 1
+    return {"ms_per_step": ms, "params_per_s": st.total / (ms / 1e3), "bytes_per_param": bpp,
+            "hbm_gb_s": bpp * st.total / (ms / 1e3) / 1e9, "launches": 3,
+            "all_gather_bytes_per_param": 1}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +204,8 @@ def main():
                     help="also time the clipped step (global grad-norm clipping) with this max_norm")
     ap.add_argument("--no-clip", dest="clip", action="store_const", const=None,
                     help="do not time the clipped step")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="do not time the step with the fp8 all-gather copy")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the step, run torch copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -206,9 +247,10 @@ def main():
 
     w = WORKLOADS[WORKLOAD_BY_NAME[args.workload]]
     bf16_out = w.bf16_out
-    st = RankState(w, 0, dev, bf16_out=bf16_out, grad_out=args.clip is not None)
+    st = RankState(w, 0, dev, bf16_out=bf16_out, grad_out=args.clip is not None,
+                   fp8_out=not args.no_fp8)
     st.load_grads(1)
-    st.make_plan(stream, with_grad_out=False)
+    st.make_plan(stream, with_grad_out=False, with_fp8=False)
     info = st.plan.info()
     total = st.total
     bpp = bytes_per_param(w, bf16_out)
@@ -274,6 +316,8 @@ def main():
     }
     if args.clip is not None:
         out["clipped_step"] = clipped_step(st, stream, args, t)
+    if not args.no_fp8:
+        out["fp8_step"] = fp8_step(st, stream, args, t)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, t + 1)
     st.close()

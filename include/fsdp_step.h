@@ -205,7 +205,9 @@ int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const float* param_fp
  *   grad_slices, slice_stride        as in fsdp_reduce_grad_shard
  *   unshard_bf16_out                 device bf16 [shard_numel] or NULL (no cast)
  *   grad_shard_out                   device fp32 [shard_numel] or NULL (the
- *                                    reduced gradient is not stored) */
+ *                                    reduced gradient is not stored)
+ *   unshard_fp8_out                  device fp8 codes [shard_numel] or NULL:
+ *                                    written only by fsdp_mt_cast_fp8 */
 typedef struct {
     float* param_fp32;
     float* exp_avg;
@@ -216,6 +218,7 @@ typedef struct {
     float* grad_shard_out;
     int64_t shard_numel;
     int64_t valid;
+    uint8_t* unshard_fp8_out;     /* NULL => no fp8 copy (see fsdp_mt_cast_fp8) */
 } fsdp_mt_tensor;
 
 typedef struct fsdp_mt_plan fsdp_mt_plan; /* opaque */
@@ -294,6 +297,40 @@ int32_t fsdp_clip_coef(float* coef_out, double* norm_out, const double* sqnorms,
  * buffers are read, not written.  One kernel launch. */
 int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                              const float* grad_scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------ fp8 all-gather copy */
+
+/* fp8 all-gather copy of the updated shards with a per-tensor scale,
+ * [FSDP ch.18] §18.27: an fp8 all-gather moves half the bytes of a bf16 one,
+ * but fp8's range is narrow, so every tensor carries its own scale with the
+ * quantised data.  The page gives no recipe; the one taken is dynamic
+ * per-tensor scaling over the whole tensor (all ranks' shards) in OCP FP8
+ * E4M3 ("e4m3fn": bias 7, 3 fraction bits, largest finite 448, no inf):
+ *   amax  = max |p| over tensor i on every rank (NaN propagates)
+ *   scale = 448 / max(amax, 1e-12)                       (fp32)
+ *   code  = RNE_e4m3(clamp(fp32(p * scale), -448, 448)), 0 in the padding
+ * A consumer recovers p ~ value(code) / scale.  Sequence:
+ *   fsdp_mt_step_amax   the fused step, plus each tensor's local amax of the
+ *                       updated parameter (no extra pass over memory)
+ *   (all-reduce max of the per-rank amax arrays: outside this library)
+ *   fsdp_mt_cast_fp8    reads the updated fp32 shards, writes the codes */
+
+/* The step of fsdp_mt_step (same outputs, bit-identical), and for every
+ * shard i of the plan, in input order, the largest |p'| of its updated local
+ * shard to amax_out[i] (device fp32 [n_tensors]; 0 for an empty shard; NaN if
+ * any updated value is NaN).  The plan must have at least one fp8 output.
+ * Uses the plan's per-chunk scratch: calls on one plan must not overlap. */
+int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, float* amax_out,
+                          hipStream_t stream);
+
+/* Write every shard's fp8 codes from its updated fp32 parameter.  The amax
+ * of shard i is the maximum over r of amax_ranks[r * n_tensors + i] (device
+ * fp32 [n_ranks][n_tensors]: the ranks' fsdp_mt_step_amax outputs, or one
+ * row that an all-reduce max already combined).  scale_out: device fp32
+ * [n_tensors] for the scales, or NULL.  Every non-empty shard must have an
+ * unshard_fp8_out (else FSDP_E_ARG).  One kernel launch. */
+int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_ranks,
+                         float* scale_out, hipStream_t stream);
 
 /* Sizes of a plan (host only). */
 int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info_out);

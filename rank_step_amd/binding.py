@@ -30,7 +30,8 @@ LAYOUTS = {"flat": 0, "shard0": 1}
 EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
            "fsdp_adamw_shard_step", "fsdp_cast_unshard_bf16", "fsdp_mt_plan_create",
            "fsdp_mt_step", "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy",
-           "fsdp_mt_reduce_sqnorm", "fsdp_clip_coef", "fsdp_mt_step_clipped")
+           "fsdp_mt_reduce_sqnorm", "fsdp_clip_coef", "fsdp_mt_step_clipped",
+           "fsdp_mt_step_amax", "fsdp_mt_cast_fp8")
 
 
 class FsdpError(RuntimeError):
@@ -67,7 +68,7 @@ class MtTensor(ctypes.Structure):
                 ("exp_avg_sq", ctypes.c_void_p), ("grad_slices", ctypes.c_void_p),
                 ("slice_stride", ctypes.c_int64), ("unshard_bf16_out", ctypes.c_void_p),
                 ("grad_shard_out", ctypes.c_void_p), ("shard_numel", ctypes.c_int64),
-                ("valid", ctypes.c_int64)]
+                ("valid", ctypes.c_int64), ("unshard_fp8_out", ctypes.c_void_p)]
 
 
 class MtPlanInfo(ctypes.Structure):
@@ -108,6 +109,8 @@ def lib():
             "fsdp_mt_reduce_sqnorm": [vp, vp, vp],
             "fsdp_clip_coef": [vp, vp, vp, i32, ctypes.c_double, vp],
             "fsdp_mt_step_clipped": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
+            "fsdp_mt_step_amax": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
+            "fsdp_mt_cast_fp8": [vp, vp, i32, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -196,7 +199,7 @@ def fsdp_mt_plan_create(tensors, n_slices, slice_dtype, stream=None):
         arr[i] = MtTensor(_ptr(t["param_fp32"]), _ptr(t["exp_avg"]), _ptr(t["exp_avg_sq"]),
                           _ptr(t.get("grad_slices")), int(t.get("slice_stride", 0)),
                           _ptr(t.get("unshard_bf16_out")), _ptr(t.get("grad_shard_out")),
-                          int(t["shard_numel"]), int(t["valid"]))
+                          int(t["shard_numel"]), int(t["valid"]), _ptr(t.get("unshard_fp8_out")))
     h = ctypes.c_void_p()
     _check(lib().fsdp_mt_plan_create(ctypes.byref(h), arr, n, int(n_slices), _dtype(slice_dtype),
                                      _stream(stream)))
@@ -232,6 +235,16 @@ def fsdp_mt_step_clipped(plan, hp, step, grad_scale, stream=None):
     _check(lib().fsdp_mt_step_clipped(plan, ctypes.byref(h), _ptr(grad_scale), _stream(stream)))
 
 
+def fsdp_mt_step_amax(plan, hp, step, amax_out, stream=None):
+    h = _hparams(hp, step)
+    _check(lib().fsdp_mt_step_amax(plan, ctypes.byref(h), _ptr(amax_out), _stream(stream)))
+
+
+def fsdp_mt_cast_fp8(plan, amax_ranks, n_ranks, scale_out=None, stream=None):
+    _check(lib().fsdp_mt_cast_fp8(plan, _ptr(amax_ranks), int(n_ranks), _ptr(scale_out),
+                                  _stream(stream)))
+
+
 class MtPlan:
     """Owns one fsdp_mt_plan handle (and keeps the Python objects whose
     buffers it references alive)."""
@@ -251,6 +264,12 @@ class MtPlan:
 
     def step_clipped(self, hp, step, grad_scale, stream=None):
         fsdp_mt_step_clipped(self.handle, hp, step, grad_scale, stream)
+
+    def step_amax(self, hp, step, amax_out, stream=None):
+        fsdp_mt_step_amax(self.handle, hp, step, amax_out, stream)
+
+    def cast_fp8(self, amax_ranks, n_ranks, scale_out=None, stream=None):
+        fsdp_mt_cast_fp8(self.handle, amax_ranks, n_ranks, scale_out, stream)
 
     def close(self):
         if self.handle is not None:

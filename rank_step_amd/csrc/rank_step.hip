@@ -82,6 +82,7 @@ constexpr int64_t kChunk = int64_t(RS_CHUNK_TILES) * kTile;  // elements per chu
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // One shard as the kernels see it.  Copied to LDS as 8-byte words.
 struct TensorDesc {
@@ -91,10 +92,12 @@ struct TensorDesc {
     const void* slices;
     uint16_t* out_bf16;  // null: no cast
     float* grad_out;     // null: reduced gradient not stored
+    uint8_t* out_fp8;    // null: no fp8 copy
     int64_t slice_stride;
     int64_t shard_numel;
     int64_t valid;
-    int64_t vec_ok;      // every buffer 16-byte aligned, slice stride a multiple of 16 bytes
+    int64_t vec_ok;      // every buffer aligned for the vector path (16 B; fp8 copy 8 B)
+    int64_t index;       // position of the shard in the plan's input list
 };
 constexpr int kDescWords = sizeof(TensorDesc) / 8;
 static_assert(sizeof(TensorDesc) % 8 == 0, "descriptor is copied as 8-byte words");
@@ -296,9 +299,12 @@ __device__ __forceinline__ void load_state(StateRegs& s, const TensorDesc& T, in
 
 // AdamW on a group and the stores of its results.  WRITE_G: also store the
 // reduced gradient when the shard has a grad_shard_out.
-template <bool WRITE_G = true>
+// AMAX: also fold |p'| of the group into *amax (fp32 bit patterns of
+// non-negative values order like the values; NaN patterns sort above all).
+template <bool WRITE_G = true, bool AMAX = false>
 __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup],
-                                             const TensorDesc& T, int64_t e, const StepConsts& c) {
+                                             const TensorDesc& T, int64_t e, const StepConsts& c,
+                                             uint32_t* amax = nullptr) {
     uint32_t b[kGroup];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -310,6 +316,7 @@ __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup]
             s.m[h][j] = m;
             s.v[h][j] = v;
             b[4 * h + j] = bf16_rne(p);
+            if constexpr (AMAX) *amax = std::max(*amax, __float_as_uint(p) & 0x7fffffffu);
         }
     }
     f32x4* p = reinterpret_cast<f32x4*>(T.param + e);
@@ -353,12 +360,14 @@ __device__ __forceinline__ float reduce_elem(const TensorDesc& T, int64_t k, con
 }
 
 // The whole fused step on element k (any alignment); +0 everywhere in the pad.
-template <bool BF16>
-__device__ __forceinline__ void fused_elem(const TensorDesc& T, int64_t k, const StepConsts& c) {
+template <bool BF16, bool AMAX = false>
+__device__ __forceinline__ void fused_elem(const TensorDesc& T, int64_t k, const StepConsts& c,
+                                           uint32_t* amax = nullptr) {
     if (k < T.valid) {
         const float g = reduce_elem<BF16>(T, k, c);
         float p = ld(T.param + k), m = ld(T.m + k), v = ld(T.v + k);
         adamw(p, m, v, g, c);
+        if constexpr (AMAX) *amax = std::max(*amax, __float_as_uint(p) & 0x7fffffffu);
         st(T.param + k, p);
         st(T.m + k, m);
         st(T.v + k, v);
@@ -398,9 +407,9 @@ __device__ __forceinline__ void scaled_elem(const TensorDesc& T, int64_t k, floa
 // The fused step on elements [begin, end) of shard T.  `begin` is a multiple
 // of kGroup.  Whole groups below `valid` take the vector path; the rest (the
 // partial group at `valid`, the padding, misaligned shards) go element by element.
-template <int NS, bool BF16, int UNROLL>
+template <int NS, bool BF16, int UNROLL, bool AMAX = false>
 __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, int64_t end,
-                                            const StepConsts& c) {
+                                            const StepConsts& c, uint32_t* amax = nullptr) {
     int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
     vend = std::max(vend, begin);
     const int64_t g1 = vend / kGroup;
@@ -419,7 +428,7 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
             for (int u = 0; u < UNROLL; ++u) {
                 float gr[kGroup];
                 reduce_regs<NS, BF16>(sr[u], gr, c);
-                update_store(st[u], gr, T, (g + u * kBlock) * kGroup, c);
+                update_store<true, AMAX>(st[u], gr, T, (g + u * kBlock) * kGroup, c, amax);
             }
         }
         for (; g < g1; g += kBlock) {
@@ -430,7 +439,7 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
             load_state(st, T, e);
             float gr[kGroup];
             reduce_regs<NS, BF16>(sr, gr, c);
-            update_store(st, gr, T, e, c);
+            update_store<true, AMAX>(st, gr, T, e, c, amax);
         }
     } else {
         for (; g < g1; g += kBlock) {
@@ -439,10 +448,10 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
             load_state(st, T, e);
             float gr[kGroup];
             reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
-            update_store(st, gr, T, e, c);
+            update_store<true, AMAX>(st, gr, T, e, c, amax);
         }
     }
-    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) fused_elem<BF16>(T, k, c);
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) fused_elem<BF16, AMAX>(T, k, c, amax);
 }
 
 // Reduce only: grad_out = mean of the slices on [begin, end).
@@ -526,6 +535,54 @@ __device__ __forceinline__ void scaled_range(const TensorDesc& T, int64_t begin,
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) scaled_elem(T, k, scale, c);
 }
 
+// fp32 -> OCP FP8 E4M3 ("e4m3fn": bias 7, 3 fraction bits, largest finite
+// 448, no infinities), round to nearest with ties to even.  The input is
+// already within [-448, 448] or NaN.  Normal results: round the fp32
+// fraction to 3 bits (the carry may raise the exponent) and rebias the
+// exponent from 127 to 7.  Below 2^-6 the grid is 2^-9: scale by 2^9 (exact)
+// and round to an integer.  NaN becomes S.1111.111.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t ua = u & 0x7fffffffu;
+    const float a = __uint_as_float(ua);
+    const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+    const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);
+    const uint32_t nrm = (r >> 20) - (120u << 3);
+    const uint32_t code = ua > 0x7f800000u ? 0x7fu : (a < 0.015625f ? sub : nrm);
+    return sign | code;
+}
+
+// The fp8 code of one updated value: the product with the tensor's scale in
+// fp32, clamped to +-448 (NaN kept), rounded once.
+__device__ __forceinline__ uint32_t fp8_code(float p, float scale) {
+    float y = p * scale;
+    y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
+    return e4m3_rne(y);
+}
+
+// fp8 copy of the updated shard on [begin, end); codes 0 in the pad.
+__device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, int64_t end,
+                                          float scale) {
+    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
+    vend = std::max(vend, begin);
+    const int64_t g1 = vend / kGroup;
+    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
+        const int64_t e = g * kGroup;
+        const f32x4* p = reinterpret_cast<const f32x4*>(T.param + e);
+        const f32x4 a = ld_state(p), b = ld_state(p + 1);
+        u32x2 o;
+        o[0] = fp8_code(a[0], scale) | (fp8_code(a[1], scale) << 8) |
+               (fp8_code(a[2], scale) << 16) | (fp8_code(a[3], scale) << 24);
+        o[1] = fp8_code(b[0], scale) | (fp8_code(b[1], scale) << 8) |
+               (fp8_code(b[2], scale) << 16) | (fp8_code(b[3], scale) << 24);
+        st_out(reinterpret_cast<u32x2*>(T.out_fp8 + e), o);
+    }
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
+        st(T.out_fp8 + k, k < T.valid ? static_cast<uint8_t>(fp8_code(ld(T.param + k), scale))
+                                      : uint8_t(0));
+}
+
 // Cast only: out_bf16 = RNE(param) on [begin, end).
 __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, int64_t end) {
     int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
@@ -561,7 +618,7 @@ __device__ __forceinline__ int64_t logical_block() {
     return b;
 }
 
-// Runs f(T, begin, end) for each chunk entry of this workgroup:
+// Runs f(T, begin, end, chunk index) for each chunk entry of this workgroup:
 // entries [b*cpb, min((b+1)*cpb, n_chunks)) of the chunk-descriptor table,
 // each naming a shard and an element range of it.
 template <typename F>
@@ -591,14 +648,14 @@ __device__ __forceinline__ void for_my_chunks(const TensorDesc* __restrict__ ten
                     uniform64(reinterpret_cast<const uint64_t*>(&s_desc[i])[j]);
             const int64_t begin = static_cast<int64_t>(uniform64(s_chunk[i].begin));
             const int64_t count = __builtin_amdgcn_readfirstlane(s_chunk[i].count);
-            f(T, begin, begin + count);
+            f(T, begin, begin + count, first + i);
         }
     } else {
         // Uniform addresses: the entries and descriptors arrive by scalar loads.
         for (int i = 0; i < cnt; ++i) {
             const ChunkDesc cd = chunks[first + i];
             const TensorDesc T = tensors[cd.tensor];
-            f(T, cd.begin, cd.begin + cd.count);
+            f(T, cd.begin, cd.begin + cd.count, first + i);
         }
     }
 }
@@ -615,6 +672,21 @@ __device__ __forceinline__ double block_sum(double x) {
     double t = 0.0;
     if (threadIdx.x == 0)
         for (int w = 0; w < kBlock / 64; ++w) t += s_wave[w];
+    __syncthreads();
+    return t;
+}
+
+// Maximum of a value over the workgroup; the result is valid in thread 0.
+__device__ __forceinline__ uint32_t block_max(uint32_t x) {
+    __shared__ uint32_t s_wave_max[kBlock / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = std::max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), off)));
+    if ((threadIdx.x & 63) == 0) s_wave_max[threadIdx.x / 64] = x;
+    __syncthreads();
+    uint32_t t = 0;
+    if (threadIdx.x == 0)
+        for (int w = 0; w < kBlock / 64; ++w) t = std::max(t, s_wave_max[w]);
+    __syncthreads();
     return t;
 }
 
@@ -624,7 +696,7 @@ __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __res
                                                          const ChunkDesc* __restrict__ chunks,
                                                          int64_t n_chunks, int32_t cpb,
                                                          StepConsts c) {
-    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e) {
+    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
         fused_range<NS, BF16, UNROLL>(T, b, e, c);
     });
 }
@@ -637,7 +709,7 @@ __global__ __launch_bounds__(kBlock) void mt_reduce_sq_kernel(const TensorDesc* 
                                                               int64_t n_chunks, int32_t cpb,
                                                               StepConsts c, double* partials) {
     double acc = 0.0;
-    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e) {
+    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
         acc += reduce_sq_range<NS, BF16>(T, b, e, c);
     });
     const double total = block_sum(acc);
@@ -650,9 +722,65 @@ __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc
                                                                 int64_t n_chunks, int32_t cpb,
                                                                 StepConsts c, const float* scale) {
     const float k = *scale;
-    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e) {
+    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
         scaled_range(T, b, e, k, c);
     });
+}
+
+// The fused step that also records, per chunk entry, the largest |p'| (as
+// fp32 bits) for the fp8 copy's per-tensor scale.
+template <int NS, bool BF16>
+__global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* __restrict__ tensors,
+                                                              const ChunkDesc* __restrict__ chunks,
+                                                              int64_t n_chunks, int32_t cpb,
+                                                              StepConsts c, uint32_t* chunk_amax) {
+    for_my_chunks(tensors, chunks, n_chunks, cpb,
+                  [&](const TensorDesc& T, int64_t b, int64_t e, int64_t ci) {
+                      uint32_t am = 0;
+                      fused_range<NS, BF16, 1, true>(T, b, e, c, &am);
+                      const uint32_t bm = block_max(am);
+                      if (threadIdx.x == 0) st(chunk_amax + ci, bm);
+                  });
+}
+
+// First chunk entry and number of entries of each shard, by input position.
+struct ShardChunks {
+    int64_t first;
+    int64_t count;
+};
+
+// Workgroup i: amax_out[i] = max over shard i's chunk entries (0 if empty).
+__global__ __launch_bounds__(kBlock) void shard_amax_kernel(const ShardChunks* sc,
+                                                            const uint32_t* chunk_amax,
+                                                            float* amax_out) {
+    const ShardChunks r = sc[blockIdx.x];
+    uint32_t m = 0;
+    for (int64_t j = threadIdx.x; j < r.count; j += kBlock) m = std::max(m, ld(chunk_amax + r.first + j));
+    const uint32_t t = block_max(m);
+    if (threadIdx.x == 0) st(amax_out + blockIdx.x, __uint_as_float(t));
+}
+
+// fp8 copy of every shard: the tensor's amax is the maximum over the ranks'
+// values (amax_ranks[r * n_shards + index]; NaN propagates), its scale
+// 448 / max(amax, 1e-12) in fp32.  The workgroup holding a shard's first
+// chunk also stores the scale.
+__global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* __restrict__ tensors,
+                                                             const ChunkDesc* __restrict__ chunks,
+                                                             int64_t n_chunks, int32_t cpb,
+                                                             const float* amax_ranks, int32_t n_ranks,
+                                                             int64_t n_shards, float* scale_out) {
+    for_my_chunks(tensors, chunks, n_chunks, cpb,
+                  [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
+                      uint32_t bits = 0;
+                      for (int32_t r = 0; r < n_ranks; ++r)
+                          bits = std::max(bits, __float_as_uint(ld(amax_ranks + r * n_shards + T.index)) &
+                                                    0x7fffffffu);
+                      const float amax = __uint_as_float(bits);
+                      const float den = (amax > 1e-12f || amax != amax) ? amax : 1e-12f;
+                      const float scale = 448.0f / den;
+                      if (b == 0 && scale_out && threadIdx.x == 0) st(scale_out + T.index, scale);
+                      fp8_range(T, b, e, scale);
+                  });
 }
 
 constexpr int kSumBlocks = 1024;        // workgroups of the first summation stage
@@ -735,6 +863,19 @@ MtKernel pick_mt(int n) {
 
 using ReduceSqKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts,
                                 double*);
+using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts,
+                            uint32_t*);
+
+template <bool BF16>
+AmaxKernel pick_amax(int n) {
+    switch (n) {
+        case 1: return mt_step_amax_kernel<1, BF16>;
+        case 2: return mt_step_amax_kernel<2, BF16>;
+        case 4: return mt_step_amax_kernel<4, BF16>;
+        case 8: return mt_step_amax_kernel<8, BF16>;
+        default: return mt_step_amax_kernel<0, BF16>;
+    }
+}
 
 template <bool BF16>
 ReduceSqKernel pick_reduce_sq(int n) {
@@ -805,6 +946,7 @@ bool vec_ok(const TensorDesc& T, int32_t slice_dtype, int32_t n_slices) {
     if (n_slices > 1 && (T.slice_stride * dtype_bytes(slice_dtype)) % 16 != 0) return false;
     if (T.out_bf16 && !aligned(T.out_bf16, 16)) return false;
     if (T.grad_out && !aligned(T.grad_out, 16)) return false;
+    if (T.out_fp8 && !aligned(T.out_fp8, 8)) return false;
     return true;
 }
 
@@ -883,6 +1025,10 @@ struct fsdp_mt_plan {
     int64_t n_tensors = 0, n_chunks = 0, n_blocks = 0, total_numel = 0, total_valid = 0;
     int64_t chunk_numel = 0;
     bool all_grad_out = false;       // every non-empty shard stores its reduced gradient
+    bool any_fp8 = false;            // some shard has an fp8 copy
+    bool all_fp8 = false;            // every non-empty shard has one
+    uint32_t* d_chunk_amax = nullptr;   // fp8: largest |p'| per chunk entry
+    ShardChunks* d_shard_chunks = nullptr;  // fp8: each input shard's run of chunk entries
     TensorDesc* d_tensors = nullptr;
     ChunkDesc* d_chunks = nullptr;
     double* d_partials = nullptr;    // clipped steps: one sum of squares per workgroup,
@@ -1022,6 +1168,8 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
     std::vector<TensorDesc> descs;
     descs.reserve(static_cast<size_t>(n_tensors));
     bool all_grad_out = true;
+    bool any_fp8 = false, all_fp8 = true;
+    std::vector<int32_t> first_desc(static_cast<size_t>(n_tensors), -1);
     std::vector<fsdp::Range> rs;
     int64_t total = 0, total_valid = 0;
     for (int32_t i = 0; i < n_tensors; ++i) {
@@ -1041,8 +1189,11 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
         if (!fsdp::add_i64(total, t.shard_numel, &total))
             return fail(FSDP_E_ARG, "%s: total size overflows", who);
         total_valid += t.valid;
+        if (t.unshard_fp8_out) any_fp8 = true;
         if (t.shard_numel == 0) continue;
         if (!t.grad_shard_out) all_grad_out = false;
+        if (!t.unshard_fp8_out) all_fp8 = false;
+        first_desc[i] = static_cast<int32_t>(descs.size());
         rs.push_back(range_of(t.param_fp32, t.shard_numel, 4, true, i, "param"));
         rs.push_back(range_of(t.exp_avg, t.shard_numel, 4, true, i, "exp_avg"));
         rs.push_back(range_of(t.exp_avg_sq, t.shard_numel, 4, true, i, "exp_avg_sq"));
@@ -1050,6 +1201,8 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
             rs.push_back(range_of(t.unshard_bf16_out, t.shard_numel, 2, true, i, "unshard_bf16_out"));
         if (t.grad_shard_out)
             rs.push_back(range_of(t.grad_shard_out, t.shard_numel, 4, true, i, "grad_shard_out"));
+        if (t.unshard_fp8_out)
+            rs.push_back(range_of(t.unshard_fp8_out, t.shard_numel, 1, true, i, "unshard_fp8_out"));
         add_slice_ranges(rs, t.grad_slices, slice_dtype, t.slice_stride, n_slices, t.valid, i);
         TensorDesc d{};
         d.param = t.param_fp32;
@@ -1058,6 +1211,8 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
         d.slices = t.grad_slices;
         d.out_bf16 = t.unshard_bf16_out;
         d.grad_out = t.grad_shard_out;
+        d.out_fp8 = t.unshard_fp8_out;
+        d.index = i;
         d.slice_stride = t.slice_stride;
         d.shard_numel = t.shard_numel;
         d.valid = t.valid;
@@ -1073,7 +1228,10 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
     // group-aligned; short-lived single-tile workgroups stream best on MI355X.
     const int64_t chunk = kChunk;
     std::vector<ChunkDesc> chunks;
+    std::vector<ShardChunks> runs(static_cast<size_t>(n_tensors), ShardChunks{0, 0});
     for (size_t i = 0; i < descs.size(); ++i) {
+        runs[static_cast<size_t>(descs[i].index)].first = static_cast<int64_t>(chunks.size());
+        runs[static_cast<size_t>(descs[i].index)].count = (descs[i].shard_numel + chunk - 1) / chunk;
         for (int64_t b = 0; b < descs[i].shard_numel; b += chunk) {
             ChunkDesc cd{};
             cd.begin = b;
@@ -1099,7 +1257,18 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
     plan->total_valid = total_valid;
     plan->chunk_numel = chunk;
     plan->all_grad_out = all_grad_out;
+    plan->any_fp8 = any_fp8;
+    plan->all_fp8 = all_fp8;
     hipError_t e = hipGetDevice(&plan->device);
+    if (e == hipSuccess && any_fp8 && n_tensors > 0) {
+        e = hipMalloc(reinterpret_cast<void**>(&plan->d_shard_chunks), runs.size() * sizeof(ShardChunks));
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(plan->d_shard_chunks, runs.data(), runs.size() * sizeof(ShardChunks),
+                               hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess && !chunks.empty())
+            e = hipMalloc(reinterpret_cast<void**>(&plan->d_chunk_amax), chunks.size() * sizeof(uint32_t));
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    }
     if (e == hipSuccess && !chunks.empty()) {
         e = hipMalloc(reinterpret_cast<void**>(&plan->d_tensors), descs.size() * sizeof(TensorDesc));
         if (e == hipSuccess)
@@ -1218,6 +1387,58 @@ extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hpa
     return launch_status(who);
 }
 
+extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                     float* amax_out, hipStream_t stream) {
+    const char* who = "fsdp_mt_step_amax";
+    if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
+    int32_t st;
+    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    if (!plan->any_fp8) return fail(FSDP_E_ARG, "%s: the plan has no fp8 outputs", who);
+    if (!amax_out) return fail(FSDP_E_ARG, "%s: null amax_out", who);
+    if (!aligned(amax_out, 4)) return fail(FSDP_E_ALIGN, "%s: amax_out misaligned", who);
+    if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    if (plan->n_tensors == 0) return FSDP_OK;
+    if (plan->n_chunks > 0) {
+        const StepConsts c = make_consts(hp, plan->n_slices);
+        const AmaxKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_amax<true>(plan->n_slices)
+                                                               : pick_amax<false>(plan->n_slices);
+        hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), 0, stream,
+                           plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb, c,
+                           plan->d_chunk_amax);
+        if ((st = launch_status(who)) != FSDP_OK) return st;
+    }
+    hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kBlock),
+                       0, stream, static_cast<const ShardChunks*>(plan->d_shard_chunks),
+                       static_cast<const uint32_t*>(plan->d_chunk_amax), amax_out);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_ranks,
+                                    float* scale_out, hipStream_t stream) {
+    const char* who = "fsdp_mt_cast_fp8";
+    if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
+    if (!plan->all_fp8) return fail(FSDP_E_ARG, "%s: every shard of the plan needs an fp8 output", who);
+    if (n_ranks < 1 || n_ranks > (1 << 20))
+        return fail(FSDP_E_ARG, "%s: n_ranks %d outside [1, 2^20]", who, n_ranks);
+    if (plan->n_tensors > 0 && !amax_ranks) return fail(FSDP_E_ARG, "%s: null amax_ranks", who);
+    if (!aligned(amax_ranks, 4) || !aligned(scale_out, 4))
+        return fail(FSDP_E_ALIGN, "%s: buffer not aligned to its element size", who);
+    if (scale_out && amax_ranks) {
+        std::vector<fsdp::Range> rs{range_of(scale_out, plan->n_tensors, 4, true, 0, "scale_out"),
+                                    range_of(amax_ranks, plan->n_tensors * n_ranks, 4, false, 0,
+                                             "amax_ranks")};
+        int32_t st;
+        if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
+    }
+    int32_t st;
+    if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    if (plan->n_chunks == 0) return FSDP_OK;
+    hipLaunchKernelGGL(mt_cast_fp8_kernel, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+                       0, stream, plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb,
+                       amax_ranks, n_ranks, plan->n_tensors, scale_out);
+    return launch_status(who);
+}
+
 extern "C" int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info) {
     if (!plan || !info) return fail(FSDP_E_ARG, "fsdp_mt_plan_get_info: null argument");
     info->n_tensors = plan->n_tensors;
@@ -1234,11 +1455,14 @@ extern "C" int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_
 extern "C" int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan) {
     if (!plan) return FSDP_OK;
     hipError_t e = hipSuccess;
-    if (plan->d_tensors || plan->d_chunks || plan->d_partials) {
+    if (plan->d_tensors || plan->d_chunks || plan->d_partials || plan->d_chunk_amax ||
+        plan->d_shard_chunks) {
         e = hipDeviceSynchronize();
         if (plan->d_tensors) (void)hipFree(plan->d_tensors);
         if (plan->d_chunks) (void)hipFree(plan->d_chunks);
         if (plan->d_partials) (void)hipFree(plan->d_partials);
+        if (plan->d_chunk_amax) (void)hipFree(plan->d_chunk_amax);
+        if (plan->d_shard_chunks) (void)hipFree(plan->d_shard_chunks);
     }
     delete plan;
     if (e != hipSuccess) return fail(FSDP_E_HIP, "fsdp_mt_plan_destroy: %s", hipGetErrorString(e));

@@ -24,7 +24,7 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 class RankState:
     def __init__(self, w, rank, device, bf16_out=True, grad_out=False, ag_full=False,
-                 garbage_pad=False):
+                 garbage_pad=False, fp8_out=False):
         self.w = w
         self.rank = rank
         self.device = device
@@ -58,18 +58,21 @@ class RankState:
             self.ag = torch.zeros(n_ag, dtype=torch.bfloat16, device=device)
             self.ag_slot = self.ag[rank * total:(rank + 1) * total] if ag_full else self.ag
         self.grad_out = torch.empty(total, **f32) if grad_out else None
+        # fp8 all-gather copy (this rank's slot), codes as bytes
+        self.fp8 = torch.zeros(total, dtype=torch.uint8, device=device) if fp8_out else None
         self.plan = None
 
     def load_grads(self, step):
         """Fill the slice buffer with step ``step``'s seeded gradients."""
         grad_slices(self.w, self.total, step, self.rank, self.device, out=self.slices)
 
-    def mt_tensors(self, with_grad_out=True):
+    def mt_tensors(self, with_grad_out=True, with_bf16=True, with_fp8=True):
         es = self.slices.element_size()
         base = {
             "param": self.master.data_ptr(), "m": self.exp_avg.data_ptr(),
             "v": self.exp_avg_sq.data_ptr(), "s": self.slices.data_ptr(),
-            "ag": self.ag_slot.data_ptr() if self.ag_slot is not None else None,
+            "ag": self.ag_slot.data_ptr() if (self.ag_slot is not None and with_bf16) else None,
+            "f8": self.fp8.data_ptr() if (self.fp8 is not None and with_fp8) else None,
             "g": self.grad_out.data_ptr() if (self.grad_out is not None and with_grad_out) else None,
         }
         out = []
@@ -82,14 +85,15 @@ class RankState:
                 "slice_stride": self.total,
                 "unshard_bf16_out": None if base["ag"] is None else base["ag"] + 2 * off,
                 "grad_shard_out": None if base["g"] is None else base["g"] + 4 * off,
+                "unshard_fp8_out": None if base["f8"] is None else base["f8"] + off,
                 "shard_numel": length,
                 "valid": held,
             })
         return out
 
-    def make_plan(self, stream=None, with_grad_out=True):
-        self.plan = binding.MtPlan(self.mt_tensors(with_grad_out), self.w.n_slices,
-                                   self.w.slice_dtype, stream)
+    def make_plan(self, stream=None, with_grad_out=True, with_bf16=True, with_fp8=True):
+        self.plan = binding.MtPlan(self.mt_tensors(with_grad_out, with_bf16, with_fp8),
+                                   self.w.n_slices, self.w.slice_dtype, stream)
         return self.plan
 
     def step(self, t, stream=None):
