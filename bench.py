@@ -192,6 +192,43 @@ def fp8_step(st, stream, args, t0):
             "all_gather_bytes_per_param": 1}
 
 
+def accumulation(st, stream, args):
+    """Time one micro-batch of gradient accumulation at the rank shard's size:
+    synchronised (reduce the N slices and add into the fp32 gradient shard,
+    2N+8 B/param) and no_sync (add one bf16 micro-batch into an fp32 gradient
+    buffer, 10 B/param; a rank's real unsharded buffer is N times longer)."""
+    import torch
+    from rank_step_amd import binding as B
+
+    w = st.w
+    plan = B.MtPlan(st.mt_tensors(with_grad_out=True), w.n_slices, w.slice_dtype, stream)
+    acc = torch.zeros(st.total, dtype=torch.float32, device=st.device)
+    micro = st.slices[0]
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_sync = timed(lambda: plan.reduce_accumulate(1, None, stream))
+    ms_nos = timed(lambda: B.fsdp_grad_accumulate(acc, micro, w.slice_dtype, st.total, 1, stream))
+    plan.close()
+    slice_b = 2 if w.slice_dtype == "bf16" else 4
+    b_sync = w.n_slices * slice_b + 8
+    b_nos = slice_b + 8
+    return {"synchronised": {"ms_per_micro_batch": ms_sync, "bytes_per_param": b_sync,
+                             "hbm_gb_s": b_sync * st.total / ms_sync / 1e6},
+            "no_sync": {"ms_per_micro_batch_per_shard_size": ms_nos, "bytes_per_param": b_nos,
+                        "hbm_gb_s": b_nos * st.total / ms_nos / 1e6}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +355,8 @@ def main():
         out["clipped_step"] = clipped_step(st, stream, args, t)
     if not args.no_fp8:
         out["fp8_step"] = fp8_step(st, stream, args, t)
+    if args.clip is not None:
+        out["grad_accumulation"] = accumulation(st, stream, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, t + 1)
     st.close()

@@ -99,10 +99,16 @@ typedef struct {
  * elements and the padding among them; bytes_param: local parameter bytes in
  * the parameters' dtypes; bytes_grad: the fp32 reduced-gradient shard;
  * bytes_optim: exp_avg + exp_avg_sq (fp32); bytes_master: fp32 master copy
- * (0 when has_master is 0).  All per rank, padding included. */
+ * (0 when has_master is 0).  All per rank, padding included.
+ * bytes_grad_unsharded: the fp32 gradient a rank holds while it accumulates
+ * micro-batches without reducing ([FSDP ch.18] §18.26 no_sync /
+ * set_requires_gradient_sync(False), §18.39: the unsharded gradient is the
+ * full size, N times the sharded one): the padded flat vector in FLAT mode,
+ * the full parameters in SHARD0 mode. */
 typedef struct {
     int64_t logical_numel, physical_numel, shard_numel, pad_numel;
     int64_t bytes_param, bytes_grad, bytes_optim, bytes_master;
+    int64_t bytes_grad_unsharded;
 } fsdp_layout_summary;
 
 /* Shard layout of `rank` among `world_size` ranks.  Host only: no device
@@ -291,12 +297,47 @@ int32_t fsdp_clip_coef(float* coef_out, double* norm_out, const double* sqnorms,
                        int32_t n_ranks, double max_norm, hipStream_t stream);
 
 /* Pass 2: AdamW and the bf16 cast on every shard of `plan`, from the reduced
- * gradient that fsdp_mt_reduce_sqnorm stored, multiplied in fp32 by
+ * gradient that fsdp_mt_reduce_sqnorm (or fsdp_mt_reduce_accumulate) stored
+ * in grad_shard_out, multiplied in fp32 by
  * *grad_scale (device fp32, e.g. fsdp_clip_coef's output).  With a scale of
  * exactly 1 the results are bit-identical to fsdp_mt_step's.  The gradient
  * buffers are read, not written.  One kernel launch. */
 int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                              const float* grad_scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------ gradient accumulation */
+
+/* Gradient accumulation over micro-batches, [FSDP ch.18] §18.26 and §18.39.
+ * Synchronised (the default): every micro-batch reduce-scatters and the
+ * reduced 1/N gradient accumulates in the shard:
+ *   fsdp_mt_reduce_accumulate(plan, 0, ...) on the first micro-batch,
+ *   fsdp_mt_reduce_accumulate(plan, 1, ...) on the others,
+ *   then fsdp_mt_step_clipped with a scale of 1 (or a clip coefficient).
+ * no_sync (set_requires_gradient_sync(False)): each rank accumulates its
+ * unsharded gradient in place with fsdp_grad_accumulate, and only the last
+ * micro-batch reduce-scatters the sums (which reach this rank as fp32
+ * slices for fsdp_mt_step).  Both give the shard sum_k (1/N) sum_q x_{q,k} up
+ * to rounding; no_sync holds the full-size gradient (bytes_grad_unsharded of
+ * the layout summary, N times the shard) and saves N-1 collectives. */
+
+/* For every shard of `plan`: grad_shard_out = mean of the slices
+ * (accumulate = 0) or grad_shard_out + mean of the slices (accumulate = 1;
+ * one fp32 add, old + new); the padding stays +0.  sqnorm_out (device fp64
+ * [1], or NULL): the rank's sum of squares of the stored values, as in
+ * fsdp_mt_reduce_sqnorm, for clipping the accumulated gradient.  Every
+ * non-empty shard needs a grad_shard_out.  Calls on one plan must not
+ * overlap. */
+int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumulate, double* sqnorm_out,
+                                  hipStream_t stream);
+
+/* In-place accumulation of one micro-batch's unsharded gradient:
+ *   acc[k] = acc[k] + x[k]   (accumulate = 1; one fp32 add)
+ *   acc[k] = x[k]            (accumulate = 0; exact copy of the widened value)
+ * acc: device fp32 [numel], read/written; micro: device [numel] of
+ * micro_dtype (fp32 or bf16, widened exactly), read.  They must not overlap.
+ * numel = 0 is a no-op. */
+int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t micro_dtype, int64_t numel,
+                             int32_t accumulate, hipStream_t stream);
 
 /* ------------------------------------------------------------------ fp8 all-gather copy */
 

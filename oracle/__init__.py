@@ -16,6 +16,10 @@ backward reduce-scatter and the next forward all-gather):
   round-to-nearest-even bf16 cast of the updated shard.  float64 throughout.
 * ``oracle.clip``    -- global gradient-norm clipping across the ranks'
   shards (squared norms summed over ranks, one coefficient for all).
+* ``oracle.fp8``     -- the fp8 (OCP E4M3) all-gather copy with per-tensor
+  dynamic scales.
+* ``oracle.accum``   -- gradient accumulation over micro-batches, with a
+  reduce-scatter every micro-batch or once at the end (no_sync).
 
 Sources (the pages this follows; cited by page title and section):
 
@@ -33,4 +37,4 @@ force; none is "parity unpinned" except where the function's docstring says
 so.
 """
 
-from . import clip, layout, step  # noqa: F401
+from . import accum, clip, fp8, layout, step  # noqa: F401

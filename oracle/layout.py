@@ -26,6 +26,8 @@ SHARD0 (FSDP-2 per-parameter Shard(0))
     rows (possibly all padding).
 
 Byte summary
+    FSDP chapter §18.39: while micro-batches accumulate under no_sync the
+    gradient stays unsharded, N times the size of the sharded one.
     ZeRO state sharding post, tables "Canonical ZeRO 状态公式" and "实测状态因子":
     at stage 3 every rank holds P/N parameters, P/N gradients and 2P/N
     optimizer state (fp32 AdamW: 4P/N bytes-worth in total), e.g. 32 / 32 /
@@ -80,6 +82,7 @@ class Summary:
     bytes_grad: int      # local fp32 gradient shard bytes (reduce dtype fp32)
     bytes_optim: int     # local exp_avg + exp_avg_sq bytes (fp32 each)
     bytes_master: int    # local fp32 master bytes (0 without a master copy)
+    bytes_grad_unsharded: int  # fp32 gradient held while accumulating without reducing
 
 
 def _ceil_div(a, b):
@@ -174,5 +177,8 @@ def layout(mode, world_size, rank, shapes, has_master):
         bytes_grad=4 * local,
         bytes_optim=8 * local,
         bytes_master=4 * local if has_master else 0,
+        # FSDP chapter §18.26 / §18.39: with no_sync the gradient stays
+        # unsharded -- the padded flat vector, or the full parameters
+        bytes_grad_unsharded=4 * (physical if mode == FLAT else P),
     )
     return views, summary

@@ -31,7 +31,8 @@ EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
            "fsdp_adamw_shard_step", "fsdp_cast_unshard_bf16", "fsdp_mt_plan_create",
            "fsdp_mt_step", "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy",
            "fsdp_mt_reduce_sqnorm", "fsdp_clip_coef", "fsdp_mt_step_clipped",
-           "fsdp_mt_step_amax", "fsdp_mt_cast_fp8")
+           "fsdp_mt_step_amax", "fsdp_mt_cast_fp8", "fsdp_mt_reduce_accumulate",
+           "fsdp_grad_accumulate")
 
 
 class FsdpError(RuntimeError):
@@ -54,7 +55,8 @@ class ShardView(ctypes.Structure):
 class LayoutSummary(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("logical_numel", "physical_numel", "shard_numel",
                                               "pad_numel", "bytes_param", "bytes_grad",
-                                              "bytes_optim", "bytes_master")]
+                                              "bytes_optim", "bytes_master",
+                                              "bytes_grad_unsharded")]
 
 
 class AdamWHparams(ctypes.Structure):
@@ -111,6 +113,8 @@ def lib():
             "fsdp_mt_step_clipped": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
             "fsdp_mt_step_amax": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
             "fsdp_mt_cast_fp8": [vp, vp, i32, vp, vp],
+            "fsdp_mt_reduce_accumulate": [vp, i32, vp, vp],
+            "fsdp_grad_accumulate": [vp, vp, i32, i64, i32, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -245,6 +249,16 @@ def fsdp_mt_cast_fp8(plan, amax_ranks, n_ranks, scale_out=None, stream=None):
                                   _stream(stream)))
 
 
+def fsdp_mt_reduce_accumulate(plan, accumulate, sqnorm_out=None, stream=None):
+    _check(lib().fsdp_mt_reduce_accumulate(plan, int(bool(accumulate)), _ptr(sqnorm_out),
+                                           _stream(stream)))
+
+
+def fsdp_grad_accumulate(acc, micro, micro_dtype, numel, accumulate, stream=None):
+    _check(lib().fsdp_grad_accumulate(_ptr(acc), _ptr(micro), _dtype(micro_dtype), int(numel),
+                                      int(bool(accumulate)), _stream(stream)))
+
+
 class MtPlan:
     """Owns one fsdp_mt_plan handle (and keeps the Python objects whose
     buffers it references alive)."""
@@ -264,6 +278,9 @@ class MtPlan:
 
     def step_clipped(self, hp, step, grad_scale, stream=None):
         fsdp_mt_step_clipped(self.handle, hp, step, grad_scale, stream)
+
+    def reduce_accumulate(self, accumulate, sqnorm_out=None, stream=None):
+        fsdp_mt_reduce_accumulate(self.handle, accumulate, sqnorm_out, stream)
 
     def step_amax(self, hp, step, amax_out, stream=None):
         fsdp_mt_step_amax(self.handle, hp, step, amax_out, stream)

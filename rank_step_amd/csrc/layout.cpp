@@ -136,6 +136,11 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
         return fail(FSDP_E_ARG, "byte counts overflow int64");
     s.bytes_grad = s.shard_numel * 4;
     s.bytes_master = has_master ? s.shard_numel * 4 : 0;
+    // no_sync accumulation holds the whole gradient: the padded flat vector
+    // (FLAT) or every full parameter (SHARD0), in fp32
+    const int64_t unsharded = mode == FSDP_LAYOUT_FLAT ? s.physical_numel : s.logical_numel;
+    if (!fsdp::mul_i64(unsharded, 4, &s.bytes_grad_unsharded))
+        return fail(FSDP_E_ARG, "byte counts overflow int64");
     for (int32_t i = 0; i < n_tensors; ++i) views_out[i] = views[i];
     if (summary_out) *summary_out = s;
     return FSDP_OK;

@@ -479,18 +479,27 @@ __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin,
         st(T.grad_out + k, k < T.valid ? reduce_elem<BF16>(T, k, c) : 0.0f);
 }
 
-// Reduce into grad_out on [begin, end) and return this thread's sum of the
-// squares of the reduced values, in fp64 (each fp32 square is exact in fp64).
-template <int NS, bool BF16>
-__device__ __forceinline__ double reduce_sq_range(const TensorDesc& T, int64_t begin, int64_t end,
-                                                  const StepConsts& c) {
-    double acc = 0.0;
+// Reduce into grad_out on [begin, end): with `acc` the mean of the slices
+// is added to what grad_out holds (one fp32 add, old + new: gradient
+// accumulation over micro-batches), else it replaces it.  SQ: return this
+// thread's sum of the squares of the stored values, in fp64 (each fp32
+// square is exact in fp64).  The padding is +0 either way.
+template <int NS, bool BF16, bool SQ>
+__device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_t begin,
+                                                     int64_t end, const StepConsts& c, bool acc) {
+    double sq = 0.0;
     int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
     vend = std::max(vend, begin);
     const int64_t g1 = vend / kGroup;
     for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
         const int64_t e = g * kGroup;
         float gr[kGroup];
+        f32x4 old0, old1;
+        f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
+        if (acc) {
+            old0 = ld_state(go);
+            old1 = ld_state(go + 1);
+        }
         if constexpr (NS > 0) {
             SliceRegs<NS, BF16> sr;
             load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
@@ -498,18 +507,73 @@ __device__ __forceinline__ double reduce_sq_range(const TensorDesc& T, int64_t b
         } else {
             reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
         }
-        f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
+        if (acc) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                gr[j] = old0[j] + gr[j];
+                gr[4 + j] = old1[j] + gr[4 + j];
+            }
+        }
         st_out(go, f32x4{gr[0], gr[1], gr[2], gr[3]});
         st_out(go + 1, f32x4{gr[4], gr[5], gr[6], gr[7]});
+        if constexpr (SQ) {
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) acc += static_cast<double>(gr[j]) * static_cast<double>(gr[j]);
+            for (int j = 0; j < kGroup; ++j) sq += static_cast<double>(gr[j]) * static_cast<double>(gr[j]);
+        }
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) {
-        const float gk = k < T.valid ? reduce_elem<BF16>(T, k, c) : 0.0f;
+        float gk = 0.0f;
+        if (k < T.valid) {
+            gk = reduce_elem<BF16>(T, k, c);
+            if (acc) gk = ld(T.grad_out + k) + gk;
+        }
         st(T.grad_out + k, gk);
-        acc += static_cast<double>(gk) * static_cast<double>(gk);
+        if constexpr (SQ) sq += static_cast<double>(gk) * static_cast<double>(gk);
     }
-    return acc;
+    return sq;
+}
+
+// In-place accumulation of one micro-batch's unsharded gradient, elements
+// [begin, end): acc = acc + x (fp32 add), or acc = x exactly for the first.
+template <bool BF16>
+__device__ __forceinline__ void accumulate_range(float* a, const void* x, int64_t begin,
+                                                 int64_t end, bool accum, bool vec) {
+    const int64_t vend = vec ? std::max(begin, end & ~int64_t(kGroup - 1)) : begin;
+    for (int64_t g = begin / kGroup + threadIdx.x; g < vend / kGroup; g += kBlock) {
+        const int64_t e = g * kGroup;
+        float xv[kGroup];
+        u32x4 w[2];
+        if constexpr (BF16) {
+            w[0] = ld_slice(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e));
+        } else {
+            const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e);
+            w[0] = ld_slice(p);
+            w[1] = ld_slice(p + 1);
+        }
+        f32x4* ap = reinterpret_cast<f32x4*>(a + e);
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+        if (accum) {
+            a0 = ld_state(ap);
+            a1 = ld_state(ap + 1);
+        }
+        widen<BF16>(w, xv);
+        if (accum) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a0[j] = a0[j] + xv[j];
+                a1[j] = a1[j] + xv[4 + j];
+            }
+        } else {
+            a0 = f32x4{xv[0], xv[1], xv[2], xv[3]};
+            a1 = f32x4{xv[4], xv[5], xv[6], xv[7]};
+        }
+        st_state(ap, a0);
+        st_state(ap + 1, a1);
+    }
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) {
+        const float xk = slice_elem<BF16>(x, k);
+        st(a + k, accum ? ld(a + k) + xk : xk);
+    }
 }
 
 // AdamW + cast on [begin, end) from the stored reduced gradient times `scale`.
@@ -701,19 +765,31 @@ __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __res
     });
 }
 
-// Pass 1 of a clipped step: reduce into grad_shard_out and write this
-// workgroup's sum of squares to partials[logical block].
-template <int NS, bool BF16>
-__global__ __launch_bounds__(kBlock) void mt_reduce_sq_kernel(const TensorDesc* __restrict__ tensors,
-                                                              const ChunkDesc* __restrict__ chunks,
-                                                              int64_t n_chunks, int32_t cpb,
-                                                              StepConsts c, double* partials) {
-    double acc = 0.0;
+// Reduce (or reduce and accumulate) into grad_shard_out; SQ: also write
+// this workgroup's sum of squares of the stored values to
+// partials[logical block].
+template <int NS, bool BF16, bool SQ>
+__global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDesc* __restrict__ tensors,
+                                                                 const ChunkDesc* __restrict__ chunks,
+                                                                 int64_t n_chunks, int32_t cpb,
+                                                                 StepConsts c, int32_t acc,
+                                                                 double* partials) {
+    double sq = 0.0;
     for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
-        acc += reduce_sq_range<NS, BF16>(T, b, e, c);
+        sq += reduce_store_range<NS, BF16, SQ>(T, b, e, c, acc != 0);
     });
-    const double total = block_sum(acc);
-    if (threadIdx.x == 0) st(partials + logical_block(), total);
+    if constexpr (SQ) {
+        const double total = block_sum(sq);
+        if (threadIdx.x == 0) st(partials + logical_block(), total);
+    }
+}
+
+// Workgroup b accumulates elements [b*kChunk, (b+1)*kChunk) of one buffer.
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(float* a, const void* x, int64_t n,
+                                                            int32_t accum, int32_t vec) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * kChunk;
+    accumulate_range<BF16>(a, x, begin, std::min(begin + kChunk, n), accum != 0, vec != 0);
 }
 
 // Pass 2 of a clipped step: AdamW and cast from grad_shard_out times *scale.
@@ -861,8 +937,25 @@ MtKernel pick_mt(int n) {
     }
 }
 
-using ReduceSqKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts,
-                                double*);
+using ReduceStoreKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t,
+                                   StepConsts, int32_t, double*);
+
+template <bool BF16, bool SQ>
+ReduceStoreKernel pick_reduce_store(int n) {
+    switch (n) {
+        case 1: return mt_reduce_store_kernel<1, BF16, SQ>;
+        case 2: return mt_reduce_store_kernel<2, BF16, SQ>;
+        case 4: return mt_reduce_store_kernel<4, BF16, SQ>;
+        case 8: return mt_reduce_store_kernel<8, BF16, SQ>;
+        default: return mt_reduce_store_kernel<0, BF16, SQ>;
+    }
+}
+
+ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq) {
+    if (dtype == FSDP_DT_BF16) return sq ? pick_reduce_store<true, true>(n) : pick_reduce_store<true, false>(n);
+    return sq ? pick_reduce_store<false, true>(n) : pick_reduce_store<false, false>(n);
+}
+
 using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts,
                             uint32_t*);
 
@@ -874,17 +967,6 @@ AmaxKernel pick_amax(int n) {
         case 4: return mt_step_amax_kernel<4, BF16>;
         case 8: return mt_step_amax_kernel<8, BF16>;
         default: return mt_step_amax_kernel<0, BF16>;
-    }
-}
-
-template <bool BF16>
-ReduceSqKernel pick_reduce_sq(int n) {
-    switch (n) {
-        case 1: return mt_reduce_sq_kernel<1, BF16>;
-        case 2: return mt_reduce_sq_kernel<2, BF16>;
-        case 4: return mt_reduce_sq_kernel<4, BF16>;
-        case 8: return mt_reduce_sq_kernel<8, BF16>;
-        default: return mt_reduce_sq_kernel<0, BF16>;
     }
 }
 
@@ -1309,26 +1391,28 @@ extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
 }
 
 
-extern "C" int32_t fsdp_mt_reduce_sqnorm(fsdp_mt_plan* plan, double* sqnorm_out,
-                                         hipStream_t stream) {
-    const char* who = "fsdp_mt_reduce_sqnorm";
+extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumulate,
+                                             double* sqnorm_out, hipStream_t stream) {
+    const char* who = "fsdp_mt_reduce_accumulate";
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
-    if (!sqnorm_out) return fail(FSDP_E_ARG, "%s: null sqnorm_out", who);
-    if (!aligned(sqnorm_out, 8)) return fail(FSDP_E_ALIGN, "%s: sqnorm_out not 8-byte aligned", who);
+    if (accumulate != 0 && accumulate != 1)
+        return fail(FSDP_E_ARG, "%s: accumulate must be 0 or 1", who);
+    if (sqnorm_out && !aligned(sqnorm_out, 8))
+        return fail(FSDP_E_ALIGN, "%s: sqnorm_out not 8-byte aligned", who);
     if (!plan->all_grad_out)
         return fail(FSDP_E_ARG, "%s: every shard of the plan needs a grad_shard_out", who);
     int32_t st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    const bool sq = sqnorm_out != nullptr;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(nullptr, plan->n_slices);
-        const ReduceSqKernel k = plan->slice_dtype == FSDP_DT_BF16
-                                     ? pick_reduce_sq<true>(plan->n_slices)
-                                     : pick_reduce_sq<false>(plan->n_slices);
+        const ReduceStoreKernel k = pick_reduce_store(plan->slice_dtype, plan->n_slices, sq);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), 0, stream,
                            plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb, c,
-                           plan->d_partials);
+                           accumulate, plan->d_partials);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
+    if (!sq) return FSDP_OK;
     if (plan->n_chunks == 0) {
         // nothing to sum: one workgroup over an empty range writes 0
         hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
@@ -1345,6 +1429,40 @@ extern "C" int32_t fsdp_mt_reduce_sqnorm(fsdp_mt_plan* plan, double* sqnorm_out,
     if ((st = launch_status(who)) != FSDP_OK) return st;
     hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
                        static_cast<const double*>(second), stage, stage, sqnorm_out);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_mt_reduce_sqnorm(fsdp_mt_plan* plan, double* sqnorm_out,
+                                         hipStream_t stream) {
+    if (!sqnorm_out) return fail(FSDP_E_ARG, "fsdp_mt_reduce_sqnorm: null sqnorm_out");
+    return fsdp_mt_reduce_accumulate(plan, 0, sqnorm_out, stream);
+}
+
+extern "C" int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t micro_dtype,
+                                        int64_t numel, int32_t accumulate, hipStream_t stream) {
+    const char* who = "fsdp_grad_accumulate";
+    int32_t st;
+    if ((st = check_sizes(numel, numel, who)) != FSDP_OK) return st;
+    if (micro_dtype != FSDP_DT_F32 && micro_dtype != FSDP_DT_BF16)
+        return fail(FSDP_E_DTYPE, "%s: unknown micro-batch dtype %d", who, micro_dtype);
+    if (accumulate != 0 && accumulate != 1)
+        return fail(FSDP_E_ARG, "%s: accumulate must be 0 or 1", who);
+    if (numel == 0) return FSDP_OK;
+    if (!acc || !micro) return fail(FSDP_E_ARG, "%s: null acc or micro", who);
+    if (!aligned(acc, 4) || !aligned(micro, dtype_bytes(micro_dtype)))
+        return fail(FSDP_E_ALIGN, "%s: buffer not aligned to its element size", who);
+    std::vector<fsdp::Range> rs{range_of(acc, numel, 4, true, 0, "acc"),
+                                range_of(micro, numel, dtype_bytes(micro_dtype), false, 0, "micro")};
+    if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
+    const int64_t blocks = blocks_for(numel, kChunk);
+    if ((st = check_grid(blocks, who)) != FSDP_OK) return st;
+    const int32_t vec = aligned(acc, 16) && aligned(micro, 16);
+    if (micro_dtype == FSDP_DT_BF16)
+        hipLaunchKernelGGL(accumulate_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
+                           0, stream, acc, micro, numel, accumulate, vec);
+    else
+        hipLaunchKernelGGL(accumulate_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
+                           0, stream, acc, micro, numel, accumulate, vec);
     return launch_status(who);
 }
 

@@ -223,3 +223,19 @@ def test_clip_argument_checks():
     assert _err(f, Bp, Bp, A, 4, 1.0, stream=0) == "ALIAS"          # both outputs at one address
     assert B.lib().fsdp_mt_reduce_sqnorm(None, A, None) == -1
     assert B.lib().fsdp_mt_step_clipped(None, None, A, None) == -1
+
+
+def test_accumulate_argument_checks():
+    f = B.fsdp_grad_accumulate
+    assert _err(f, None, A, "f32", 100, 1, stream=0) == "ARG"
+    assert _err(f, A, None, "bf16", 100, 1, stream=0) == "ARG"
+    assert _err(f, A, Bp, 7, 100, 1, stream=0) == "DTYPE"
+    assert _err(f, A, Bp, "f32", -1, 1, stream=0) == "ARG"
+    assert _err(f, A + 2, Bp, "f32", 100, 1, stream=0) == "ALIGN"
+    assert _err(f, A, Bp + 1, "bf16", 100, 1, stream=0) == "ALIGN"
+    assert _err(f, A, A + 200, "f32", 100, 1, stream=0) == "ALIAS"
+    assert B.lib().fsdp_grad_accumulate(A, Bp, 0, 100, 2, None) == -1    # accumulate not 0/1
+    B.fsdp_grad_accumulate(None, None, "f32", 0, 1, stream=0)              # empty: no-op
+    assert B.lib().fsdp_mt_reduce_accumulate(None, 0, None, None) == -1
+    assert B.lib().fsdp_mt_step_amax(None, None, A, None) == -1
+    assert B.lib().fsdp_mt_cast_fp8(None, A, 1, None, None) == -1

@@ -200,3 +200,17 @@ def test_stage3_formula_random_shapes():
             _, s = L.layout(L.FLAT, N, r, shapes, False)
             total = s.bytes_param + s.bytes_grad + s.bytes_optim
             assert total * N == 4 * 4 * phys      # 4 fp32 words per physical element
+
+
+def test_no_sync_gradient_is_n_times_the_shard():
+    # FSDP chapter §18.39: the unsharded gradient kept under no_sync is N times
+    # the sharded gradient (not multiplied by the number of micro-batches)
+    w = WORKLOADS[2]
+    for r in range(4):
+        _, s = L.layout(L.FLAT, 4, r, shapes_of(w), False)
+        assert s.bytes_grad_unsharded == 4 * s.bytes_grad == 4 * (1 << 25)
+    _, s = L.layout(L.FLAT, 3, 0, [(10, 10, "f32")], False)
+    assert s.bytes_grad_unsharded == 4 * 12 == 3 * s.bytes_grad
+    w = WORKLOADS[4]
+    _, s = L.layout(L.SHARD0, 8, 0, shapes_of(w), True)
+    assert s.bytes_grad_unsharded == 8 * s.bytes_grad == 4 * 6_738_415_616
