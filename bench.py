@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["rank_step_amd/csrc/rank_step.hip"]
 WORKLOAD_BY_NAME = {"llama7b_full_n8": 4, "llama7b_block_n8": 3, "mlp128m_flat_n4": 2,
-                    "tiny_mlp_flat_n4": 1, "llama70b_full_n32": 5}
+                    "tiny_mlp_flat_n4": 1, "llama70b_full_n32": 5, "mlp128m_zero1_n4": 6}
 
 
 def kernel_source_hash():
@@ -327,7 +327,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name,
-            "layout": "shard0" if w.mode == "shard0" else "flat",
+            "layout": w.mode,
             "world_size": w.world_size,
             "rank": 0,
             "local_params": total,

@@ -59,7 +59,7 @@ enum {
 };
 
 typedef enum { FSDP_DT_F32 = 0, FSDP_DT_BF16 = 1 } fsdp_dtype;
-typedef enum { FSDP_LAYOUT_FLAT = 0, FSDP_LAYOUT_SHARD0 = 1 } fsdp_layout_mode;
+typedef enum { FSDP_LAYOUT_FLAT = 0, FSDP_LAYOUT_SHARD0 = 1, FSDP_LAYOUT_OWNER = 2 } fsdp_layout_mode;
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* fsdp_last_error(void);
@@ -88,10 +88,15 @@ typedef struct {
  *                  the rank's shards in the order given)
  *   view_numel     elements of the parameter the rank holds (may be 0)
  *   tensor_offset  index, in the flattened parameter, of the first one held
+ *   owner          OWNER mode: the rank that holds and updates the whole
+ *                  parameter; -1 in the other modes (every rank holds a piece)
  * For an empty FLAT view, with lo = max(global_offset, rank*S):
- * view_offset = min(lo - rank*S, S), tensor_offset = min(lo - global_offset, numel). */
+ * view_offset = min(lo - rank*S, S), tensor_offset = min(lo - global_offset, numel).
+ * In OWNER mode a parameter the rank does not own has shard_numel = valid =
+ * view_numel = tensor_offset = 0 and view_offset = where it would be packed. */
 typedef struct {
     int64_t shard_numel, valid, global_offset, view_offset, view_numel, tensor_offset;
+    int64_t owner;
 } fsdp_shard_view;
 
 /* Per-rank totals.  logical_numel: sum of numel; physical_numel: padded
@@ -124,6 +129,16 @@ typedef struct {
  *   each parameter is sharded on its own along dim 0, (d0, ...) ->
  *   (d0/N, ...); when N does not divide d0, every rank gets ceil(d0/N) rows
  *   and the trailing ranks' missing rows are padding.
+ * FSDP_LAYOUT_OWNER -- ZeRO-1 (ZeroRedundancyOptimizer), [ZeRO post] "ZeRO-1：
+ *   Optimizer State Sharding" and "Optimizer Step 的所有权": whole parameters
+ *   are given to owner ranks; only the owner keeps their optimizer state and
+ *   updates them (then broadcasts them).  Ownership is balanced by bytes, not
+ *   by parameter count (the post lists count-balancing among its mistakes):
+ *   parameters in decreasing byte size (ties: lower index first) each go to
+ *   the rank with the fewest bytes so far (ties: lower rank).  A rank's owned
+ *   parameters are packed whole, in the order given.  Parameters and
+ *   gradients stay replicated: bytes_param and bytes_grad count every
+ *   parameter; bytes_optim and bytes_master count the owned ones.
  * Byte totals follow [ZeRO post] tables "Canonical ZeRO 状态公式" /
  * "实测状态因子" (stage 3: P/N params, P/N grads, 2P/N optimizer state per
  * rank) and [titan FSDP2] §2.3 (master + moments = 12 bytes per parameter).

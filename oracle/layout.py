@@ -25,6 +25,18 @@ SHARD0 (FSDP-2 per-parameter Shard(0))
     taken is ceil(d0/N) rows per rank with trailing ranks padded with zero
     rows (possibly all padding).
 
+OWNER (ZeRO-1, ZeroRedundancyOptimizer)
+    ZeRO state sharding post, "ZeRO-1：Optimizer State Sharding" and
+    "Optimizer Step 的所有权": whole parameters are handed to owner ranks; only
+    the owner keeps their optimizer state and updates them, then broadcasts
+    them; parameters and gradients stay replicated (its measured table: 128 /
+    128 / 64 MiB per rank for 128 MiB of fp32 at N = 4, factors 4 / 4 / 2).
+    Owners should be balanced by bytes, not by parameter count (the post lists
+    count-balancing among its mistakes).  The assignment rule is not printed;
+    the reading taken is the greedy largest-first one: parameters in
+    decreasing byte size (ties: lower index first) each go to the rank with
+    the fewest bytes so far (ties: lower rank).
+
 Byte summary
     FSDP chapter §18.39: while micro-batches accumulate under no_sync the
     gradient stays unsharded, N times the size of the sharded one.
@@ -58,6 +70,7 @@ from dataclasses import dataclass
 
 FLAT = 0
 SHARD0 = 1
+OWNER = 2
 
 DTYPE_SIZE = {"f32": 4, "bf16": 2}
 
@@ -70,6 +83,7 @@ class View:
     view_offset: int
     view_numel: int
     tensor_offset: int
+    owner: int = -1
 
 
 @dataclass(frozen=True)
@@ -132,6 +146,20 @@ def shard0_view(numel, dim0, world_size, rank):
     return c * row, rows_held * row, first_row * row
 
 
+def owner_assignment(sizes, world_size):
+    """ZeRO-1 owners of whole parameters, balanced by bytes: (numel, dtype)
+    pairs in, one rank per parameter out (greedy, largest first)."""
+    nbytes = [n * DTYPE_SIZE[d] for n, d in sizes]
+    order = sorted(range(len(sizes)), key=lambda i: (-nbytes[i], i))
+    load = [0] * world_size
+    owners = [0] * len(sizes)
+    for i in order:
+        q = min(range(world_size), key=lambda r: (load[r], r))
+        owners[i] = q
+        load[q] += nbytes[i]
+    return owners
+
+
 def layout(mode, world_size, rank, shapes, has_master):
     """Views and byte summary for ``rank``.
 
@@ -166,6 +194,23 @@ def layout(mode, world_size, rank, shapes, has_master):
             pad += sn - valid
         P = o
         local = packed
+    elif mode == OWNER:
+        owners = owner_assignment([(n, d) for n, _, d in shapes], world_size)
+        views = []
+        o = 0
+        packed = 0
+        for (numel, _, _), own in zip(shapes, owners):
+            mine = own == rank
+            views.append(View(numel if mine else 0, numel if mine else 0, o, packed,
+                              numel if mine else 0, 0, own))
+            o += numel
+            if mine:
+                packed += numel
+        P = o
+        local = packed
+        physical = P
+        pad = 0
+        bytes_param = sum(n * DTYPE_SIZE[d] for n, _, d in shapes)
     else:
         raise ValueError("unknown layout mode")
     summary = Summary(
@@ -174,7 +219,7 @@ def layout(mode, world_size, rank, shapes, has_master):
         shard_numel=local,
         pad_numel=pad,
         bytes_param=bytes_param,
-        bytes_grad=4 * local,
+        bytes_grad=4 * (P if mode == OWNER else local),   # ZeRO-1: gradients replicated
         bytes_optim=8 * local,
         bytes_master=4 * local if has_master else 0,
         # FSDP chapter §18.26 / §18.39: with no_sync the gradient stays

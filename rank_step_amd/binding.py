@@ -24,7 +24,7 @@ FSDP_OK = 0
 ERRORS = {-1: "FSDP_E_ARG", -2: "FSDP_E_DTYPE", -3: "FSDP_E_ALIGN", -4: "FSDP_E_ALIAS",
           -5: "FSDP_E_HIP", -6: "FSDP_E_CAPACITY", -7: "FSDP_E_STATE"}
 DTYPES = {"f32": 0, "bf16": 1}
-LAYOUTS = {"flat": 0, "shard0": 1}
+LAYOUTS = {"flat": 0, "shard0": 1, "owner": 2}
 
 # Every function the header declares; the CPU tests check each is exported.
 EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
@@ -49,7 +49,8 @@ class TensorShape(ctypes.Structure):
 
 class ShardView(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("shard_numel", "valid", "global_offset",
-                                              "view_offset", "view_numel", "tensor_offset")]
+                                              "view_offset", "view_numel", "tensor_offset",
+                                              "owner")]
 
 
 class LayoutSummary(ctypes.Structure):

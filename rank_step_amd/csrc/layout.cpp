@@ -7,11 +7,17 @@
 // per-rank views of the original parameters are from the ZeRO state sharding
 // post (blog.cptz.space), section "FlatParameter 与 Padding".
 //
+// OWNER mode is ZeRO-1's owner assignment (ZeroRedundancyOptimizer) from the
+// ZeRO state sharding post, sections "ZeRO-1：Optimizer State Sharding" and
+// "Optimizer Step 的所有权": whole parameters go to owner ranks, balanced by
+// bytes rather than by parameter count.
+//
 // SHARD0 mode follows FSDP2's per-parameter Shard(0) (MindSpeed-LLM FSDP2 doc,
 // section "DTensor"; torchtitan FSDP2 article, §2.3): each parameter is split
 // along dim 0 on its own.  When N does not divide dim 0 every rank still gets
 // ceil(dim0 / N) rows and the rows past the end are padding.
 
+#include <algorithm>
 #include <cstdint>
 #include <vector>
 
@@ -34,7 +40,7 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
                                      const fsdp_tensor_shape* tensors, int32_t n_tensors,
                                      int32_t has_master, fsdp_shard_view* views_out,
                                      fsdp_layout_summary* summary_out) {
-    if (mode != FSDP_LAYOUT_FLAT && mode != FSDP_LAYOUT_SHARD0)
+    if (mode != FSDP_LAYOUT_FLAT && mode != FSDP_LAYOUT_SHARD0 && mode != FSDP_LAYOUT_OWNER)
         return fail(FSDP_E_ARG, "fsdp_shard_layout: unknown mode %d", mode);
     if (world_size < 1) return fail(FSDP_E_ARG, "fsdp_shard_layout: world_size %d < 1", world_size);
     if (rank < 0 || rank >= world_size)
@@ -91,6 +97,7 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
                 v.view_numel = 0;
                 v.tensor_offset = min64(lo - off, n);
             }
+            v.owner = -1;
             off += n;
         }
         const int64_t esize = n_tensors > 0 ? dtype_size(tensors[0].dtype) : 4;
@@ -98,7 +105,7 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
         s.shard_numel = S;
         s.pad_numel = S - valid;
         s.bytes_param = S * esize;
-    } else {
+    } else if (mode == FSDP_LAYOUT_SHARD0) {
         int64_t off = 0, packed = 0, phys = 0, bytes_param = 0, pad = 0;
         for (int32_t i = 0; i < n_tensors; ++i) {
             const fsdp_tensor_shape& t = tensors[i];
@@ -118,6 +125,7 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
             v.view_offset = packed;
             v.view_numel = valid;
             v.tensor_offset = toff;
+            v.owner = -1;
             int64_t sn_all, b;
             if (!fsdp::mul_i64(sn, N, &sn_all) || !fsdp::add_i64(phys, sn_all, &phys) ||
                 !fsdp::add_i64(packed, sn, &packed) ||
@@ -131,6 +139,47 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
         s.shard_numel = packed;
         s.pad_numel = pad;
         s.bytes_param = bytes_param;
+    } else {
+        // OWNER: largest parameters first, each to the least-loaded rank.
+        std::vector<int64_t> bytes(static_cast<size_t>(n_tensors));
+        std::vector<int32_t> order(static_cast<size_t>(n_tensors));
+        int64_t all_bytes = 0;
+        for (int32_t i = 0; i < n_tensors; ++i) {
+            bytes[i] = tensors[i].numel * dtype_size(tensors[i].dtype);
+            order[i] = i;
+            if (!fsdp::add_i64(all_bytes, bytes[i], &all_bytes))
+                return fail(FSDP_E_ARG, "layout sizes overflow int64");
+        }
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t a, int32_t b) { return bytes[a] > bytes[b]; });
+        std::vector<int64_t> load(static_cast<size_t>(N), 0);
+        std::vector<int64_t> owner(static_cast<size_t>(n_tensors), 0);
+        for (int32_t i : order) {
+            int64_t best = 0;
+            for (int64_t q = 1; q < N; ++q)
+                if (load[q] < load[best]) best = q;
+            owner[i] = best;
+            load[best] += bytes[i];
+        }
+        int64_t off = 0, packed = 0;
+        for (int32_t i = 0; i < n_tensors; ++i) {
+            const int64_t n = tensors[i].numel;
+            fsdp_shard_view& v = views[i];
+            const bool mine = owner[i] == r;
+            v.shard_numel = mine ? n : 0;
+            v.valid = mine ? n : 0;
+            v.global_offset = off;
+            v.view_offset = packed;
+            v.view_numel = mine ? n : 0;
+            v.tensor_offset = 0;
+            v.owner = owner[i];
+            if (mine) packed += n;
+            off += n;
+        }
+        s.physical_numel = logical;
+        s.shard_numel = packed;
+        s.pad_numel = 0;
+        s.bytes_param = all_bytes;
     }
     if (!fsdp::mul_i64(s.shard_numel, 8, &s.bytes_optim))
         return fail(FSDP_E_ARG, "byte counts overflow int64");
@@ -139,6 +188,9 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
     // no_sync accumulation holds the whole gradient: the padded flat vector
     // (FLAT) or every full parameter (SHARD0), in fp32
     const int64_t unsharded = mode == FSDP_LAYOUT_FLAT ? s.physical_numel : s.logical_numel;
+    // ZeRO-1 keeps the whole (all-reduced) gradient on every rank
+    if (mode == FSDP_LAYOUT_OWNER && !fsdp::mul_i64(logical, 4, &s.bytes_grad))
+        return fail(FSDP_E_ARG, "byte counts overflow int64");
     if (!fsdp::mul_i64(unsharded, 4, &s.bytes_grad_unsharded))
         return fail(FSDP_E_ARG, "byte counts overflow int64");
     for (int32_t i = 0; i < n_tensors; ++i) views_out[i] = views[i];

@@ -186,7 +186,7 @@ template <typename T> __device__ __forceinline__ T ld_state(const T* p) { return
 template <typename T> __device__ __forceinline__ void st_state(T* p, T x) { st_s<RS_NT_STATE_ST>(p, x); }
 template <typename T> __device__ __forceinline__ void st_out(T* p, T x) { st_s<RS_NT_OUT>(p, x); }
 
-__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+[[maybe_unused]] __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
     return (static_cast<uint64_t>(hi) << 32) | lo;

@@ -20,6 +20,9 @@ Workloads (all synthetic; the pages use no dataset):
                       [32000,4096] + final norm = 291 local shards.
 5. llama70b_full_n32  Shard(0), N=32: 80 blocks of hidden 8192, FFN 28672,
                       8 KV heads of 128, vocab 128256 = 723 local shards.
+6. mlp128m_zero1_n4   ZeRO-1 owners, N=4: the ZeRO state sharding post's MLP
+                      as 8 equal fp32 Linear weights [2048,2048] (128 MiB),
+                      two whole weights updated per rank.
 
 Value recipe: weights ~ N(0, 0.02) fp32, norm weights 1.0, moments 0.  Slice
 q of rank r at step t is drawn with seed 1000*cfg + 100*t + 10*r + q (mask /
@@ -113,6 +116,9 @@ def _workloads():
         5: Workload(5, "llama70b_full_n32", "shard0", 32,
                     _llama(80, 8192, 28672, 1024, 128256, "bf16"),
                     "f32", 1, True, True, 3, 1e-4),
+        6: Workload(6, "mlp128m_zero1_n4", "owner", 4,
+                    tuple(Param(f"linear{i}", (2048, 2048), "f32") for i in range(8)),
+                    "f32", 4, False, False, 3, 1e-3),
     }
 
 

@@ -42,10 +42,13 @@ def test_library_exports_every_declared_function():
 
 # ---------------------------------------------------------------- layout parity
 
+MODES = {"flat": OL.FLAT, "shard0": OL.SHARD0, "owner": OL.OWNER}
+
+
 def _cmp(mode, N, shapes, has_master):
     for r in range(N):
         got_v, got_s = B.fsdp_shard_layout(mode, N, r, shapes, has_master)
-        ref_v, ref_s = OL.layout(OL.FLAT if mode == "flat" else OL.SHARD0, N, r, shapes, has_master)
+        ref_v, ref_s = OL.layout(MODES[mode], N, r, shapes, has_master)
         assert got_v == [v.__dict__ for v in ref_v], (mode, N, r)
         assert got_s == ref_s.__dict__, (mode, N, r)
 
@@ -239,3 +242,17 @@ def test_accumulate_argument_checks():
     assert B.lib().fsdp_mt_reduce_accumulate(None, 0, None, None) == -1
     assert B.lib().fsdp_mt_step_amax(None, None, A, None) == -1
     assert B.lib().fsdp_mt_cast_fp8(None, A, 1, None, None) == -1
+
+
+def test_layout_owner_matches_oracle():
+    import random
+    rnd = random.Random(5)
+    for _ in range(100):
+        N = rnd.randint(1, 9)
+        shapes = [(rnd.choice([0, 1, 7, 64, 4096, 5000]) * rnd.randint(1, 3), 1,
+                   rnd.choice(["f32", "bf16"])) for _ in range(rnd.randint(0, 10))]
+        shapes = [(n, max(n, 1), d) for n, _, d in shapes]
+        _cmp("owner", N, shapes, rnd.random() < 0.5)
+    for cfg in (2, 4):
+        w = WORKLOADS[cfg]
+        _cmp("owner", w.world_size, shapes_of(w), w.has_master)

@@ -26,8 +26,8 @@ pytestmark = pytest.mark.gpu
 
 def _layout_matches_oracle(st):
     w = st.w
-    ref_v, ref_s = OL.layout(OL.FLAT if w.mode == "flat" else OL.SHARD0, w.world_size, st.rank,
-                             shapes_of(w), w.has_master)
+    mode = {"flat": OL.FLAT, "shard0": OL.SHARD0, "owner": OL.OWNER}[w.mode]
+    ref_v, ref_s = OL.layout(mode, w.world_size, st.rank, shapes_of(w), w.has_master)
     assert st.views == [v.__dict__ for v in ref_v]
     assert st.summary == ref_s.__dict__
 

@@ -214,3 +214,61 @@ def test_no_sync_gradient_is_n_times_the_shard():
     w = WORKLOADS[4]
     _, s = L.layout(L.SHARD0, 8, 0, shapes_of(w), True)
     assert s.bytes_grad_unsharded == 8 * s.bytes_grad == 4 * 6_738_415_616
+
+
+def test_zero1_page_table():
+    g = GOLD["zero1_bytes"]
+    n = g["param_dims"][0] * g["param_dims"][1]
+    shapes = [(n, g["param_dims"][0], "f32")] * g["n_params"]
+    N = g["world_size"]
+    MiB = 1 << 20
+    P_bytes = 4 * n * g["n_params"]
+    tot = [0, 0, 0]
+    for r in range(N):
+        views, s = L.layout(L.OWNER, N, r, shapes, False)
+        assert s.bytes_param == g["per_rank_param_mib"] * MiB
+        assert s.bytes_grad == g["per_rank_grad_mib"] * MiB
+        assert s.bytes_optim == g["per_rank_optim_mib"] * MiB
+        assert sum(v.owner == r for v in views) == 2
+        tot = [tot[0] + s.bytes_param, tot[1] + s.bytes_grad, tot[2] + s.bytes_optim]
+    assert [t / P_bytes for t in tot] == g["factors"]
+
+
+def test_owner_balances_bytes_not_counts():
+    # one large and three small parameters at N=2: byte balance gives the large
+    # one a rank of its own (count balance would pair it with a small one)
+    views, _ = L.layout(L.OWNER, 2, 0, [(1000, 1, "f32"), (10, 1, "f32"), (10, 1, "f32"),
+                                        (10, 1, "f32")], False)
+    assert [v.owner for v in views] == [0, 1, 1, 1]
+    # bf16 parameters weigh half as much per element: by bytes the order is
+    # 400 B, 360 B, 240 B -> owners 1, 0, 1 (by element count it would be 0, 1, 1)
+    views, _ = L.layout(L.OWNER, 2, 0, [(120, 1, "bf16"), (100, 1, "f32"), (90, 1, "f32")], False)
+    assert [v.owner for v in views] == [1, 0, 1]
+
+
+def test_owner_bruteforce_invariants():
+    import random
+    rnd = random.Random(11)
+    for _ in range(300):
+        N = rnd.randint(1, 9)
+        shapes = [(rnd.randint(0, 5000), 1, rnd.choice(["f32", "bf16"])) for _ in range(rnd.randint(0, 12))]
+        shapes = [(n, max(n, 1), d) for n, _, d in shapes]
+        owners = None
+        loads = []
+        for r in range(N):
+            views, s = L.layout(L.OWNER, N, r, shapes, True)
+            if owners is None:
+                owners = [v.owner for v in views]
+            assert [v.owner for v in views] == owners          # one assignment seen by all ranks
+            off = 0
+            for (n, _, d), v in zip(shapes, views):
+                mine = v.owner == r
+                assert v.view_offset == off and v.view_numel == (n if mine else 0)
+                assert v.shard_numel == v.valid == v.view_numel and v.tensor_offset == 0
+                off += v.view_numel
+            assert s.shard_numel == off and s.pad_numel == 0
+            assert s.bytes_optim == 8 * off and s.bytes_master == 4 * off
+            loads.append(sum(n * L.DTYPE_SIZE[d] for (n, _, d), o in zip(shapes, owners) if o == r))
+        assert all(0 <= o < N for o in owners)
+        biggest = max([n * L.DTYPE_SIZE[d] for n, _, d in shapes], default=0)
+        assert max(loads) - min(loads) <= biggest                # greedy balance bound
