@@ -229,6 +229,44 @@ def accumulation(st, stream, args):
                         "hbm_gb_s": b_nos * st.total / ms_nos / 1e6}}
 
 
+def unfused_chain(st, stream, args, t0):
+    """Time the same step as three separate calls per shard (reduce -> AdamW
+    -> cast, 3 launches x shards), which moves 2N+4 + 28 + 6 B/param, beside
+    the fused one-pass launch."""
+    import torch
+    from rank_step_amd import binding as B
+
+    w = st.w
+    g = torch.empty(st.total, dtype=torch.float32, device=st.device)
+    tens = st.mt_tensors(with_grad_out=False, with_fp8=False)
+    gp = g.data_ptr()
+    steps = max(1, min(args.steps, 10))
+
+    def one(t):
+        for d, (off, length, held, _) in zip(tens, st.segments):
+            B.fsdp_reduce_grad_shard(gp + 4 * off, d["grad_slices"], w.slice_dtype, d["slice_stride"],
+                                     w.n_slices, length, held, stream)
+            B.fsdp_adamw_shard_step(d["param_fp32"], d["exp_avg"], d["exp_avg_sq"], gp + 4 * off,
+                                    length, held, w.hparams, t, stream)
+            if d["unshard_bf16_out"] is not None:
+                B.fsdp_cast_unshard_bf16(d["unshard_bf16_out"], d["param_fp32"], length, held, stream)
+
+    t = t0
+    one(t + 1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(steps):
+        one(t + 2 + k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    slice_b = 2 if w.slice_dtype == "bf16" else 4
+    bpp = w.n_slices * slice_b + 4 + 28 + (6 if w.bf16_out else 0)
+    return {"ms_per_step": ms, "bytes_per_param": bpp, "hbm_gb_s": bpp * st.total / ms / 1e6,
+            "launches": 3 * len(tens), "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +279,8 @@ def main():
                     help="also time the clipped step (global grad-norm clipping) with this max_norm")
     ap.add_argument("--no-clip", dest="clip", action="store_const", const=None,
                     help="do not time the clipped step")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="do not time the unfused three-call chain")
     ap.add_argument("--no-fp8", action="store_true",
                     help="do not time the step with the fp8 all-gather copy")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -357,6 +397,8 @@ def main():
         out["fp8_step"] = fp8_step(st, stream, args, t)
     if args.clip is not None:
         out["grad_accumulation"] = accumulation(st, stream, args)
+    if not args.no_chain:
+        out["unfused_chain"] = unfused_chain(st, stream, args, t)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, t + 1)
     st.close()

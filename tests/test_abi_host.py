@@ -256,3 +256,10 @@ def test_layout_owner_matches_oracle():
     for cfg in (2, 4):
         w = WORKLOADS[cfg]
         _cmp("owner", w.world_size, shapes_of(w), w.has_master)
+
+
+def test_capacity_error_before_any_device_work():
+    # 2**44 elements need more than 2**31 - 1 workgroups of 2048: refused on the host
+    big = 1 << 44
+    assert _err(B.fsdp_cast_unshard_bf16, A, None, big, 0, stream=0) == "CAPACITY"
+    assert _err(B.fsdp_reduce_grad_shard, A, None, "f32", big, 1, big, 0, stream=0) == "CAPACITY"

@@ -1,0 +1,39 @@
+"""Host-side checks of bench.py (CPU only): the multi-GPU refusal, the
+algorithmic byte counts and the measured-traffic record's staleness rule."""
+
+import json
+import os
+import subprocess
+import sys
+
+import bench
+from rank_step_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bytes_per_param():
+    assert bench.bytes_per_param(WORKLOADS[4], True) == 42      # 8 bf16 slices + 12 + 12 + 2
+    assert bench.bytes_per_param(WORKLOADS[2], False) == 40     # 4 fp32 slices + 12 + 12
+    assert bench.bytes_per_param(WORKLOADS[5], True) == 30      # 1 fp32 slice + 12 + 12 + 2
+
+
+def test_traffic_record_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
+    rec = {"kernel_source_hash": bench.kernel_source_hash(), "total_numel": 123,
+           "bytes_per_launch": 4567}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic_x.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [os.path.join(ROOT, s) for s in bench.KERNEL_SOURCES])
+    assert bench.measured_traffic("x", 123) == 4567
+    assert bench.measured_traffic("x", 124) is None              # another workload size
+    rec["kernel_source_hash"] = "0" * 16                        # taken on another kernel
+    (tmp_path / "profiles" / "traffic_x.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("x", 123) is None
+    assert bench.measured_traffic("missing", 123) is None
