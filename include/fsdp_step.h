@@ -375,7 +375,7 @@ int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t micro_dtype,
  * shard i of the plan, in input order, the largest |p'| of its updated local
  * shard to amax_out[i] (device fp32 [n_tensors]; 0 for an empty shard; NaN if
  * any updated value is NaN).  The plan must have at least one fp8 output.
- * Uses the plan's per-chunk scratch: calls on one plan must not overlap. */
+ * Uses the plan's per-workgroup scratch: calls on one plan must not overlap. */
 int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, float* amax_out,
                           hipStream_t stream);
 

@@ -7,17 +7,25 @@
 // and its sources are stated at each device function below and in the header.
 //
 // The path is bound by HBM bandwidth (about half a flop per byte), so there is
-// no matrix-core work: every kernel is a streaming pass.  Each thread moves 8
-// consecutive elements per access -- one 16-byte load of bf16, two 16-byte
-// loads of fp32 -- and a 256-thread workgroup (four wave64s) covers 2048
-// elements per iteration.  Every load of an iteration is issued before its
-// first use; gradient slices and the bf16 copy are touched once and use
-// non-temporal accesses.  Shards whose buffers are not 16-byte aligned take an
-// element-by-element path with the same arithmetic (bit-identical results).
+// no matrix-core work: every kernel is a streaming pass.  A workgroup is one
+// wave64 and covers one 256-element tile: each lane moves 4 consecutive
+// elements per access (one 16-byte load per fp32 array, one 8-byte load per
+// bf16 slice), and every load of the tile is issued before its first use.
+// Gradient slices and the low-precision copies are touched once and use
+// non-temporal accesses.  Shards whose buffers are not aligned for those
+// vectors take an element-by-element path with the same arithmetic
+// (bit-identical results).
 //
-// The multi-tensor launch reads a host-built chunk-descriptor table: each
-// workgroup stages its run of chunk entries and the shard descriptors they
-// point to in LDS, then streams through the chunks.
+// Residency is capped on purpose: each streaming launch reserves enough LDS
+// (which the kernels do not otherwise use) that only a few workgroups share a
+// compute unit.  On MI355X the HBM stacks deliver markedly more bandwidth to
+// this mix of reads and in-place writes when each CU keeps tens of kilobytes
+// of loads in flight rather than the few hundred that full occupancy issues.
+//
+// The multi-tensor launch reads a host-built chunk-descriptor table: entry
+// b/8 names a shard and a 2048-element range of it, and workgroup b takes the
+// (b%8)-th tile of that range, reading the entry and the shard's descriptor
+// with scalar loads.
 //
 // Floating point: fp32, FMA only where written (built with -ffp-contract=off),
 // IEEE-correct division and square root, denormals kept.
@@ -37,19 +45,8 @@ using fsdp::fail;
 
 namespace {
 
-// Build-time tunables.  The defaults are the fastest measured on MI355X for
-// the 7B rank shard (one 2048-element tile per workgroup, chunk entries and
-// shard descriptors read with scalar loads, non-temporal slice loads and bf16
-// stores, ordinary cached state accesses); other values exist for measurement.
-#ifndef RS_CHUNK_TILES
-#define RS_CHUNK_TILES 1        // 2048-element tiles per chunk-table entry
-#endif
-#ifndef RS_CHUNKS_PER_BLOCK
-#define RS_CHUNKS_PER_BLOCK 1   // chunk-table entries per workgroup
-#endif
-#ifndef RS_UNROLL
-#define RS_UNROLL 1
-#endif
+// Build-time tunables.  The defaults are the fastest measured on MI355X;
+// other values exist for measurement.
 // Non-temporal hints: 1 = nt on the access class, 0 = ordinary access.
 #ifndef RS_NT_SLICES
 #define RS_NT_SLICES 1
@@ -63,28 +60,55 @@ namespace {
 #ifndef RS_NT_STATE_ST
 #define RS_NT_STATE_ST 0
 #endif
-// 1: stage the workgroup's chunk entries and shard descriptors in LDS;
-// 0: read them with scalar loads straight from the device tables.
-#ifndef RS_DESC_LDS
-#define RS_DESC_LDS 0
+// Bytes of HBM traffic (loads and stores) one CU should keep in flight: each
+// launch caps its resident workgroups at this divided by what one workgroup
+// moves, through its LDS reservation.
+#ifndef RS_INFLIGHT_KB
+#define RS_INFLIGHT_KB 90
 #endif
-// 1: map workgroup ids so that each XCD walks a contiguous run of chunks.
-#ifndef RS_XCD_REMAP
-#define RS_XCD_REMAP 0
+// A launch whose share of that budget would allow this many resident
+// workgroups per CU or more is left uncapped (light kernels want every wave).
+#ifndef RS_OCC_UNCAPPED
+#define RS_OCC_UNCAPPED 32
 #endif
 
-constexpr int kBlock = 256;             // threads per workgroup: four wave64s
-constexpr int kGroup = 8;               // elements per thread access
-constexpr int kTile = kBlock * kGroup;  // elements per workgroup iteration
+constexpr int kBlock = 64;              // threads per workgroup: one wave64
+constexpr int kGroup = 4;               // elements per lane access
+constexpr int kTile = kBlock * kGroup;  // elements per workgroup
+constexpr int kTilesPerChunk = 8;
+constexpr int64_t kChunk = int64_t(kTilesPerChunk) * kTile;  // elements per chunk entry
 constexpr int kMaxSlices = 1024;
-constexpr int kChunksPerBlock = RS_CHUNKS_PER_BLOCK;
-constexpr int64_t kChunk = int64_t(RS_CHUNK_TILES) * kTile;  // elements per chunk entry
+constexpr int kLdsPerCu = 160 * 1024;   // gfx950
+
+// Dynamic LDS that leaves room for `occ` workgroups per CU but not occ + 1.
+constexpr size_t lds_for(int occ) {
+    return occ <= 0 ? 0 : static_cast<size_t>(2 * kLdsPerCu / (2 * occ + 1)) & ~size_t(255);
+}
+constexpr bool lds_admits(int occ) {
+    return occ <= 0 || (lds_for(occ) <= 64 * 1024 && lds_for(occ) * occ <= kLdsPerCu &&
+                        lds_for(occ) * (occ + 1) > kLdsPerCu);
+}
+constexpr int kMinOcc = 4, kMaxOcc = 16;   // residency range a cap may set
+constexpr bool all_admitted(int occ) {
+    return occ > kMaxOcc || (lds_admits(occ) && all_admitted(occ + 1));
+}
+static_assert(all_admitted(kMinOcc),
+              "every capped residency fits one workgroup's LDS limit and admits exactly its count");
+
+// The LDS reservation of a streaming launch whose lanes each move
+// `bytes_per_elem` bytes for each of their kGroup elements.
+constexpr size_t lds_reserve(int64_t bytes_per_elem) {
+    const int64_t per_wg = bytes_per_elem * kTile;
+    const int64_t occ = per_wg > 0 ? int64_t(RS_INFLIGHT_KB) * 1024 / per_wg : RS_OCC_UNCAPPED;
+    if (occ >= RS_OCC_UNCAPPED) return 0;
+    return lds_for(static_cast<int>(std::min<int64_t>(std::max<int64_t>(occ, kMinOcc), kMaxOcc)));
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// One shard as the kernels see it.  Copied to LDS as 8-byte words.
+// One shard as the kernels see it.
 struct TensorDesc {
     float* param;
     float* m;
@@ -96,11 +120,9 @@ struct TensorDesc {
     int64_t slice_stride;
     int64_t shard_numel;
     int64_t valid;
-    int64_t vec_ok;      // every buffer aligned for the vector path (16 B; fp8 copy 8 B)
+    int64_t vec_ok;      // every buffer aligned for the vector path
     int64_t index;       // position of the shard in the plan's input list
 };
-constexpr int kDescWords = sizeof(TensorDesc) / 8;
-static_assert(sizeof(TensorDesc) % 8 == 0, "descriptor is copied as 8-byte words");
 
 // One entry of the chunk-descriptor table: elements [begin, begin+count) of a shard.
 struct ChunkDesc {
@@ -186,19 +208,51 @@ template <typename T> __device__ __forceinline__ T ld_state(const T* p) { return
 template <typename T> __device__ __forceinline__ void st_state(T* p, T x) { st_s<RS_NT_STATE_ST>(p, x); }
 template <typename T> __device__ __forceinline__ void st_out(T* p, T x) { st_s<RS_NT_OUT>(p, x); }
 
-[[maybe_unused]] __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
-    return (static_cast<uint64_t>(hi) << 32) | lo;
+// Sums and maxima over the wave in a fixed order (xor-shuffle steps); every
+// lane ends with the result.
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        x = std::max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), off)));
+    return x;
 }
 
-// ---------------------------------------------------------------- 8-element groups
+// ---------------------------------------------------------------- 4-element groups
+
+// One group of a slice: 4 bf16 in 8 bytes or 4 fp32 in 16 bytes.
+template <bool BF16> struct SliceVecT { using type = u32x4; };
+template <> struct SliceVecT<true> { using type = u32x2; };
+template <bool BF16> using SliceVec = typename SliceVecT<BF16>::type;
+
+template <bool BF16>
+__device__ __forceinline__ SliceVec<BF16> load_group(const void* base, int64_t i) {
+    using V = SliceVec<BF16>;
+    if constexpr (BF16) return ld_slice(reinterpret_cast<const V*>(static_cast<const uint16_t*>(base) + i));
+    else return ld_slice(reinterpret_cast<const V*>(static_cast<const float*>(base) + i));
+}
+
+template <bool BF16>
+__device__ __forceinline__ void widen(const SliceVec<BF16>& w, float x[kGroup]) {
+    if constexpr (BF16) {
+        x[0] = bf16_lo(w[0]);
+        x[1] = bf16_hi(w[0]);
+        x[2] = bf16_lo(w[1]);
+        x[3] = bf16_hi(w[1]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(w[j]);
+    }
+}
 
 // Raw slice data of one group, loaded before any arithmetic.
 template <int NS, bool BF16>
 struct SliceRegs {
-    static constexpr int kWords = BF16 ? 1 : 2;  // 16-byte vectors per slice
-    u32x4 w[NS > 0 ? NS : 1][kWords];
+    SliceVec<BF16> w[NS > 0 ? NS : 1];
 };
 
 template <int NS, bool BF16>
@@ -206,35 +260,7 @@ __device__ __forceinline__ void load_slices(SliceRegs<NS, BF16>& r, const void* 
                                             int64_t stride, int64_t e) {
     static_assert(NS > 0, "compile-time slice count");
 #pragma unroll
-    for (int q = 0; q < NS; ++q) {
-        if constexpr (BF16) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(
-                static_cast<const uint16_t*>(slices) + q * stride + e);
-            r.w[q][0] = ld_slice(p);
-        } else {
-            const u32x4* p = reinterpret_cast<const u32x4*>(
-                static_cast<const float*>(slices) + q * stride + e);
-            r.w[q][0] = ld_slice(p);
-            r.w[q][1] = ld_slice(p + 1);
-        }
-    }
-}
-
-template <bool BF16>
-__device__ __forceinline__ void widen(const u32x4* w, float x[kGroup]) {
-    if constexpr (BF16) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[2 * j] = bf16_lo(w[0][j]);
-            x[2 * j + 1] = bf16_hi(w[0][j]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[j] = __uint_as_float(w[0][j]);
-            x[4 + j] = __uint_as_float(w[1][j]);
-        }
-    }
+    for (int q = 0; q < NS; ++q) r.w[q] = load_group<BF16>(slices, q * stride + e);
 }
 
 template <int NS, bool BF16>
@@ -256,24 +282,10 @@ __device__ __forceinline__ void reduce_regs(const SliceRegs<NS, BF16>& r, float 
 template <bool BF16>
 __device__ __forceinline__ void reduce_runtime(const void* slices, int64_t stride, int64_t e,
                                                float g[kGroup], const StepConsts& c) {
-    u32x4 w[2];
-    auto load = [&](int q) {
-        if constexpr (BF16) {
-            w[0] = ld_slice(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(slices) +
-                                                           q * stride + e));
-        } else {
-            const u32x4* p =
-                reinterpret_cast<const u32x4*>(static_cast<const float*>(slices) + q * stride + e);
-            w[0] = ld_slice(p);
-            w[1] = ld_slice(p + 1);
-        }
-    };
-    load(0);
-    widen<BF16>(w, g);
+    widen<BF16>(load_group<BF16>(slices, e), g);
     for (int q = 1; q < c.n; ++q) {
-        load(q);
         float x[kGroup];
-        widen<BF16>(w, x);
+        widen<BF16>(load_group<BF16>(slices, q * stride + e), x);
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) g[j] = g[j] + x[j];
     }
@@ -281,20 +293,31 @@ __device__ __forceinline__ void reduce_runtime(const void* slices, int64_t strid
     for (int j = 0; j < kGroup; ++j) g[j] = finish_mean(g[j], c);
 }
 
+// The mean of the slices on the group at e, N known at compile time or not.
+template <int NS, bool BF16>
+__device__ __forceinline__ void reduce_group(const TensorDesc& T, int64_t e, float g[kGroup],
+                                             const StepConsts& c) {
+    if constexpr (NS > 0) {
+        SliceRegs<NS, BF16> sr;
+        load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
+        reduce_regs<NS, BF16>(sr, g, c);
+    } else {
+        reduce_runtime<BF16>(T.slices, T.slice_stride, e, g, c);
+    }
+}
+
 struct StateRegs {
-    f32x4 p[2], m[2], v[2];
+    f32x4 p, m, v;
 };
 
 __device__ __forceinline__ void load_state(StateRegs& s, const TensorDesc& T, int64_t e) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(T.param + e);
-    const f32x4* m = reinterpret_cast<const f32x4*>(T.m + e);
-    const f32x4* v = reinterpret_cast<const f32x4*>(T.v + e);
-    s.p[0] = ld_state(p);
-    s.p[1] = ld_state(p + 1);
-    s.m[0] = ld_state(m);
-    s.m[1] = ld_state(m + 1);
-    s.v[0] = ld_state(v);
-    s.v[1] = ld_state(v + 1);
+    s.p = ld_state(reinterpret_cast<const f32x4*>(T.param + e));
+    s.m = ld_state(reinterpret_cast<const f32x4*>(T.m + e));
+    s.v = ld_state(reinterpret_cast<const f32x4*>(T.v + e));
+}
+
+__device__ __forceinline__ u32x2 pack_bf16(const f32x4& p) {
+    return u32x2{bf16_rne(p[0]) | (bf16_rne(p[1]) << 16), bf16_rne(p[2]) | (bf16_rne(p[3]) << 16)};
 }
 
 // AdamW on a group and the stores of its results.  WRITE_G: also store the
@@ -305,40 +328,21 @@ template <bool WRITE_G = true, bool AMAX = false>
 __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup],
                                              const TensorDesc& T, int64_t e, const StepConsts& c,
                                              uint32_t* amax = nullptr) {
-    uint32_t b[kGroup];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float p = s.p[h][j], m = s.m[h][j], v = s.v[h][j];
-            adamw(p, m, v, g[4 * h + j], c);
-            s.p[h][j] = p;
-            s.m[h][j] = m;
-            s.v[h][j] = v;
-            b[4 * h + j] = bf16_rne(p);
-            if constexpr (AMAX) *amax = std::max(*amax, __float_as_uint(p) & 0x7fffffffu);
-        }
+    for (int j = 0; j < 4; ++j) {
+        float p = s.p[j], m = s.m[j], v = s.v[j];
+        adamw(p, m, v, g[j], c);
+        s.p[j] = p;
+        s.m[j] = m;
+        s.v[j] = v;
+        if constexpr (AMAX) *amax = std::max(*amax, __float_as_uint(p) & 0x7fffffffu);
     }
-    f32x4* p = reinterpret_cast<f32x4*>(T.param + e);
-    f32x4* m = reinterpret_cast<f32x4*>(T.m + e);
-    f32x4* v = reinterpret_cast<f32x4*>(T.v + e);
-    st_state(p, s.p[0]);
-    st_state(p + 1, s.p[1]);
-    st_state(m, s.m[0]);
-    st_state(m + 1, s.m[1]);
-    st_state(v, s.v[0]);
-    st_state(v + 1, s.v[1]);
-    if (T.out_bf16) {
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = b[2 * j] | (b[2 * j + 1] << 16);
-        st_out(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
-    }
-    if (WRITE_G && T.grad_out) {
-        f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
-        st_out(go, f32x4{g[0], g[1], g[2], g[3]});
-        st_out(go + 1, f32x4{g[4], g[5], g[6], g[7]});
-    }
+    st_state(reinterpret_cast<f32x4*>(T.param + e), s.p);
+    st_state(reinterpret_cast<f32x4*>(T.m + e), s.m);
+    st_state(reinterpret_cast<f32x4*>(T.v + e), s.v);
+    if (T.out_bf16) st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(s.p));
+    if (WRITE_G && T.grad_out)
+        st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
 }
 
 // ---------------------------------------------------------------- single elements
@@ -404,51 +408,34 @@ __device__ __forceinline__ void scaled_elem(const TensorDesc& T, int64_t k, floa
 
 // ---------------------------------------------------------------- ranges of a shard
 
-// The fused step on elements [begin, end) of shard T.  `begin` is a multiple
-// of kGroup.  Whole groups below `valid` take the vector path; the rest (the
-// partial group at `valid`, the padding, misaligned shards) go element by element.
-template <int NS, bool BF16, int UNROLL, bool AMAX = false>
+// End of the vector part of [begin, end): whole groups below `valid` when the
+// shard's buffers allow vector accesses; the rest (the partial group at
+// `valid`, the padding, misaligned shards) goes element by element.
+__device__ __forceinline__ int64_t vector_end(const TensorDesc& T, int64_t begin, int64_t end) {
+    const int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
+    return std::max(vend, begin);
+}
+
+// The fused step on elements [begin, end) of shard T; `begin` is a multiple of kGroup.
+template <int NS, bool BF16, bool AMAX = false>
 __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, int64_t end,
                                             const StepConsts& c, uint32_t* amax = nullptr) {
-    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
-    vend = std::max(vend, begin);
-    const int64_t g1 = vend / kGroup;
-    int64_t g = begin / kGroup + threadIdx.x;
-    if constexpr (NS > 0) {
-        for (; g + (UNROLL - 1) * kBlock < g1; g += UNROLL * kBlock) {
-            SliceRegs<NS, BF16> sr[UNROLL];
-            StateRegs st[UNROLL];
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int64_t e = (g + u * kBlock) * kGroup;
-                load_slices<NS, BF16>(sr[u], T.slices, T.slice_stride, e);
-                load_state(st[u], T, e);
-            }
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                float gr[kGroup];
-                reduce_regs<NS, BF16>(sr[u], gr, c);
-                update_store<true, AMAX>(st[u], gr, T, (g + u * kBlock) * kGroup, c, amax);
-            }
-        }
-        for (; g < g1; g += kBlock) {
+    const int64_t vend = vector_end(T, begin, end);
+    for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
+        StateRegs s;
+        if constexpr (NS > 0) {
+            // every load of the group before the first arithmetic
             SliceRegs<NS, BF16> sr;
-            StateRegs st;
-            const int64_t e = g * kGroup;
             load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
-            load_state(st, T, e);
-            float gr[kGroup];
-            reduce_regs<NS, BF16>(sr, gr, c);
-            update_store<true, AMAX>(st, gr, T, e, c, amax);
-        }
-    } else {
-        for (; g < g1; g += kBlock) {
-            const int64_t e = g * kGroup;
-            StateRegs st;
-            load_state(st, T, e);
-            float gr[kGroup];
-            reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
-            update_store<true, AMAX>(st, gr, T, e, c, amax);
+            load_state(s, T, e);
+            float g[kGroup];
+            reduce_regs<NS, BF16>(sr, g, c);
+            update_store<true, AMAX>(s, g, T, e, c, amax);
+        } else {
+            load_state(s, T, e);
+            float g[kGroup];
+            reduce_runtime<BF16>(T.slices, T.slice_stride, e, g, c);
+            update_store<true, AMAX>(s, g, T, e, c, amax);
         }
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) fused_elem<BF16, AMAX>(T, k, c, amax);
@@ -458,22 +445,11 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
 template <int NS, bool BF16>
 __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin, int64_t end,
                                              const StepConsts& c) {
-    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
-    vend = std::max(vend, begin);
-    const int64_t g1 = vend / kGroup;
-    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
-        const int64_t e = g * kGroup;
-        float gr[kGroup];
-        if constexpr (NS > 0) {
-            SliceRegs<NS, BF16> sr;
-            load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
-            reduce_regs<NS, BF16>(sr, gr, c);
-        } else {
-            reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
-        }
-        f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
-        st_out(go, f32x4{gr[0], gr[1], gr[2], gr[3]});
-        st_out(go + 1, f32x4{gr[4], gr[5], gr[6], gr[7]});
+    const int64_t vend = vector_end(T, begin, end);
+    for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
+        float g[kGroup];
+        reduce_group<NS, BF16>(T, e, g, c);
+        st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.grad_out + k, k < T.valid ? reduce_elem<BF16>(T, k, c) : 0.0f);
@@ -482,43 +458,27 @@ __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin,
 // Reduce into grad_out on [begin, end): with `acc` the mean of the slices
 // is added to what grad_out holds (one fp32 add, old + new: gradient
 // accumulation over micro-batches), else it replaces it.  SQ: return this
-// thread's sum of the squares of the stored values, in fp64 (each fp32
+// lane's sum of the squares of the stored values, in fp64 (each fp32
 // square is exact in fp64).  The padding is +0 either way.
 template <int NS, bool BF16, bool SQ>
 __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_t begin,
                                                      int64_t end, const StepConsts& c, bool acc) {
     double sq = 0.0;
-    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
-    vend = std::max(vend, begin);
-    const int64_t g1 = vend / kGroup;
-    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
-        const int64_t e = g * kGroup;
-        float gr[kGroup];
-        f32x4 old0, old1;
+    const int64_t vend = vector_end(T, begin, end);
+    for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
-        if (acc) {
-            old0 = ld_state(go);
-            old1 = ld_state(go + 1);
-        }
-        if constexpr (NS > 0) {
-            SliceRegs<NS, BF16> sr;
-            load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
-            reduce_regs<NS, BF16>(sr, gr, c);
-        } else {
-            reduce_runtime<BF16>(T.slices, T.slice_stride, e, gr, c);
-        }
+        f32x4 old = {0.f, 0.f, 0.f, 0.f};
+        if (acc) old = ld_state(go);
+        float g[kGroup];
+        reduce_group<NS, BF16>(T, e, g, c);
         if (acc) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                gr[j] = old0[j] + gr[j];
-                gr[4 + j] = old1[j] + gr[4 + j];
-            }
+            for (int j = 0; j < kGroup; ++j) g[j] = old[j] + g[j];
         }
-        st_out(go, f32x4{gr[0], gr[1], gr[2], gr[3]});
-        st_out(go + 1, f32x4{gr[4], gr[5], gr[6], gr[7]});
+        st_out(go, f32x4{g[0], g[1], g[2], g[3]});
         if constexpr (SQ) {
 #pragma unroll
-            for (int j = 0; j < kGroup; ++j) sq += static_cast<double>(gr[j]) * static_cast<double>(gr[j]);
+            for (int j = 0; j < kGroup; ++j) sq += static_cast<double>(g[j]) * static_cast<double>(g[j]);
         }
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) {
@@ -539,36 +499,16 @@ template <bool BF16>
 __device__ __forceinline__ void accumulate_range(float* a, const void* x, int64_t begin,
                                                  int64_t end, bool accum, bool vec) {
     const int64_t vend = vec ? std::max(begin, end & ~int64_t(kGroup - 1)) : begin;
-    for (int64_t g = begin / kGroup + threadIdx.x; g < vend / kGroup; g += kBlock) {
-        const int64_t e = g * kGroup;
-        float xv[kGroup];
-        u32x4 w[2];
-        if constexpr (BF16) {
-            w[0] = ld_slice(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e));
-        } else {
-            const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e);
-            w[0] = ld_slice(p);
-            w[1] = ld_slice(p + 1);
-        }
+    for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         f32x4* ap = reinterpret_cast<f32x4*>(a + e);
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-        if (accum) {
-            a0 = ld_state(ap);
-            a1 = ld_state(ap + 1);
-        }
+        const SliceVec<BF16> w = load_group<BF16>(x, e);
+        f32x4 av = {0.f, 0.f, 0.f, 0.f};
+        if (accum) av = ld_state(ap);
+        float xv[kGroup];
         widen<BF16>(w, xv);
-        if (accum) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                a0[j] = a0[j] + xv[j];
-                a1[j] = a1[j] + xv[4 + j];
-            }
-        } else {
-            a0 = f32x4{xv[0], xv[1], xv[2], xv[3]};
-            a1 = f32x4{xv[4], xv[5], xv[6], xv[7]};
-        }
-        st_state(ap, a0);
-        st_state(ap + 1, a1);
+        for (int j = 0; j < kGroup; ++j) av[j] = accum ? av[j] + xv[j] : xv[j];
+        st_state(ap, av);
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) {
         const float xk = slice_elem<BF16>(x, k);
@@ -579,22 +519,15 @@ __device__ __forceinline__ void accumulate_range(float* a, const void* x, int64_
 // AdamW + cast on [begin, end) from the stored reduced gradient times `scale`.
 __device__ __forceinline__ void scaled_range(const TensorDesc& T, int64_t begin, int64_t end,
                                              float scale, const StepConsts& c) {
-    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
-    vend = std::max(vend, begin);
-    const int64_t g1 = vend / kGroup;
-    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
-        const int64_t e = g * kGroup;
-        const f32x4* gp = reinterpret_cast<const f32x4*>(T.grad_out + e);
-        const f32x4 a = ld_slice(gp), b = ld_slice(gp + 1);
-        StateRegs st;
-        load_state(st, T, e);
-        float gr[kGroup];
+    const int64_t vend = vector_end(T, begin, end);
+    for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
+        const f32x4 gv = ld_slice(reinterpret_cast<const f32x4*>(T.grad_out + e));
+        StateRegs s;
+        load_state(s, T, e);
+        float g[kGroup];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            gr[j] = a[j] * scale;
-            gr[4 + j] = b[j] * scale;
-        }
-        update_store<false>(st, gr, T, e, c);
+        for (int j = 0; j < kGroup; ++j) g[j] = gv[j] * scale;
+        update_store<false>(s, g, T, e, c);
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) scaled_elem(T, k, scale, c);
 }
@@ -628,19 +561,12 @@ __device__ __forceinline__ uint32_t fp8_code(float p, float scale) {
 // fp8 copy of the updated shard on [begin, end); codes 0 in the pad.
 __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, int64_t end,
                                           float scale) {
-    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
-    vend = std::max(vend, begin);
-    const int64_t g1 = vend / kGroup;
-    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
-        const int64_t e = g * kGroup;
-        const f32x4* p = reinterpret_cast<const f32x4*>(T.param + e);
-        const f32x4 a = ld_state(p), b = ld_state(p + 1);
-        u32x2 o;
-        o[0] = fp8_code(a[0], scale) | (fp8_code(a[1], scale) << 8) |
-               (fp8_code(a[2], scale) << 16) | (fp8_code(a[3], scale) << 24);
-        o[1] = fp8_code(b[0], scale) | (fp8_code(b[1], scale) << 8) |
-               (fp8_code(b[2], scale) << 16) | (fp8_code(b[3], scale) << 24);
-        st_out(reinterpret_cast<u32x2*>(T.out_fp8 + e), o);
+    const int64_t vend = vector_end(T, begin, end);
+    for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
+        const f32x4 a = ld_state(reinterpret_cast<const f32x4*>(T.param + e));
+        const uint32_t o = fp8_code(a[0], scale) | (fp8_code(a[1], scale) << 8) |
+                           (fp8_code(a[2], scale) << 16) | (fp8_code(a[3], scale) << 24);
+        st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), o);
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.out_fp8 + k, k < T.valid ? static_cast<uint8_t>(fp8_code(ld(T.param + k), scale))
@@ -649,19 +575,10 @@ __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, in
 
 // Cast only: out_bf16 = RNE(param) on [begin, end).
 __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, int64_t end) {
-    int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
-    vend = std::max(vend, begin);
-    const int64_t g1 = vend / kGroup;
-    for (int64_t g = begin / kGroup + threadIdx.x; g < g1; g += kBlock) {
-        const int64_t e = g * kGroup;
-        const f32x4* p = reinterpret_cast<const f32x4*>(T.param + e);
-        const f32x4 a = ld_state(p), b = ld_state(p + 1);
-        u32x4 o;
-        o[0] = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
-        o[1] = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
-        o[2] = bf16_rne(b[0]) | (bf16_rne(b[1]) << 16);
-        o[3] = bf16_rne(b[2]) | (bf16_rne(b[3]) << 16);
-        st_out(reinterpret_cast<u32x4*>(T.out_bf16 + e), o);
+    const int64_t vend = vector_end(T, begin, end);
+    for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
+        const f32x4 a = ld_state(reinterpret_cast<const f32x4*>(T.param + e));
+        st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(a));
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.out_bf16 + k, k < T.valid ? static_cast<uint16_t>(bf16_rne(ld(T.param + k))) : uint16_t(0));
@@ -669,201 +586,122 @@ __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, i
 
 // ---------------------------------------------------------------- kernels
 
-// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).
-// With the remap on, the logical index of workgroup b is chosen so that every
-// XCD walks one contiguous run of logical indices.
-__device__ __forceinline__ int64_t logical_block() {
-    const int64_t b = blockIdx.x;
-    if constexpr (RS_XCD_REMAP) {
-        const int64_t nb = gridDim.x, q = nb / 8, r = nb % 8;
-        const int64_t x = b % 8, k = b / 8;
-        return x * q + std::min<int64_t>(x, r) + k;
-    }
-    return b;
-}
-
-// Runs f(T, begin, end, chunk index) for each chunk entry of this workgroup:
-// entries [b*cpb, min((b+1)*cpb, n_chunks)) of the chunk-descriptor table,
-// each naming a shard and an element range of it.
+// Runs f(T, begin, end) on this workgroup's tile: tile b % 8 of chunk entry
+// b / 8, which names a shard and an element range of it.  The range is empty
+// for the tiles past the end of a shard's last, shorter entry.  Every value
+// here is uniform, so the entry and the descriptor arrive by scalar loads.
 template <typename F>
-__device__ __forceinline__ void for_my_chunks(const TensorDesc* __restrict__ tensors,
-                                              const ChunkDesc* __restrict__ chunks,
-                                              int64_t n_chunks, int32_t cpb, F&& f) {
-    const int64_t first = logical_block() * cpb;
-    const int cnt = static_cast<int>(std::min<int64_t>(cpb, n_chunks - first));
-    if constexpr (RS_DESC_LDS) {
-        // Stage this workgroup's run of the table, and the descriptors of the
-        // shards it names, in LDS with one parallel copy.
-        __shared__ ChunkDesc s_chunk[kChunksPerBlock];
-        __shared__ TensorDesc s_desc[kChunksPerBlock];
-        if (static_cast<int>(threadIdx.x) < cnt) s_chunk[threadIdx.x] = chunks[first + threadIdx.x];
-        __syncthreads();
-        for (int w = threadIdx.x; w < cnt * kDescWords; w += kBlock) {
-            const int i = w / kDescWords, j = w % kDescWords;
-            reinterpret_cast<uint64_t*>(&s_desc[i])[j] =
-                reinterpret_cast<const uint64_t*>(&tensors[s_chunk[i].tensor])[j];
-        }
-        __syncthreads();
-        for (int i = 0; i < cnt; ++i) {
-            TensorDesc T;
-#pragma unroll
-            for (int j = 0; j < kDescWords; ++j)
-                reinterpret_cast<uint64_t*>(&T)[j] =
-                    uniform64(reinterpret_cast<const uint64_t*>(&s_desc[i])[j]);
-            const int64_t begin = static_cast<int64_t>(uniform64(s_chunk[i].begin));
-            const int64_t count = __builtin_amdgcn_readfirstlane(s_chunk[i].count);
-            f(T, begin, begin + count, first + i);
-        }
-    } else {
-        // Uniform addresses: the entries and descriptors arrive by scalar loads.
-        for (int i = 0; i < cnt; ++i) {
-            const ChunkDesc cd = chunks[first + i];
-            const TensorDesc T = tensors[cd.tensor];
-            f(T, cd.begin, cd.begin + cd.count, first + i);
-        }
-    }
+__device__ __forceinline__ void for_my_tile(const TensorDesc* __restrict__ tensors,
+                                            const ChunkDesc* __restrict__ chunks, F&& f) {
+    const uint32_t b = blockIdx.x;
+    const ChunkDesc cd = chunks[b / kTilesPerChunk];
+    const TensorDesc T = tensors[cd.tensor];
+    const int32_t lo = static_cast<int32_t>(b % kTilesPerChunk) * kTile;
+    const int32_t n = std::max(0, std::min(kTile, cd.count - lo));
+    f(T, cd.begin + lo, cd.begin + lo + n);
 }
 
-// Sum of a value over the workgroup in a fixed order (lanes by xor-shuffle
-// steps, then the four waves in index order); the result is valid in thread 0.
-__device__ __forceinline__ double block_sum(double x) {
-    __shared__ double s_wave[kBlock / 64];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    const int wave = threadIdx.x / 64;
-    if ((threadIdx.x & 63) == 0) s_wave[wave] = x;
-    __syncthreads();
-    double t = 0.0;
-    if (threadIdx.x == 0)
-        for (int w = 0; w < kBlock / 64; ++w) t += s_wave[w];
-    __syncthreads();
-    return t;
-}
-
-// Maximum of a value over the workgroup; the result is valid in thread 0.
-__device__ __forceinline__ uint32_t block_max(uint32_t x) {
-    __shared__ uint32_t s_wave_max[kBlock / 64];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = std::max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), off)));
-    if ((threadIdx.x & 63) == 0) s_wave_max[threadIdx.x / 64] = x;
-    __syncthreads();
-    uint32_t t = 0;
-    if (threadIdx.x == 0)
-        for (int w = 0; w < kBlock / 64; ++w) t = std::max(t, s_wave_max[w]);
-    __syncthreads();
-    return t;
-}
-
-// Multi-tensor fused step: reduce, AdamW and cast for every chunk.
-template <int NS, bool BF16, int UNROLL>
+// Multi-tensor fused step: reduce, AdamW and cast for every tile.
+template <int NS, bool BF16>
 __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
                                                          const ChunkDesc* __restrict__ chunks,
-                                                         int64_t n_chunks, int32_t cpb,
                                                          StepConsts c) {
-    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
-        fused_range<NS, BF16, UNROLL>(T, b, e, c);
+    for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
+        fused_range<NS, BF16>(T, b, e, c);
     });
 }
 
 // Reduce (or reduce and accumulate) into grad_shard_out; SQ: also write
-// this workgroup's sum of squares of the stored values to
-// partials[logical block].
+// this workgroup's sum of squares of the stored values to partials[b].
 template <int NS, bool BF16, bool SQ>
 __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDesc* __restrict__ tensors,
                                                                  const ChunkDesc* __restrict__ chunks,
-                                                                 int64_t n_chunks, int32_t cpb,
                                                                  StepConsts c, int32_t acc,
                                                                  double* partials) {
     double sq = 0.0;
-    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
-        sq += reduce_store_range<NS, BF16, SQ>(T, b, e, c, acc != 0);
+    for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
+        sq = reduce_store_range<NS, BF16, SQ>(T, b, e, c, acc != 0);
     });
     if constexpr (SQ) {
-        const double total = block_sum(sq);
-        if (threadIdx.x == 0) st(partials + logical_block(), total);
+        const double total = wave_sum(sq);
+        if (threadIdx.x == 0) st(partials + blockIdx.x, total);
     }
 }
 
-// Workgroup b accumulates elements [b*kChunk, (b+1)*kChunk) of one buffer.
+// Workgroup b accumulates elements [b*kTile, (b+1)*kTile) of one buffer.
 template <bool BF16>
 __global__ __launch_bounds__(kBlock) void accumulate_kernel(float* a, const void* x, int64_t n,
                                                             int32_t accum, int32_t vec) {
-    const int64_t begin = static_cast<int64_t>(blockIdx.x) * kChunk;
-    accumulate_range<BF16>(a, x, begin, std::min(begin + kChunk, n), accum != 0, vec != 0);
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
+    accumulate_range<BF16>(a, x, begin, std::min(begin + kTile, n), accum != 0, vec != 0);
 }
 
 // Pass 2 of a clipped step: AdamW and cast from grad_shard_out times *scale.
 __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc* __restrict__ tensors,
                                                                 const ChunkDesc* __restrict__ chunks,
-                                                                int64_t n_chunks, int32_t cpb,
                                                                 StepConsts c, const float* scale) {
     const float k = *scale;
-    for_my_chunks(tensors, chunks, n_chunks, cpb, [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
+    for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         scaled_range(T, b, e, k, c);
     });
 }
 
-// The fused step that also records, per chunk entry, the largest |p'| (as
+// The fused step that also records, per workgroup, the largest |p'| (as
 // fp32 bits) for the fp8 copy's per-tensor scale.
 template <int NS, bool BF16>
 __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* __restrict__ tensors,
                                                               const ChunkDesc* __restrict__ chunks,
-                                                              int64_t n_chunks, int32_t cpb,
-                                                              StepConsts c, uint32_t* chunk_amax) {
-    for_my_chunks(tensors, chunks, n_chunks, cpb,
-                  [&](const TensorDesc& T, int64_t b, int64_t e, int64_t ci) {
-                      uint32_t am = 0;
-                      fused_range<NS, BF16, 1, true>(T, b, e, c, &am);
-                      const uint32_t bm = block_max(am);
-                      if (threadIdx.x == 0) st(chunk_amax + ci, bm);
-                  });
+                                                              StepConsts c, uint32_t* tile_amax) {
+    uint32_t am = 0;
+    for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
+        fused_range<NS, BF16, true>(T, b, e, c, &am);
+    });
+    const uint32_t wm = wave_max(am);
+    if (threadIdx.x == 0) st(tile_amax + blockIdx.x, wm);
 }
 
-// First chunk entry and number of entries of each shard, by input position.
-struct ShardChunks {
+// First workgroup and number of workgroups of each shard, by input position.
+struct ShardTiles {
     int64_t first;
     int64_t count;
 };
 
-// Workgroup i: amax_out[i] = max over shard i's chunk entries (0 if empty).
-__global__ __launch_bounds__(kBlock) void shard_amax_kernel(const ShardChunks* sc,
-                                                            const uint32_t* chunk_amax,
+// Workgroup i: amax_out[i] = max over shard i's workgroups (0 if empty).
+__global__ __launch_bounds__(kBlock) void shard_amax_kernel(const ShardTiles* sc,
+                                                            const uint32_t* tile_amax,
                                                             float* amax_out) {
-    const ShardChunks r = sc[blockIdx.x];
+    const ShardTiles r = sc[blockIdx.x];
     uint32_t m = 0;
-    for (int64_t j = threadIdx.x; j < r.count; j += kBlock) m = std::max(m, ld(chunk_amax + r.first + j));
-    const uint32_t t = block_max(m);
+    for (int64_t j = threadIdx.x; j < r.count; j += kBlock) m = std::max(m, ld(tile_amax + r.first + j));
+    const uint32_t t = wave_max(m);
     if (threadIdx.x == 0) st(amax_out + blockIdx.x, __uint_as_float(t));
 }
 
 // fp8 copy of every shard: the tensor's amax is the maximum over the ranks'
 // values (amax_ranks[r * n_shards + index]; NaN propagates), its scale
 // 448 / max(amax, 1e-12) in fp32.  The workgroup holding a shard's first
-// chunk also stores the scale.
+// tile also stores the scale.
 __global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* __restrict__ tensors,
                                                              const ChunkDesc* __restrict__ chunks,
-                                                             int64_t n_chunks, int32_t cpb,
                                                              const float* amax_ranks, int32_t n_ranks,
                                                              int64_t n_shards, float* scale_out) {
-    for_my_chunks(tensors, chunks, n_chunks, cpb,
-                  [&](const TensorDesc& T, int64_t b, int64_t e, int64_t) {
-                      uint32_t bits = 0;
-                      for (int32_t r = 0; r < n_ranks; ++r)
-                          bits = std::max(bits, __float_as_uint(ld(amax_ranks + r * n_shards + T.index)) &
-                                                    0x7fffffffu);
-                      const float amax = __uint_as_float(bits);
-                      const float den = (amax > 1e-12f || amax != amax) ? amax : 1e-12f;
-                      const float scale = 448.0f / den;
-                      if (b == 0 && scale_out && threadIdx.x == 0) st(scale_out + T.index, scale);
-                      fp8_range(T, b, e, scale);
-                  });
+    for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
+        uint32_t bits = 0;
+        for (int32_t r = 0; r < n_ranks; ++r)
+            bits = std::max(bits, __float_as_uint(ld(amax_ranks + r * n_shards + T.index)) & 0x7fffffffu);
+        const float amax = __uint_as_float(bits);
+        const float den = (amax > 1e-12f || amax != amax) ? amax : 1e-12f;
+        const float scale = 448.0f / den;
+        if (b == 0 && scale_out && threadIdx.x == 0) st(scale_out + T.index, scale);
+        fp8_range(T, b, e, scale);
+    });
 }
 
 constexpr int kSumBlocks = 1024;        // workgroups of the first summation stage
 
-// Workgroup b sums partials[b*per, min(n, (b+1)*per)) into out[b]: thread t
-// adds the elements t, t+256, ... of the range (coalesced, several loads in
-// flight), then the workgroup sum.  The order is fixed, so the sum is too.
+// Workgroup b sums partials[b*per, min(n, (b+1)*per)) into out[b]: lane t
+// adds the elements t, t+64, ... of the range (coalesced, several loads in
+// flight), then the wave sum.  The order is fixed, so the sum is too.
 __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const double* partials, int64_t n,
                                                               int64_t per, double* out) {
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
@@ -879,7 +717,7 @@ __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const double* part
         acc += d;
     }
     for (; i < hi; i += kBlock) acc += ld(partials + i);
-    const double total = block_sum(acc);
+    const double total = wave_sum(acc);
     if (threadIdx.x == 0) st(out + blockIdx.x, total);
 }
 
@@ -898,47 +736,41 @@ __global__ void clip_coef_kernel(float* coef_out, double* norm_out, const double
     if (norm_out) st(norm_out, norm);
 }
 
-// Single-shard kernels: workgroup b covers elements [b*chunk, (b+1)*chunk).
-template <int NS, bool BF16, int UNROLL>
-__global__ __launch_bounds__(kBlock) void fused_single_kernel(TensorDesc T, int64_t chunk,
-                                                              StepConsts c) {
-    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
-    fused_range<NS, BF16, UNROLL>(T, begin, std::min(begin + chunk, T.shard_numel), c);
+// Single-shard kernels: workgroup b covers elements [b*kTile, (b+1)*kTile).
+template <int NS, bool BF16>
+__global__ __launch_bounds__(kBlock) void fused_single_kernel(TensorDesc T, StepConsts c) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
+    fused_range<NS, BF16>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
 }
 
 template <int NS, bool BF16>
-__global__ __launch_bounds__(kBlock) void reduce_single_kernel(TensorDesc T, int64_t chunk,
-                                                               StepConsts c) {
-    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
-    reduce_range<NS, BF16>(T, begin, std::min(begin + chunk, T.shard_numel), c);
+__global__ __launch_bounds__(kBlock) void reduce_single_kernel(TensorDesc T, StepConsts c) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
+    reduce_range<NS, BF16>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
 }
 
-__global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T, int64_t chunk) {
-    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
-    cast_range(T, begin, std::min(begin + chunk, T.shard_numel));
+__global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
+    cast_range(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel));
 }
 
 // ---------------------------------------------------------------- kernel selection
 
-constexpr int kUnroll = RS_UNROLL;
-
-using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts);
-using FusedKernel = void (*)(TensorDesc, int64_t, StepConsts);
-using ReduceKernel = void (*)(TensorDesc, int64_t, StepConsts);
+using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts);
+using ReduceKernel = void (*)(TensorDesc, StepConsts);
 
 template <bool BF16>
 MtKernel pick_mt(int n) {
     switch (n) {
-        case 1: return mt_step_kernel<1, BF16, kUnroll>;
-        case 2: return mt_step_kernel<2, BF16, kUnroll>;
-        case 4: return mt_step_kernel<4, BF16, kUnroll>;
-        case 8: return mt_step_kernel<8, BF16, kUnroll>;
-        default: return mt_step_kernel<0, BF16, 1>;
+        case 1: return mt_step_kernel<1, BF16>;
+        case 2: return mt_step_kernel<2, BF16>;
+        case 4: return mt_step_kernel<4, BF16>;
+        case 8: return mt_step_kernel<8, BF16>;
+        default: return mt_step_kernel<0, BF16>;
     }
 }
 
-using ReduceStoreKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t,
-                                   StepConsts, int32_t, double*);
+using ReduceStoreKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, int32_t, double*);
 
 template <bool BF16, bool SQ>
 ReduceStoreKernel pick_reduce_store(int n) {
@@ -956,8 +788,7 @@ ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq) {
     return sq ? pick_reduce_store<false, true>(n) : pick_reduce_store<false, false>(n);
 }
 
-using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, int64_t, int32_t, StepConsts,
-                            uint32_t*);
+using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, uint32_t*);
 
 template <bool BF16>
 AmaxKernel pick_amax(int n) {
@@ -1022,24 +853,32 @@ StepConsts make_consts(const fsdp_adamw_hparams* hp, int32_t n) {
     return c;
 }
 
+// Bytes of one 4-element group of each buffer class: the vector path needs
+// every buffer aligned to it (and slice q's start too, through the stride).
+constexpr uintptr_t kF32Vec = 4 * kGroup, kBf16Vec = 2 * kGroup, kFp8Vec = kGroup;
+
+bool slices_vec_ok(const void* slices, int32_t slice_dtype, int64_t stride, int32_t n_slices) {
+    const uintptr_t a = slice_dtype == FSDP_DT_BF16 ? kBf16Vec : kF32Vec;
+    if (slices && !aligned(slices, a)) return false;
+    return n_slices == 1 || (stride * dtype_bytes(slice_dtype)) % static_cast<int64_t>(a) == 0;
+}
+
 bool vec_ok(const TensorDesc& T, int32_t slice_dtype, int32_t n_slices) {
-    if (!aligned(T.param, 16) || !aligned(T.m, 16) || !aligned(T.v, 16)) return false;
-    if (T.slices && !aligned(T.slices, 16)) return false;
-    if (n_slices > 1 && (T.slice_stride * dtype_bytes(slice_dtype)) % 16 != 0) return false;
-    if (T.out_bf16 && !aligned(T.out_bf16, 16)) return false;
-    if (T.grad_out && !aligned(T.grad_out, 16)) return false;
-    if (T.out_fp8 && !aligned(T.out_fp8, 8)) return false;
+    if (!aligned(T.param, kF32Vec) || !aligned(T.m, kF32Vec) || !aligned(T.v, kF32Vec)) return false;
+    if (!slices_vec_ok(T.slices, slice_dtype, T.slice_stride, n_slices)) return false;
+    if (T.out_bf16 && !aligned(T.out_bf16, kBf16Vec)) return false;
+    if (T.grad_out && !aligned(T.grad_out, kF32Vec)) return false;
+    if (T.out_fp8 && !aligned(T.out_fp8, kFp8Vec)) return false;
     return true;
 }
 
-int64_t single_chunk(int64_t) { return kChunk; }
+int64_t tiles_for(int64_t S) { return (S + kTile - 1) / kTile; }
 
-int64_t blocks_for(int64_t S, int64_t chunk) { return (S + chunk - 1) / chunk; }
-
-constexpr int64_t kMaxGrid = 0x7fffffff;  // workgroups in one launch
+// One launch covers at most 2^32 - 1 work-items in a grid dimension.
+constexpr int64_t kMaxBlocks = 0xffffffffLL / kBlock;
 
 int32_t check_grid(int64_t blocks, const char* who) {
-    if (blocks > kMaxGrid)
+    if (blocks > kMaxBlocks)
         return fail(FSDP_E_CAPACITY, "%s: %lld workgroups exceed one launch", who,
                     static_cast<long long>(blocks));
     return FSDP_OK;
@@ -1103,14 +942,15 @@ struct fsdp_mt_plan {
     int device = -1;
     int32_t n_slices = 1;
     int32_t slice_dtype = FSDP_DT_F32;
-    int32_t cpb = kChunksPerBlock;
     int64_t n_tensors = 0, n_chunks = 0, n_blocks = 0, total_numel = 0, total_valid = 0;
     int64_t chunk_numel = 0;
     bool all_grad_out = false;       // every non-empty shard stores its reduced gradient
     bool any_fp8 = false;            // some shard has an fp8 copy
     bool all_fp8 = false;            // every non-empty shard has one
-    uint32_t* d_chunk_amax = nullptr;   // fp8: largest |p'| per chunk entry
-    ShardChunks* d_shard_chunks = nullptr;  // fp8: each input shard's run of chunk entries
+    bool any_bf16 = false;           // some shard has a bf16 copy
+    bool any_grad_out = false;       // some shard stores its reduced gradient
+    uint32_t* d_tile_amax = nullptr;      // fp8: largest |p'| per workgroup
+    ShardTiles* d_shard_tiles = nullptr;  // fp8: each input shard's run of workgroups
     TensorDesc* d_tensors = nullptr;
     ChunkDesc* d_chunks = nullptr;
     double* d_partials = nullptr;    // clipped steps: one sum of squares per workgroup,
@@ -1129,6 +969,14 @@ int32_t check_plan_device(const fsdp_mt_plan* plan, const char* who) {
         return fail(FSDP_E_STATE, "%s: plan made on device %d used on device %d", who, plan->device,
                     dev);
     return FSDP_OK;
+}
+
+// Bytes per element of the plan's slices, and of its fused step.
+int64_t slice_bytes(const fsdp_mt_plan* plan) {
+    return dtype_bytes(plan->slice_dtype) * plan->n_slices;
+}
+int64_t step_bytes(const fsdp_mt_plan* plan) {
+    return slice_bytes(plan) + 24 + 2 * plan->any_bf16 + 4 * plan->any_grad_out;
 }
 
 }  // namespace
@@ -1156,15 +1004,14 @@ extern "C" int32_t fsdp_reduce_grad_shard(float* grad_shard_out, const void* gra
     T.slice_stride = slice_stride;
     T.shard_numel = shard_numel;
     T.valid = valid;
-    T.vec_ok = aligned(grad_shard_out, 16) && (!grad_slices || aligned(grad_slices, 16)) &&
-               (n_slices == 1 || (slice_stride * dtype_bytes(slice_dtype)) % 16 == 0);
+    T.vec_ok = aligned(grad_shard_out, kF32Vec) &&
+               slices_vec_ok(grad_slices, slice_dtype, slice_stride, n_slices);
     const StepConsts c = make_consts(nullptr, n_slices);
-    const int64_t chunk = single_chunk(shard_numel);
-    if ((st = check_grid(blocks_for(shard_numel, chunk), who)) != FSDP_OK) return st;
+    if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
     const ReduceKernel k = slice_dtype == FSDP_DT_BF16 ? pick_reduce<true>(n_slices)
                                                        : pick_reduce<false>(n_slices);
-    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(blocks_for(shard_numel, chunk))),
-                       dim3(kBlock), 0, stream, T, chunk, c);
+    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(tiles_for(shard_numel))), dim3(kBlock),
+                       lds_reserve(dtype_bytes(slice_dtype) * n_slices + 4), stream, T, c);
     return launch_status(who);
 }
 
@@ -1199,11 +1046,9 @@ extern "C" int32_t fsdp_adamw_shard_step(float* param_fp32, float* exp_avg, floa
     T.valid = valid;
     T.vec_ok = vec_ok(T, FSDP_DT_F32, 1);
     const StepConsts c = make_consts(hp, 1);
-    const int64_t chunk = single_chunk(shard_numel);
-    if ((st = check_grid(blocks_for(shard_numel, chunk), who)) != FSDP_OK) return st;
-    hipLaunchKernelGGL((fused_single_kernel<1, false, kUnroll>),
-                       dim3(static_cast<uint32_t>(blocks_for(shard_numel, chunk))), dim3(kBlock), 0,
-                       stream, T, chunk, c);
+    if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
+    hipLaunchKernelGGL((fused_single_kernel<1, false>), dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
+                       dim3(kBlock), lds_reserve(4 + 24), stream, T, c);
     return launch_status(who);
 }
 
@@ -1226,11 +1071,10 @@ extern "C" int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const floa
     T.out_bf16 = unshard_bf16_out;
     T.shard_numel = shard_numel;
     T.valid = valid;
-    T.vec_ok = aligned(unshard_bf16_out, 16) && aligned(param_fp32, 16);
-    const int64_t chunk = single_chunk(shard_numel);
-    if ((st = check_grid(blocks_for(shard_numel, chunk), who)) != FSDP_OK) return st;
-    hipLaunchKernelGGL(cast_single_kernel, dim3(static_cast<uint32_t>(blocks_for(shard_numel, chunk))),
-                       dim3(kBlock), 0, stream, T, chunk);
+    T.vec_ok = aligned(unshard_bf16_out, kBf16Vec) && aligned(param_fp32, kF32Vec);
+    if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
+    hipLaunchKernelGGL(cast_single_kernel, dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
+                       dim3(kBlock), lds_reserve(4 + 2), stream, T);
     return launch_status(who);
 }
 
@@ -1250,7 +1094,7 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
     std::vector<TensorDesc> descs;
     descs.reserve(static_cast<size_t>(n_tensors));
     bool all_grad_out = true;
-    bool any_fp8 = false, all_fp8 = true;
+    bool any_fp8 = false, all_fp8 = true, any_bf16 = false, any_grad_out = false;
     std::vector<int32_t> first_desc(static_cast<size_t>(n_tensors), -1);
     std::vector<fsdp::Range> rs;
     int64_t total = 0, total_valid = 0;
@@ -1275,6 +1119,8 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
         if (t.shard_numel == 0) continue;
         if (!t.grad_shard_out) all_grad_out = false;
         if (!t.unshard_fp8_out) all_fp8 = false;
+        if (t.grad_shard_out) any_grad_out = true;
+        if (t.unshard_bf16_out) any_bf16 = true;
         first_desc[i] = static_cast<int32_t>(descs.size());
         rs.push_back(range_of(t.param_fp32, t.shard_numel, 4, true, i, "param"));
         rs.push_back(range_of(t.exp_avg, t.shard_numel, 4, true, i, "exp_avg"));
@@ -1306,14 +1152,15 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
         if (st != FSDP_OK) return st;
     }
 
-    // Every chunk but a shard's last is kChunk elements, so every chunk starts
-    // group-aligned; short-lived single-tile workgroups stream best on MI355X.
+    // Every chunk but a shard's last is kChunk elements, so every chunk and
+    // every tile starts group-aligned.  Workgroup b takes tile b % 8 of entry b / 8.
     const int64_t chunk = kChunk;
     std::vector<ChunkDesc> chunks;
-    std::vector<ShardChunks> runs(static_cast<size_t>(n_tensors), ShardChunks{0, 0});
+    std::vector<ShardTiles> runs(static_cast<size_t>(n_tensors), ShardTiles{0, 0});
     for (size_t i = 0; i < descs.size(); ++i) {
-        runs[static_cast<size_t>(descs[i].index)].first = static_cast<int64_t>(chunks.size());
-        runs[static_cast<size_t>(descs[i].index)].count = (descs[i].shard_numel + chunk - 1) / chunk;
+        runs[static_cast<size_t>(descs[i].index)].first = static_cast<int64_t>(chunks.size()) * kTilesPerChunk;
+        runs[static_cast<size_t>(descs[i].index)].count =
+            (descs[i].shard_numel + chunk - 1) / chunk * kTilesPerChunk;
         for (int64_t b = 0; b < descs[i].shard_numel; b += chunk) {
             ChunkDesc cd{};
             cd.begin = b;
@@ -1324,8 +1171,7 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
     }
 
     {
-        const int64_t blocks = (static_cast<int64_t>(chunks.size()) + kChunksPerBlock - 1) / kChunksPerBlock;
-        const int32_t st = check_grid(blocks, who);
+        const int32_t st = check_grid(static_cast<int64_t>(chunks.size()) * kTilesPerChunk, who);
         if (st != FSDP_OK) return st;
     }
     fsdp_mt_plan* plan = new (std::nothrow) fsdp_mt_plan();
@@ -1334,21 +1180,24 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
     plan->slice_dtype = slice_dtype;
     plan->n_tensors = n_tensors;
     plan->n_chunks = static_cast<int64_t>(chunks.size());
-    plan->n_blocks = (plan->n_chunks + plan->cpb - 1) / plan->cpb;
+    plan->n_blocks = plan->n_chunks * kTilesPerChunk;
     plan->total_numel = total;
     plan->total_valid = total_valid;
     plan->chunk_numel = chunk;
     plan->all_grad_out = all_grad_out;
     plan->any_fp8 = any_fp8;
     plan->all_fp8 = all_fp8;
+    plan->any_bf16 = any_bf16;
+    plan->any_grad_out = any_grad_out;
     hipError_t e = hipGetDevice(&plan->device);
     if (e == hipSuccess && any_fp8 && n_tensors > 0) {
-        e = hipMalloc(reinterpret_cast<void**>(&plan->d_shard_chunks), runs.size() * sizeof(ShardChunks));
+        e = hipMalloc(reinterpret_cast<void**>(&plan->d_shard_tiles), runs.size() * sizeof(ShardTiles));
         if (e == hipSuccess)
-            e = hipMemcpyAsync(plan->d_shard_chunks, runs.data(), runs.size() * sizeof(ShardChunks),
+            e = hipMemcpyAsync(plan->d_shard_tiles, runs.data(), runs.size() * sizeof(ShardTiles),
                                hipMemcpyHostToDevice, stream);
         if (e == hipSuccess && !chunks.empty())
-            e = hipMalloc(reinterpret_cast<void**>(&plan->d_chunk_amax), chunks.size() * sizeof(uint32_t));
+            e = hipMalloc(reinterpret_cast<void**>(&plan->d_tile_amax),
+                          static_cast<size_t>(plan->n_blocks) * sizeof(uint32_t));
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
     }
     if (e == hipSuccess && !chunks.empty()) {
@@ -1385,8 +1234,8 @@ extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     const StepConsts c = make_consts(hp, plan->n_slices);
     const MtKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_mt<true>(plan->n_slices)
                                                          : pick_mt<false>(plan->n_slices);
-    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), 0, stream,
-                       plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb, c);
+    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+                       lds_reserve(step_bytes(plan)), stream, plan->d_tensors, plan->d_chunks, c);
     return launch_status(who);
 }
 
@@ -1407,8 +1256,9 @@ extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumul
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(nullptr, plan->n_slices);
         const ReduceStoreKernel k = pick_reduce_store(plan->slice_dtype, plan->n_slices, sq);
-        hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), 0, stream,
-                           plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb, c,
+        hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+                           lds_reserve(slice_bytes(plan) + 4 + 4 * accumulate), stream,
+                           plan->d_tensors, plan->d_chunks, c,
                            accumulate, plan->d_partials);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
@@ -1454,15 +1304,18 @@ extern "C" int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t m
     std::vector<fsdp::Range> rs{range_of(acc, numel, 4, true, 0, "acc"),
                                 range_of(micro, numel, dtype_bytes(micro_dtype), false, 0, "micro")};
     if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
-    const int64_t blocks = blocks_for(numel, kChunk);
+    const int64_t blocks = tiles_for(numel);
     if ((st = check_grid(blocks, who)) != FSDP_OK) return st;
-    const int32_t vec = aligned(acc, 16) && aligned(micro, 16);
+    const int32_t vec = aligned(acc, kF32Vec) &&
+                        aligned(micro, micro_dtype == FSDP_DT_BF16 ? kBf16Vec : kF32Vec);
     if (micro_dtype == FSDP_DT_BF16)
         hipLaunchKernelGGL(accumulate_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
-                           0, stream, acc, micro, numel, accumulate, vec);
+                           lds_reserve(dtype_bytes(micro_dtype) + 4 + 4 * accumulate), stream, acc,
+                           micro, numel, accumulate, vec);
     else
         hipLaunchKernelGGL(accumulate_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
-                           0, stream, acc, micro, numel, accumulate, vec);
+                           lds_reserve(dtype_bytes(micro_dtype) + 4 + 4 * accumulate), stream, acc,
+                           micro, numel, accumulate, vec);
     return launch_status(who);
 }
 
@@ -1500,8 +1353,9 @@ extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hpa
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
     hipLaunchKernelGGL(mt_scaled_step_kernel, dim3(static_cast<uint32_t>(plan->n_blocks)),
-                       dim3(kBlock), 0, stream, plan->d_tensors, plan->d_chunks, plan->n_chunks,
-                       plan->cpb, c, grad_scale);
+                       dim3(kBlock), lds_reserve(4 + 24 + 2 * plan->any_bf16), stream,
+                       plan->d_tensors, plan->d_chunks,
+                       c, grad_scale);
     return launch_status(who);
 }
 
@@ -1520,14 +1374,14 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
         const StepConsts c = make_consts(hp, plan->n_slices);
         const AmaxKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_amax<true>(plan->n_slices)
                                                                : pick_amax<false>(plan->n_slices);
-        hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), 0, stream,
-                           plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb, c,
-                           plan->d_chunk_amax);
+        hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+                           lds_reserve(step_bytes(plan)), stream, plan->d_tensors, plan->d_chunks, c,
+                           plan->d_tile_amax);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
     hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kBlock),
-                       0, stream, static_cast<const ShardChunks*>(plan->d_shard_chunks),
-                       static_cast<const uint32_t*>(plan->d_chunk_amax), amax_out);
+                       0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
+                       static_cast<const uint32_t*>(plan->d_tile_amax), amax_out);
     return launch_status(who);
 }
 
@@ -1552,8 +1406,8 @@ extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks,
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     hipLaunchKernelGGL(mt_cast_fp8_kernel, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
-                       0, stream, plan->d_tensors, plan->d_chunks, plan->n_chunks, plan->cpb,
-                       amax_ranks, n_ranks, plan->n_tensors, scale_out);
+                       lds_reserve(4 + 1), stream, plan->d_tensors, plan->d_chunks, amax_ranks,
+                       n_ranks, plan->n_tensors, scale_out);
     return launch_status(who);
 }
 
@@ -1573,14 +1427,14 @@ extern "C" int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_
 extern "C" int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan) {
     if (!plan) return FSDP_OK;
     hipError_t e = hipSuccess;
-    if (plan->d_tensors || plan->d_chunks || plan->d_partials || plan->d_chunk_amax ||
-        plan->d_shard_chunks) {
+    if (plan->d_tensors || plan->d_chunks || plan->d_partials || plan->d_tile_amax ||
+        plan->d_shard_tiles) {
         e = hipDeviceSynchronize();
         if (plan->d_tensors) (void)hipFree(plan->d_tensors);
         if (plan->d_chunks) (void)hipFree(plan->d_chunks);
         if (plan->d_partials) (void)hipFree(plan->d_partials);
-        if (plan->d_chunk_amax) (void)hipFree(plan->d_chunk_amax);
-        if (plan->d_shard_chunks) (void)hipFree(plan->d_shard_chunks);
+        if (plan->d_tile_amax) (void)hipFree(plan->d_tile_amax);
+        if (plan->d_shard_tiles) (void)hipFree(plan->d_shard_tiles);
     }
     delete plan;
     if (e != hipSuccess) return fail(FSDP_E_HIP, "fsdp_mt_plan_destroy: %s", hipGetErrorString(e));

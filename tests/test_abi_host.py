@@ -259,7 +259,7 @@ def test_layout_owner_matches_oracle():
 
 
 def test_capacity_error_before_any_device_work():
-    # 2**44 elements need more than 2**31 - 1 workgroups of 2048: refused on the host
+    # 2**44 elements need more workgroups of 256 than one launch holds: refused on the host
     big = 1 << 44
     assert _err(B.fsdp_cast_unshard_bf16, A, None, big, 0, stream=0) == "CAPACITY"
     assert _err(B.fsdp_reduce_grad_shard, A, None, "f32", big, 1, big, 0, stream=0) == "CAPACITY"

@@ -1,7 +1,8 @@
 """GPU parity of each entry point against the oracle, on small ragged shards.
 
 Every call goes through the C ABI (rank_step_amd.binding).  Sizes span
-several 2048-element workgroup tiles and a ragged tail; the cases cover empty
+several 2048-element chunk entries (eight 256-element workgroup tiles each)
+and a ragged tail; the cases cover empty
 shards, all-padding shards (valid = 0), partial groups, misaligned buffers
 (element-by-element path), slice strides wider than the shard, N that is not
 a power of two, NaN/Inf inputs, guard words around every buffer, and the
