@@ -66,6 +66,13 @@ namespace {
 #ifndef RS_INFLIGHT_KB
 #define RS_INFLIGHT_KB 90
 #endif
+// 256-element tiles per workgroup of the fp8 code pass (1, 2, 4 or 8): it
+// moves 5 bytes per element, so its lanes take several groups each.  It reads
+// four bytes for every one it writes and runs uncapped: the residency cap
+// helps the passes that write back what they read, not this one.
+#ifndef RS_CAST_TILES
+#define RS_CAST_TILES 4
+#endif
 // A launch whose share of that budget would allow this many resident
 // workgroups per CU or more is left uncapped (light kernels want every wave).
 #ifndef RS_OCC_UNCAPPED
@@ -558,15 +565,26 @@ __device__ __forceinline__ uint32_t fp8_code(float p, float scale) {
     return e4m3_rne(y);
 }
 
-// fp8 copy of the updated shard on [begin, end); codes 0 in the pad.
+// fp8 copy of the updated shard on [begin, end), at most TILES tiles; codes 0
+// in the pad.  Each lane loads all of its groups before converting any.
+template <int TILES>
 __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, int64_t end,
                                           float scale) {
     const int64_t vend = vector_end(T, begin, end);
-    for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
-        const f32x4 a = ld_state(reinterpret_cast<const f32x4*>(T.param + e));
-        const uint32_t o = fp8_code(a[0], scale) | (fp8_code(a[1], scale) << 8) |
-                           (fp8_code(a[2], scale) << 16) | (fp8_code(a[3], scale) << 24);
-        st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), o);
+    f32x4 a[TILES];
+#pragma unroll
+    for (int u = 0; u < TILES; ++u) {
+        const int64_t e = begin + (u * kBlock + threadIdx.x) * kGroup;
+        if (e < vend) a[u] = ld_state(reinterpret_cast<const f32x4*>(T.param + e));
+    }
+#pragma unroll
+    for (int u = 0; u < TILES; ++u) {
+        const int64_t e = begin + (u * kBlock + threadIdx.x) * kGroup;
+        if (e < vend) {
+            const uint32_t o = fp8_code(a[u][0], scale) | (fp8_code(a[u][1], scale) << 8) |
+                               (fp8_code(a[u][2], scale) << 16) | (fp8_code(a[u][3], scale) << 24);
+            st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), o);
+        }
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.out_fp8 + k, k < T.valid ? static_cast<uint8_t>(fp8_code(ld(T.param + k), scale))
@@ -586,18 +604,21 @@ __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, i
 
 // ---------------------------------------------------------------- kernels
 
-// Runs f(T, begin, end) on this workgroup's tile: tile b % 8 of chunk entry
-// b / 8, which names a shard and an element range of it.  The range is empty
-// for the tiles past the end of a shard's last, shorter entry.  Every value
-// here is uniform, so the entry and the descriptor arrive by scalar loads.
-template <typename F>
+// Runs f(T, begin, end) on this workgroup's span of TILES tiles: span
+// b % (8 / TILES) of chunk entry b / (8 / TILES), which names a shard and an
+// element range of it.  The range is empty for spans past the end of a
+// shard's last, shorter entry.  Every value here is uniform, so the entry and
+// the descriptor arrive by scalar loads.
+template <int TILES = 1, typename F>
 __device__ __forceinline__ void for_my_tile(const TensorDesc* __restrict__ tensors,
                                             const ChunkDesc* __restrict__ chunks, F&& f) {
+    static_assert(TILES >= 1 && kTilesPerChunk % TILES == 0, "spans tile a chunk entry");
+    constexpr int kSpans = kTilesPerChunk / TILES;
     const uint32_t b = blockIdx.x;
-    const ChunkDesc cd = chunks[b / kTilesPerChunk];
+    const ChunkDesc cd = chunks[b / kSpans];
     const TensorDesc T = tensors[cd.tensor];
-    const int32_t lo = static_cast<int32_t>(b % kTilesPerChunk) * kTile;
-    const int32_t n = std::max(0, std::min(kTile, cd.count - lo));
+    const int32_t lo = static_cast<int32_t>(b % kSpans) * (TILES * kTile);
+    const int32_t n = std::max(0, std::min(TILES * kTile, cd.count - lo));
     f(T, cd.begin + lo, cd.begin + lo + n);
 }
 
@@ -666,15 +687,33 @@ struct ShardTiles {
     int64_t count;
 };
 
-// Workgroup i: amax_out[i] = max over shard i's workgroups (0 if empty).
-__global__ __launch_bounds__(kBlock) void shard_amax_kernel(const ShardTiles* sc,
-                                                            const uint32_t* tile_amax,
-                                                            float* amax_out) {
+constexpr int kAmaxBlock = 1024;        // threads of the per-shard amax reduction
+
+// Workgroup i: amax_out[i] = max over shard i's workgroups (0 if empty).  A
+// large shard has tens of thousands of entries: each lane keeps four loads in
+// flight, then the 16 waves combine through LDS.
+__global__ __launch_bounds__(kAmaxBlock) void shard_amax_kernel(const ShardTiles* sc,
+                                                                const uint32_t* tile_amax,
+                                                                float* amax_out) {
+    __shared__ uint32_t s_max[kAmaxBlock / 64];
     const ShardTiles r = sc[blockIdx.x];
+    const uint32_t* p = tile_amax + r.first;
     uint32_t m = 0;
-    for (int64_t j = threadIdx.x; j < r.count; j += kBlock) m = std::max(m, ld(tile_amax + r.first + j));
-    const uint32_t t = wave_max(m);
-    if (threadIdx.x == 0) st(amax_out + blockIdx.x, __uint_as_float(t));
+    int64_t j = threadIdx.x;
+    for (; j + 3 * kAmaxBlock < r.count; j += 4 * kAmaxBlock) {
+        const uint32_t a = ld(p + j), b = ld(p + j + kAmaxBlock);
+        const uint32_t c = ld(p + j + 2 * kAmaxBlock), d = ld(p + j + 3 * kAmaxBlock);
+        m = std::max(std::max(m, std::max(a, b)), std::max(c, d));
+    }
+    for (; j < r.count; j += kAmaxBlock) m = std::max(m, ld(p + j));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x / 64] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < kAmaxBlock / 64; ++w) t = std::max(t, s_max[w]);
+        st(amax_out + blockIdx.x, __uint_as_float(t));
+    }
 }
 
 // fp8 copy of every shard: the tensor's amax is the maximum over the ranks'
@@ -685,7 +724,7 @@ __global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* _
                                                              const ChunkDesc* __restrict__ chunks,
                                                              const float* amax_ranks, int32_t n_ranks,
                                                              int64_t n_shards, float* scale_out) {
-    for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
+    for_my_tile<RS_CAST_TILES>(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         uint32_t bits = 0;
         for (int32_t r = 0; r < n_ranks; ++r)
             bits = std::max(bits, __float_as_uint(ld(amax_ranks + r * n_shards + T.index)) & 0x7fffffffu);
@@ -693,7 +732,7 @@ __global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* _
         const float den = (amax > 1e-12f || amax != amax) ? amax : 1e-12f;
         const float scale = 448.0f / den;
         if (b == 0 && scale_out && threadIdx.x == 0) st(scale_out + T.index, scale);
-        fp8_range(T, b, e, scale);
+        fp8_range<RS_CAST_TILES>(T, b, e, scale);
     });
 }
 
@@ -1379,7 +1418,7 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
                            plan->d_tile_amax);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
-    hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kBlock),
+    hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kAmaxBlock),
                        0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
                        static_cast<const uint32_t*>(plan->d_tile_amax), amax_out);
     return launch_status(who);
@@ -1405,9 +1444,10 @@ extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks,
     int32_t st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
-    hipLaunchKernelGGL(mt_cast_fp8_kernel, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
-                       lds_reserve(4 + 1), stream, plan->d_tensors, plan->d_chunks, amax_ranks,
-                       n_ranks, plan->n_tensors, scale_out);
+    hipLaunchKernelGGL(mt_cast_fp8_kernel,
+                       dim3(static_cast<uint32_t>(plan->n_chunks * (kTilesPerChunk / RS_CAST_TILES))),
+                       dim3(kBlock), 0, stream, plan->d_tensors,
+                       plan->d_chunks, amax_ranks, n_ranks, plan->n_tensors, scale_out);
     return launch_status(who);
 }
 
