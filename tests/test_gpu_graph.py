@@ -1,0 +1,113 @@
+"""HIP graph capture of the step entry points: replays equal eager calls bit for bit.
+
+A caller may capture a whole optimizer step in a HIP graph (torch's
+CUDAGraph on ROCm) once its plan exists.  The plan calls only launch
+kernels on the caller's stream: no allocation, no host synchronisation and no
+memset.  Three sequences are captured:
+  * the fused step (one launch);
+  * the clipped step: reduce + sum of squares, clip coefficient, scaled update;
+  * the fp8 step: step with amax, per-tensor amax, fp8 codes.
+Each graph is replayed several times, with eager work (fresh gradients) and
+synchronisations between the replays.  After every replay, the state and
+outputs must equal a twin state driven by the same calls made eagerly.  The
+eager calls are themselves checked against the oracle in the other GPU tests.
+"""
+
+import pytest
+import torch
+
+from rank_step_amd import binding as B
+from rank_step_amd.state import RankState
+from rank_step_amd.workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 4
+
+
+def _bits(t):
+    if t is None:
+        return None
+    return t.view(torch.int16) if t.element_size() == 2 else (
+        t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int32))
+
+
+def _same(a, b, what):
+    for name in ("master", "exp_avg", "exp_avg_sq", "grad_out", "ag_slot", "fp8"):
+        x, y = getattr(a, name), getattr(b, name)
+        if x is None:
+            continue
+        assert torch.equal(_bits(x), _bits(y)), f"{what}: {name} differs"
+
+
+def _pair(w, gpu, **kw):
+    a = RankState(w, 0, gpu, **kw)
+    b = RankState(w, 0, gpu, **kw)
+    return a, b
+
+
+def _run(w, a, b, gpu, calls, extra=()):
+    """calls(state, bufs) enqueues one step on the current stream; bufs holds
+    that state's own scalars.  Captures calls(b) once, then replays."""
+    bufs_a = {k: torch.zeros(n, dtype=dt, device=gpu) for k, (n, dt) in extra}
+    bufs_b = {k: torch.zeros(n, dtype=dt, device=gpu) for k, (n, dt) in extra}
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(b, bufs_b)
+    torch.cuda.synchronize()
+    # capture recorded the launches without running them
+    for rep in range(REPLAYS):
+        a.load_grads(rep + 1)
+        b.load_grads(rep + 1)
+        calls(a, bufs_a)
+        g.replay()
+        torch.cuda.synchronize()
+        _same(a, b, f"{w.name} replay {rep}")
+        for k in bufs_a:
+            assert torch.equal(bufs_a[k], bufs_b[k]) or (
+                torch.isnan(bufs_a[k]).all() and torch.isnan(bufs_b[k]).all()), f"{k} replay {rep}"
+    del g
+
+
+def test_fused_step_graph(gpu):
+    w = WORKLOADS[3]
+    a, b = _pair(w, gpu, bf16_out=True)
+    a.make_plan(with_grad_out=False)
+    b.make_plan(with_grad_out=False)
+    _run(w, a, b, gpu, lambda st, _: st.plan.step(w.hparams, 3))
+    a.close()
+    b.close()
+
+
+def test_clipped_step_graph(gpu):
+    w = WORKLOADS[3]
+    a, b = _pair(w, gpu, bf16_out=True, grad_out=True)
+    a.make_plan()
+    b.make_plan()
+
+    def calls(st, bufs):
+        st.plan.reduce_sqnorm(bufs["sq"])
+        B.fsdp_clip_coef(bufs["coef"], bufs["norm"], bufs["sq"], 1, 0.05)
+        st.plan.step_clipped(w.hparams, 2, bufs["coef"])
+
+    _run(w, a, b, gpu, calls, extra=(("sq", (1, torch.float64)), ("coef", (1, torch.float32)),
+                                     ("norm", (1, torch.float64))))
+    a.close()
+    b.close()
+
+
+def test_fp8_step_graph(gpu):
+    w = WORKLOADS[3]
+    a, b = _pair(w, gpu, bf16_out=False, fp8_out=True)
+    a.make_plan(with_grad_out=False, with_bf16=False)
+    b.make_plan(with_grad_out=False, with_bf16=False)
+    n = len(a.segments)
+
+    def calls(st, bufs):
+        st.plan.step_amax(w.hparams, 4, bufs["amax"])
+        st.plan.cast_fp8(bufs["amax"], 1, bufs["scale"])
+
+    _run(w, a, b, gpu, calls, extra=(("amax", (n, torch.float32)), ("scale", (n, torch.float32))))
+    a.close()
+    b.close()
