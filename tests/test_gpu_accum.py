@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("n,off", [(0, 0), (1, 0), (7, 0), (8, 0), (2048 * 3 + 517, 0), (70001, 1)])
+@pytest.mark.parametrize("n,off", [(0, 0), (1, 0), (7, 0), (8, 0), (2048 * 3 + 517, 0), (70001, 1),
+                                   (4096 + 257, 2), (4096 + 257, 4)])
 def test_grad_accumulate(gpu, dt, n, off):
     g = torch.Generator(device=gpu)
     g.manual_seed(n + off)

@@ -102,7 +102,9 @@ def test_amax_step_is_the_fused_step_bitwise_and_block_codes(gpu):
 
 
 SPECS = [(0, 0, 0), (1, 1, 0), (7, 0, 0), (8, 8, 0), (2048 * 5 + 1237, 2048 * 5 + 1230, 0),
-         (9001, 8999, 1), (4096, 3, 0), (70001, 70001, 0)]
+         (9001, 8999, 1), (4096, 3, 0), (70001, 70001, 0),
+         # one and a bit of the code pass's 1024-element spans; 4-byte aligned codes
+         (1024, 1024, 0), (1025, 1021, 0), (2048 * 3 + 1100, 2048 * 3 + 1100, 4)]
 
 
 def test_ragged_shards_and_nan(gpu):

@@ -28,7 +28,9 @@ CANARY_F32 = -7.0e33
 class Buf:
     """A device buffer with guard words on both sides; ``t`` is the payload view.
 
-    ``offset`` shifts the payload by whole elements (1 breaks 16-byte alignment).
+    ``offset`` shifts the payload by whole elements: 1 breaks every vector
+    alignment, 4 keeps fp32 buffers 16-byte aligned and bf16 buffers 8-byte
+    (but not 16-byte) aligned.
     """
 
     def __init__(self, n, dtype, device, fill=float("nan"), offset=0):
@@ -123,6 +125,11 @@ SPECS = [  # (S, valid, offset, stride_extra)
     (9001, 8999, 1, 0),                            # misaligned: element path
     (4096, 3, 0, 0),                               # nearly all padding
     (70001, 70001, 0, 0),
+    (256, 256, 0, 0),                              # exactly one workgroup tile
+    (257, 255, 0, 0),                              # one tile and one element, partial group at valid
+    (2048 + 256, 2048 + 252, 4, 0),                # bf16 buffers 8- but not 16-byte aligned: vector path
+    (4096 + 1000, 4096 + 1000, 4, 4),              # the same with a wider stride that keeps slices aligned
+    (4095, 4095, 0, 2),                            # stride that misaligns slice q > 0
 ]
 
 
