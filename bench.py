@@ -337,16 +337,19 @@ def main():
         t += 1
         st.step(t, stream)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the first and last bracket the
+    # timed region, the rest give the per-step spread
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         t += 1
         st.step(t, stream)
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     sec = ms / 1e3
     params_s = total / sec
     gbs = bpp * total / sec / 1e9
@@ -381,6 +384,9 @@ def main():
         },
         "hbm_gb_s": gbs,
         "hbm_frac_of_peak": gbs / HBM_PEAK_GBS,
+        "step_ms": {"median": per_step[len(per_step) // 2],
+                    "p95": per_step[min(len(per_step) - 1, (95 * len(per_step)) // 100)],
+                    "min": per_step[0], "max": per_step[-1]},
         "host_wall_s_timed": wall,
         "roofline": {
             "bound": "hbm",
