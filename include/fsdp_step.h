@@ -34,6 +34,12 @@
  *     Inf in inputs are not errors: they propagate per IEEE 754.
  *   - Floating point: fp32 with IEEE-correct division and square root, no
  *     flush of denormals.  Results are deterministic run to run (no atomics).
+ *   - Resources: the streaming kernels run one wave64 per workgroup and,
+ *     except the fp8 code pass, reserve up to 36 KB of LDS per workgroup that
+ *     they never touch.  The reservation caps how many of their workgroups
+ *     share a compute unit (4 to 16, from the bytes the launch moves per
+ *     element), which is where HBM serves their read/write mix best; kernels
+ *     running concurrently on the same CUs have that much less LDS.
  */
 #ifndef FSDP_STEP_H
 #define FSDP_STEP_H
