@@ -622,6 +622,15 @@ __device__ __forceinline__ void for_my_tile(const TensorDesc* __restrict__ tenso
     f(T, cd.begin + lo, cd.begin + lo + n);
 }
 
+// Slot of workgroup b's partial result among n (a multiple of 8).  Workgroups
+// are dealt to the 8 XCDs round-robin, so XCD-major slots let each XCD's L2
+// gather its workgroups' small stores into whole lines before writing back.
+constexpr int kXcds = 8;
+static_assert(kTilesPerChunk % kXcds == 0, "plan launches hold a multiple of 8 workgroups");
+__device__ __forceinline__ uint32_t xcd_slot(uint32_t b, uint32_t n) {
+    return (b % kXcds) * (n / kXcds) + b / kXcds;
+}
+
 // Multi-tensor fused step: reduce, AdamW and cast for every tile.
 template <int NS, bool BF16>
 __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
@@ -633,7 +642,7 @@ __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __res
 }
 
 // Reduce (or reduce and accumulate) into grad_shard_out; SQ: also write
-// this workgroup's sum of squares of the stored values to partials[b].
+// this workgroup's sum of squares of the stored values to its partials slot.
 template <int NS, bool BF16, bool SQ>
 __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDesc* __restrict__ tensors,
                                                                  const ChunkDesc* __restrict__ chunks,
@@ -645,7 +654,7 @@ __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDes
     });
     if constexpr (SQ) {
         const double total = wave_sum(sq);
-        if (threadIdx.x == 0) st(partials + blockIdx.x, total);
+        if (threadIdx.x == 0) st(partials + xcd_slot(blockIdx.x, gridDim.x), total);
     }
 }
 
@@ -668,7 +677,7 @@ __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc
 }
 
 // The fused step that also records, per workgroup, the largest |p'| (as
-// fp32 bits) for the fp8 copy's per-tensor scale.
+// fp32 bits, in the workgroup's slot) for the fp8 copy's per-tensor scale.
 template <int NS, bool BF16>
 __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* __restrict__ tensors,
                                                               const ChunkDesc* __restrict__ chunks,
@@ -678,10 +687,11 @@ __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* 
         fused_range<NS, BF16, true>(T, b, e, c, &am);
     });
     const uint32_t wm = wave_max(am);
-    if (threadIdx.x == 0) st(tile_amax + blockIdx.x, wm);
+    if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
 }
 
-// First workgroup and number of workgroups of each shard, by input position.
+// First workgroup and number of workgroups of each shard, by input position
+// (both multiples of 8: a shard's chunk entries are whole).
 struct ShardTiles {
     int64_t first;
     int64_t count;
@@ -689,23 +699,27 @@ struct ShardTiles {
 
 constexpr int kAmaxBlock = 1024;        // threads of the per-shard amax reduction
 
-// Workgroup i: amax_out[i] = max over shard i's workgroups (0 if empty).  A
-// large shard has tens of thousands of entries: each lane keeps four loads in
-// flight, then the 16 waves combine through LDS.
+// Workgroup i: amax_out[i] = max over shard i's workgroups (0 if empty).
+// Their slots are XCD-major (see xcd_slot): one run of count/8 in each of the
+// 8 regions of `region` slots.  A large shard has tens of thousands of them:
+// each lane keeps four loads in flight, then the 16 waves combine through LDS.
 __global__ __launch_bounds__(kAmaxBlock) void shard_amax_kernel(const ShardTiles* sc,
                                                                 const uint32_t* tile_amax,
-                                                                float* amax_out) {
+                                                                int64_t region, float* amax_out) {
     __shared__ uint32_t s_max[kAmaxBlock / 64];
     const ShardTiles r = sc[blockIdx.x];
-    const uint32_t* p = tile_amax + r.first;
+    const int64_t run = r.count / kXcds;
     uint32_t m = 0;
-    int64_t j = threadIdx.x;
-    for (; j + 3 * kAmaxBlock < r.count; j += 4 * kAmaxBlock) {
-        const uint32_t a = ld(p + j), b = ld(p + j + kAmaxBlock);
-        const uint32_t c = ld(p + j + 2 * kAmaxBlock), d = ld(p + j + 3 * kAmaxBlock);
-        m = std::max(std::max(m, std::max(a, b)), std::max(c, d));
+    for (int x = 0; x < kXcds; ++x) {
+        const uint32_t* p = tile_amax + x * region + r.first / kXcds;
+        int64_t j = threadIdx.x;
+        for (; j + 3 * kAmaxBlock < run; j += 4 * kAmaxBlock) {
+            const uint32_t a = ld(p + j), b = ld(p + j + kAmaxBlock);
+            const uint32_t c = ld(p + j + 2 * kAmaxBlock), d = ld(p + j + 3 * kAmaxBlock);
+            m = std::max(std::max(m, std::max(a, b)), std::max(c, d));
+        }
+        for (; j < run; j += kAmaxBlock) m = std::max(m, ld(p + j));
     }
-    for (; j < r.count; j += kAmaxBlock) m = std::max(m, ld(p + j));
     m = wave_max(m);
     if ((threadIdx.x & 63) == 0) s_max[threadIdx.x / 64] = m;
     __syncthreads();
@@ -1420,7 +1434,8 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
     }
     hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kAmaxBlock),
                        0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
-                       static_cast<const uint32_t*>(plan->d_tile_amax), amax_out);
+                       static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds,
+                       amax_out);
     return launch_status(who);
 }
 
