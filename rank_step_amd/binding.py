@@ -265,6 +265,7 @@ class MtPlan:
     buffers it references alive)."""
 
     def __init__(self, tensors, n_slices, slice_dtype, stream=None):
+        self.handle = None
         self._keep = tensors
         self.handle = fsdp_mt_plan_create(tensors, n_slices, slice_dtype, stream)
 
