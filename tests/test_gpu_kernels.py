@@ -92,11 +92,11 @@ class Shard:
                 "grad_shard_out": self.gout.t if self.gout else None,
                 "shard_numel": self.S, "valid": self.valid}
 
-    def check(self, name, snap, t, check_g=True):
+    def check(self, name, snap, t, check_g=True, hp=HP):
         p0, m0, v0, sl = snap
-        ref = O.rank_step(p0, m0, v0, sl, self.valid, t, HP)
+        ref = O.rank_step(p0, m0, v0, sl, self.valid, t, hp)
         va = self.valid
-        fl = PR.floors(p0[:va], m0[:va], v0[:va], sl[:, :va], {k: r[:va] for k, r in ref.items()}, HP, t)
+        fl = PR.floors(p0[:va], m0[:va], v0[:va], sl[:, :va], {k: r[:va] for k, r in ref.items()}, hp, t)
         gp = self.p.t.cpu().numpy()
         PR.assert_close(f"{name} p", gp[:va], ref["p"][:va], fl["p"])
         PR.assert_close(f"{name} m", self.m.t.cpu().numpy()[:va], ref["m"][:va], fl["m"])
@@ -265,3 +265,37 @@ def test_cast_rounding_classes(gpu):
     with np.errstate(invalid="ignore"):
         ref = O.bf16_rne(f)
     assert np.array_equal(got, ref)
+
+
+# Hyperparameters at the edges of their ranges: no step, no decay, no first or
+# second moment memory, no epsilon, and step counts where both bias
+# corrections have reached 1.
+EDGE_HPARAMS = [
+    ("lr 0", dict(HP, lr=0.0), 1),
+    ("no weight decay", dict(HP, weight_decay=0.0), 2),
+    ("beta1 0", dict(HP, beta1=0.0), 2),
+    ("beta2 0", dict(HP, beta2=0.0), 2),
+    ("eps 0", dict(HP, eps=0.0), 1),
+    ("step 10000", HP, 10000),
+    ("step 2^40", HP, 1 << 40),
+    ("large lr and decay", dict(HP, lr=0.5, weight_decay=0.5), 3),
+]
+
+
+@pytest.mark.parametrize("name,hp,t", EDGE_HPARAMS, ids=[e[0] for e in EDGE_HPARAMS])
+def test_hparam_edges(gpu, name, hp, t):
+    N, sdt = 4, "bf16"
+    shards = [Shard(S, va, N, sdt, gpu, seed=300 + i, offset=o, stride_extra=x)
+              for i, (S, va, o, x) in enumerate(SPECS)]
+    snaps = [s.snapshot() for s in shards]
+    plan = B.MtPlan([s.mt() for s in shards], N, sdt)
+    plan.step(hp, t)
+    torch.cuda.synchronize()
+    for i, (s, snap) in enumerate(zip(shards, snaps)):
+        s.check(f"{name} shard {i}", snap, t, hp=hp)
+        if hp["lr"] == 0.0:
+            # no step at all: decay factor 1 and a zero update leave p's bits alone
+            va = s.valid
+            assert np.array_equal(s.p.t.cpu().numpy()[:va].view(np.uint32),
+                                  snap[0][:va].astype(np.float32).view(np.uint32)), name
+    plan.close()
