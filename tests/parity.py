@@ -68,7 +68,10 @@ def free_floors(prev, sl, ref, hp, t):
     return {"g": sG, "m": s_m, "v": s_v, "p": s_p}
 
 
-def assert_close(name, got, ref, floor, tol=TOL):
+def assert_close(name, got, ref, floor, tol=TOL, abs_tol=0.0):
+    """``abs_tol`` adds an absolute allowance: used only where results lie in
+    fp32's subnormal range, whose spacing 2**-149 is coarser than any
+    relative bound there."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     bad_nan = np.isnan(got) != np.isnan(ref)
@@ -77,7 +80,7 @@ def assert_close(name, got, ref, floor, tol=TOL):
     assert np.array_equal(got[inf], ref[inf]), f"{name}: infinity mismatch"
     ok = ~np.isnan(ref) & ~inf
     err = np.abs(got[ok] - ref[ok])
-    lim = tol * np.maximum(np.abs(ref[ok]), floor[ok])
+    lim = tol * np.maximum(np.abs(ref[ok]), floor[ok]) + abs_tol
     bad = err > lim
     if bad.any():
         i = np.flatnonzero(ok)[np.flatnonzero(bad)[:5]]

@@ -299,3 +299,57 @@ def test_hparam_edges(gpu, name, hp, t):
             assert np.array_equal(s.p.t.cpu().numpy()[:va].view(np.uint32),
                                   snap[0][:va].astype(np.float32).view(np.uint32)), name
     plan.close()
+
+
+def test_fp32_range_edges(gpu):
+    """Where fp32's range, not its precision, decides the result.
+
+    * Overflow: a mean gradient of about 1e30 has a square beyond fp32, so v'
+      saturates to +inf, m'/(sqrt(v')+eps) is 0 and p' is exactly p*(1-lr*wd),
+      as fp32 AdamW computes it (the float64 oracle keeps the square finite and
+      is not the reference for these elements).
+    * Subnormals: parameters, first moments and gradients in fp32's subnormal
+      range, compared with the oracle with an absolute allowance of a few
+      subnormal spacings (2**-149) on top of the relative bound.  The second
+      moments stay normal: where eps alone bounds the denominator, the
+      update multiplies a subnormal moment's absolute error by lr/eps, a
+      property of fp32 arithmetic rather than of the kernel.
+    """
+    N, sdt, S = 4, "f32", 4096
+    s = Shard(S, S, N, sdt, gpu, seed=21)
+    sl = s.sl.t.view(N, S)
+    big = slice(0, 256)
+    sl[:, big] = 0.0
+    sl[0, big] = torch.linspace(-1e30, 1e30, 256, device=gpu)
+    sl[0, 128] = 3e30                                   # no exact zero in the group
+    sub = slice(256, 512)                                # subnormal p and m, zero gradient
+    sl[:, sub] = 0.0
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(3)
+    s.p.t[sub] = torch.randn(256, generator=gen, device=gpu) * 1e-40
+    s.m.t[sub] = torch.randn(256, generator=gen, device=gpu) * 1e-40
+    s.v.t[sub] = torch.rand(256, generator=gen, device=gpu) * 1e-6 + 1e-7
+    tiny = slice(512, 768)                               # subnormal gradients
+    sl[:, tiny] = torch.randn(N, 256, generator=gen, device=gpu) * 1e-39
+    snap = s.snapshot()
+    plan = B.MtPlan([s.mt()], N, sdt)
+    plan.step(HP, 1)
+    torch.cuda.synchronize()
+    p0, m0, v0, x = snap
+    gp, gm, gv = (b.t.cpu().numpy() for b in (s.p, s.m, s.v))
+
+    decay = np.float32(1.0 - HP["lr"] * HP["weight_decay"])
+    assert np.all(np.isposinf(gv[big])), "v' of an overflowing square must be +inf"
+    want = (p0[big].astype(np.float32) * decay).astype(np.float32)
+    assert np.array_equal(gp[big].view(np.uint32), want.view(np.uint32)), "p' must be p*(1-lr*wd)"
+    ref = O.rank_step(p0, m0, v0, x, S, 1, HP)
+    fl = PR.floors(p0, m0, v0, x, ref, HP, 1)
+    PR.assert_close("overflow m", gm[big], ref["m"][big], fl["m"][big])
+
+    rest = np.r_[256:S]
+    allowance = 4 * 2.0 ** -149
+    for nm, got in (("p", gp), ("m", gm), ("v", gv)):
+        PR.assert_close(f"range {nm}", got[rest], ref[nm][rest], fl[nm][rest], abs_tol=allowance)
+    bits = PR.bf16_bits(s.out.t)
+    assert np.array_equal(bits, O.bf16_rne(gp.astype(np.float64))), "bf16 is RNE of the fp32 result"
+    plan.close()
