@@ -10,7 +10,14 @@ where s_x is the magnitude of the terms that form x, so that cancellation
     s_G = mean_q |x_q|                               reduced gradient
     s_m = beta1*|m| + (1-beta1)*s_G                  first moment
     s_v = beta2*v + (1-beta2)*s_G^2                  second moment
-    s_p = |p|*(1-lr*wd) + lr*(s_m/bc1)/(sqrt(vhat)+eps)   parameter
+    s_p = |p|*(1-lr*wd) + lr*(s_m/bc1)/(sqrt(vhat)+eps) + d_p   parameter
+
+d_p carries the allowed error of G through the denominator: G's allowance
+moves vhat by dvhat = (1-beta2)*2*|G|*s_G/bc2, and the update
+lr*mhat/(sqrt(vhat)+eps) by lr*|mhat|*dvhat / (2*sqrt(vhat)*(sqrt(vhat)+eps)^2)
+(first order).  It matters only where G cancels and v is tiny beside m, so
+that the update hangs on a few bits of G; elsewhere it is about one more
+update's worth.
 
 The inputs of the oracle are the GPU's own state before the step, widened
 exactly (per-step resynchronisation), so one step's rounding is judged.
@@ -42,6 +49,22 @@ def widen_slices(t, dtype):
     return t.detach().to("cpu").numpy().astype(np.float64)
 
 
+def _denominator_term(ref, sl, sG, hp, t):
+    """d_p above: the update's sensitivity to G's allowance through vhat.
+    ``sl`` are the slices as the update sees them (already scaled by a clip
+    coefficient), so their mean is the G the update uses."""
+    lr, b1, b2, eps = hp["lr"], hp["beta1"], hp["beta2"], hp["eps"]
+    bc1 = 1 - b1 ** t
+    bc2 = 1 - b2 ** t
+    sq = np.sqrt(ref["v"] / bc2)
+    g = np.mean(sl, axis=0) if sl.shape[0] else np.zeros(0)
+    dvhat = (1 - b2) * 2 * np.abs(g) * sG / bc2
+    mhat = np.abs(ref["m"]) / bc1
+    with np.errstate(divide="ignore", invalid="ignore"):
+        d = lr * mhat * dvhat / (2 * sq * (sq + eps) ** 2)
+    return np.where(sq > 0, d, 0.0)
+
+
 def floors(p, m, v, sl, ref, hp, t):
     lr, b1, b2, eps, wd = hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"]
     sG = np.mean(np.abs(sl), axis=0) if sl.shape[0] else np.zeros(0)
@@ -50,7 +73,8 @@ def floors(p, m, v, sl, ref, hp, t):
     bc1 = 1 - b1 ** t
     bc2 = 1 - b2 ** t
     vhat = ref["v"] / bc2
-    s_p = np.abs(p) * (1 - lr * wd) + lr * (s_m / bc1) / (np.sqrt(vhat) + eps)
+    s_p = (np.abs(p) * (1 - lr * wd) + lr * (s_m / bc1) / (np.sqrt(vhat) + eps)
+           + _denominator_term(ref, sl, sG, hp, t))
     return {"g": sG, "m": s_m, "v": s_v, "p": s_p}
 
 
@@ -64,7 +88,8 @@ def free_floors(prev, sl, ref, hp, t):
     s_m = b1 * prev["m"] + (1 - b1) * sG
     s_v = b2 * prev["v"] + (1 - b2) * sG * sG
     vhat = ref["v"] / (1 - b2 ** t)
-    s_p = prev["p"] * (1 - lr * wd) + lr * (s_m / (1 - b1 ** t)) / (np.sqrt(vhat) + eps)
+    s_p = (prev["p"] * (1 - lr * wd) + lr * (s_m / (1 - b1 ** t)) / (np.sqrt(vhat) + eps)
+           + _denominator_term(ref, sl, sG, hp, t))
     return {"g": sG, "m": s_m, "v": s_v, "p": s_p}
 
 

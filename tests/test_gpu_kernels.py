@@ -134,7 +134,7 @@ SPECS = [  # (S, valid, offset, stride_extra)
 
 
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 8, 16, 33])
 def test_mt_step_parity(gpu, N, sdt):
     shards = [Shard(S, va, N, sdt, gpu, seed=100 * N + i, offset=o, stride_extra=x,
                     bf16=(i % 3 != 1), gout=(i % 2 == 0))
@@ -158,7 +158,7 @@ def test_mt_step_parity(gpu, N, sdt):
 
 
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 3, 4, 8])
+@pytest.mark.parametrize("N", [1, 3, 4, 8, 33])
 def test_single_calls_parity(gpu, N, sdt):
     for i, (S, va, o, x) in enumerate(SPECS):
         s = Shard(S, va, N, sdt, gpu, seed=1000 + i, offset=o, stride_extra=x)
