@@ -146,3 +146,47 @@ def check_pad_zero(name, arr, valid):
     else:
         assert np.all(tail.view(np.uint32 if tail.dtype == np.float32 else np.uint64) == 0), \
             f"{name}: pad not +0"
+
+
+def fp32_replica_step(p, m, v, x, valid, t, hp, grad_scale=None):
+    """The kernel's fp32 operation sequence, replayed in numpy (test-side
+    only; the oracle stays float64).  Sum of the slices in slice order,
+    one division by N (a multiplication by 1/N when N is a power of two);
+    then AdamW with the fused multiply-adds the kernel writes, each rounded
+    once (the exact product plus the addend, in 64-bit extended precision,
+    rounded to fp32), correctly rounded division and square root, no flush
+    of subnormals.  ``grad_scale`` (fp32, the clip coefficient) multiplies the
+    reduced gradient once, in fp32.  Returns fp32 p', m', v' over the first
+    ``valid`` elements."""
+    f32 = np.float32
+    ld = np.longdouble
+    N = x.shape[0]
+
+    def fma(a, b, c):
+        return (a.astype(ld) * b.astype(ld) + c.astype(ld)).astype(f32)
+
+    xs = x[:, :valid].astype(f32)
+    s = xs[0].copy()
+    for q in range(1, N):
+        s = (s + xs[q]).astype(f32)
+    if N > 1:
+        s = s * f32(1.0 / N) if N & (N - 1) == 0 else s / f32(N)
+    g = s.astype(f32)
+    if grad_scale is not None:
+        g = (g * f32(grad_scale)).astype(f32)
+    bc1 = 1.0 - hp["beta1"] ** t
+    bc2 = 1.0 - hp["beta2"] ** t
+    decay = f32(1.0 - hp["lr"] * hp["weight_decay"])
+    b1, omb1 = f32(hp["beta1"]), f32(1.0 - hp["beta1"])
+    b2, omb2 = f32(hp["beta2"]), f32(1.0 - hp["beta2"])
+    step = f32(hp["lr"] / bc1)
+    isb = f32(1.0 / np.sqrt(bc2))
+    eps = f32(hp["eps"])
+    p, m, v = (a[:valid].astype(f32) for a in (p, m, v))
+    full = np.full(valid, 1, dtype=f32)
+    p1 = (p * decay).astype(f32)
+    mn = fma(b1 * full, m, (omb1 * g).astype(f32))
+    vn = fma(b2 * full, v, (omb2 * (g * g).astype(f32)).astype(f32))
+    den = fma(np.sqrt(vn).astype(f32), isb * full, eps * full)
+    pn = fma(-step * full, (mn / den).astype(f32), p1)
+    return pn, mn, vn

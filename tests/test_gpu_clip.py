@@ -26,6 +26,16 @@ from tests import parity as PR
 pytestmark = pytest.mark.gpu
 
 
+def _replica_equal(name, st, p0, m0, v0, sl, valid, t, hp, coef, idx=None):
+    """The clipped update, bit for bit against the kernel's stated fp32
+    sequence: the stored fp32 mean gradient times the fp32 coefficient."""
+    rp, rm, rv = PR.fp32_replica_step(p0, m0, v0, sl, valid, t, hp, grad_scale=coef)
+    for nm, got, want in (("p", st.master, rp), ("m", st.exp_avg, rm), ("v", st.exp_avg_sq, rv)):
+        g = (got if idx is None else got[idx]).cpu().numpy()[:valid]
+        bad = g.view(np.uint32) != want.view(np.uint32)
+        assert not bad.any(), f"{name} {nm}: {bad.sum()} elements differ from the fp32 replica"
+
+
 def _clipped_round(states, max_norm, t, dev):
     """One clipped step over several ranks held on one device."""
     n = len(states)
@@ -85,6 +95,7 @@ def test_tiny_mlp_clipped_every_rank(gpu):
             PR.assert_close(f"clip rank {i} t={t} m", st.exp_avg.cpu().numpy(), ref["m"], fl["m"])
             PR.assert_close(f"clip rank {i} t={t} v", st.exp_avg_sq.cpu().numpy(), ref["v"], fl["v"])
             PR.check_bf16(f"clip rank {i} t={t} bf16", PR.bf16_bits(st.ag_slot), gp, ref["p"], fl["p"])
+            _replica_equal(f"clip rank {i} t={t}", st, p0, m0, v0, sl, held, t, w.hparams, coef)
     for st in states:
         st.close()
 
@@ -142,6 +153,7 @@ def test_llama7b_clipped_full_size(gpu):
     PR.assert_close("7b clipped m", PR.f64(st.exp_avg[idx]), ref["m"], fl["m"])
     PR.assert_close("7b clipped v", PR.f64(st.exp_avg_sq[idx]), ref["v"], fl["v"])
     PR.check_bf16("7b clipped bf16", PR.bf16_bits(st.ag_slot[idx]), gp, ref["p"], fl["p"])
+    _replica_equal("7b clipped", st, p0, m0, v0, sl, p0.size, 1, w.hparams, coef, idx)
     st.close()
     del st
     torch.cuda.empty_cache()

@@ -355,46 +355,6 @@ def test_fp32_range_edges(gpu):
     plan.close()
 
 
-def _fp32_replica(p, m, v, x, valid, t, hp):
-    """The kernel's fp32 operation sequence, replayed in numpy (test-side
-    only; the oracle stays float64).  Sum of the slices in slice order,
-    one division by N (a multiplication by 1/N when N is a power of two);
-    then AdamW with the fused multiply-adds the kernel writes, each rounded
-    once (the exact product plus the addend, in 64-bit extended precision,
-    rounded to fp32), correctly rounded division and square root, no flush
-    of subnormals.  Returns fp32 p', m', v' over the first ``valid`` elements."""
-    f32 = np.float32
-    ld = np.longdouble
-    N = x.shape[0]
-
-    def fma(a, b, c):
-        return (a.astype(ld) * b.astype(ld) + c.astype(ld)).astype(f32)
-
-    xs = x[:, :valid].astype(f32)
-    s = xs[0].copy()
-    for q in range(1, N):
-        s = (s + xs[q]).astype(f32)
-    if N > 1:
-        s = s * f32(1.0 / N) if N & (N - 1) == 0 else s / f32(N)
-    g = s.astype(f32)
-    bc1 = 1.0 - hp["beta1"] ** t
-    bc2 = 1.0 - hp["beta2"] ** t
-    decay = f32(1.0 - hp["lr"] * hp["weight_decay"])
-    b1, omb1 = f32(hp["beta1"]), f32(1.0 - hp["beta1"])
-    b2, omb2 = f32(hp["beta2"]), f32(1.0 - hp["beta2"])
-    step = f32(hp["lr"] / bc1)
-    isb = f32(1.0 / np.sqrt(bc2))
-    eps = f32(hp["eps"])
-    p, m, v = (a[:valid].astype(f32) for a in (p, m, v))
-    full = np.full(valid, 1, dtype=f32)
-    p1 = (p * decay).astype(f32)
-    mn = fma(b1 * full, m, (omb1 * g).astype(f32))
-    vn = fma(b2 * full, v, (omb2 * (g * g).astype(f32)).astype(f32))
-    den = fma(np.sqrt(vn).astype(f32), isb * full, eps * full)
-    pn = fma(-step * full, (mn / den).astype(f32), p1)
-    return pn, mn, vn
-
-
 @pytest.mark.parametrize("sdt,N", [("f32", 1), ("bf16", 3), ("bf16", 8), ("f32", 16), ("f32", 33)])
 def test_fp32_replica_bit_exact(gpu, sdt, N):
     """Every element of the fused step equals the kernel's stated fp32
@@ -411,7 +371,7 @@ def test_fp32_replica_bit_exact(gpu, sdt, N):
             va = s.valid
             if va == 0:
                 continue
-            rp, rm, rv = _fp32_replica(p0, m0, v0, x, va, t, HP)
+            rp, rm, rv = PR.fp32_replica_step(p0, m0, v0, x, va, t, HP)
             for nm, got, want in (("p", s.p.t, rp), ("m", s.m.t, rm), ("v", s.v.t, rv)):
                 g = got.cpu().numpy()[:va]
                 bad = g.view(np.uint32) != want.view(np.uint32)

@@ -146,6 +146,12 @@ def _check_sampled(st, idx_t, before, t, name):
     PR.assert_close(f"{name} v", PR.f64(st.exp_avg_sq[idx_t]), ref["v"], fl["v"])
     if st.ag_slot is not None:
         PR.check_bf16(f"{name} bf16", PR.bf16_bits(st.ag_slot[idx_t]), gp, ref["p"], fl["p"])
+    # and bit for bit against the kernel's stated fp32 sequence
+    rp, rm, rv = PR.fp32_replica_step(p0, m0, v0, sl, p0.size, t, hp)
+    for nm, got, want in (("p", st.master, rp), ("m", st.exp_avg, rm), ("v", st.exp_avg_sq, rv)):
+        g = got[idx_t].cpu().numpy()
+        bad = g.view(np.uint32) != want.view(np.uint32)
+        assert not bad.any(), f"{name} {nm}: {bad.sum()} elements differ from the fp32 replica"
 
 
 def _run_sampled(cfg, gpu, n_sample, full_steps=()):
