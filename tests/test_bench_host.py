@@ -37,3 +37,12 @@ def test_traffic_record_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
     (tmp_path / "profiles" / "traffic_x.json").write_text(json.dumps(rec))
     assert bench.measured_traffic("x", 123) is None
     assert bench.measured_traffic("missing", 123) is None
+
+
+def test_committed_traffic_record_matches_the_current_kernels():
+    """The counters in profiles/ were taken on the kernels as they stand: a
+    kernel change without a new counter run would leave the bench's
+    roofline traffic empty."""
+    rec = bench.measured_traffic("llama7b_full_n8", 842_301_952)
+    assert rec is not None, "profiles/traffic_llama7b_full_n8.json is stale: re-run the counters"
+    assert 1.0 <= rec / (42 * 842_301_952) < 1.05     # FETCH+WRITE within 5 % of the algorithmic bytes
