@@ -234,7 +234,8 @@ int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const float* param_fp
  *   grad_shard_out                   device fp32 [shard_numel] or NULL (the
  *                                    reduced gradient is not stored)
  *   unshard_fp8_out                  device fp8 codes [shard_numel] or NULL:
- *                                    written only by fsdp_mt_cast_fp8 */
+ *                                    written only by fsdp_mt_cast_fp8 and
+ *                                    fsdp_mt_step_fp8 */
 typedef struct {
     float* param_fp32;
     float* exp_avg;
@@ -245,7 +246,7 @@ typedef struct {
     float* grad_shard_out;
     int64_t shard_numel;
     int64_t valid;
-    uint8_t* unshard_fp8_out;     /* NULL => no fp8 copy (see fsdp_mt_cast_fp8) */
+    uint8_t* unshard_fp8_out;     /* NULL => no fp8 copy (see fsdp_mt_cast_fp8, fsdp_mt_step_fp8) */
 } fsdp_mt_tensor;
 
 typedef struct fsdp_mt_plan fsdp_mt_plan; /* opaque */
@@ -375,7 +376,11 @@ int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t micro_dtype,
  *   fsdp_mt_step_amax   the fused step, plus each tensor's local amax of the
  *                       updated parameter (no extra pass over memory)
  *   (all-reduce max of the per-rank amax arrays: outside this library)
- *   fsdp_mt_cast_fp8    reads the updated fp32 shards, writes the codes */
+ *   fsdp_mt_cast_fp8    reads the updated fp32 shards, writes the codes
+ * or, with the scale fixed before the step (delayed scaling: the scale the
+ * previous step derived from its amax), in one pass:
+ *   fsdp_mt_step_fp8    the fused step writing the codes with the given
+ *                       scales, plus this step's amax for the next scales */
 
 /* The step of fsdp_mt_step (same outputs, bit-identical), and for every
  * shard i of the plan, in input order, the largest |p'| of its updated local
@@ -393,6 +398,24 @@ int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, floa
  * unshard_fp8_out (else FSDP_E_ARG).  One kernel launch. */
 int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_ranks,
                          float* scale_out, hipStream_t stream);
+
+/* The step of fsdp_mt_step (same fp32 outputs and bf16 copies,
+ * bit-identical), which also writes every shard's fp8 codes in the same pass:
+ *   code = RNE_e4m3(clamp(fp32(p' * scale_in[i]), -448, 448)), 0 in the pad
+ * and, as fsdp_mt_step_amax does, each shard's largest |p'| to amax_out[i].
+ *   scale_in  device fp32 [n_tensors], read: shard i's scale, chosen before
+ *             the step (e.g. the scale_out of the previous step's
+ *             fsdp_mt_cast_fp8, or 448 / max(amax, 1e-12) of the previous
+ *             step's all-reduced amax)
+ *   amax_out  device fp32 [n_tensors], written; must not overlap scale_in
+ * This is the delayed-scaling reading of [FSDP ch.18] §18.27 (the page fixes
+ * neither recipe): values that grew past the previous amax saturate to
+ * +-448 until the next scale catches up.  Every non-empty shard must have an
+ * unshard_fp8_out (else FSDP_E_ARG).  Two kernel launches (the step and the
+ * per-shard amax), none when the plan is empty.  Uses the plan's
+ * per-workgroup scratch: calls on one plan must not overlap. */
+int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, const float* scale_in,
+                         float* amax_out, hipStream_t stream);
 
 /* Sizes of a plan (host only). */
 int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info_out);

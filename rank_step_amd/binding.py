@@ -31,8 +31,8 @@ EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
            "fsdp_adamw_shard_step", "fsdp_cast_unshard_bf16", "fsdp_mt_plan_create",
            "fsdp_mt_step", "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy",
            "fsdp_mt_reduce_sqnorm", "fsdp_clip_coef", "fsdp_mt_step_clipped",
-           "fsdp_mt_step_amax", "fsdp_mt_cast_fp8", "fsdp_mt_reduce_accumulate",
-           "fsdp_grad_accumulate")
+           "fsdp_mt_step_amax", "fsdp_mt_cast_fp8", "fsdp_mt_step_fp8",
+           "fsdp_mt_reduce_accumulate", "fsdp_grad_accumulate")
 
 
 class FsdpError(RuntimeError):
@@ -114,6 +114,7 @@ def lib():
             "fsdp_mt_step_clipped": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
             "fsdp_mt_step_amax": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
             "fsdp_mt_cast_fp8": [vp, vp, i32, vp, vp],
+            "fsdp_mt_step_fp8": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp],
             "fsdp_mt_reduce_accumulate": [vp, i32, vp, vp],
             "fsdp_grad_accumulate": [vp, vp, i32, i64, i32, vp],
         }
@@ -250,6 +251,12 @@ def fsdp_mt_cast_fp8(plan, amax_ranks, n_ranks, scale_out=None, stream=None):
                                   _stream(stream)))
 
 
+def fsdp_mt_step_fp8(plan, hp, step, scale_in, amax_out, stream=None):
+    h = _hparams(hp, step)
+    _check(lib().fsdp_mt_step_fp8(plan, ctypes.byref(h), _ptr(scale_in), _ptr(amax_out),
+                                  _stream(stream)))
+
+
 def fsdp_mt_reduce_accumulate(plan, accumulate, sqnorm_out=None, stream=None):
     _check(lib().fsdp_mt_reduce_accumulate(plan, int(bool(accumulate)), _ptr(sqnorm_out),
                                            _stream(stream)))
@@ -289,6 +296,9 @@ class MtPlan:
 
     def cast_fp8(self, amax_ranks, n_ranks, scale_out=None, stream=None):
         fsdp_mt_cast_fp8(self.handle, amax_ranks, n_ranks, scale_out, stream)
+
+    def step_fp8(self, hp, step, scale_in, amax_out, stream=None):
+        fsdp_mt_step_fp8(self.handle, hp, step, scale_in, amax_out, stream)
 
     def close(self):
         if self.handle is not None:

@@ -66,12 +66,22 @@ namespace {
 #ifndef RS_INFLIGHT_KB
 #define RS_INFLIGHT_KB 90
 #endif
+// The fused steps that also reduce |p'| and write fp8 codes keep each wave
+// longer for the same bytes, so they need more resident waves: their budget.
+#ifndef RS_INFLIGHT_KB_FP8
+#define RS_INFLIGHT_KB_FP8 105
+#endif
 // 256-element tiles per workgroup of the fp8 code pass (1, 2, 4 or 8): it
 // moves 5 bytes per element, so its lanes take several groups each.  It reads
 // four bytes for every one it writes and runs uncapped: the residency cap
 // helps the passes that write back what they read, not this one.
 #ifndef RS_CAST_TILES
 #define RS_CAST_TILES 4
+#endif
+// 1: fp8 codes from the hardware's packed fp32 -> OCP E4M3 conversion;
+// 0: from the integer rounding e4m3_rne.
+#ifndef RS_FP8_HW
+#define RS_FP8_HW 1
 #endif
 // A launch whose share of that budget would allow this many resident
 // workgroups per CU or more is left uncapped (light kernels want every wave).
@@ -103,10 +113,11 @@ static_assert(all_admitted(kMinOcc),
               "every capped residency fits one workgroup's LDS limit and admits exactly its count");
 
 // The LDS reservation of a streaming launch whose lanes each move
-// `bytes_per_elem` bytes for each of their kGroup elements.
-constexpr size_t lds_reserve(int64_t bytes_per_elem) {
+// `bytes_per_elem` bytes for each of their kGroup elements, for an in-flight
+// budget of `budget_kb` per CU.
+constexpr size_t lds_reserve(int64_t bytes_per_elem, int64_t budget_kb = RS_INFLIGHT_KB) {
     const int64_t per_wg = bytes_per_elem * kTile;
-    const int64_t occ = per_wg > 0 ? int64_t(RS_INFLIGHT_KB) * 1024 / per_wg : RS_OCC_UNCAPPED;
+    const int64_t occ = per_wg > 0 ? budget_kb * 1024 / per_wg : RS_OCC_UNCAPPED;
     if (occ >= RS_OCC_UNCAPPED) return 0;
     return lds_for(static_cast<int>(std::min<int64_t>(std::max<int64_t>(occ, kMinOcc), kMaxOcc)));
 }
@@ -166,6 +177,54 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
     const uint32_t qnan = ((u >> 16) & 0x8000u) | 0x7fc0u;
     return (u & 0x7fffffffu) > 0x7f800000u ? qnan : rounded;
+}
+
+// fp32 -> OCP FP8 E4M3 ("e4m3fn": bias 7, 3 fraction bits, largest finite
+// 448, no infinities), round to nearest with ties to even.  The input is
+// already within [-448, 448] or NaN.  Normal results: round the fp32
+// fraction to 3 bits (the carry may raise the exponent) and rebias the
+// exponent from 127 to 7.  Below 2^-6 the grid is 2^-9: scale by 2^9 (exact)
+// and round to an integer.  NaN becomes S.1111.111.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t ua = u & 0x7fffffffu;
+    const float a = __uint_as_float(ua);
+    const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+    const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);
+    const uint32_t nrm = (r >> 20) - (120u << 3);
+    const uint32_t code = ua > 0x7f800000u ? 0x7fu : (a < 0.015625f ? sub : nrm);
+    return sign | code;
+}
+
+// The value an fp8 code encodes: the product with the tensor's scale in fp32,
+// clamped to +-448 (NaN kept).
+__device__ __forceinline__ float fp8_scaled(float p, float scale) {
+    const float y = p * scale;
+    return y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
+}
+
+// The fp8 code of one updated value, rounded once.  gfx950's packed
+// conversion rounds fp32 to OCP E4M3 to nearest even; on the clamped range
+// it gives the same codes as e4m3_rne (checked over every fp32 pattern), in
+// one instruction per pair instead of about fifteen per value.
+__device__ __forceinline__ uint32_t fp8_code(float p, float scale) {
+    if constexpr (RS_FP8_HW)
+        return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(fp8_scaled(p, scale), 0.0f, 0, false)) & 0xffu;
+    else
+        return e4m3_rne(fp8_scaled(p, scale));
+}
+
+// Codes of four values, element j in byte j.
+__device__ __forceinline__ uint32_t pack_fp8(const f32x4& p, float scale) {
+    if constexpr (RS_FP8_HW) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_scaled(p[0], scale), fp8_scaled(p[1], scale), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_scaled(p[2], scale), fp8_scaled(p[3], scale), w, true);
+        return static_cast<uint32_t>(w);
+    } else {
+        return fp8_code(p[0], scale) | (fp8_code(p[1], scale) << 8) | (fp8_code(p[2], scale) << 16) |
+               (fp8_code(p[3], scale) << 24);
+    }
 }
 
 // Mean of the slices: the fp32 sum in slice order, then one division by N.
@@ -331,10 +390,11 @@ __device__ __forceinline__ u32x2 pack_bf16(const f32x4& p) {
 // reduced gradient when the shard has a grad_shard_out.
 // AMAX: also fold |p'| of the group into *amax (fp32 bit patterns of
 // non-negative values order like the values; NaN patterns sort above all).
-template <bool WRITE_G = true, bool AMAX = false>
+// FP8: also store the fp8 codes of p' with the given per-tensor scale.
+template <bool WRITE_G = true, bool AMAX = false, bool FP8 = false>
 __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup],
                                              const TensorDesc& T, int64_t e, const StepConsts& c,
-                                             uint32_t* amax = nullptr) {
+                                             uint32_t* amax = nullptr, float fp8_scale = 0.0f) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float p = s.p[j], m = s.m[j], v = s.v[j];
@@ -348,6 +408,9 @@ __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup]
     st_state(reinterpret_cast<f32x4*>(T.m + e), s.m);
     st_state(reinterpret_cast<f32x4*>(T.v + e), s.v);
     if (T.out_bf16) st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(s.p));
+    if constexpr (FP8) {
+        if (T.out_fp8) st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), pack_fp8(s.p, fp8_scale));
+    }
     if (WRITE_G && T.grad_out)
         st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
 }
@@ -370,10 +433,11 @@ __device__ __forceinline__ float reduce_elem(const TensorDesc& T, int64_t k, con
     return finish_mean(s, c);
 }
 
-// The whole fused step on element k (any alignment); +0 everywhere in the pad.
-template <bool BF16, bool AMAX = false>
+// The whole fused step on element k (any alignment); +0 everywhere in the pad
+// (fp8 code 0).
+template <bool BF16, bool AMAX = false, bool FP8 = false>
 __device__ __forceinline__ void fused_elem(const TensorDesc& T, int64_t k, const StepConsts& c,
-                                           uint32_t* amax = nullptr) {
+                                           uint32_t* amax = nullptr, float fp8_scale = 0.0f) {
     if (k < T.valid) {
         const float g = reduce_elem<BF16>(T, k, c);
         float p = ld(T.param + k), m = ld(T.m + k), v = ld(T.v + k);
@@ -383,12 +447,14 @@ __device__ __forceinline__ void fused_elem(const TensorDesc& T, int64_t k, const
         st(T.m + k, m);
         st(T.v + k, v);
         if (T.out_bf16) st(T.out_bf16 + k, static_cast<uint16_t>(bf16_rne(p)));
+        if (FP8 && T.out_fp8) st(T.out_fp8 + k, static_cast<uint8_t>(fp8_code(p, fp8_scale)));
         if (T.grad_out) st(T.grad_out + k, g);
     } else {
         st(T.param + k, 0.0f);
         st(T.m + k, 0.0f);
         st(T.v + k, 0.0f);
         if (T.out_bf16) st(T.out_bf16 + k, uint16_t(0));
+        if (FP8 && T.out_fp8) st(T.out_fp8 + k, uint8_t(0));
         if (T.grad_out) st(T.grad_out + k, 0.0f);
     }
 }
@@ -423,10 +489,12 @@ __device__ __forceinline__ int64_t vector_end(const TensorDesc& T, int64_t begin
     return std::max(vend, begin);
 }
 
-// The fused step on elements [begin, end) of shard T; `begin` is a multiple of kGroup.
-template <int NS, bool BF16, bool AMAX = false>
+// The fused step on elements [begin, end) of shard T; `begin` is a multiple of
+// kGroup.  AMAX and FP8 as in update_store.
+template <int NS, bool BF16, bool AMAX = false, bool FP8 = false>
 __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, int64_t end,
-                                            const StepConsts& c, uint32_t* amax = nullptr) {
+                                            const StepConsts& c, uint32_t* amax = nullptr,
+                                            float fp8_scale = 0.0f) {
     const int64_t vend = vector_end(T, begin, end);
     for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         StateRegs s;
@@ -437,15 +505,16 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
             load_state(s, T, e);
             float g[kGroup];
             reduce_regs<NS, BF16>(sr, g, c);
-            update_store<true, AMAX>(s, g, T, e, c, amax);
+            update_store<true, AMAX, FP8>(s, g, T, e, c, amax, fp8_scale);
         } else {
             load_state(s, T, e);
             float g[kGroup];
             reduce_runtime<BF16>(T.slices, T.slice_stride, e, g, c);
-            update_store<true, AMAX>(s, g, T, e, c, amax);
+            update_store<true, AMAX, FP8>(s, g, T, e, c, amax, fp8_scale);
         }
     }
-    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) fused_elem<BF16, AMAX>(T, k, c, amax);
+    for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
+        fused_elem<BF16, AMAX, FP8>(T, k, c, amax, fp8_scale);
 }
 
 // Reduce only: grad_out = mean of the slices on [begin, end).
@@ -539,32 +608,6 @@ __device__ __forceinline__ void scaled_range(const TensorDesc& T, int64_t begin,
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) scaled_elem(T, k, scale, c);
 }
 
-// fp32 -> OCP FP8 E4M3 ("e4m3fn": bias 7, 3 fraction bits, largest finite
-// 448, no infinities), round to nearest with ties to even.  The input is
-// already within [-448, 448] or NaN.  Normal results: round the fp32
-// fraction to 3 bits (the carry may raise the exponent) and rebias the
-// exponent from 127 to 7.  Below 2^-6 the grid is 2^-9: scale by 2^9 (exact)
-// and round to an integer.  NaN becomes S.1111.111.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-    const uint32_t u = __float_as_uint(y);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t ua = u & 0x7fffffffu;
-    const float a = __uint_as_float(ua);
-    const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-    const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);
-    const uint32_t nrm = (r >> 20) - (120u << 3);
-    const uint32_t code = ua > 0x7f800000u ? 0x7fu : (a < 0.015625f ? sub : nrm);
-    return sign | code;
-}
-
-// The fp8 code of one updated value: the product with the tensor's scale in
-// fp32, clamped to +-448 (NaN kept), rounded once.
-__device__ __forceinline__ uint32_t fp8_code(float p, float scale) {
-    float y = p * scale;
-    y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
-    return e4m3_rne(y);
-}
-
 // fp8 copy of the updated shard on [begin, end), at most TILES tiles; codes 0
 // in the pad.  Each lane loads all of its groups before converting any.
 template <int TILES>
@@ -580,11 +623,7 @@ __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, in
 #pragma unroll
     for (int u = 0; u < TILES; ++u) {
         const int64_t e = begin + (u * kBlock + threadIdx.x) * kGroup;
-        if (e < vend) {
-            const uint32_t o = fp8_code(a[u][0], scale) | (fp8_code(a[u][1], scale) << 8) |
-                               (fp8_code(a[u][2], scale) << 16) | (fp8_code(a[u][3], scale) << 24);
-            st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), o);
-        }
+        if (e < vend) st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), pack_fp8(a[u], scale));
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.out_fp8 + k, k < T.valid ? static_cast<uint8_t>(fp8_code(ld(T.param + k), scale))
@@ -685,6 +724,23 @@ __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* 
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         fused_range<NS, BF16, true>(T, b, e, c, &am);
+    });
+    const uint32_t wm = wave_max(am);
+    if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
+}
+
+// The fused step that also writes the fp8 codes of p' with a per-tensor scale
+// given in advance (scale_in[index], e.g. from the previous step's amax) and
+// records this step's per-workgroup largest |p'|, all in the one pass.
+template <int NS, bool BF16>
+__global__ __launch_bounds__(kBlock) void mt_step_fp8_kernel(const TensorDesc* __restrict__ tensors,
+                                                             const ChunkDesc* __restrict__ chunks,
+                                                             StepConsts c, const float* scale_in,
+                                                             uint32_t* tile_amax) {
+    uint32_t am = 0;
+    for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
+        const float scale = ld(scale_in + T.index);
+        fused_range<NS, BF16, true, true>(T, b, e, c, &am, scale);
     });
     const uint32_t wm = wave_max(am);
     if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
@@ -851,6 +907,20 @@ AmaxKernel pick_amax(int n) {
         case 4: return mt_step_amax_kernel<4, BF16>;
         case 8: return mt_step_amax_kernel<8, BF16>;
         default: return mt_step_amax_kernel<0, BF16>;
+    }
+}
+
+using Fp8StepKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const float*,
+                               uint32_t*);
+
+template <bool BF16>
+Fp8StepKernel pick_fp8_step(int n) {
+    switch (n) {
+        case 1: return mt_step_fp8_kernel<1, BF16>;
+        case 2: return mt_step_fp8_kernel<2, BF16>;
+        case 4: return mt_step_fp8_kernel<4, BF16>;
+        case 8: return mt_step_fp8_kernel<8, BF16>;
+        default: return mt_step_fp8_kernel<0, BF16>;
     }
 }
 
@@ -1428,8 +1498,8 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
         const AmaxKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_amax<true>(plan->n_slices)
                                                                : pick_amax<false>(plan->n_slices);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
-                           lds_reserve(step_bytes(plan)), stream, plan->d_tensors, plan->d_chunks, c,
-                           plan->d_tile_amax);
+                           lds_reserve(step_bytes(plan), RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
+                           plan->d_chunks, c, plan->d_tile_amax);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
     hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kAmaxBlock),
@@ -1463,6 +1533,40 @@ extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks,
                        dim3(static_cast<uint32_t>(plan->n_chunks * (kTilesPerChunk / RS_CAST_TILES))),
                        dim3(kBlock), 0, stream, plan->d_tensors,
                        plan->d_chunks, amax_ranks, n_ranks, plan->n_tensors, scale_out);
+    return launch_status(who);
+}
+
+extern "C" int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                    const float* scale_in, float* amax_out, hipStream_t stream) {
+    const char* who = "fsdp_mt_step_fp8";
+    if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
+    int32_t st;
+    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    if (!plan->all_fp8) return fail(FSDP_E_ARG, "%s: every shard of the plan needs an fp8 output", who);
+    if (plan->n_tensors > 0 && (!scale_in || !amax_out))
+        return fail(FSDP_E_ARG, "%s: null scale_in or amax_out", who);
+    if (!aligned(scale_in, 4) || !aligned(amax_out, 4))
+        return fail(FSDP_E_ALIGN, "%s: buffer not aligned to its element size", who);
+    if (scale_in && amax_out) {
+        std::vector<fsdp::Range> rs{range_of(amax_out, plan->n_tensors, 4, true, 0, "amax_out"),
+                                    range_of(scale_in, plan->n_tensors, 4, false, 0, "scale_in")};
+        if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
+    }
+    if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    if (plan->n_tensors == 0) return FSDP_OK;
+    if (plan->n_chunks > 0) {
+        const StepConsts c = make_consts(hp, plan->n_slices);
+        const Fp8StepKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_fp8_step<true>(plan->n_slices)
+                                                                  : pick_fp8_step<false>(plan->n_slices);
+        hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+                           lds_reserve(step_bytes(plan) + 1, RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
+                           plan->d_chunks, c, scale_in, plan->d_tile_amax);
+        if ((st = launch_status(who)) != FSDP_OK) return st;
+    }
+    hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kAmaxBlock),
+                       0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
+                       static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds,
+                       amax_out);
     return launch_status(who);
 }
 

@@ -184,3 +184,81 @@ def test_llama7b_full_size(gpu):
     st.close()
     del st
     torch.cuda.empty_cache()
+
+
+def _ragged_set(gpu, seed, N=3, sdt="bf16"):
+    """The ragged/misaligned shards of SPECS, each with an fp8 output and garbage codes."""
+    g = torch.Generator(device=gpu)
+    g.manual_seed(seed)
+    shards = []
+    for S, valid, off in SPECS:
+        base = lambda n, dt: torch.zeros(n + off, dtype=dt, device=gpu)[off:]
+        p = base(S, torch.float32)
+        p[:valid] = torch.randn(valid, generator=g, device=gpu) * 0.02
+        m, v = base(S, torch.float32), base(S, torch.float32)
+        sl = torch.zeros(N * S + off, dtype=torch.bfloat16, device=gpu)[off:]
+        sl[:] = (torch.randn(N * S, generator=g, device=gpu) * 1e-2).to(torch.bfloat16)
+        f8 = torch.full((S + off,), 0xAB, dtype=torch.uint8, device=gpu)[off:]
+        shards.append(dict(p=p, m=m, v=v, sl=sl, f8=f8, S=S, valid=valid))
+    plan = B.MtPlan([{"param_fp32": s["p"], "exp_avg": s["m"], "exp_avg_sq": s["v"],
+                      "grad_slices": s["sl"], "slice_stride": s["S"], "shard_numel": s["S"],
+                      "valid": s["valid"], "unshard_fp8_out": s["f8"]} for s in shards], N, sdt)
+    return shards, plan
+
+
+def test_step_fp8_with_given_scales(gpu):
+    """fsdp_mt_step_fp8: fp32 outputs bit-identical to fsdp_mt_step_amax's (the
+    plain step), the same amax, and codes equal to the oracle's quantisation of
+    the GPU's own p' with the given scales (tiny, huge and ordinary ones)."""
+    a, plan_a = _ragged_set(gpu, 31)
+    b, plan_b = _ragged_set(gpu, 31)
+    n = len(a)
+    scales = np.array([448.0 / 0.05, 1e-30, 1e30, 448.0 / 0.02, 3.0e4, 1.0, 448.0 / 0.08, 12345.678,
+                       0.5, 2.0 ** -10, 7.0e5][:n], dtype=np.float32)
+    scale_in = torch.from_numpy(scales).to(gpu)
+    amax_a = torch.full((n,), -1.0, dtype=torch.float32, device=gpu)
+    amax_b = torch.full((n,), -1.0, dtype=torch.float32, device=gpu)
+    for t in (1, 2):
+        plan_a.step_fp8(HPARAMS, t, scale_in, amax_a)
+        plan_b.step_amax(HPARAMS, t, amax_b)
+        torch.cuda.synchronize()
+        assert torch.equal(amax_a.view(torch.int32), amax_b.view(torch.int32)), t
+        for i, (x, y) in enumerate(zip(a, b)):
+            for k in ("p", "m", "v"):
+                assert torch.equal(x[k].view(torch.int32), y[k].view(torch.int32)), (i, k, t)
+            if x["S"] == 0:
+                continue
+            p = x["p"].cpu().numpy()
+            codes = _codes(x["f8"])
+            _check_codes(f"step_fp8 shard {i} t={t}", p[:x["valid"]], codes[:x["valid"]], scales[i])
+            assert np.all(codes[x["valid"]:] == 0), f"step_fp8 shard {i}: pad codes not 0"
+    plan_a.close()
+    plan_b.close()
+
+
+def test_delayed_scaling_two_steps(gpu):
+    """Step 1 scales dynamically (step with amax, then the code pass); step 2
+    takes step 1's scales in the one-pass fp8 step.  Step 2's codes are the
+    oracle's quantisation of its own p' with step 1's scales, and its amax is
+    the new |p'| maximum."""
+    w = WORKLOADS[3]
+    st = RankState(w, 0, gpu, bf16_out=True, fp8_out=True)
+    st.make_plan(with_grad_out=False)
+    n = len(st.segments)
+    amax = torch.zeros(n, dtype=torch.float32, device=gpu)
+    scale1 = torch.zeros(n, dtype=torch.float32, device=gpu)
+    st.load_grads(1)
+    st.plan.step_amax(w.hparams, 1, amax)
+    st.plan.cast_fp8(amax, 1, scale1)
+    st.load_grads(2)
+    st.plan.step_fp8(w.hparams, 2, scale1, amax)
+    torch.cuda.synchronize()
+    sc = scale1.cpu().numpy()
+    am = amax.cpu().numpy()
+    for i, (off, length, held, _) in enumerate(st.segments):
+        p = st.master[off:off + held].cpu().numpy()
+        assert am[i] == np.float32(F.amax(p)), i
+        _check_codes(f"delayed shard {i}", p, _codes(st.fp8[off:off + held]), sc[i])
+        bf = PR.bf16_bits(st.ag_slot[off:off + held])
+        assert np.array_equal(bf, O.bf16_rne(p.astype(np.float64))), i
+    st.close()
