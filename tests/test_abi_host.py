@@ -242,6 +242,7 @@ def test_accumulate_argument_checks():
     assert B.lib().fsdp_mt_reduce_accumulate(None, 0, None, None) == -1
     assert B.lib().fsdp_mt_step_amax(None, None, A, None) == -1
     assert B.lib().fsdp_mt_cast_fp8(None, A, 1, None, None) == -1
+    assert B.lib().fsdp_mt_step_fp8(None, None, A, Bp, None) == -1
 
 
 def test_layout_owner_matches_oracle():

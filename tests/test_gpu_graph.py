@@ -46,11 +46,13 @@ def _pair(w, gpu, **kw):
     return a, b
 
 
-def _run(w, a, b, gpu, calls, extra=()):
+def _run(w, a, b, gpu, calls, extra=(), init=None):
     """calls(state, bufs) enqueues one step on the current stream; bufs holds
-    that state's own scalars.  Captures calls(b) once, then replays."""
-    bufs_a = {k: torch.zeros(n, dtype=dt, device=gpu) for k, (n, dt) in extra}
-    bufs_b = {k: torch.zeros(n, dtype=dt, device=gpu) for k, (n, dt) in extra}
+    that state's own scalars (zero, or the value ``init`` gives the name).
+    Captures calls(b) once, then replays."""
+    init = init or {}
+    bufs_a = {k: torch.full((n,), init.get(k, 0.0), dtype=dt, device=gpu) for k, (n, dt) in extra}
+    bufs_b = {k: torch.full((n,), init.get(k, 0.0), dtype=dt, device=gpu) for k, (n, dt) in extra}
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -109,5 +111,24 @@ def test_fp8_step_graph(gpu):
         st.plan.cast_fp8(bufs["amax"], 1, bufs["scale"])
 
     _run(w, a, b, gpu, calls, extra=(("amax", (n, torch.float32)), ("scale", (n, torch.float32))))
+    a.close()
+    b.close()
+
+
+
+def test_delayed_fp8_step_graph(gpu):
+    """The one-pass fp8 step with scales fixed before the step: captured once,
+    replayed with the same scale buffer; codes, amax and state equal eager."""
+    w = WORKLOADS[3]
+    a, b = _pair(w, gpu, bf16_out=True, fp8_out=True)
+    a.make_plan(with_grad_out=False)
+    b.make_plan(with_grad_out=False)
+    n = len(a.segments)
+
+    def calls(st, bufs):
+        st.plan.step_fp8(w.hparams, 5, bufs["scale"], bufs["amax"])
+
+    _run(w, a, b, gpu, calls, extra=(("scale", (n, torch.float32)), ("amax", (n, torch.float32))),
+         init={"scale": 448.0 / 0.05})
     a.close()
     b.close()
