@@ -312,7 +312,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(each rank's step is independent: see the sharding section of DESIGN.md)",
+              "(each rank's step is independent of the others; one GPU shows one rank's share)",
               file=sys.stderr)
         sys.exit(2)
 
