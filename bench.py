@@ -311,7 +311,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(each rank's step is independent of the others; one GPU shows one rank's share)",
               file=sys.stderr)
         sys.exit(2)
