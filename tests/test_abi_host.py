@@ -264,3 +264,23 @@ def test_capacity_error_before_any_device_work():
     big = 1 << 44
     assert _err(B.fsdp_cast_unshard_bf16, A, None, big, 0, stream=0) == "CAPACITY"
     assert _err(B.fsdp_reduce_grad_shard, A, None, "f32", big, 1, big, 0, stream=0) == "CAPACITY"
+
+
+def test_layout_extreme_sizes_match_oracle_or_refuse():
+    # sizes far beyond any device, where 32-bit or careless 64-bit arithmetic
+    # would wrap: the library agrees with the oracle's exact integers ...
+    big = [("flat", 1 << 30, [(7, 7, "f32")], True),
+           ("shard0", 1000, [((1 << 40), (1 << 20), "bf16")], True),
+           ("flat", 3, [((1 << 40) + 1, 1, "f32"), ((1 << 41) + 1, 3, "f32")], False),
+           ("owner", 7, [((1 << 40) + k, 1, "bf16") for k in range(9)], True)]
+    for mode, N, shapes, master in big:
+        for r in (0, 1, N // 2, N - 1):
+            got_v, got_s = B.fsdp_shard_layout(mode, N, r, shapes, master)
+            ref_v, ref_s = OL.layout(MODES[mode], N, r, shapes, master)
+            assert got_v == [v.__dict__ for v in ref_v], (mode, N, r)
+            assert got_s == ref_s.__dict__, (mode, N, r)
+    # ... or refuses when a count or byte total would not fit in int64
+    for mode, N, shapes in (("flat", 3, [((1 << 62), 1, "f32")] * 2),
+                            ("owner", 4, [((1 << 61), 1, "f32")] * 3),
+                            ("flat", 8, [((1 << 61), 1, "f32")] * 5)):
+        assert _err(B.fsdp_shard_layout, mode, N, 0, shapes, True) == "ARG"
