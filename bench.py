@@ -265,14 +265,14 @@ def unfused_chain(st, stream, args, t0):
     gp = g.data_ptr()
     steps = max(1, min(args.steps, 10))
 
-    def one(t):
+    def one(t, s=stream):
         for d, (off, length, held, _) in zip(tens, st.segments):
             B.fsdp_reduce_grad_shard(gp + 4 * off, d["grad_slices"], w.slice_dtype, d["slice_stride"],
-                                     w.n_slices, length, held, stream)
+                                     w.n_slices, length, held, s)
             B.fsdp_adamw_shard_step(d["param_fp32"], d["exp_avg"], d["exp_avg_sq"], gp + 4 * off,
-                                    length, held, w.hparams, t, stream)
+                                    length, held, w.hparams, t, s)
             if d["unshard_bf16_out"] is not None:
-                B.fsdp_cast_unshard_bf16(d["unshard_bf16_out"], d["param_fp32"], length, held, stream)
+                B.fsdp_cast_unshard_bf16(d["unshard_bf16_out"], d["param_fp32"], length, held, s)
 
     t = t0
     one(t + 1)
@@ -284,10 +284,27 @@ def unfused_chain(st, stream, args, t0):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+
+    # the same chain captured once in a HIP graph and replayed: no host launch
+    # cost per kernel, so what remains beside the fused pass is the extra
+    # bytes and the gaps between dependent kernels
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one(t + 2 + steps, s=None)          # the capture stream is torch's current one
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1) / steps
+    del graph
     slice_b = 2 if w.slice_dtype == "bf16" else 4
     bpp = w.n_slices * slice_b + 4 + 28 + (6 if w.bf16_out else 0)
     return {"ms_per_step": ms, "bytes_per_param": bpp, "hbm_gb_s": bpp * st.total / ms / 1e6,
-            "launches": 3 * len(tens), "steps": steps}
+            "launches": 3 * len(tens), "steps": steps,
+            "hip_graph": {"ms_per_step": ms_graph, "hbm_gb_s": bpp * st.total / ms_graph / 1e6}}
 
 
 def main():
