@@ -21,7 +21,8 @@
  * Conventions for every call:
  *   - Return value: FSDP_OK (0) or a negative FSDP_E_* code; on error
  *     fsdp_last_error() gives a message (thread-local, valid until the next
- *     failing call on the same thread).  Nothing aborts, nothing throws.
+ *     failing call on the same thread).  Nothing aborts, nothing throws: a
+ *     host allocation that fails returns FSDP_E_CAPACITY.
  *   - All arguments are checked on the host before any device work is queued.
  *   - Device pointers are plain HIP device addresses on the current device.
  *     The caller owns every buffer it passes; the library never allocates or
@@ -273,7 +274,9 @@ typedef struct {
  * sum per workgroup for fsdp_mt_reduce_sqnorm.  Synchronises
  * `stream` once.  The caller keeps every referenced buffer alive and in
  * place while the plan exists.  n_tensors may be 0 (an empty plan).
- * Errors: as the single-shard calls; FSDP_E_HIP if the upload fails. */
+ * Errors: as the single-shard calls; FSDP_E_CAPACITY if one launch cannot
+ * hold the plan's workgroups (checked before any table is built); FSDP_E_HIP
+ * if the upload fails. */
 int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tensors,
                             int32_t n_tensors, int32_t n_slices, int32_t slice_dtype,
                             hipStream_t stream);

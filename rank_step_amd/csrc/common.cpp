@@ -2,23 +2,22 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
-#include <string>
 
 #include "internal.h"
 
 namespace fsdp {
 
 namespace {
-thread_local std::string g_last_error;
+// A fixed buffer, so that recording an error never allocates (and so never
+// throws, even when host memory has run out).
+thread_local char g_last_error[512];
 }
 
 int32_t fail(int32_t code, const char* fmt, ...) {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
     return code;
 }
 
@@ -52,4 +51,4 @@ int32_t check_aliases(std::vector<Range>& ranges) {
 
 }  // namespace fsdp
 
-extern "C" const char* fsdp_last_error(void) { return fsdp::g_last_error.c_str(); }
+extern "C" const char* fsdp_last_error(void) { return fsdp::g_last_error; }

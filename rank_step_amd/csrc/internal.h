@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstdint>
+#include <new>
 #include <vector>
 
 #include "fsdp_step.h"
@@ -28,5 +29,19 @@ struct Range {
 // FSDP_E_ALIAS if a written range overlaps any other range (read-only ranges
 // may overlap each other); empty ranges never overlap.
 int32_t check_aliases(std::vector<Range>& ranges);
+
+// Runs an entry point's body and turns a C++ exception into an error code, so
+// that nothing throws across the C ABI.  The only one the bodies can raise is
+// std::bad_alloc, from host-side tables and lists when host memory runs out.
+template <typename F>
+int32_t guarded(const char* who, F&& body) noexcept {
+    try {
+        return body();
+    } catch (const std::bad_alloc&) {
+        return fail(FSDP_E_CAPACITY, "%s: out of host memory", who);
+    } catch (...) {
+        return fail(FSDP_E_ARG, "%s: unexpected host-side error", who);
+    }
+}
 
 }  // namespace fsdp

@@ -19,6 +19,9 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <functional>
+#include <queue>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -34,12 +37,9 @@ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 int64_t dtype_size(int32_t dt) { return dt == FSDP_DT_F32 ? 4 : 2; }
 
-}  // namespace
-
-extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t rank,
-                                     const fsdp_tensor_shape* tensors, int32_t n_tensors,
-                                     int32_t has_master, fsdp_shard_view* views_out,
-                                     fsdp_layout_summary* summary_out) {
+int32_t shard_layout(int32_t mode, int32_t world_size, int32_t rank,
+                     const fsdp_tensor_shape* tensors, int32_t n_tensors, int32_t has_master,
+                     fsdp_shard_view* views_out, fsdp_layout_summary* summary_out) {
     if (mode != FSDP_LAYOUT_FLAT && mode != FSDP_LAYOUT_SHARD0 && mode != FSDP_LAYOUT_OWNER)
         return fail(FSDP_E_ARG, "fsdp_shard_layout: unknown mode %d", mode);
     if (world_size < 1) return fail(FSDP_E_ARG, "fsdp_shard_layout: world_size %d < 1", world_size);
@@ -104,7 +104,8 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
         s.physical_numel = phys;
         s.shard_numel = S;
         s.pad_numel = S - valid;
-        s.bytes_param = S * esize;
+        if (!fsdp::mul_i64(S, esize, &s.bytes_param))
+            return fail(FSDP_E_ARG, "byte counts overflow int64");
     } else if (mode == FSDP_LAYOUT_SHARD0) {
         int64_t off = 0, packed = 0, phys = 0, bytes_param = 0, pad = 0;
         for (int32_t i = 0; i < n_tensors; ++i) {
@@ -140,26 +141,33 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
         s.pad_numel = pad;
         s.bytes_param = bytes_param;
     } else {
-        // OWNER: largest parameters first, each to the least-loaded rank.
+        // OWNER: largest parameters first, each to the least-loaded rank
+        // (ties: the lower rank).  Only the first min(N, n_tensors) ranks can
+        // ever be chosen: until every one of them holds bytes, one of them
+        // still has load 0, the least possible, and it has the lowest index
+        // among the ranks at 0.  So a heap of (load, rank) over those ranks
+        // gives the same choices as a scan over all N, in memory independent
+        // of N.
         std::vector<int64_t> bytes(static_cast<size_t>(n_tensors));
         std::vector<int32_t> order(static_cast<size_t>(n_tensors));
         int64_t all_bytes = 0;
         for (int32_t i = 0; i < n_tensors; ++i) {
-            bytes[i] = tensors[i].numel * dtype_size(tensors[i].dtype);
             order[i] = i;
-            if (!fsdp::add_i64(all_bytes, bytes[i], &all_bytes))
+            if (!fsdp::mul_i64(tensors[i].numel, dtype_size(tensors[i].dtype), &bytes[i]) ||
+                !fsdp::add_i64(all_bytes, bytes[i], &all_bytes))
                 return fail(FSDP_E_ARG, "layout sizes overflow int64");
         }
         std::stable_sort(order.begin(), order.end(),
                          [&](int32_t a, int32_t b) { return bytes[a] > bytes[b]; });
-        std::vector<int64_t> load(static_cast<size_t>(N), 0);
+        using Load = std::pair<int64_t, int64_t>;  // (bytes held, rank)
+        std::priority_queue<Load, std::vector<Load>, std::greater<Load>> least;
+        for (int64_t q = 0; q < std::min<int64_t>(N, n_tensors); ++q) least.push({0, q});
         std::vector<int64_t> owner(static_cast<size_t>(n_tensors), 0);
         for (int32_t i : order) {
-            int64_t best = 0;
-            for (int64_t q = 1; q < N; ++q)
-                if (load[q] < load[best]) best = q;
-            owner[i] = best;
-            load[best] += bytes[i];
+            const Load top = least.top();
+            least.pop();
+            owner[i] = top.second;
+            least.push({top.first + bytes[i], top.second});
         }
         int64_t off = 0, packed = 0;
         for (int32_t i = 0; i < n_tensors; ++i) {
@@ -196,4 +204,16 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
     for (int32_t i = 0; i < n_tensors; ++i) views_out[i] = views[i];
     if (summary_out) *summary_out = s;
     return FSDP_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t rank,
+                                     const fsdp_tensor_shape* tensors, int32_t n_tensors,
+                                     int32_t has_master, fsdp_shard_view* views_out,
+                                     fsdp_layout_summary* summary_out) {
+    return fsdp::guarded("fsdp_shard_layout", [&] {
+        return shard_layout(mode, world_size, rank, tensors, n_tensors, has_master, views_out,
+                            summary_out);
+    });
 }

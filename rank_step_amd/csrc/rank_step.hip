@@ -1104,10 +1104,10 @@ int64_t step_bytes(const fsdp_mt_plan* plan) {
 
 }  // namespace
 
-extern "C" int32_t fsdp_reduce_grad_shard(float* grad_shard_out, const void* grad_slices,
-                                          int32_t slice_dtype, int64_t slice_stride,
-                                          int32_t n_slices, int64_t shard_numel, int64_t valid,
-                                          hipStream_t stream) {
+static int32_t reduce_grad_shard_impl(float* grad_shard_out, const void* grad_slices,
+                                      int32_t slice_dtype, int64_t slice_stride,
+                                      int32_t n_slices, int64_t shard_numel, int64_t valid,
+                                      hipStream_t stream) {
     const char* who = "fsdp_reduce_grad_shard";
     int32_t st;
     if ((st = check_sizes(shard_numel, valid, who)) != FSDP_OK) return st;
@@ -1138,10 +1138,10 @@ extern "C" int32_t fsdp_reduce_grad_shard(float* grad_shard_out, const void* gra
     return launch_status(who);
 }
 
-extern "C" int32_t fsdp_adamw_shard_step(float* param_fp32, float* exp_avg, float* exp_avg_sq,
-                                         const float* grad_shard, int64_t shard_numel,
-                                         int64_t valid, const fsdp_adamw_hparams* hp,
-                                         hipStream_t stream) {
+static int32_t adamw_shard_step_impl(float* param_fp32, float* exp_avg, float* exp_avg_sq,
+                                     const float* grad_shard, int64_t shard_numel,
+                                     int64_t valid, const fsdp_adamw_hparams* hp,
+                                     hipStream_t stream) {
     const char* who = "fsdp_adamw_shard_step";
     int32_t st;
     if ((st = check_sizes(shard_numel, valid, who)) != FSDP_OK) return st;
@@ -1175,8 +1175,8 @@ extern "C" int32_t fsdp_adamw_shard_step(float* param_fp32, float* exp_avg, floa
     return launch_status(who);
 }
 
-extern "C" int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const float* param_fp32,
-                                          int64_t shard_numel, int64_t valid, hipStream_t stream) {
+static int32_t cast_unshard_bf16_impl(uint16_t* unshard_bf16_out, const float* param_fp32,
+                                      int64_t shard_numel, int64_t valid, hipStream_t stream) {
     const char* who = "fsdp_cast_unshard_bf16";
     int32_t st;
     if ((st = check_sizes(shard_numel, valid, who)) != FSDP_OK) return st;
@@ -1201,9 +1201,9 @@ extern "C" int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const floa
     return launch_status(who);
 }
 
-extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tensors,
-                                       int32_t n_tensors, int32_t n_slices, int32_t slice_dtype,
-                                       hipStream_t stream) {
+static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tensors,
+                                   int32_t n_tensors, int32_t n_slices, int32_t slice_dtype,
+                                   hipStream_t stream) {
     const char* who = "fsdp_mt_plan_create";
     if (!plan_out) return fail(FSDP_E_ARG, "%s: null plan_out", who);
     *plan_out = nullptr;
@@ -1218,7 +1218,6 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
     descs.reserve(static_cast<size_t>(n_tensors));
     bool all_grad_out = true;
     bool any_fp8 = false, all_fp8 = true, any_bf16 = false, any_grad_out = false;
-    std::vector<int32_t> first_desc(static_cast<size_t>(n_tensors), -1);
     std::vector<fsdp::Range> rs;
     int64_t total = 0, total_valid = 0;
     for (int32_t i = 0; i < n_tensors; ++i) {
@@ -1244,7 +1243,6 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
         if (!t.unshard_fp8_out) all_fp8 = false;
         if (t.grad_shard_out) any_grad_out = true;
         if (t.unshard_bf16_out) any_bf16 = true;
-        first_desc[i] = static_cast<int32_t>(descs.size());
         rs.push_back(range_of(t.param_fp32, t.shard_numel, 4, true, i, "param"));
         rs.push_back(range_of(t.exp_avg, t.shard_numel, 4, true, i, "exp_avg"));
         rs.push_back(range_of(t.exp_avg_sq, t.shard_numel, 4, true, i, "exp_avg_sq"));
@@ -1277,8 +1275,17 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
 
     // Every chunk but a shard's last is kChunk elements, so every chunk and
     // every tile starts group-aligned.  Workgroup b takes tile b % 8 of entry b / 8.
+    // The launch's size is checked before any table is built: a shard too
+    // large for one launch is refused without building its entries.
     const int64_t chunk = kChunk;
+    int64_t n_chunks = 0;
+    for (const TensorDesc& d : descs) n_chunks += (d.shard_numel + chunk - 1) / chunk;
+    {
+        const int32_t st = check_grid(n_chunks * kTilesPerChunk, who);
+        if (st != FSDP_OK) return st;
+    }
     std::vector<ChunkDesc> chunks;
+    chunks.reserve(static_cast<size_t>(n_chunks));
     std::vector<ShardTiles> runs(static_cast<size_t>(n_tensors), ShardTiles{0, 0});
     for (size_t i = 0; i < descs.size(); ++i) {
         runs[static_cast<size_t>(descs[i].index)].first = static_cast<int64_t>(chunks.size()) * kTilesPerChunk;
@@ -1293,12 +1300,8 @@ extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_te
         }
     }
 
-    {
-        const int32_t st = check_grid(static_cast<int64_t>(chunks.size()) * kTilesPerChunk, who);
-        if (st != FSDP_OK) return st;
-    }
     fsdp_mt_plan* plan = new (std::nothrow) fsdp_mt_plan();
-    if (!plan) return fail(FSDP_E_ARG, "%s: out of host memory", who);
+    if (!plan) return fail(FSDP_E_CAPACITY, "%s: out of host memory", who);
     plan->n_slices = n_slices;
     plan->slice_dtype = slice_dtype;
     plan->n_tensors = n_tensors;
@@ -1411,8 +1414,8 @@ extern "C" int32_t fsdp_mt_reduce_sqnorm(fsdp_mt_plan* plan, double* sqnorm_out,
     return fsdp_mt_reduce_accumulate(plan, 0, sqnorm_out, stream);
 }
 
-extern "C" int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t micro_dtype,
-                                        int64_t numel, int32_t accumulate, hipStream_t stream) {
+static int32_t grad_accumulate_impl(float* acc, const void* micro, int32_t micro_dtype,
+                                    int64_t numel, int32_t accumulate, hipStream_t stream) {
     const char* who = "fsdp_grad_accumulate";
     int32_t st;
     if ((st = check_sizes(numel, numel, who)) != FSDP_OK) return st;
@@ -1442,8 +1445,8 @@ extern "C" int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t m
     return launch_status(who);
 }
 
-extern "C" int32_t fsdp_clip_coef(float* coef_out, double* norm_out, const double* sqnorms,
-                                  int32_t n_ranks, double max_norm, hipStream_t stream) {
+static int32_t clip_coef_impl(float* coef_out, double* norm_out, const double* sqnorms,
+                              int32_t n_ranks, double max_norm, hipStream_t stream) {
     const char* who = "fsdp_clip_coef";
     if (!coef_out || !sqnorms) return fail(FSDP_E_ARG, "%s: null coef_out or sqnorms", who);
     if (n_ranks < 1 || n_ranks > (1 << 20))
@@ -1509,8 +1512,8 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
     return launch_status(who);
 }
 
-extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_ranks,
-                                    float* scale_out, hipStream_t stream) {
+static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_ranks,
+                                float* scale_out, hipStream_t stream) {
     const char* who = "fsdp_mt_cast_fp8";
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     if (!plan->all_fp8) return fail(FSDP_E_ARG, "%s: every shard of the plan needs an fp8 output", who);
@@ -1536,8 +1539,8 @@ extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks,
     return launch_status(who);
 }
 
-extern "C" int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                    const float* scale_in, float* amax_out, hipStream_t stream) {
+static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                const float* scale_in, float* amax_out, hipStream_t stream) {
     const char* who = "fsdp_mt_step_fp8";
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
@@ -1568,6 +1571,72 @@ extern "C" int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams
                        static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds,
                        amax_out);
     return launch_status(who);
+}
+
+// ---------------------------------------------------------------- entry points that allocate
+// host memory: no C++ exception crosses the ABI
+
+extern "C" int32_t fsdp_reduce_grad_shard(float* grad_shard_out, const void* grad_slices,
+                                          int32_t slice_dtype, int64_t slice_stride,
+                                          int32_t n_slices, int64_t shard_numel, int64_t valid,
+                                          hipStream_t stream) {
+    return fsdp::guarded("fsdp_reduce_grad_shard", [&] {
+        return reduce_grad_shard_impl(grad_shard_out, grad_slices, slice_dtype, slice_stride,
+                                      n_slices, shard_numel, valid, stream);
+    });
+}
+
+extern "C" int32_t fsdp_adamw_shard_step(float* param_fp32, float* exp_avg, float* exp_avg_sq,
+                                         const float* grad_shard, int64_t shard_numel,
+                                         int64_t valid, const fsdp_adamw_hparams* hp,
+                                         hipStream_t stream) {
+    return fsdp::guarded("fsdp_adamw_shard_step", [&] {
+        return adamw_shard_step_impl(param_fp32, exp_avg, exp_avg_sq, grad_shard, shard_numel,
+                                     valid, hp, stream);
+    });
+}
+
+extern "C" int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const float* param_fp32,
+                                          int64_t shard_numel, int64_t valid, hipStream_t stream) {
+    return fsdp::guarded("fsdp_cast_unshard_bf16", [&] {
+        return cast_unshard_bf16_impl(unshard_bf16_out, param_fp32, shard_numel, valid, stream);
+    });
+}
+
+extern "C" int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tensors,
+                                       int32_t n_tensors, int32_t n_slices, int32_t slice_dtype,
+                                       hipStream_t stream) {
+    return fsdp::guarded("fsdp_mt_plan_create", [&] {
+        return mt_plan_create_impl(plan_out, tensors, n_tensors, n_slices, slice_dtype, stream);
+    });
+}
+
+extern "C" int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t micro_dtype,
+                                        int64_t numel, int32_t accumulate, hipStream_t stream) {
+    return fsdp::guarded("fsdp_grad_accumulate", [&] {
+        return grad_accumulate_impl(acc, micro, micro_dtype, numel, accumulate, stream);
+    });
+}
+
+extern "C" int32_t fsdp_clip_coef(float* coef_out, double* norm_out, const double* sqnorms,
+                                  int32_t n_ranks, double max_norm, hipStream_t stream) {
+    return fsdp::guarded("fsdp_clip_coef", [&] {
+        return clip_coef_impl(coef_out, norm_out, sqnorms, n_ranks, max_norm, stream);
+    });
+}
+
+extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_ranks,
+                                    float* scale_out, hipStream_t stream) {
+    return fsdp::guarded("fsdp_mt_cast_fp8", [&] {
+        return mt_cast_fp8_impl(plan, amax_ranks, n_ranks, scale_out, stream);
+    });
+}
+
+extern "C" int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                    const float* scale_in, float* amax_out, hipStream_t stream) {
+    return fsdp::guarded("fsdp_mt_step_fp8", [&] {
+        return mt_step_fp8_impl(plan, hp, scale_in, amax_out, stream);
+    });
 }
 
 extern "C" int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info) {

@@ -266,6 +266,22 @@ def test_capacity_error_before_any_device_work():
     assert _err(B.fsdp_reduce_grad_shard, A, None, "f32", big, 1, big, 0, stream=0) == "CAPACITY"
 
 
+def test_plan_capacity_checked_before_its_table_is_built():
+    # a shard of 2**44 elements needs 2**33 chunk entries (128 GiB of host
+    # table): the plan is refused from the launch size alone, at once and
+    # without building any of it (fake device addresses, never touched)
+    import time
+    big = 1 << 44
+    t0 = time.perf_counter()
+    huge = [_t(1 << 40, 2 << 46, 3 << 46, 4 << 46, S=big, valid=big, stride=big)]
+    assert _err(B.fsdp_mt_plan_create, huge, 1, "f32", stream=0) == "CAPACITY"
+    # the same total spread over many shards
+    many = [_t((k + 1) << 42, (k + 1) << 42 | (1 << 41), (k + 65) << 42, (k + 129) << 42,
+               S=1 << 33, valid=1 << 33, stride=1 << 33) for k in range(40)]
+    assert _err(B.fsdp_mt_plan_create, many, 1, "f32", stream=0) == "CAPACITY"
+    assert time.perf_counter() - t0 < 5.0
+
+
 def test_layout_extreme_sizes_match_oracle_or_refuse():
     # sizes far beyond any device, where 32-bit or careless 64-bit arithmetic
     # would wrap: the library agrees with the oracle's exact integers ...
