@@ -86,12 +86,27 @@ def _flat_brute(numels, N):
                 owner.setdefault(gidx, []).append((r, k))
             else:
                 assert gidx >= P
+        o = 0
         for i, v in enumerate(views):
             for j in range(v.view_numel):
                 # element j of the view is tensor i's element tensor_offset + j
                 k = v.view_offset + j
                 assert k < valid_r
                 assert tensor_of[r * S + k] == (i, v.tensor_offset + j)
+            assert v.global_offset == o
+            if v.view_numel == 0:
+                # an empty view sits where the tensor meets the shard: a tensor
+                # that ends at or before the shard's start is seen at offset 0,
+                # past its last element; one that starts at or after the
+                # shard's end, at offset S, before its first element
+                n = numels[i]
+                if o + n <= r * S:
+                    assert (v.view_offset, v.tensor_offset) == (0, n)
+                elif o >= r * S + S:
+                    assert (v.view_offset, v.tensor_offset) == (S, 0)
+                else:
+                    assert (v.view_offset, v.tensor_offset) == (o - r * S, 0)
+            o += numels[i]
     assert valid_sum == P
     assert sorted(owner) == list(range(P))
     assert all(len(o) == 1 for o in owner.values())
@@ -129,6 +144,10 @@ def test_shard0_bruteforce_small():
                     sizes.add(v.shard_numel)
                     assert v.shard_numel % max(row, 1) == 0
                     assert 0 <= v.valid <= v.shard_numel
+                    # the rank's first row, or the tensor's end for an all-padding rank
+                    assert 0 <= v.tensor_offset <= numel
+                    if v.valid == 0:
+                        assert v.tensor_offset == numel
                     seen += list(range(v.tensor_offset, v.tensor_offset + v.valid))
                     valid_sum += v.valid
                     assert s.pad_numel == v.shard_numel - v.valid
