@@ -24,6 +24,22 @@ def test_bytes_per_param():
     assert bench.bytes_per_param(WORKLOADS[5], True) == 30      # 1 fp32 slice + 12 + 12 + 2
 
 
+def test_infinity_cache_rotation_rule():
+    # the headline and 70B shards stream tens of GB per step and step one copy
+    # of the state; the Llama block and the 128 MiB unit fit within a few
+    # Infinity Caches and rotate through enough copies that at least
+    # ROTATE_BYTES of other traffic passes between two steps on one copy
+    local = {4: 842_301_952, 5: 2_204_803_328, 3: 25_297_920, 2: 8_388_608}
+    for cfg, rotated in ((4, False), (5, False), (3, True), (2, True)):
+        w = WORKLOADS[cfg]
+        step_bytes = bench.bytes_per_param(w, w.bf16_out) * local[cfg]
+        assert (step_bytes < bench.ROTATE_BYTES) == rotated, cfg
+        if rotated:
+            n = -(-bench.ROTATE_BYTES // step_bytes) + 1
+            assert n <= bench.MAX_COPIES and (n - 1) * step_bytes >= bench.ROTATE_BYTES
+    assert bench.ROTATE_BYTES >= 4 * bench.INFINITY_CACHE_BYTES
+
+
 def test_traffic_record_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
     rec = {"kernel_source_hash": bench.kernel_source_hash(), "total_numel": 123,
            "bytes_per_launch": 4567}
