@@ -300,3 +300,30 @@ def test_layout_extreme_sizes_match_oracle_or_refuse():
                             ("owner", 4, [((1 << 61), 1, "f32")] * 3),
                             ("flat", 8, [((1 << 61), 1, "f32")] * 5)):
         assert _err(B.fsdp_shard_layout, mode, N, 0, shapes, True) == "ARG"
+
+
+def test_last_error_is_per_thread():
+    # four threads fail concurrently with different ranks; each must read back
+    # the message of its own last failing call (ctypes drops the GIL in calls)
+    import threading
+    L = B.lib()
+    shape = (B.TensorShape * 1)(B.TensorShape(4, 4, 0, 0))
+    views = (B.ShardView * 1)()
+    summ = B.LayoutSummary()
+    bad = []
+
+    def worker(k):
+        rank = 100 + k
+        for _ in range(2000):
+            rc = L.fsdp_shard_layout(0, 2, rank, shape, 1, 0, views, ctypes.byref(summ))
+            msg = L.fsdp_last_error().decode()
+            if rc != -1 or f"rank {rank} " not in msg:
+                bad.append((k, rc, msg))
+                return
+
+    ts = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not bad, bad[:3]
