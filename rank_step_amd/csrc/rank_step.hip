@@ -78,6 +78,11 @@ namespace {
 #ifndef RS_CAST_TILES
 #define RS_CAST_TILES 4
 #endif
+// 1: the copy passes (fp8 codes, bf16 cast) read the updated parameter with
+// non-temporal loads: it is read once there, and the code pass ran 4 % faster.
+#ifndef RS_NT_CAST_LD
+#define RS_NT_CAST_LD 1
+#endif
 // 1: fp8 codes from the hardware's packed fp32 -> OCP E4M3 conversion;
 // 0: from the integer rounding e4m3_rne.
 #ifndef RS_FP8_HW
@@ -618,7 +623,7 @@ __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, in
 #pragma unroll
     for (int u = 0; u < TILES; ++u) {
         const int64_t e = begin + (u * kBlock + threadIdx.x) * kGroup;
-        if (e < vend) a[u] = ld_state(reinterpret_cast<const f32x4*>(T.param + e));
+        if (e < vend) a[u] = ld_s<RS_NT_CAST_LD>(reinterpret_cast<const f32x4*>(T.param + e));
     }
 #pragma unroll
     for (int u = 0; u < TILES; ++u) {
@@ -634,7 +639,7 @@ __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, in
 __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, int64_t end) {
     const int64_t vend = vector_end(T, begin, end);
     for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
-        const f32x4 a = ld_state(reinterpret_cast<const f32x4*>(T.param + e));
+        const f32x4 a = ld_s<RS_NT_CAST_LD>(reinterpret_cast<const f32x4*>(T.param + e));
         st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(a));
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
