@@ -11,7 +11,7 @@
 //                    by a pairwise brute force; prints "cases mismatches".
 //
 // Any out-of-bounds access, signed overflow or other undefined behaviour
-// aborts the run (the build uses -fno-sanitize-recover=all).
+// aborts the run (it is compiled with -fno-sanitize-recover=all).
 #include <cinttypes>
 #include <cstdint>
 #include <cstdio>
