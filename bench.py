@@ -262,6 +262,45 @@ def accumulation(st, stream, args):
                         "hbm_gb_s": b_nos * st.total / ms_nos / 1e6}}
 
 
+def slice_table_step(st, stream, args, t0):
+    """Time the fused step with every shard reading its N slices through a
+    table of slice pointers (the form for N receive buffers that do not share
+    an allocation).  The entries point at the rows of the same slice buffer,
+    so the bytes and addresses equal the stride form's."""
+    import torch
+    from rank_step_amd import binding as B
+
+    w = st.w
+    es = st.slices.element_size()
+    base = st.slices.data_ptr()
+    recs = []
+    for d, (off, length, held, _) in zip(st.mt_tensors(with_grad_out=False, with_fp8=False),
+                                         st.segments):
+        d = dict(d)
+        d.pop("grad_slices")
+        d.pop("slice_stride")
+        d["grad_slice_ptrs"] = [base + es * (q * st.total + off) for q in range(w.n_slices)]
+        recs.append(d)
+    plan = B.MtPlan(recs, w.n_slices, w.slice_dtype, stream)
+    t = t0
+    for _ in range(args.warmup):
+        t += 1
+        plan.step(w.hparams, t, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        t += 1
+        plan.step(w.hparams, t, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    plan.close()
+    bpp = bytes_per_param(w, w.bf16_out)
+    return {"ms_per_step": ms, "params_per_s": st.total / (ms / 1e3),
+            "hbm_gb_s": bpp * st.total / ms / 1e6, "bytes_per_param": bpp}
+
+
 def unfused_chain(st, stream, args, t0):
     """Time the same step as three separate calls per shard (reduce -> AdamW
     -> cast, 3 launches x shards), which moves 2N+4 + 28 + 6 B/param, beside
@@ -331,6 +370,8 @@ def main():
                     help="do not time the clipped step")
     ap.add_argument("--no-chain", action="store_true",
                     help="do not time the unfused three-call chain")
+    ap.add_argument("--no-table", action="store_true",
+                    help="do not time the step with slices read through tables of pointers")
     ap.add_argument("--no-fp8", action="store_true",
                     help="do not time the step with the fp8 all-gather copy")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -481,6 +522,8 @@ def main():
         out["fp8_step"] = fp8_step(st, stream, args, t)
     if args.clip is not None:
         out["grad_accumulation"] = accumulation(st, stream, args)
+    if not args.no_table:
+        out["slice_table_step"] = slice_table_step(st, stream, args, t)
     if not args.no_chain:
         out["unfused_chain"] = unfused_chain(st, stream, args, t)
     if not args.no_cpu_baseline:

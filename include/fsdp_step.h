@@ -236,7 +236,23 @@ int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const float* param_fp
  *                                    reduced gradient is not stored)
  *   unshard_fp8_out                  device fp8 codes [shard_numel] or NULL:
  *                                    written only by fsdp_mt_cast_fp8 and
- *                                    fsdp_mt_step_fp8 */
+ *                                    fsdp_mt_step_fp8
+ *   grad_slice_ptrs                  NULL: slice q starts at grad_slices +
+ *                                    q*slice_stride.  Else a host array of
+ *                                    n_slices device pointers: slice q starts at
+ *                                    grad_slice_ptrs[q], and grad_slices and
+ *                                    slice_stride are ignored.  This is the form
+ *                                    for N receive buffers that do not share one
+ *                                    allocation: in the backward reduce-scatter
+ *                                    the rank receives its 1/N of every rank's
+ *                                    gradient ([FSDP ch.18] §18.3), and FSDP-2
+ *                                    lets a custom reduce-scatter replace the
+ *                                    built-in one (§18.5), e.g. one in which the
+ *                                    rank reads its slices from its peers' buffers.
+ *                                    The plan copies the array; entries may be
+ *                                    NULL only when valid is 0, must be aligned
+ *                                    to the element size, and are read in
+ *                                    [0, valid) only. */
 typedef struct {
     float* param_fp32;
     float* exp_avg;
@@ -248,6 +264,7 @@ typedef struct {
     int64_t shard_numel;
     int64_t valid;
     uint8_t* unshard_fp8_out;     /* NULL => no fp8 copy (see fsdp_mt_cast_fp8, fsdp_mt_step_fp8) */
+    const void* const* grad_slice_ptrs; /* NULL => grad_slices + q*slice_stride */
 } fsdp_mt_tensor;
 
 typedef struct fsdp_mt_plan fsdp_mt_plan; /* opaque */

@@ -71,7 +71,8 @@ class MtTensor(ctypes.Structure):
                 ("exp_avg_sq", ctypes.c_void_p), ("grad_slices", ctypes.c_void_p),
                 ("slice_stride", ctypes.c_int64), ("unshard_bf16_out", ctypes.c_void_p),
                 ("grad_shard_out", ctypes.c_void_p), ("shard_numel", ctypes.c_int64),
-                ("valid", ctypes.c_int64), ("unshard_fp8_out", ctypes.c_void_p)]
+                ("valid", ctypes.c_int64), ("unshard_fp8_out", ctypes.c_void_p),
+                ("grad_slice_ptrs", ctypes.c_void_p)]
 
 
 class MtPlanInfo(ctypes.Structure):
@@ -201,11 +202,18 @@ def fsdp_mt_plan_create(tensors, n_slices, slice_dtype, stream=None):
     handle (int) to pass to fsdp_mt_step / fsdp_mt_plan_destroy."""
     n = len(tensors)
     arr = (MtTensor * max(n, 1))()
+    tables = []  # host arrays of slice pointers, alive until the plan has copied them
     for i, t in enumerate(tensors):
+        table = None
+        if t.get("grad_slice_ptrs") is not None:
+            ptrs = [_ptr(p) for p in t["grad_slice_ptrs"]]
+            table = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+            tables.append(table)
         arr[i] = MtTensor(_ptr(t["param_fp32"]), _ptr(t["exp_avg"]), _ptr(t["exp_avg_sq"]),
                           _ptr(t.get("grad_slices")), int(t.get("slice_stride", 0)),
                           _ptr(t.get("unshard_bf16_out")), _ptr(t.get("grad_shard_out")),
-                          int(t["shard_numel"]), int(t["valid"]), _ptr(t.get("unshard_fp8_out")))
+                          int(t["shard_numel"]), int(t["valid"]), _ptr(t.get("unshard_fp8_out")),
+                          ctypes.cast(table, ctypes.c_void_p) if table is not None else None)
     h = ctypes.c_void_p()
     _check(lib().fsdp_mt_plan_create(ctypes.byref(h), arr, n, int(n_slices), _dtype(slice_dtype),
                                      _stream(stream)))

@@ -37,6 +37,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "internal.h"
@@ -140,6 +141,8 @@ struct TensorDesc {
     uint16_t* out_bf16;  // null: no cast
     float* grad_out;     // null: reduced gradient not stored
     uint8_t* out_fp8;    // null: no fp8 copy
+    const void* const* slice_ptrs;  // null: slice q at slices + q*slice_stride;
+                                    // else slice q at slice_ptrs[q] (device table)
     int64_t slice_stride;
     int64_t shard_numel;
     int64_t valid;
@@ -326,12 +329,31 @@ struct SliceRegs {
     SliceVec<BF16> w[NS > 0 ? NS : 1];
 };
 
-template <int NS, bool BF16>
-__device__ __forceinline__ void load_slices(SliceRegs<NS, BF16>& r, const void* slices,
-                                            int64_t stride, int64_t e) {
+// Start of slice q of a shard.  TABLE: the shard has a table of slice
+// pointers (N receive buffers that need not share an allocation), read
+// through the constant address space, so the uniform entries arrive by
+// scalar loads.  Otherwise q slice strides past the first slice.  The
+// kernels choose TABLE once per tile, on the shard's uniform descriptor, so
+// the stride form's code is the same as without tables.
+template <typename T>
+using const_ptr = const __attribute__((address_space(4))) T*;
+
+template <bool BF16, bool TABLE>
+__device__ __forceinline__ const void* slice_base(const TensorDesc& T, int q) {
+    if constexpr (TABLE) {
+        return *(const_ptr<const void*>)(T.slice_ptrs + q);
+    } else {
+        using E = typename std::conditional<BF16, uint16_t, float>::type;
+        return static_cast<const E*>(T.slices) + q * T.slice_stride;
+    }
+}
+
+template <int NS, bool BF16, bool TABLE>
+__device__ __forceinline__ void load_slices(SliceRegs<NS, BF16>& r, const TensorDesc& T,
+                                            int64_t e) {
     static_assert(NS > 0, "compile-time slice count");
 #pragma unroll
-    for (int q = 0; q < NS; ++q) r.w[q] = load_group<BF16>(slices, q * stride + e);
+    for (int q = 0; q < NS; ++q) r.w[q] = load_group<BF16>(slice_base<BF16, TABLE>(T, q), e);
 }
 
 template <int NS, bool BF16>
@@ -350,13 +372,13 @@ __device__ __forceinline__ void reduce_regs(const SliceRegs<NS, BF16>& r, float 
 }
 
 // Runtime slice count: load and accumulate slice by slice.
-template <bool BF16>
-__device__ __forceinline__ void reduce_runtime(const void* slices, int64_t stride, int64_t e,
-                                               float g[kGroup], const StepConsts& c) {
-    widen<BF16>(load_group<BF16>(slices, e), g);
+template <bool BF16, bool TABLE>
+__device__ __forceinline__ void reduce_runtime(const TensorDesc& T, int64_t e, float g[kGroup],
+                                               const StepConsts& c) {
+    widen<BF16>(load_group<BF16>(slice_base<BF16, TABLE>(T, 0), e), g);
     for (int q = 1; q < c.n; ++q) {
         float x[kGroup];
-        widen<BF16>(load_group<BF16>(slices, q * stride + e), x);
+        widen<BF16>(load_group<BF16>(slice_base<BF16, TABLE>(T, q), e), x);
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) g[j] = g[j] + x[j];
     }
@@ -365,15 +387,15 @@ __device__ __forceinline__ void reduce_runtime(const void* slices, int64_t strid
 }
 
 // The mean of the slices on the group at e, N known at compile time or not.
-template <int NS, bool BF16>
+template <int NS, bool BF16, bool TABLE = false>
 __device__ __forceinline__ void reduce_group(const TensorDesc& T, int64_t e, float g[kGroup],
                                              const StepConsts& c) {
     if constexpr (NS > 0) {
         SliceRegs<NS, BF16> sr;
-        load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
+        load_slices<NS, BF16, TABLE>(sr, T, e);
         reduce_regs<NS, BF16>(sr, g, c);
     } else {
-        reduce_runtime<BF16>(T.slices, T.slice_stride, e, g, c);
+        reduce_runtime<BF16, TABLE>(T, e, g, c);
     }
 }
 
@@ -431,20 +453,20 @@ __device__ __forceinline__ float slice_elem(const void* slices, int64_t i) {
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool TABLE = false>
 __device__ __forceinline__ float reduce_elem(const TensorDesc& T, int64_t k, const StepConsts& c) {
-    float s = slice_elem<BF16>(T.slices, k);
-    for (int q = 1; q < c.n; ++q) s = s + slice_elem<BF16>(T.slices, q * T.slice_stride + k);
+    float s = slice_elem<BF16>(slice_base<BF16, TABLE>(T, 0), k);
+    for (int q = 1; q < c.n; ++q) s = s + slice_elem<BF16>(slice_base<BF16, TABLE>(T, q), k);
     return finish_mean(s, c);
 }
 
 // The whole fused step on element k (any alignment); +0 everywhere in the pad
 // (fp8 code 0).
-template <bool BF16, bool AMAX = false, bool FP8 = false>
+template <bool BF16, bool AMAX = false, bool FP8 = false, bool TABLE = false>
 __device__ __forceinline__ void fused_elem(const TensorDesc& T, int64_t k, const StepConsts& c,
                                            uint32_t* amax = nullptr, float fp8_scale = 0.0f) {
     if (k < T.valid) {
-        const float g = reduce_elem<BF16>(T, k, c);
+        const float g = reduce_elem<BF16, TABLE>(T, k, c);
         float p = ld(T.param + k), m = ld(T.m + k), v = ld(T.v + k);
         adamw(p, m, v, g, c);
         if constexpr (AMAX) *amax = std::max(*amax, __float_as_uint(p) & 0x7fffffffu);
@@ -495,8 +517,8 @@ __device__ __forceinline__ int64_t vector_end(const TensorDesc& T, int64_t begin
 }
 
 // The fused step on elements [begin, end) of shard T; `begin` is a multiple of
-// kGroup.  AMAX and FP8 as in update_store.
-template <int NS, bool BF16, bool AMAX = false, bool FP8 = false>
+// kGroup.  AMAX and FP8 as in update_store; TABLE as in slice_base.
+template <int NS, bool BF16, bool AMAX = false, bool FP8 = false, bool TABLE = false>
 __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, int64_t end,
                                             const StepConsts& c, uint32_t* amax = nullptr,
                                             float fp8_scale = 0.0f) {
@@ -506,7 +528,7 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
         if constexpr (NS > 0) {
             // every load of the group before the first arithmetic
             SliceRegs<NS, BF16> sr;
-            load_slices<NS, BF16>(sr, T.slices, T.slice_stride, e);
+            load_slices<NS, BF16, TABLE>(sr, T, e);
             load_state(s, T, e);
             float g[kGroup];
             reduce_regs<NS, BF16>(sr, g, c);
@@ -514,12 +536,12 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
         } else {
             load_state(s, T, e);
             float g[kGroup];
-            reduce_runtime<BF16>(T.slices, T.slice_stride, e, g, c);
+            reduce_runtime<BF16, TABLE>(T, e, g, c);
             update_store<true, AMAX, FP8>(s, g, T, e, c, amax, fp8_scale);
         }
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
-        fused_elem<BF16, AMAX, FP8>(T, k, c, amax, fp8_scale);
+        fused_elem<BF16, AMAX, FP8, TABLE>(T, k, c, amax, fp8_scale);
 }
 
 // Reduce only: grad_out = mean of the slices on [begin, end).
@@ -541,7 +563,7 @@ __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin,
 // accumulation over micro-batches), else it replaces it.  SQ: return this
 // lane's sum of the squares of the stored values, in fp64 (each fp32
 // square is exact in fp64).  The padding is +0 either way.
-template <int NS, bool BF16, bool SQ>
+template <int NS, bool BF16, bool SQ, bool TABLE = false>
 __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_t begin,
                                                      int64_t end, const StepConsts& c, bool acc) {
     double sq = 0.0;
@@ -551,7 +573,7 @@ __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_
         f32x4 old = {0.f, 0.f, 0.f, 0.f};
         if (acc) old = ld_state(go);
         float g[kGroup];
-        reduce_group<NS, BF16>(T, e, g, c);
+        reduce_group<NS, BF16, TABLE>(T, e, g, c);
         if (acc) {
 #pragma unroll
             for (int j = 0; j < kGroup; ++j) g[j] = old[j] + g[j];
@@ -565,7 +587,7 @@ __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) {
         float gk = 0.0f;
         if (k < T.valid) {
-            gk = reduce_elem<BF16>(T, k, c);
+            gk = reduce_elem<BF16, TABLE>(T, k, c);
             if (acc) gk = ld(T.grad_out + k) + gk;
         }
         st(T.grad_out + k, gk);
@@ -675,26 +697,33 @@ __device__ __forceinline__ uint32_t xcd_slot(uint32_t b, uint32_t n) {
     return (b % kXcds) * (n / kXcds) + b / kXcds;
 }
 
-// Multi-tensor fused step: reduce, AdamW and cast for every tile.
-template <int NS, bool BF16>
+// Multi-tensor fused step: reduce, AdamW and cast for every tile.  TABLES:
+// some shard of the plan reads its slices through a table of pointers (the
+// choice per tile then follows the shard's descriptor); plans without
+// tables run the stride form only.
+template <int NS, bool BF16, bool TABLES>
 __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
                                                          const ChunkDesc* __restrict__ chunks,
                                                          StepConsts c) {
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        fused_range<NS, BF16>(T, b, e, c);
+        if (TABLES && T.slice_ptrs)
+            fused_range<NS, BF16, false, false, TABLES>(T, b, e, c);
+        else
+            fused_range<NS, BF16>(T, b, e, c);
     });
 }
 
 // Reduce (or reduce and accumulate) into grad_shard_out; SQ: also write
 // this workgroup's sum of squares of the stored values to its partials slot.
-template <int NS, bool BF16, bool SQ>
+template <int NS, bool BF16, bool SQ, bool TABLES>
 __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDesc* __restrict__ tensors,
                                                                  const ChunkDesc* __restrict__ chunks,
                                                                  StepConsts c, int32_t acc,
                                                                  double* partials) {
     double sq = 0.0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        sq = reduce_store_range<NS, BF16, SQ>(T, b, e, c, acc != 0);
+        sq = TABLES && T.slice_ptrs ? reduce_store_range<NS, BF16, SQ, TABLES>(T, b, e, c, acc != 0)
+                                    : reduce_store_range<NS, BF16, SQ>(T, b, e, c, acc != 0);
     });
     if constexpr (SQ) {
         const double total = wave_sum(sq);
@@ -722,13 +751,16 @@ __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc
 
 // The fused step that also records, per workgroup, the largest |p'| (as
 // fp32 bits, in the workgroup's slot) for the fp8 copy's per-tensor scale.
-template <int NS, bool BF16>
+template <int NS, bool BF16, bool TABLES>
 __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* __restrict__ tensors,
                                                               const ChunkDesc* __restrict__ chunks,
                                                               StepConsts c, uint32_t* tile_amax) {
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        fused_range<NS, BF16, true>(T, b, e, c, &am);
+        if (TABLES && T.slice_ptrs)
+            fused_range<NS, BF16, true, false, TABLES>(T, b, e, c, &am);
+        else
+            fused_range<NS, BF16, true>(T, b, e, c, &am);
     });
     const uint32_t wm = wave_max(am);
     if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
@@ -737,7 +769,7 @@ __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* 
 // The fused step that also writes the fp8 codes of p' with a per-tensor scale
 // given in advance (scale_in[index], e.g. from the previous step's amax) and
 // records this step's per-workgroup largest |p'|, all in the one pass.
-template <int NS, bool BF16>
+template <int NS, bool BF16, bool TABLES>
 __global__ __launch_bounds__(kBlock) void mt_step_fp8_kernel(const TensorDesc* __restrict__ tensors,
                                                              const ChunkDesc* __restrict__ chunks,
                                                              StepConsts c, const float* scale_in,
@@ -745,7 +777,10 @@ __global__ __launch_bounds__(kBlock) void mt_step_fp8_kernel(const TensorDesc* _
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         const float scale = ld(scale_in + T.index);
-        fused_range<NS, BF16, true, true>(T, b, e, c, &am, scale);
+        if (TABLES && T.slice_ptrs)
+            fused_range<NS, BF16, true, true, TABLES>(T, b, e, c, &am, scale);
+        else
+            fused_range<NS, BF16, true, true>(T, b, e, c, &am, scale);
     });
     const uint32_t wm = wave_max(am);
     if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
@@ -873,60 +908,81 @@ __global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T) {
 using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts);
 using ReduceKernel = void (*)(TensorDesc, StepConsts);
 
-template <bool BF16>
+template <bool BF16, bool TABLES>
 MtKernel pick_mt(int n) {
     switch (n) {
-        case 1: return mt_step_kernel<1, BF16>;
-        case 2: return mt_step_kernel<2, BF16>;
-        case 4: return mt_step_kernel<4, BF16>;
-        case 8: return mt_step_kernel<8, BF16>;
-        default: return mt_step_kernel<0, BF16>;
+        case 1: return mt_step_kernel<1, BF16, TABLES>;
+        case 2: return mt_step_kernel<2, BF16, TABLES>;
+        case 4: return mt_step_kernel<4, BF16, TABLES>;
+        case 8: return mt_step_kernel<8, BF16, TABLES>;
+        default: return mt_step_kernel<0, BF16, TABLES>;
     }
+}
+
+MtKernel pick_mt(int dtype, int n, bool tables) {
+    if (dtype == FSDP_DT_BF16) return tables ? pick_mt<true, true>(n) : pick_mt<true, false>(n);
+    return tables ? pick_mt<false, true>(n) : pick_mt<false, false>(n);
 }
 
 using ReduceStoreKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, int32_t, double*);
 
-template <bool BF16, bool SQ>
+template <bool BF16, bool SQ, bool TABLES>
 ReduceStoreKernel pick_reduce_store(int n) {
     switch (n) {
-        case 1: return mt_reduce_store_kernel<1, BF16, SQ>;
-        case 2: return mt_reduce_store_kernel<2, BF16, SQ>;
-        case 4: return mt_reduce_store_kernel<4, BF16, SQ>;
-        case 8: return mt_reduce_store_kernel<8, BF16, SQ>;
-        default: return mt_reduce_store_kernel<0, BF16, SQ>;
+        case 1: return mt_reduce_store_kernel<1, BF16, SQ, TABLES>;
+        case 2: return mt_reduce_store_kernel<2, BF16, SQ, TABLES>;
+        case 4: return mt_reduce_store_kernel<4, BF16, SQ, TABLES>;
+        case 8: return mt_reduce_store_kernel<8, BF16, SQ, TABLES>;
+        default: return mt_reduce_store_kernel<0, BF16, SQ, TABLES>;
     }
 }
 
+template <bool TABLES>
 ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq) {
-    if (dtype == FSDP_DT_BF16) return sq ? pick_reduce_store<true, true>(n) : pick_reduce_store<true, false>(n);
-    return sq ? pick_reduce_store<false, true>(n) : pick_reduce_store<false, false>(n);
+    if (dtype == FSDP_DT_BF16)
+        return sq ? pick_reduce_store<true, true, TABLES>(n) : pick_reduce_store<true, false, TABLES>(n);
+    return sq ? pick_reduce_store<false, true, TABLES>(n) : pick_reduce_store<false, false, TABLES>(n);
+}
+
+ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq, bool tables) {
+    return tables ? pick_reduce_store<true>(dtype, n, sq) : pick_reduce_store<false>(dtype, n, sq);
 }
 
 using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, uint32_t*);
 
-template <bool BF16>
+template <bool BF16, bool TABLES>
 AmaxKernel pick_amax(int n) {
     switch (n) {
-        case 1: return mt_step_amax_kernel<1, BF16>;
-        case 2: return mt_step_amax_kernel<2, BF16>;
-        case 4: return mt_step_amax_kernel<4, BF16>;
-        case 8: return mt_step_amax_kernel<8, BF16>;
-        default: return mt_step_amax_kernel<0, BF16>;
+        case 1: return mt_step_amax_kernel<1, BF16, TABLES>;
+        case 2: return mt_step_amax_kernel<2, BF16, TABLES>;
+        case 4: return mt_step_amax_kernel<4, BF16, TABLES>;
+        case 8: return mt_step_amax_kernel<8, BF16, TABLES>;
+        default: return mt_step_amax_kernel<0, BF16, TABLES>;
     }
+}
+
+AmaxKernel pick_amax(int dtype, int n, bool tables) {
+    if (dtype == FSDP_DT_BF16) return tables ? pick_amax<true, true>(n) : pick_amax<true, false>(n);
+    return tables ? pick_amax<false, true>(n) : pick_amax<false, false>(n);
 }
 
 using Fp8StepKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const float*,
                                uint32_t*);
 
-template <bool BF16>
+template <bool BF16, bool TABLES>
 Fp8StepKernel pick_fp8_step(int n) {
     switch (n) {
-        case 1: return mt_step_fp8_kernel<1, BF16>;
-        case 2: return mt_step_fp8_kernel<2, BF16>;
-        case 4: return mt_step_fp8_kernel<4, BF16>;
-        case 8: return mt_step_fp8_kernel<8, BF16>;
-        default: return mt_step_fp8_kernel<0, BF16>;
+        case 1: return mt_step_fp8_kernel<1, BF16, TABLES>;
+        case 2: return mt_step_fp8_kernel<2, BF16, TABLES>;
+        case 4: return mt_step_fp8_kernel<4, BF16, TABLES>;
+        case 8: return mt_step_fp8_kernel<8, BF16, TABLES>;
+        default: return mt_step_fp8_kernel<0, BF16, TABLES>;
     }
+}
+
+Fp8StepKernel pick_fp8_step(int dtype, int n, bool tables) {
+    if (dtype == FSDP_DT_BF16) return tables ? pick_fp8_step<true, true>(n) : pick_fp8_step<true, false>(n);
+    return tables ? pick_fp8_step<false, true>(n) : pick_fp8_step<false, false>(n);
 }
 
 template <bool BF16>
@@ -1039,6 +1095,32 @@ int32_t check_slices(const void* slices, int32_t slice_dtype, int64_t slice_stri
     return FSDP_OK;
 }
 
+// Checks of a shard's table of slice pointers (the slices of the shard in
+// separate buffers): every entry set and aligned to the element size when the
+// shard has data to read.
+int32_t check_slice_table(const void* const* ptrs, int32_t slice_dtype, int32_t n_slices,
+                          int64_t valid, const char* who) {
+    if (valid == 0) return FSDP_OK;
+    for (int32_t q = 0; q < n_slices; ++q) {
+        if (!ptrs[q]) return fail(FSDP_E_ARG, "%s: null grad_slice_ptrs[%d]", who, q);
+        if (!aligned(ptrs[q], dtype_bytes(slice_dtype)))
+            return fail(FSDP_E_ALIGN, "%s: grad_slice_ptrs[%d] not aligned to its element size",
+                        who, q);
+    }
+    int64_t bytes;
+    if (!fsdp::mul_i64(valid, dtype_bytes(slice_dtype), &bytes))
+        return fail(FSDP_E_ARG, "%s: slice extent overflows int64", who);
+    return FSDP_OK;
+}
+
+// Whether every slice of a table is aligned for the vector path.
+bool slice_table_vec_ok(const void* const* ptrs, int32_t slice_dtype, int32_t n_slices) {
+    const uintptr_t a = slice_dtype == FSDP_DT_BF16 ? kBf16Vec : kF32Vec;
+    for (int32_t q = 0; q < n_slices; ++q)
+        if (!aligned(ptrs[q], a)) return false;
+    return true;
+}
+
 int32_t check_sizes(int64_t S, int64_t valid, const char* who) {
     if (S < 0 || valid < 0 || valid > S)
         return fail(FSDP_E_ARG, "%s: need 0 <= valid (%lld) <= shard_numel (%lld)", who,
@@ -1077,10 +1159,12 @@ struct fsdp_mt_plan {
     bool all_fp8 = false;            // every non-empty shard has one
     bool any_bf16 = false;           // some shard has a bf16 copy
     bool any_grad_out = false;       // some shard stores its reduced gradient
+    bool any_table = false;          // some shard reads its slices through a table of pointers
     uint32_t* d_tile_amax = nullptr;      // fp8: largest |p'| per workgroup
     ShardTiles* d_shard_tiles = nullptr;  // fp8: each input shard's run of workgroups
     TensorDesc* d_tensors = nullptr;
     ChunkDesc* d_chunks = nullptr;
+    const void** d_slice_ptrs = nullptr;  // the shards' tables of slice pointers, if any
     double* d_partials = nullptr;    // clipped steps: one sum of squares per workgroup,
                                      // then kSumBlocks second-stage sums
 };
@@ -1224,6 +1308,8 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
     bool all_grad_out = true;
     bool any_fp8 = false, all_fp8 = true, any_bf16 = false, any_grad_out = false;
     std::vector<fsdp::Range> rs;
+    std::vector<const void*> table_host;  // the tables of slice pointers, shard after shard
+    std::vector<int64_t> table_off;       // per desc: its table's offset, or -1
     int64_t total = 0, total_valid = 0;
     for (int32_t i = 0; i < n_tensors; ++i) {
         const fsdp_mt_tensor& t = tensors[i];
@@ -1231,9 +1317,15 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
         snprintf(tag, sizeof tag, "%s: shard %d", who, i);
         int32_t st;
         if ((st = check_sizes(t.shard_numel, t.valid, tag)) != FSDP_OK) return st;
-        if ((st = check_slices(t.grad_slices, slice_dtype, t.slice_stride, n_slices, t.shard_numel,
-                               t.valid, tag)) != FSDP_OK)
+        const bool table = t.grad_slice_ptrs != nullptr;
+        if (table) {
+            if ((st = check_slice_table(t.grad_slice_ptrs, slice_dtype, n_slices, t.valid, tag)) !=
+                FSDP_OK)
+                return st;
+        } else if ((st = check_slices(t.grad_slices, slice_dtype, t.slice_stride, n_slices,
+                                      t.shard_numel, t.valid, tag)) != FSDP_OK) {
             return st;
+        }
         if (t.shard_numel > 0 && (!t.param_fp32 || !t.exp_avg || !t.exp_avg_sq))
             return fail(FSDP_E_ARG, "%s: null param / exp_avg / exp_avg_sq", tag);
         if (!aligned(t.param_fp32, 4) || !aligned(t.exp_avg, 4) || !aligned(t.exp_avg_sq, 4) ||
@@ -1257,20 +1349,30 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
             rs.push_back(range_of(t.grad_shard_out, t.shard_numel, 4, true, i, "grad_shard_out"));
         if (t.unshard_fp8_out)
             rs.push_back(range_of(t.unshard_fp8_out, t.shard_numel, 1, true, i, "unshard_fp8_out"));
-        add_slice_ranges(rs, t.grad_slices, slice_dtype, t.slice_stride, n_slices, t.valid, i);
+        if (table) {
+            for (int32_t q = 0; q < n_slices && t.valid > 0; ++q)
+                rs.push_back(range_of(t.grad_slice_ptrs[q], t.valid, dtype_bytes(slice_dtype), false,
+                                      i, "grad_slice_ptrs"));
+            table_off.push_back(static_cast<int64_t>(table_host.size()));
+            table_host.insert(table_host.end(), t.grad_slice_ptrs, t.grad_slice_ptrs + n_slices);
+        } else {
+            add_slice_ranges(rs, t.grad_slices, slice_dtype, t.slice_stride, n_slices, t.valid, i);
+            table_off.push_back(-1);
+        }
         TensorDesc d{};
         d.param = t.param_fp32;
         d.m = t.exp_avg;
         d.v = t.exp_avg_sq;
-        d.slices = t.grad_slices;
+        d.slices = table ? nullptr : t.grad_slices;
         d.out_bf16 = t.unshard_bf16_out;
         d.grad_out = t.grad_shard_out;
         d.out_fp8 = t.unshard_fp8_out;
         d.index = i;
-        d.slice_stride = t.slice_stride;
+        d.slice_stride = table ? 0 : t.slice_stride;
         d.shard_numel = t.shard_numel;
         d.valid = t.valid;
-        d.vec_ok = vec_ok(d, slice_dtype, n_slices);
+        d.vec_ok = vec_ok(d, slice_dtype, n_slices) &&
+                   (!table || slice_table_vec_ok(t.grad_slice_ptrs, slice_dtype, n_slices));
         descs.push_back(d);
     }
     {
@@ -1320,6 +1422,7 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
     plan->all_fp8 = all_fp8;
     plan->any_bf16 = any_bf16;
     plan->any_grad_out = any_grad_out;
+    plan->any_table = !table_host.empty();
     hipError_t e = hipGetDevice(&plan->device);
     if (e == hipSuccess && any_fp8 && n_tensors > 0) {
         e = hipMalloc(reinterpret_cast<void**>(&plan->d_shard_tiles), runs.size() * sizeof(ShardTiles));
@@ -1330,6 +1433,16 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
             e = hipMalloc(reinterpret_cast<void**>(&plan->d_tile_amax),
                           static_cast<size_t>(plan->n_blocks) * sizeof(uint32_t));
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    }
+    if (e == hipSuccess && !chunks.empty() && !table_host.empty()) {
+        e = hipMalloc(reinterpret_cast<void**>(&plan->d_slice_ptrs),
+                      table_host.size() * sizeof(const void*));
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(plan->d_slice_ptrs, table_host.data(),
+                               table_host.size() * sizeof(const void*), hipMemcpyHostToDevice,
+                               stream);
+        for (size_t k = 0; e == hipSuccess && k < descs.size(); ++k)
+            if (table_off[k] >= 0) descs[k].slice_ptrs = plan->d_slice_ptrs + table_off[k];
     }
     if (e == hipSuccess && !chunks.empty()) {
         e = hipMalloc(reinterpret_cast<void**>(&plan->d_tensors), descs.size() * sizeof(TensorDesc));
@@ -1363,8 +1476,7 @@ extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
-    const MtKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_mt<true>(plan->n_slices)
-                                                         : pick_mt<false>(plan->n_slices);
+    const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_table);
     hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                        lds_reserve(step_bytes(plan)), stream, plan->d_tensors, plan->d_chunks, c);
     return launch_status(who);
@@ -1386,7 +1498,8 @@ extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumul
     const bool sq = sqnorm_out != nullptr;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(nullptr, plan->n_slices);
-        const ReduceStoreKernel k = pick_reduce_store(plan->slice_dtype, plan->n_slices, sq);
+        const ReduceStoreKernel k = pick_reduce_store(plan->slice_dtype, plan->n_slices, sq,
+                                                      plan->any_table);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(slice_bytes(plan) + 4 + 4 * accumulate), stream,
                            plan->d_tensors, plan->d_chunks, c,
@@ -1503,8 +1616,7 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(hp, plan->n_slices);
-        const AmaxKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_amax<true>(plan->n_slices)
-                                                               : pick_amax<false>(plan->n_slices);
+        const AmaxKernel k = pick_amax(plan->slice_dtype, plan->n_slices, plan->any_table);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(step_bytes(plan), RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
                            plan->d_chunks, c, plan->d_tile_amax);
@@ -1564,8 +1676,7 @@ static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(hp, plan->n_slices);
-        const Fp8StepKernel k = plan->slice_dtype == FSDP_DT_BF16 ? pick_fp8_step<true>(plan->n_slices)
-                                                                  : pick_fp8_step<false>(plan->n_slices);
+        const Fp8StepKernel k = pick_fp8_step(plan->slice_dtype, plan->n_slices, plan->any_table);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(step_bytes(plan) + 1, RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
                            plan->d_chunks, c, scale_in, plan->d_tile_amax);
@@ -1661,8 +1772,9 @@ extern "C" int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan) {
     if (!plan) return FSDP_OK;
     hipError_t e = hipSuccess;
     if (plan->d_tensors || plan->d_chunks || plan->d_partials || plan->d_tile_amax ||
-        plan->d_shard_tiles) {
+        plan->d_shard_tiles || plan->d_slice_ptrs) {
         e = hipDeviceSynchronize();
+        if (plan->d_slice_ptrs) (void)hipFree(plan->d_slice_ptrs);
         if (plan->d_tensors) (void)hipFree(plan->d_tensors);
         if (plan->d_chunks) (void)hipFree(plan->d_chunks);
         if (plan->d_partials) (void)hipFree(plan->d_partials);

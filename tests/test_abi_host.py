@@ -327,3 +327,23 @@ def test_last_error_is_per_thread():
     for t in ts:
         t.join()
     assert not bad, bad[:3]
+
+
+def test_mt_plan_slice_table_checks():
+    # a shard whose N slices sit in separate buffers (a table of pointers);
+    # fake device addresses, refused before any device work
+    f = B.fsdp_mt_plan_create
+
+    def tab(ptrs, valid=1024):
+        t = _t(A, A + 8192, A + 16384, None, valid=valid)
+        t.pop("grad_slices")
+        t["grad_slice_ptrs"] = ptrs
+        return t
+
+    assert _err(f, [tab([Bp, None, C])], 3, "f32", stream=0) == "ARG"          # a null entry
+    assert _err(f, [tab([Bp, C + 2, D])], 3, "f32", stream=0) == "ALIGN"       # not 4-byte aligned
+    assert _err(f, [tab([Bp, C + 1, D])], 3, "bf16", stream=0) == "ALIGN"      # not 2-byte aligned
+    assert _err(f, [tab([Bp, A + 400, D])], 3, "f32", stream=0) == "ALIAS"     # inside param
+    # another shard's written buffer overlapping a table entry
+    other = _t(E, E + 8192, E + 16384, F)
+    assert _err(f, [tab([Bp, C, E + 100]), other], 3, "f32", stream=0) == "ALIAS"
