@@ -3,10 +3,12 @@
 A caller may capture a whole optimizer step in a HIP graph (torch's
 CUDAGraph on ROCm) once its plan exists.  The plan calls only launch
 kernels on the caller's stream: no allocation, no host synchronisation and no
-memset.  Three sequences are captured:
+memset.  The sequences captured:
   * the fused step (one launch);
   * the clipped step: reduce + sum of squares, clip coefficient, scaled update;
-  * the fp8 step: step with amax, per-tensor amax, fp8 codes.
+  * the fp8 step: step with amax, per-tensor amax, fp8 codes;
+  * the fused and clipped steps of a plan whose shards name their slices
+    through tables of pointers (its own kernel variants).
 Each graph is replayed several times, with eager work (fresh gradients) and
 synchronisations between the replays.  After every replay, the state and
 outputs must equal a twin state driven by the same calls made eagerly.  The
@@ -132,3 +134,36 @@ def test_delayed_fp8_step_graph(gpu):
          init={"scale": 448.0 / 0.05})
     a.close()
     b.close()
+
+
+def _table_plan(st):
+    """A plan over st whose shards name their slices through tables of
+    pointers (the rows of st's slice buffer)."""
+    es = st.slices.element_size()
+    base = st.slices.data_ptr()
+    recs = []
+    for d, (off, length, held, _) in zip(st.mt_tensors(with_grad_out=True, with_fp8=False),
+                                         st.segments):
+        d = dict(d)
+        d.pop("grad_slices")
+        d.pop("slice_stride")
+        d["grad_slice_ptrs"] = [base + es * (q * st.total + off) for q in range(st.w.n_slices)]
+        recs.append(d)
+    st.plan = B.MtPlan(recs, st.w.n_slices, st.w.slice_dtype)
+
+
+def test_slice_table_steps_graph(gpu):
+    """A plan with tables of slice pointers runs its own kernel variants:
+    the fused step and the clipped step captured and replayed."""
+    w = WORKLOADS[3]
+    a, b = _pair(w, gpu, bf16_out=True, grad_out=True)
+    _table_plan(a)
+    _table_plan(b)
+
+    def calls(st, bufs):
+        st.plan.step(w.hparams, 3)
+        st.plan.reduce_sqnorm(bufs["sq"])
+        B.fsdp_clip_coef(bufs["coef"], None, bufs["sq"], 1, 0.05)
+        st.plan.step_clipped(w.hparams, 4, bufs["coef"])
+
+    _run(w, a, b, gpu, calls, extra=(("sq", (1, torch.float64)), ("coef", (1, torch.float32))))
