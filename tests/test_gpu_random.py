@@ -7,7 +7,9 @@ strides wider than the shard, the slice count N and dtype, which shards write
 the bf16 copy and the reduced gradient, and the AdamW hyperparameters and step.
 Every shard is checked against the float64 oracle (per-step resync) with guard
 words around every buffer, over two consecutive steps.  The same random tables
-drive the accumulated and clipped step and the one-pass fp8 step.
+drive the accumulated and clipped step and the one-pass fp8 step.  In the
+fused-step plans about 30 % of the shards name their slices through tables
+of pointers to separate buffers.
 """
 
 import math
@@ -22,6 +24,7 @@ from oracle import step as O
 from rank_step_amd import binding as B
 from tests import parity as PR
 from tests.test_gpu_kernels import Shard
+from tests.test_gpu_slice_table import _tabled
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +71,19 @@ def test_random_plan(gpu, plan_id):
     shards = [Shard(S, va, N, sdt, gpu, seed=40_000 + 100 * plan_id + i, offset=o,
                     stride_extra=x, bf16=bf, gout=go)
               for i, (S, va, o, x, bf, go) in enumerate(specs)]
-    plan = B.MtPlan([s.mt() for s in shards], N, sdt)
+    # about 30 % of the shards name their slices through a table of pointers
+    # (separate buffers, half of them misaligned for the vector path)
+    trng = np.random.default_rng(60_000 + plan_id)
+    tables, recs = {}, []
+    for i, s in enumerate(shards):
+        if trng.random() < 0.3:
+            tables[i], rec = _tabled(s, gpu, misalign=bool(trng.random() < 0.5))
+            recs.append(rec)
+        else:
+            recs.append(s.mt())
+    print(f"  {len(tables)} shards through slice tables", flush=True)
+    plan = B.MtPlan(recs, N, sdt)
+    del recs
     info = plan.info()
     assert info["n_tensors"] == len(specs)
     assert info["total_numel"] == sum(s[0] for s in specs)
@@ -78,11 +93,16 @@ def test_random_plan(gpu, plan_id):
             g.manual_seed(50_000 + 1000 * plan_id + 10 * t + i)
             x = torch.randn(N, s.S, generator=g, device=gpu) * 1e-2
             s.sl.t.view(N, s.stride)[:, :s.valid] = x[:, :s.valid].to(s.sl.t.dtype)
+            for q, buf in enumerate(tables.get(i, ())):
+                buf.t.copy_(s.sl.t.view(N, s.stride)[q, :s.S])
         snaps = [s.snapshot() for s in shards]
         plan.step(hp, t)
         torch.cuda.synchronize()
         for i, (s, snap) in enumerate(zip(shards, snaps)):
             s.check(f"{label} shard {i} t={t}", snap, t, hp=hp)
+        for i, bufs in tables.items():
+            for buf in bufs:
+                buf.check_guards(f"{label} shard {i} slice buffer")
     plan.close()
 
 
