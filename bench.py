@@ -443,7 +443,12 @@ def main():
     st = RankState(w, 0, dev, bf16_out=bf16_out, grad_out=args.clip is not None,
                    fp8_out=not args.no_fp8)
     st.load_grads(1)
+    # plan creation: once per wrap, on the host (layout of the chunk and
+    # descriptor tables, argument and alias checks, one upload)
+    torch.cuda.synchronize()
+    p0 = time.perf_counter()
     st.make_plan(stream, with_grad_out=False, with_fp8=False)
+    plan_s = time.perf_counter() - p0
     info = st.plan.info()
     total = st.total
     bpp = bytes_per_param(w, bf16_out)
@@ -532,6 +537,7 @@ def main():
                         "min": per_step[0], "max": per_step[-1],
                         "from": "a second pass of K steps with an event between consecutive steps"},
         "host_wall_s_timed": wall,
+        "plan_create_ms": plan_s * 1e3,
         "roofline": {
             "bound": "hbm",
             "achieved": gbs,
