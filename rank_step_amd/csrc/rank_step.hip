@@ -65,12 +65,18 @@ namespace {
 // launch caps its resident workgroups at this divided by what one workgroup
 // moves, through its LDS reservation.
 #ifndef RS_INFLIGHT_KB
-#define RS_INFLIGHT_KB 90
+#define RS_INFLIGHT_KB 96
 #endif
 // The fused steps that also reduce |p'| and write fp8 codes keep each wave
 // longer for the same bytes, so they need more resident waves: their budget.
 #ifndef RS_INFLIGHT_KB_FP8
 #define RS_INFLIGHT_KB_FP8 105
+#endif
+// The synchronised accumulation pass (reduce, then add into the stored
+// gradient) ran 7 % slower at 16 resident workgroups per CU than at 15, which
+// the general budget would give it: its budget.
+#ifndef RS_INFLIGHT_KB_ACC
+#define RS_INFLIGHT_KB_ACC 90
 #endif
 // 256-element tiles per workgroup of the fp8 code pass (1, 2, 4 or 8): it
 // moves 5 bytes per element, so its lanes take several groups each.  It reads
@@ -1501,7 +1507,8 @@ extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumul
         const ReduceStoreKernel k = pick_reduce_store(plan->slice_dtype, plan->n_slices, sq,
                                                       plan->any_table);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
-                           lds_reserve(slice_bytes(plan) + 4 + 4 * accumulate), stream,
+                           lds_reserve(slice_bytes(plan) + 4 + 4 * accumulate,
+                                       accumulate ? RS_INFLIGHT_KB_ACC : RS_INFLIGHT_KB), stream,
                            plan->d_tensors, plan->d_chunks, c,
                            accumulate, plan->d_partials);
         if ((st = launch_status(who)) != FSDP_OK) return st;
