@@ -65,7 +65,7 @@ namespace {
 // launch caps its resident workgroups at this divided by what one workgroup
 // moves, through its LDS reservation.
 #ifndef RS_INFLIGHT_KB
-#define RS_INFLIGHT_KB 96
+#define RS_INFLIGHT_KB 100
 #endif
 // The fused steps that also reduce |p'| and write fp8 codes keep each wave
 // longer for the same bytes, so they need more resident waves: their budget.
