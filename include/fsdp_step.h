@@ -291,6 +291,11 @@ typedef struct {
  * sum per workgroup for fsdp_mt_reduce_sqnorm.  Synchronises
  * `stream` once.  The caller keeps every referenced buffer alive and in
  * place while the plan exists.  n_tensors may be 0 (an empty plan).
+ * The plan keeps the byte ranges of its shards' buffers: the further device
+ * buffers that the calls on it take (grad_scale, scale_in, amax_ranks as
+ * inputs; sqnorm_out, amax_out, scale_out as outputs) are checked against
+ * them.  An input may overlap only the read-only gradient slices, an output
+ * no buffer of the plan (else FSDP_E_ALIAS, before any work is queued).
  * Errors: as the single-shard calls; FSDP_E_CAPACITY if one launch cannot
  * hold the plan's workgroups (checked before any table is built); FSDP_E_HIP
  * if the upload fails. */

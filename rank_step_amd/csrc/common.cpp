@@ -49,6 +49,45 @@ int32_t check_aliases(std::vector<Range>& ranges) {
     return FSDP_OK;
 }
 
+void Footprint::merge(std::vector<Span>& spans) {
+    std::sort(spans.begin(), spans.end());
+    size_t n = 0;
+    for (const Span& s : spans) {
+        if (n > 0 && s.first <= spans[n - 1].second)
+            spans[n - 1].second = std::max(spans[n - 1].second, s.second);
+        else
+            spans[n++] = s;
+    }
+    spans.resize(n);
+    spans.shrink_to_fit();
+}
+
+void Footprint::build(const std::vector<Range>& ranges) {
+    written_.clear();
+    read_.clear();
+    for (const Range& r : ranges) {
+        if (r.hi <= r.lo) continue;
+        (r.written ? written_ : read_).emplace_back(r.lo, r.hi);
+    }
+    merge(written_);
+    merge(read_);
+}
+
+bool Footprint::hits(const std::vector<Span>& spans, uintptr_t lo, uintptr_t hi) {
+    if (hi <= lo) return false;
+    // the first span that ends after lo; the spans are disjoint and sorted, so
+    // their ends are sorted too
+    const auto it = std::upper_bound(spans.begin(), spans.end(), lo,
+                                     [](uintptr_t x, const Span& s) { return x < s.second; });
+    return it != spans.end() && it->first < hi;
+}
+
+bool Footprint::hits_written(uintptr_t lo, uintptr_t hi) const { return hits(written_, lo, hi); }
+
+bool Footprint::hits_any(uintptr_t lo, uintptr_t hi) const {
+    return hits(written_, lo, hi) || hits(read_, lo, hi);
+}
+
 }  // namespace fsdp
 
 extern "C" const char* fsdp_last_error(void) { return fsdp::g_last_error; }

@@ -3,6 +3,7 @@
 
 #include <cstdint>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "fsdp_step.h"
@@ -29,6 +30,26 @@ struct Range {
 // FSDP_E_ALIAS if a written range overlaps any other range (read-only ranges
 // may overlap each other); empty ranges never overlap.
 int32_t check_aliases(std::vector<Range>& ranges);
+
+// The byte ranges of every buffer a plan's shards name, kept so that the
+// further device buffers a plan call takes (a scale, an amax array, a sum)
+// can be checked against them in O(log n).  `written` holds the buffers some
+// plan call writes, `read` the read-only ones (the gradient slices); each is
+// kept as a sorted union of disjoint intervals.
+class Footprint {
+public:
+    void build(const std::vector<Range>& ranges);
+    // Whether [lo, hi) overlaps a written buffer of the plan.
+    bool hits_written(uintptr_t lo, uintptr_t hi) const;
+    // Whether [lo, hi) overlaps any buffer of the plan.
+    bool hits_any(uintptr_t lo, uintptr_t hi) const;
+
+private:
+    using Span = std::pair<uintptr_t, uintptr_t>;
+    static void merge(std::vector<Span>& spans);
+    static bool hits(const std::vector<Span>& spans, uintptr_t lo, uintptr_t hi);
+    std::vector<Span> written_, read_;
+};
 
 // Runs an entry point's body and turns a C++ exception into an error code, so
 // that nothing throws across the C ABI.  The only one the bodies can raise is

@@ -1173,6 +1173,7 @@ struct fsdp_mt_plan {
     const void** d_slice_ptrs = nullptr;  // the shards' tables of slice pointers, if any
     double* d_partials = nullptr;    // clipped steps: one sum of squares per workgroup,
                                      // then kSumBlocks second-stage sums
+    fsdp::Footprint footprint;       // the shards' buffers, for checking the calls' other buffers
 };
 
 namespace {
@@ -1186,6 +1187,20 @@ int32_t check_plan_device(const fsdp_mt_plan* plan, const char* who) {
     if (dev != plan->device)
         return fail(FSDP_E_STATE, "%s: plan made on device %d used on device %d", who, plan->device,
                     dev);
+    return FSDP_OK;
+}
+
+// A further device buffer of a plan call (`bytes` long at p) against the
+// plan's own buffers: an input may overlap only the read-only gradient
+// slices, an output none of them.
+int32_t check_extra(const fsdp_mt_plan* plan, const void* p, int64_t bytes, bool output,
+                    const char* who, const char* what) {
+    if (!p || bytes <= 0) return FSDP_OK;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    const uintptr_t hi = lo + static_cast<uintptr_t>(bytes);
+    if (output ? plan->footprint.hits_any(lo, hi) : plan->footprint.hits_written(lo, hi))
+        return fail(FSDP_E_ALIAS, "%s: %s overlaps %s buffer of the plan's shards", who, what,
+                    output ? "a" : "a written");
     return FSDP_OK;
 }
 
@@ -1385,6 +1400,8 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
         const int32_t st = fsdp::check_aliases(rs);
         if (st != FSDP_OK) return st;
     }
+    fsdp::Footprint footprint;
+    footprint.build(rs);
 
     // Every chunk but a shard's last is kChunk elements, so every chunk and
     // every tile starts group-aligned.  Workgroup b takes tile b % 8 of entry b / 8.
@@ -1429,6 +1446,7 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
     plan->any_bf16 = any_bf16;
     plan->any_grad_out = any_grad_out;
     plan->any_table = !table_host.empty();
+    plan->footprint = std::move(footprint);
     hipError_t e = hipGetDevice(&plan->device);
     if (e == hipSuccess && any_fp8 && n_tensors > 0) {
         e = hipMalloc(reinterpret_cast<void**>(&plan->d_shard_tiles), runs.size() * sizeof(ShardTiles));
@@ -1500,6 +1518,7 @@ extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumul
     if (!plan->all_grad_out)
         return fail(FSDP_E_ARG, "%s: every shard of the plan needs a grad_shard_out", who);
     int32_t st;
+    if ((st = check_extra(plan, sqnorm_out, 8, true, who, "sqnorm_out")) != FSDP_OK) return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     const bool sq = sqnorm_out != nullptr;
     if (plan->n_chunks > 0) {
@@ -1600,6 +1619,7 @@ extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hpa
     if (!aligned(grad_scale, 4)) return fail(FSDP_E_ALIGN, "%s: grad_scale misaligned", who);
     if (!plan->all_grad_out)
         return fail(FSDP_E_ARG, "%s: every shard of the plan needs a grad_shard_out", who);
+    if ((st = check_extra(plan, grad_scale, 4, false, who, "grad_scale")) != FSDP_OK) return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
@@ -1619,6 +1639,8 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
     if (!plan->any_fp8) return fail(FSDP_E_ARG, "%s: the plan has no fp8 outputs", who);
     if (!amax_out) return fail(FSDP_E_ARG, "%s: null amax_out", who);
     if (!aligned(amax_out, 4)) return fail(FSDP_E_ALIGN, "%s: amax_out misaligned", who);
+    if ((st = check_extra(plan, amax_out, 4 * plan->n_tensors, true, who, "amax_out")) != FSDP_OK)
+        return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
@@ -1654,6 +1676,10 @@ static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int
         if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
     }
     int32_t st;
+    if ((st = check_extra(plan, amax_ranks, 4 * plan->n_tensors * n_ranks, false, who,
+                          "amax_ranks")) != FSDP_OK ||
+        (st = check_extra(plan, scale_out, 4 * plan->n_tensors, true, who, "scale_out")) != FSDP_OK)
+        return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     hipLaunchKernelGGL(mt_cast_fp8_kernel,
@@ -1679,6 +1705,9 @@ static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
                                     range_of(scale_in, plan->n_tensors, 4, false, 0, "scale_in")};
         if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
     }
+    if ((st = check_extra(plan, scale_in, 4 * plan->n_tensors, false, who, "scale_in")) != FSDP_OK ||
+        (st = check_extra(plan, amax_out, 4 * plan->n_tensors, true, who, "amax_out")) != FSDP_OK)
+        return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {

@@ -9,6 +9,9 @@
 //                    view and the 9 fields of the summary, space-separated.
 //   alias SEED K     K random sets of byte ranges checked by check_aliases and
 //                    by a pairwise brute force; prints "cases mismatches".
+//   footprint SEED K K random sets of byte ranges indexed by Footprint, each
+//                    queried with random intervals against a brute force;
+//                    prints "cases queries mismatches".
 //
 // Any out-of-bounds access, signed overflow or other undefined behaviour
 // aborts the run (it is compiled with -fno-sanitize-recover=all).
@@ -106,12 +109,46 @@ int run_alias(uint64_t seed, int cases) {
     return 0;
 }
 
+int run_footprint(uint64_t seed, int cases) {
+    uint64_t s = seed;
+    long queries = 0, mismatches = 0;
+    for (int c = 0; c < cases; ++c) {
+        const int n = static_cast<int>(mix(s) % 16);
+        const uint64_t span = 16 + mix(s) % 512;
+        std::vector<fsdp::Range> rs;
+        for (int i = 0; i < n; ++i) {
+            const uintptr_t lo = 4096 + mix(s) % span;
+            const uintptr_t len = (mix(s) % 5 == 0) ? 0 : mix(s) % 64;
+            rs.push_back(fsdp::Range{lo, lo + len, mix(s) % 2 == 0, i, "r"});
+        }
+        fsdp::Footprint fp;
+        fp.build(rs);
+        for (int k = 0; k < 32; ++k) {
+            const uintptr_t lo = 4000 + mix(s) % (span + 200);
+            const uintptr_t len = (mix(s) % 6 == 0) ? 0 : 1 + mix(s) % 48;
+            const uintptr_t hi = lo + len;
+            bool want_w = false, want_any = false;
+            for (const auto& r : rs) {
+                const bool meet = r.lo < r.hi && lo < hi && r.lo < hi && lo < r.hi;
+                want_any = want_any || meet;
+                want_w = want_w || (meet && r.written);
+            }
+            ++queries;
+            if (fp.hits_written(lo, hi) != want_w || fp.hits_any(lo, hi) != want_any) ++mismatches;
+        }
+    }
+    std::printf("%d %ld %ld\n", cases, queries, mismatches);
+    return 0;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
     if (argc >= 2 && std::strcmp(argv[1], "layout") == 0) return run_layout();
     if (argc >= 4 && std::strcmp(argv[1], "alias") == 0)
         return run_alias(std::strtoull(argv[2], nullptr, 10), std::atoi(argv[3]));
-    std::fprintf(stderr, "usage: %s layout < cases | alias SEED K\n", argv[0]);
+    if (argc >= 4 && std::strcmp(argv[1], "footprint") == 0)
+        return run_footprint(std::strtoull(argv[2], nullptr, 10), std::atoi(argv[3]));
+    std::fprintf(stderr, "usage: %s layout < cases | alias SEED K | footprint SEED K\n", argv[0]);
     return 2;
 }

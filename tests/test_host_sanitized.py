@@ -8,7 +8,9 @@ to 12, empty and ragged tensors, invalid arguments), layouts at sizes where
 int64 arithmetic would wrap, and world sizes up to 2^31 - 1; every result is
 compared with the oracle's exact integers, and every refusal with the
 condition that calls for it.  The alias sweep that guards every written
-buffer is compared with a pairwise brute force on random byte ranges.
+buffer is compared with a pairwise brute force on random byte ranges, and so
+is the index of a plan's buffers that the plan calls check their further
+buffers against.
 """
 
 import os
@@ -196,3 +198,11 @@ def test_alias_sweep_matches_brute_force(exe):
     assert p.returncode == 0, p.stderr[-4000:]
     cases, mismatches = (int(x) for x in p.stdout.split())
     assert cases == 200000 and mismatches == 0
+
+
+def test_plan_footprint_matches_brute_force(exe):
+    p = subprocess.run([exe, "footprint", "777", "50000"], capture_output=True, text=True,
+                       timeout=600, env=_env())
+    assert p.returncode == 0, p.stderr[-4000:]
+    cases, queries, mismatches = (int(x) for x in p.stdout.split())
+    assert cases == 50000 and queries == 32 * 50000 and mismatches == 0
