@@ -95,6 +95,14 @@ namespace {
 #ifndef RS_FP8_HW
 #define RS_FP8_HW 1
 #endif
+// Slice counts other than 1, 2, 4 and 8 are read in batches of this many
+// bytes per lane (4 bf16 or 2 fp32 slices): a batch's loads are issued
+// together, before its first add, and a launch sizes its residency from one
+// batch.  Slice by slice, N = 16 bf16 slices ran at 2.5 TB/s; in these
+// batches, at 6.1-6.4.
+#ifndef RS_RT_BATCH_BYTES
+#define RS_RT_BATCH_BYTES 32
+#endif
 // A launch whose share of that budget would allow this many resident
 // workgroups per CU or more is left uncapped (light kernels want every wave).
 #ifndef RS_OCC_UNCAPPED
@@ -377,16 +385,39 @@ __device__ __forceinline__ void reduce_regs(const SliceRegs<NS, BF16>& r, float 
     for (int j = 0; j < kGroup; ++j) g[j] = finish_mean(g[j], c);
 }
 
-// Runtime slice count: load and accumulate slice by slice.
+// Slices per batch of the runtime slice-count loop.
+template <bool BF16>
+constexpr int rt_batch() {
+    return std::max<int>(1, RS_RT_BATCH_BYTES / static_cast<int>(sizeof(SliceVec<BF16>)));
+}
+
+// Runtime slice count: the slices in batches of rt_batch().  Every load of a
+// batch is issued before the batch's first add, and the adds run in slice
+// order, so the sum is the one taken slice by slice.  The batch bounds are
+// uniform, so the tests on them are scalar branches.
 template <bool BF16, bool TABLE>
 __device__ __forceinline__ void reduce_runtime(const TensorDesc& T, int64_t e, float g[kGroup],
                                                const StepConsts& c) {
-    widen<BF16>(load_group<BF16>(slice_base<BF16, TABLE>(T, 0), e), g);
-    for (int q = 1; q < c.n; ++q) {
-        float x[kGroup];
-        widen<BF16>(load_group<BF16>(slice_base<BF16, TABLE>(T, q), e), x);
+    constexpr int KB = rt_batch<BF16>();
+    for (int q0 = 0; q0 < c.n; q0 += KB) {
+        SliceVec<BF16> w[KB];
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) g[j] = g[j] + x[j];
+        for (int j = 0; j < KB; ++j)
+            if (q0 + j < c.n) w[j] = load_group<BF16>(slice_base<BF16, TABLE>(T, q0 + j), e);
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            if (q0 + j < c.n) {
+                float x[kGroup];
+                widen<BF16>(w[j], x);
+                if (j == 0 && q0 == 0) {
+#pragma unroll
+                    for (int k = 0; k < kGroup; ++k) g[k] = x[k];
+                } else {
+#pragma unroll
+                    for (int k = 0; k < kGroup; ++k) g[k] = g[k] + x[k];
+                }
+            }
+        }
     }
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) g[j] = finish_mean(g[j], c);
@@ -1064,6 +1095,14 @@ bool vec_ok(const TensorDesc& T, int32_t slice_dtype, int32_t n_slices) {
 
 int64_t tiles_for(int64_t S) { return (S + kTile - 1) / kTile; }
 
+// Slices whose loads a tile has in flight together: all N when N is compiled
+// in (1, 2, 4, 8), one batch of the runtime loop otherwise.
+int64_t inflight_slices(int32_t n, int32_t slice_dtype) {
+    const bool compiled = n == 1 || n == 2 || n == 4 || n == 8;
+    const int64_t batch = std::max<int64_t>(1, RS_RT_BATCH_BYTES / (kGroup * dtype_bytes(slice_dtype)));
+    return compiled ? n : std::min<int64_t>(n, batch);
+}
+
 // One launch covers at most 2^32 - 1 work-items in a grid dimension.
 constexpr int64_t kMaxBlocks = 0xffffffffLL / kBlock;
 
@@ -1204,9 +1243,11 @@ int32_t check_extra(const fsdp_mt_plan* plan, const void* p, int64_t bytes, bool
     return FSDP_OK;
 }
 
-// Bytes per element of the plan's slices, and of its fused step.
+// Bytes per element of the plan's slices that a tile has in flight at once
+// (all N for the slice counts compiled in, one batch for the others), and
+// of its fused step.
 int64_t slice_bytes(const fsdp_mt_plan* plan) {
-    return dtype_bytes(plan->slice_dtype) * plan->n_slices;
+    return dtype_bytes(plan->slice_dtype) * inflight_slices(plan->n_slices, plan->slice_dtype);
 }
 int64_t step_bytes(const fsdp_mt_plan* plan) {
     return slice_bytes(plan) + 24 + 2 * plan->any_bf16 + 4 * plan->any_grad_out;
@@ -1244,7 +1285,8 @@ static int32_t reduce_grad_shard_impl(float* grad_shard_out, const void* grad_sl
     const ReduceKernel k = slice_dtype == FSDP_DT_BF16 ? pick_reduce<true>(n_slices)
                                                        : pick_reduce<false>(n_slices);
     hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(tiles_for(shard_numel))), dim3(kBlock),
-                       lds_reserve(dtype_bytes(slice_dtype) * n_slices + 4), stream, T, c);
+                       lds_reserve(dtype_bytes(slice_dtype) * inflight_slices(n_slices, slice_dtype) + 4),
+                       stream, T, c);
     return launch_status(who);
 }
 

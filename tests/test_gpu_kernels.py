@@ -134,7 +134,9 @@ SPECS = [  # (S, valid, offset, stride_extra)
 
 
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 8, 16, 33])
+# N outside 1, 2, 4, 8 reads its slices in batches (4 bf16 or 2 fp32 slices
+# each): 5, 6, 7 and 33 end on every partial batch, 16 on whole ones.
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8, 16, 33])
 def test_mt_step_parity(gpu, N, sdt):
     shards = [Shard(S, va, N, sdt, gpu, seed=100 * N + i, offset=o, stride_extra=x,
                     bf16=(i % 3 != 1), gout=(i % 2 == 0))
@@ -158,7 +160,7 @@ def test_mt_step_parity(gpu, N, sdt):
 
 
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 3, 4, 8, 33])
+@pytest.mark.parametrize("N", [1, 3, 4, 6, 8, 33])
 def test_single_calls_parity(gpu, N, sdt):
     for i, (S, va, o, x) in enumerate(SPECS):
         s = Shard(S, va, N, sdt, gpu, seed=1000 + i, offset=o, stride_extra=x)
@@ -170,7 +172,7 @@ def test_single_calls_parity(gpu, N, sdt):
         s.check(f"single N={N} {sdt} case {i}", snap, 1)
 
 
-@pytest.mark.parametrize("sdt,N", [("bf16", 8), ("f32", 4), ("f32", 3), ("bf16", 1)])
+@pytest.mark.parametrize("sdt,N", [("bf16", 8), ("f32", 4), ("f32", 3), ("bf16", 1), ("bf16", 7)])
 def test_fused_equals_chain_bitwise(gpu, sdt, N):
     a = [Shard(S, va, N, sdt, gpu, seed=5000 + i, offset=o, stride_extra=x)
          for i, (S, va, o, x) in enumerate(SPECS)]
