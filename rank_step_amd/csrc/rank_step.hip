@@ -1166,6 +1166,37 @@ bool slice_table_vec_ok(const void* const* ptrs, int32_t slice_dtype, int32_t n_
     return true;
 }
 
+// How many elements past a vector boundary every buffer of shard d starts
+// (0-3), or -1 when its buffers disagree (then no split aligns them all).
+// The slices count only when the shard has data to read.
+int element_phase(const TensorDesc& d, int32_t slice_dtype, int32_t n_slices,
+                  const void* const* table) {
+    int phase = -1;
+    bool agree = true;
+    const auto take = [&](const void* p, int64_t esize) {
+        if (!p) return;
+        const int ph = static_cast<int>((reinterpret_cast<uintptr_t>(p) / esize) & 3);
+        if (phase < 0) phase = ph;
+        else if (ph != phase) agree = false;
+    };
+    take(d.param, 4);
+    take(d.m, 4);
+    take(d.v, 4);
+    take(d.grad_out, 4);
+    take(d.out_bf16, 2);
+    take(d.out_fp8, 1);
+    if (d.valid > 0) {
+        const int64_t es = dtype_bytes(slice_dtype);
+        if (table) {
+            for (int32_t q = 0; q < n_slices; ++q) take(table[q], es);
+        } else {
+            take(d.slices, es);
+            if (n_slices > 1 && (d.slice_stride & 3) != 0) agree = false;
+        }
+    }
+    return agree ? phase : -1;
+}
+
 int32_t check_sizes(int64_t S, int64_t valid, const char* who) {
     if (S < 0 || valid < 0 || valid > S)
         return fail(FSDP_E_ARG, "%s: need 0 <= valid (%lld) <= shard_numel (%lld)", who,
@@ -1436,8 +1467,48 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
         d.valid = t.valid;
         d.vec_ok = vec_ok(d, slice_dtype, n_slices) &&
                    (!table || slice_table_vec_ok(t.grad_slice_ptrs, slice_dtype, n_slices));
-        descs.push_back(d);
+        // A shard whose buffers all start the same 1-3 elements before a
+        // vector boundary (shards packed back to back after one whose size is
+        // not a multiple of 4) is split in two under its index: a head of
+        // those elements, which takes the element path, and the aligned rest,
+        // which streams in vectors.  Their chunk entries are adjacent, so the
+        // shard's workgroups stay one run.
+        const int phase = d.vec_ok ? 0 : element_phase(d, slice_dtype, n_slices,
+                                                        table ? t.grad_slice_ptrs : nullptr);
+        const int64_t head = phase > 0 ? 4 - phase : 0;
+        if (head > 0 && d.valid >= head + kGroup) {
+            const int64_t es = dtype_bytes(slice_dtype);
+            TensorDesc b = d;
+            b.param += head;
+            b.m += head;
+            b.v += head;
+            if (b.grad_out) b.grad_out += head;
+            if (b.out_bf16) b.out_bf16 += head;
+            if (b.out_fp8) b.out_fp8 += head;
+            if (b.slices) b.slices = static_cast<const char*>(b.slices) + head * es;
+            b.shard_numel -= head;
+            b.valid -= head;
+            d.shard_numel = head;
+            d.valid = head;
+            d.vec_ok = 0;
+            if (table) {
+                table_off.push_back(static_cast<int64_t>(table_host.size()));
+                for (int32_t q = 0; q < n_slices; ++q)
+                    table_host.push_back(static_cast<const char*>(t.grad_slice_ptrs[q]) + head * es);
+                b.vec_ok = vec_ok(b, slice_dtype, n_slices) &&
+                           slice_table_vec_ok(table_host.data() + table_off.back(), slice_dtype, n_slices);
+            } else {
+                table_off.push_back(-1);
+                b.vec_ok = vec_ok(b, slice_dtype, n_slices);
+            }
+            descs.push_back(d);
+            descs.push_back(b);
+        } else {
+            descs.push_back(d);
+        }
     }
+    if (descs.size() > static_cast<size_t>(INT32_MAX))
+        return fail(FSDP_E_CAPACITY, "%s: too many shards", who);
     {
         const int32_t st = fsdp::check_aliases(rs);
         if (st != FSDP_OK) return st;
@@ -1460,9 +1531,10 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
     chunks.reserve(static_cast<size_t>(n_chunks));
     std::vector<ShardTiles> runs(static_cast<size_t>(n_tensors), ShardTiles{0, 0});
     for (size_t i = 0; i < descs.size(); ++i) {
-        runs[static_cast<size_t>(descs[i].index)].first = static_cast<int64_t>(chunks.size()) * kTilesPerChunk;
-        runs[static_cast<size_t>(descs[i].index)].count =
-            (descs[i].shard_numel + chunk - 1) / chunk * kTilesPerChunk;
+        // a split shard's two parts are adjacent: one run of workgroups
+        ShardTiles& run = runs[static_cast<size_t>(descs[i].index)];
+        if (run.count == 0) run.first = static_cast<int64_t>(chunks.size()) * kTilesPerChunk;
+        run.count += (descs[i].shard_numel + chunk - 1) / chunk * kTilesPerChunk;
         for (int64_t b = 0; b < descs[i].shard_numel; b += chunk) {
             ChunkDesc cd{};
             cd.begin = b;

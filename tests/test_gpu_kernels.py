@@ -4,8 +4,9 @@ Every call goes through the C ABI (rank_step_amd.binding).  Sizes span
 several 2048-element chunk entries (eight 256-element workgroup tiles each)
 and a ragged tail; the cases cover empty
 shards, all-padding shards (valid = 0), partial groups, misaligned buffers
-(element-by-element path), slice strides wider than the shard, N that is not
-a power of two, NaN/Inf inputs, guard words around every buffer, and the
+(element-by-element path, or a split into a short head and an aligned body
+when every buffer is misaligned alike), slice strides wider than the shard,
+N that is not a power of two, NaN/Inf inputs, guard words around every buffer, and the
 bit-identity of the fused multi-tensor step with the chain of three calls.
 """
 
@@ -130,6 +131,12 @@ SPECS = [  # (S, valid, offset, stride_extra)
     (2048 + 256, 2048 + 252, 4, 0),                # bf16 buffers 8- but not 16-byte aligned: vector path
     (4096 + 1000, 4096 + 1000, 4, 4),              # the same with a wider stride that keeps slices aligned
     (4095, 4095, 0, 2),                            # stride that misaligns slice q > 0
+    (5013, 5009, 1, 3),                            # every buffer 1 element past a vector boundary:
+                                                   # split into a head of 3 and an aligned body
+    (4099, 4099, 2, 1),                            # the same 2 elements past: head of 2
+    (3001, 2990, 3, 3),                            # 3 past: head of 1
+    (12, 7, 1, 0),                                 # just long enough to split (head + one group)
+    (10, 6, 1, 2),                                 # one element too short: element path
 ]
 
 
@@ -380,3 +387,30 @@ def test_fp32_replica_bit_exact(gpu, sdt, N):
                 assert not bad.any(), (f"N={N} {sdt} shard {i} t={t} {nm}: {bad.sum()} differ, "
                                        f"first {np.flatnonzero(bad)[:3]} got {g[bad][:3]} want {want[bad][:3]}")
     plan.close()
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("off,head", [(1, 3), (2, 2), (3, 1)])
+def test_misaligned_shard_split_equals_element_path(gpu, sdt, off, head):
+    """A shard whose buffers all start `off` elements past a vector boundary is
+    split into a head of 4 - off elements and an aligned body (one more chunk
+    entry); the same data with one slice stride out of phase cannot be split
+    and runs element by element.  Both give identical bits."""
+    N, S, va = 3, 5013, 5009
+    a = Shard(S, va, N, sdt, gpu, seed=8100 + off, offset=off, stride_extra=3)   # stride % 4 == 0
+    b = Shard(S, va, N, sdt, gpu, seed=8100 + off, offset=off, stride_extra=1)   # stride % 4 == 2
+    pa, pb = B.MtPlan([a.mt()], N, sdt), B.MtPlan([b.mt()], N, sdt)
+    assert pa.info()["n_chunks"] == 1 + -(-(S - head) // 2048)
+    assert pb.info()["n_chunks"] == -(-S // 2048)
+    for t in (1, 2):
+        snap = a.snapshot()
+        pa.step(HP, t)
+        pb.step(HP, t)
+        torch.cuda.synchronize()
+        a.check(f"split off={off} {sdt} t={t}", snap, t)
+        for nm in ("p", "m", "v", "gout"):
+            x, y = getattr(a, nm).t, getattr(b, nm).t
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (nm, t)
+        assert torch.equal(a.out.t.view(torch.int16), b.out.t.view(torch.int16)), t
+    pa.close()
+    pb.close()

@@ -4,8 +4,11 @@ padding, and the per-shard amax of the fp8 path (one workgroup per shard).
 
 Every shard is carved out of a few large buffers, a random gap after its
 neighbour, so shards start at arbitrary element offsets: about a quarter of
-them are aligned for the vector path, the rest take the element path.  The
-gaps hold guard values that must survive.  The oracle runs once over all
+them are aligned for the vector path.  In the rest every buffer starts the
+same 1-3 elements past a vector boundary (the slice stride is a multiple of
+4), so the plan splits each into a short element-path head and an aligned
+body under one index; their amax must still be the shard's.  The gaps hold
+guard values that must survive.  The oracle runs once over all
 valid elements, since every shard shares the step's hyperparameters, and
 each shard's padding must come out +0.
 """
@@ -34,6 +37,7 @@ def _layout(rng):
     gaps = rng.choice([4, 5, 6, 7, 8], N_SHARDS)
     offs = np.concatenate([[0], np.cumsum(sizes + gaps)[:-1]]) + 8
     total = int(offs[-1] + sizes[-1] + 64)
+    total += (-total) % 4              # slices of one shard share their phase
     return sizes, valid, offs, total
 
 
@@ -79,6 +83,12 @@ def test_twenty_thousand_shards(gpu):
     plan = B.MtPlan(recs, N, SDT)
     info = plan.info()
     assert info["n_tensors"] == N_SHARDS and info["total_numel"] == int(sizes.sum())
+    # a shard 1-3 elements past a boundary splits when its body keeps a group
+    head = (4 - offs % 4) % 4
+    split = (head > 0) & (valid >= head + 4)
+    entries = np.where(split, 1 + -(-(sizes - head) // 2048), -(-sizes // 2048))
+    assert info["n_chunks"] == int(entries.sum()), (info["n_chunks"], int(entries.sum()))
+    print(f"{int(split.sum())} shards split into head and body", flush=True)
 
     p0, m0, v0 = PR.f64(p[mk]), PR.f64(m[mk]), PR.f64(v[mk])
     x = PR.widen_slices(sl[:, mk], SDT)

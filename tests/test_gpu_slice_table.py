@@ -20,13 +20,17 @@ from tests.test_gpu_kernels import SPECS, Buf, Shard
 pytestmark = pytest.mark.gpu
 
 
-def _tabled(s, gpu, misalign):
-    """Copies of shard s's slices, one buffer each, and its plan record."""
+def _tabled(s, gpu, misalign, offset=None):
+    """Copies of shard s's slices, one buffer each, and its plan record.
+    ``offset``: every buffer that many elements past its allocation's start."""
     N, S = s.N, s.S
     dt = s.sl.t.dtype
     bufs = []
     for q in range(N):
-        off = (q * 3 + 1) % 5 if misalign else 4 * (q % 2)
+        if offset is not None:
+            off = offset
+        else:
+            off = (q * 3 + 1) % 5 if misalign else 4 * (q % 2)
         b = Buf(S, dt, s.p.t.device, fill=float("nan"), offset=off)
         b.t.copy_(s.sl.t.view(N, s.stride)[q, :S])
         b.seal()
@@ -117,5 +121,43 @@ def test_table_fp8_step_and_oracle(gpu):
         assert torch.equal(fa, fb)
     for i, (s, snap) in enumerate(zip(b, snaps)):
         s.check(f"table shard {i}", snap, 1, check_g=False)
+    plan_a.close()
+    plan_b.close()
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_table_shard_split_when_misaligned_alike(gpu, sdt):
+    """Shards whose buffers, slice buffers included, all start 1-3 elements
+    past a vector boundary are split into a short head and an aligned body
+    in the table form too (the plan's copy of the table is shifted for the
+    body): bit-identical to the same shards with their slices at a stride."""
+    N = 5
+    specs = [(5013, 5009, 1), (4099, 4099, 2), (3001, 2990, 3), (700, 700, 1)]
+    mk = lambda: [Shard(S, va, N, sdt, gpu, seed=9700 + i, offset=o, stride_extra=(-S) % 4)
+                  for i, (S, va, o) in enumerate(specs)]
+    a, b = mk(), mk()
+    tables, recs = [], []
+    for (S, va, o), s in zip(specs, b):
+        bufs, rec = _tabled(s, gpu, misalign=False, offset=o)
+        tables.append(bufs)
+        recs.append(rec)
+    plan_a = B.MtPlan([s.mt() for s in a], N, sdt)
+    plan_b = B.MtPlan(recs, N, sdt)
+    del recs
+    split_chunks = sum(1 + -(-(S - (4 - o)) // 2048) for S, va, o in specs)
+    assert plan_a.info()["n_chunks"] == split_chunks
+    assert plan_b.info()["n_chunks"] == split_chunks
+    for t in (1, 2):
+        snaps = [s.snapshot() for s in b]
+        plan_a.step(HPARAMS, t)
+        plan_b.step(HPARAMS, t)
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(_outputs(a), _outputs(b))):
+            assert torch.equal(x, y), f"{sdt} t={t}: output {i} differs between the two forms"
+        for i, (s, snap) in enumerate(zip(b, snaps)):
+            s.check(f"split table shard {i} t={t}", snap, t)
+    for bufs in tables:
+        for buf in bufs:
+            buf.check_guards("slice buffer")
     plan_a.close()
     plan_b.close()
