@@ -414,3 +414,38 @@ def test_misaligned_shard_split_equals_element_path(gpu, sdt, off, head):
         assert torch.equal(a.out.t.view(torch.int16), b.out.t.view(torch.int16)), t
     pa.close()
     pb.close()
+
+
+# the largest slice count the ABI accepts, and one short of it (a partial
+# last batch), on small ragged shards
+MAX_N_SPECS = [(2048 + 300, 2048 + 297, 0, 0), (1001, 1001, 0, 3), (255, 250, 4, 1), (37, 37, 1, 3)]
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1023, 1024])
+def test_max_slice_count(gpu, N, sdt):
+    shards = [Shard(S, va, N, sdt, gpu, seed=7700 + i, offset=o, stride_extra=x)
+              for i, (S, va, o, x) in enumerate(MAX_N_SPECS)]
+    plan = B.MtPlan([s.mt() for s in shards], N, sdt)
+    snaps = [s.snapshot() for s in shards]
+    plan.step(HP, 1)
+    torch.cuda.synchronize()
+    for i, (s, snap) in enumerate(zip(shards, snaps)):
+        s.check(f"N={N} {sdt} shard {i}", snap, 1)
+        p0, m0, v0, x = snap
+        rp, rm, rv = PR.fp32_replica_step(p0, m0, v0, x, s.valid, 1, HP)
+        for nm, got, want in (("p", s.p.t, rp), ("m", s.m.t, rm), ("v", s.v.t, rv)):
+            assert np.array_equal(got.cpu().numpy()[:s.valid].view(np.uint32), want.view(np.uint32)), \
+                f"N={N} {sdt} shard {i} {nm}: differs from the fp32 replica"
+    plan.close()
+    # the single-shard reduce of the same slices, bit for bit against their fp32 sum
+    s = shards[0]
+    B.fsdp_reduce_grad_shard(s.gout.t, s.sl.t, sdt, s.stride, N, s.S, s.valid)
+    torch.cuda.synchronize()
+    x = snaps[0][3]
+    want = x[:, :s.valid].astype(np.float32)
+    acc = want[0].copy()
+    for q in range(1, N):
+        acc = (acc + want[q]).astype(np.float32)
+    acc = acc * np.float32(1.0 / N) if N & (N - 1) == 0 else acc / np.float32(N)
+    assert np.array_equal(s.gout.t.cpu().numpy()[:s.valid].view(np.uint32), acc.astype(np.float32).view(np.uint32))
