@@ -253,6 +253,14 @@ int32_t fsdp_cast_unshard_bf16(uint16_t* unshard_bf16_out, const float* param_fp
  *                                    NULL only when valid is 0, must be aligned
  *                                    to the element size, and are read in
  *                                    [0, valid) only. */
+/* Speed, not correctness: a shard streams in 16-byte vectors when
+ * param_fp32, exp_avg, exp_avg_sq and grad_shard_out start at the same
+ * element phase (address / 4 mod 4): all 16-byte aligned, or all 1-3
+ * elements past, when the plan splits off a head of the 1-3 elements before
+ * the boundary.  The slices and the bf16 and fp8 copies may start at any
+ * element (e.g. slot rank*S of a packed buffer with S not a multiple of 4).
+ * A shard whose fp32 buffers disagree runs element by element.  Results are
+ * bit-identical either way. */
 typedef struct {
     float* param_fp32;
     float* exp_avg;

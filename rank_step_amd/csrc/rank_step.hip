@@ -160,8 +160,9 @@ struct TensorDesc {
     int64_t slice_stride;
     int64_t shard_numel;
     int64_t valid;
-    int64_t vec_ok;      // every buffer aligned for the vector path
+    int64_t vec_ok;      // the buffers the vector path needs aligned are aligned
     int64_t index;       // position of the shard in the plan's input list
+    int64_t gen;         // some slice or low-precision copy is not vector-aligned
 };
 
 // One entry of the chunk-descriptor table: elements [begin, begin+count) of a shard.
@@ -324,6 +325,52 @@ __device__ __forceinline__ SliceVec<BF16> load_group(const void* base, int64_t i
     else return ld_slice(reinterpret_cast<const V*>(static_cast<const float*>(base) + i));
 }
 
+// The group starting `sh` bytes into A (0 < sh < sizeof A, a multiple of
+// the element size), given A and the vector B that follows it.
+template <bool BF16>
+__device__ __forceinline__ SliceVec<BF16> join_shifted(const SliceVec<BF16>& A, const SliceVec<BF16>& B,
+                                                       uint32_t sh) {
+    if constexpr (BF16) {
+        // sh = 2, 4 or 6: dword offset w, byte offset b within it
+        const bool w = sh >= 4;
+        const uint32_t b = sh & 3u;
+        const uint32_t x0 = w ? A[1] : A[0];
+        const uint32_t x1 = w ? B[0] : A[1];
+        const uint32_t x2 = w ? B[1] : B[0];
+        return u32x2{__builtin_amdgcn_alignbyte(x1, x0, b), __builtin_amdgcn_alignbyte(x2, x1, b)};
+    } else {
+        // sh = 4, 8 or 12: whole dwords
+        const bool d1 = sh == 4, d2 = sh == 8;
+        return u32x4{d1 ? A[1] : (d2 ? A[2] : A[3]), d1 ? A[2] : (d2 ? A[3] : B[0]),
+                     d1 ? A[3] : (d2 ? B[0] : B[1]), d1 ? B[0] : (d2 ? B[1] : B[2])};
+    }
+}
+
+// Group i of a slice that starts at any element alignment.  Every group of
+// the slice starts `sh` bytes past a vector boundary, sh taken from the
+// slice's base (uniform, so the test is a scalar branch).  sh == 0: one
+// vector load.  Otherwise the two aligned vectors that hold the group,
+// joined: each holds bytes of the group, so neither reaches past the page
+// (or the allocation) the group lies in.
+template <bool BF16>
+__device__ __forceinline__ SliceVec<BF16> load_group_any(const void* base, int64_t i) {
+    using V = SliceVec<BF16>;
+    constexpr uintptr_t W = sizeof(V);
+    const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base) & (W - 1));
+    const uintptr_t a = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(i) * (W / kGroup);
+    if (sh == 0) return ld_slice(reinterpret_cast<const V*>(a));
+    const V A = ld_slice(reinterpret_cast<const V*>(a - sh));
+    const V B = ld_slice(reinterpret_cast<const V*>(a - sh + W));
+    return join_shifted<BF16>(A, B, sh);
+}
+
+// GEN: the slice may start at any element alignment.
+template <bool BF16, bool GEN>
+__device__ __forceinline__ SliceVec<BF16> load_slice_group(const void* base, int64_t i) {
+    if constexpr (GEN) return load_group_any<BF16>(base, i);
+    else return load_group<BF16>(base, i);
+}
+
 template <bool BF16>
 __device__ __forceinline__ void widen(const SliceVec<BF16>& w, float x[kGroup]) {
     if constexpr (BF16) {
@@ -362,12 +409,12 @@ __device__ __forceinline__ const void* slice_base(const TensorDesc& T, int q) {
     }
 }
 
-template <int NS, bool BF16, bool TABLE>
+template <int NS, bool BF16, bool TABLE, bool GEN = false>
 __device__ __forceinline__ void load_slices(SliceRegs<NS, BF16>& r, const TensorDesc& T,
                                             int64_t e) {
     static_assert(NS > 0, "compile-time slice count");
 #pragma unroll
-    for (int q = 0; q < NS; ++q) r.w[q] = load_group<BF16>(slice_base<BF16, TABLE>(T, q), e);
+    for (int q = 0; q < NS; ++q) r.w[q] = load_slice_group<BF16, GEN>(slice_base<BF16, TABLE>(T, q), e);
 }
 
 template <int NS, bool BF16>
@@ -395,7 +442,7 @@ constexpr int rt_batch() {
 // batch is issued before the batch's first add, and the adds run in slice
 // order, so the sum is the one taken slice by slice.  The batch bounds are
 // uniform, so the tests on them are scalar branches.
-template <bool BF16, bool TABLE>
+template <bool BF16, bool TABLE, bool GEN = false>
 __device__ __forceinline__ void reduce_runtime(const TensorDesc& T, int64_t e, float g[kGroup],
                                                const StepConsts& c) {
     constexpr int KB = rt_batch<BF16>();
@@ -403,7 +450,7 @@ __device__ __forceinline__ void reduce_runtime(const TensorDesc& T, int64_t e, f
         SliceVec<BF16> w[KB];
 #pragma unroll
         for (int j = 0; j < KB; ++j)
-            if (q0 + j < c.n) w[j] = load_group<BF16>(slice_base<BF16, TABLE>(T, q0 + j), e);
+            if (q0 + j < c.n) w[j] = load_slice_group<BF16, GEN>(slice_base<BF16, TABLE>(T, q0 + j), e);
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
             if (q0 + j < c.n) {
@@ -424,15 +471,15 @@ __device__ __forceinline__ void reduce_runtime(const TensorDesc& T, int64_t e, f
 }
 
 // The mean of the slices on the group at e, N known at compile time or not.
-template <int NS, bool BF16, bool TABLE = false>
+template <int NS, bool BF16, bool TABLE = false, bool GEN = false>
 __device__ __forceinline__ void reduce_group(const TensorDesc& T, int64_t e, float g[kGroup],
                                              const StepConsts& c) {
     if constexpr (NS > 0) {
         SliceRegs<NS, BF16> sr;
-        load_slices<NS, BF16, TABLE>(sr, T, e);
+        load_slices<NS, BF16, TABLE, GEN>(sr, T, e);
         reduce_regs<NS, BF16>(sr, g, c);
     } else {
-        reduce_runtime<BF16, TABLE>(T, e, g, c);
+        reduce_runtime<BF16, TABLE, GEN>(T, e, g, c);
     }
 }
 
@@ -450,12 +497,48 @@ __device__ __forceinline__ u32x2 pack_bf16(const f32x4& p) {
     return u32x2{bf16_rne(p[0]) | (bf16_rne(p[1]) << 16), bf16_rne(p[2]) | (bf16_rne(p[3]) << 16)};
 }
 
+// The 4 bf16 of a group (w, element j in half j) at p, which lies `sh` bytes
+// past an 8-byte boundary (sh uniform, from the copy's base).  Unaligned:
+// 4-byte pieces where the address allows, 2-byte ones at the ends.
+__device__ __forceinline__ void store_bf16_any(uint16_t* p, const u32x2& w, uint32_t sh) {
+    if (sh == 0) {
+        st_out(reinterpret_cast<u32x2*>(p), w);
+    } else if (sh == 4) {
+        st_out(reinterpret_cast<uint32_t*>(p), w[0]);
+        st_out(reinterpret_cast<uint32_t*>(p + 2), w[1]);
+    } else {
+        st_out(p, static_cast<uint16_t>(w[0]));
+        st_out(reinterpret_cast<uint32_t*>(p + 1), (w[0] >> 16) | (w[1] << 16));
+        st_out(p + 3, static_cast<uint16_t>(w[1] >> 16));
+    }
+}
+
+// The 4 fp8 codes of a group (byte j of w) at p, `sh` bytes past a 4-byte
+// boundary (uniform).
+__device__ __forceinline__ void store_fp8_any(uint8_t* p, uint32_t w, uint32_t sh) {
+    if (sh == 0) {
+        st_out(reinterpret_cast<uint32_t*>(p), w);
+    } else if (sh == 2) {
+        st_out(reinterpret_cast<uint16_t*>(p), static_cast<uint16_t>(w));
+        st_out(reinterpret_cast<uint16_t*>(p + 2), static_cast<uint16_t>(w >> 16));
+    } else {
+        st_out(p, static_cast<uint8_t>(w));
+        st_out(reinterpret_cast<uint16_t*>(p + 1), static_cast<uint16_t>(w >> 8));
+        st_out(p + 3, static_cast<uint8_t>(w >> 24));
+    }
+}
+
+__device__ __forceinline__ uint32_t misalign(const void* p, uintptr_t w) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & (w - 1));
+}
+
 // AdamW on a group and the stores of its results.  WRITE_G: also store the
 // reduced gradient when the shard has a grad_shard_out.
 // AMAX: also fold |p'| of the group into *amax (fp32 bit patterns of
 // non-negative values order like the values; NaN patterns sort above all).
 // FP8: also store the fp8 codes of p' with the given per-tensor scale.
-template <bool WRITE_G = true, bool AMAX = false, bool FP8 = false>
+// GEN: the low-precision copies may start at any element alignment.
+template <bool WRITE_G = true, bool AMAX = false, bool FP8 = false, bool GEN = false>
 __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup],
                                              const TensorDesc& T, int64_t e, const StepConsts& c,
                                              uint32_t* amax = nullptr, float fp8_scale = 0.0f) {
@@ -471,9 +554,15 @@ __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup]
     st_state(reinterpret_cast<f32x4*>(T.param + e), s.p);
     st_state(reinterpret_cast<f32x4*>(T.m + e), s.m);
     st_state(reinterpret_cast<f32x4*>(T.v + e), s.v);
-    if (T.out_bf16) st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(s.p));
+    if (T.out_bf16) {
+        if constexpr (GEN) store_bf16_any(T.out_bf16 + e, pack_bf16(s.p), misalign(T.out_bf16, 8));
+        else st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(s.p));
+    }
     if constexpr (FP8) {
-        if (T.out_fp8) st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), pack_fp8(s.p, fp8_scale));
+        if (T.out_fp8) {
+            if constexpr (GEN) store_fp8_any(T.out_fp8 + e, pack_fp8(s.p, fp8_scale), misalign(T.out_fp8, 4));
+            else st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), pack_fp8(s.p, fp8_scale));
+        }
     }
     if (WRITE_G && T.grad_out)
         st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
@@ -554,8 +643,10 @@ __device__ __forceinline__ int64_t vector_end(const TensorDesc& T, int64_t begin
 }
 
 // The fused step on elements [begin, end) of shard T; `begin` is a multiple of
-// kGroup.  AMAX and FP8 as in update_store; TABLE as in slice_base.
-template <int NS, bool BF16, bool AMAX = false, bool FP8 = false, bool TABLE = false>
+// kGroup.  AMAX, FP8 and GEN as in update_store; TABLE as in slice_base;
+// GEN also lets the slices start at any element alignment.
+template <int NS, bool BF16, bool AMAX = false, bool FP8 = false, bool TABLE = false,
+          bool GEN = false>
 __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, int64_t end,
                                             const StepConsts& c, uint32_t* amax = nullptr,
                                             float fp8_scale = 0.0f) {
@@ -565,16 +656,16 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
         if constexpr (NS > 0) {
             // every load of the group before the first arithmetic
             SliceRegs<NS, BF16> sr;
-            load_slices<NS, BF16, TABLE>(sr, T, e);
+            load_slices<NS, BF16, TABLE, GEN>(sr, T, e);
             load_state(s, T, e);
             float g[kGroup];
             reduce_regs<NS, BF16>(sr, g, c);
-            update_store<true, AMAX, FP8>(s, g, T, e, c, amax, fp8_scale);
+            update_store<true, AMAX, FP8, GEN>(s, g, T, e, c, amax, fp8_scale);
         } else {
             load_state(s, T, e);
             float g[kGroup];
-            reduce_runtime<BF16, TABLE>(T, e, g, c);
-            update_store<true, AMAX, FP8>(s, g, T, e, c, amax, fp8_scale);
+            reduce_runtime<BF16, TABLE, GEN>(T, e, g, c);
+            update_store<true, AMAX, FP8, GEN>(s, g, T, e, c, amax, fp8_scale);
         }
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
@@ -600,7 +691,7 @@ __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin,
 // accumulation over micro-batches), else it replaces it.  SQ: return this
 // lane's sum of the squares of the stored values, in fp64 (each fp32
 // square is exact in fp64).  The padding is +0 either way.
-template <int NS, bool BF16, bool SQ, bool TABLE = false>
+template <int NS, bool BF16, bool SQ, bool TABLE = false, bool GEN = false>
 __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_t begin,
                                                      int64_t end, const StepConsts& c, bool acc) {
     double sq = 0.0;
@@ -610,7 +701,7 @@ __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_
         f32x4 old = {0.f, 0.f, 0.f, 0.f};
         if (acc) old = ld_state(go);
         float g[kGroup];
-        reduce_group<NS, BF16, TABLE>(T, e, g, c);
+        reduce_group<NS, BF16, TABLE, GEN>(T, e, g, c);
         if (acc) {
 #pragma unroll
             for (int j = 0; j < kGroup; ++j) g[j] = old[j] + g[j];
@@ -657,6 +748,7 @@ __device__ __forceinline__ void accumulate_range(float* a, const void* x, int64_
 }
 
 // AdamW + cast on [begin, end) from the stored reduced gradient times `scale`.
+template <bool GEN = false>
 __device__ __forceinline__ void scaled_range(const TensorDesc& T, int64_t begin, int64_t end,
                                              float scale, const StepConsts& c) {
     const int64_t vend = vector_end(T, begin, end);
@@ -667,14 +759,14 @@ __device__ __forceinline__ void scaled_range(const TensorDesc& T, int64_t begin,
         float g[kGroup];
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) g[j] = gv[j] * scale;
-        update_store<false>(s, g, T, e, c);
+        update_store<false, false, false, GEN>(s, g, T, e, c);
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) scaled_elem(T, k, scale, c);
 }
 
 // fp8 copy of the updated shard on [begin, end), at most TILES tiles; codes 0
 // in the pad.  Each lane loads all of its groups before converting any.
-template <int TILES>
+template <int TILES, bool GEN = false>
 __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, int64_t end,
                                           float scale) {
     const int64_t vend = vector_end(T, begin, end);
@@ -687,7 +779,10 @@ __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, in
 #pragma unroll
     for (int u = 0; u < TILES; ++u) {
         const int64_t e = begin + (u * kBlock + threadIdx.x) * kGroup;
-        if (e < vend) st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), pack_fp8(a[u], scale));
+        if (e < vend) {
+            if constexpr (GEN) store_fp8_any(T.out_fp8 + e, pack_fp8(a[u], scale), misalign(T.out_fp8, 4));
+            else st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), pack_fp8(a[u], scale));
+        }
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.out_fp8 + k, k < T.valid ? static_cast<uint8_t>(fp8_code(ld(T.param + k), scale))
@@ -734,33 +829,55 @@ __device__ __forceinline__ uint32_t xcd_slot(uint32_t b, uint32_t n) {
     return (b % kXcds) * (n / kXcds) + b / kXcds;
 }
 
-// Multi-tensor fused step: reduce, AdamW and cast for every tile.  TABLES:
-// some shard of the plan reads its slices through a table of pointers (the
-// choice per tile then follows the shard's descriptor); plans without
-// tables run the stride form only.
-template <int NS, bool BF16, bool TABLES>
+// The fused step on one tile.  GENERAL: some shard of the plan reads its
+// slices through a table of pointers, or has a slice or a low-precision copy
+// that is not vector-aligned; the form is then chosen per tile from the
+// shard's descriptor.  Plans with neither run the plain form only, compiled
+// without the others.
+template <int NS, bool BF16, bool AMAX, bool FP8, bool GENERAL>
+__device__ __forceinline__ void fused_tile(const TensorDesc& T, int64_t b, int64_t e, const StepConsts& c,
+                                           uint32_t* amax = nullptr, float fp8_scale = 0.0f) {
+    if constexpr (GENERAL) {
+        if (T.slice_ptrs) {
+            if (T.gen) fused_range<NS, BF16, AMAX, FP8, true, true>(T, b, e, c, amax, fp8_scale);
+            else fused_range<NS, BF16, AMAX, FP8, true, false>(T, b, e, c, amax, fp8_scale);
+            return;
+        }
+        if (T.gen) {
+            fused_range<NS, BF16, AMAX, FP8, false, true>(T, b, e, c, amax, fp8_scale);
+            return;
+        }
+    }
+    fused_range<NS, BF16, AMAX, FP8>(T, b, e, c, amax, fp8_scale);
+}
+
+// Multi-tensor fused step: reduce, AdamW and cast for every tile.
+template <int NS, bool BF16, bool GENERAL>
 __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
                                                          const ChunkDesc* __restrict__ chunks,
                                                          StepConsts c) {
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        if (TABLES && T.slice_ptrs)
-            fused_range<NS, BF16, false, false, TABLES>(T, b, e, c);
-        else
-            fused_range<NS, BF16>(T, b, e, c);
+        fused_tile<NS, BF16, false, false, GENERAL>(T, b, e, c);
     });
 }
 
 // Reduce (or reduce and accumulate) into grad_shard_out; SQ: also write
 // this workgroup's sum of squares of the stored values to its partials slot.
-template <int NS, bool BF16, bool SQ, bool TABLES>
+template <int NS, bool BF16, bool SQ, bool GENERAL>
 __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDesc* __restrict__ tensors,
                                                                  const ChunkDesc* __restrict__ chunks,
                                                                  StepConsts c, int32_t acc,
                                                                  double* partials) {
     double sq = 0.0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        sq = TABLES && T.slice_ptrs ? reduce_store_range<NS, BF16, SQ, TABLES>(T, b, e, c, acc != 0)
-                                    : reduce_store_range<NS, BF16, SQ>(T, b, e, c, acc != 0);
+        const bool a = acc != 0;
+        if (GENERAL && T.slice_ptrs)
+            sq = T.gen ? reduce_store_range<NS, BF16, SQ, true, true>(T, b, e, c, a)
+                       : reduce_store_range<NS, BF16, SQ, true>(T, b, e, c, a);
+        else if (GENERAL && T.gen)
+            sq = reduce_store_range<NS, BF16, SQ, false, true>(T, b, e, c, a);
+        else
+            sq = reduce_store_range<NS, BF16, SQ>(T, b, e, c, a);
     });
     if constexpr (SQ) {
         const double total = wave_sum(sq);
@@ -777,27 +894,26 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(float* a, const void
 }
 
 // Pass 2 of a clipped step: AdamW and cast from grad_shard_out times *scale.
+template <bool GENERAL>
 __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc* __restrict__ tensors,
                                                                 const ChunkDesc* __restrict__ chunks,
                                                                 StepConsts c, const float* scale) {
     const float k = *scale;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        scaled_range(T, b, e, k, c);
+        if (GENERAL && T.gen) scaled_range<true>(T, b, e, k, c);
+        else scaled_range(T, b, e, k, c);
     });
 }
 
 // The fused step that also records, per workgroup, the largest |p'| (as
 // fp32 bits, in the workgroup's slot) for the fp8 copy's per-tensor scale.
-template <int NS, bool BF16, bool TABLES>
+template <int NS, bool BF16, bool GENERAL>
 __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* __restrict__ tensors,
                                                               const ChunkDesc* __restrict__ chunks,
                                                               StepConsts c, uint32_t* tile_amax) {
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        if (TABLES && T.slice_ptrs)
-            fused_range<NS, BF16, true, false, TABLES>(T, b, e, c, &am);
-        else
-            fused_range<NS, BF16, true>(T, b, e, c, &am);
+        fused_tile<NS, BF16, true, false, GENERAL>(T, b, e, c, &am);
     });
     const uint32_t wm = wave_max(am);
     if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
@@ -806,7 +922,7 @@ __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* 
 // The fused step that also writes the fp8 codes of p' with a per-tensor scale
 // given in advance (scale_in[index], e.g. from the previous step's amax) and
 // records this step's per-workgroup largest |p'|, all in the one pass.
-template <int NS, bool BF16, bool TABLES>
+template <int NS, bool BF16, bool GENERAL>
 __global__ __launch_bounds__(kBlock) void mt_step_fp8_kernel(const TensorDesc* __restrict__ tensors,
                                                              const ChunkDesc* __restrict__ chunks,
                                                              StepConsts c, const float* scale_in,
@@ -814,10 +930,7 @@ __global__ __launch_bounds__(kBlock) void mt_step_fp8_kernel(const TensorDesc* _
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         const float scale = ld(scale_in + T.index);
-        if (TABLES && T.slice_ptrs)
-            fused_range<NS, BF16, true, true, TABLES>(T, b, e, c, &am, scale);
-        else
-            fused_range<NS, BF16, true, true>(T, b, e, c, &am, scale);
+        fused_tile<NS, BF16, true, true, GENERAL>(T, b, e, c, &am, scale);
     });
     const uint32_t wm = wave_max(am);
     if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
@@ -866,7 +979,9 @@ __global__ __launch_bounds__(kAmaxBlock) void shard_amax_kernel(const ShardTiles
 // fp8 copy of every shard: the tensor's amax is the maximum over the ranks'
 // values (amax_ranks[r * n_shards + index]; NaN propagates), its scale
 // 448 / max(amax, 1e-12) in fp32.  The workgroup holding a shard's first
-// tile also stores the scale.
+// tile also stores the scale (both parts of a split shard store the same
+// value).  GENERAL: some shard's fp8 copy is not vector-aligned.
+template <bool GENERAL>
 __global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* __restrict__ tensors,
                                                              const ChunkDesc* __restrict__ chunks,
                                                              const float* amax_ranks, int32_t n_ranks,
@@ -879,7 +994,8 @@ __global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* _
         const float den = (amax > 1e-12f || amax != amax) ? amax : 1e-12f;
         const float scale = 448.0f / den;
         if (b == 0 && scale_out && threadIdx.x == 0) st(scale_out + T.index, scale);
-        fp8_range<RS_CAST_TILES>(T, b, e, scale);
+        if (GENERAL && T.gen) fp8_range<RS_CAST_TILES, true>(T, b, e, scale);
+        else fp8_range<RS_CAST_TILES>(T, b, e, scale);
     });
 }
 
@@ -945,81 +1061,81 @@ __global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T) {
 using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts);
 using ReduceKernel = void (*)(TensorDesc, StepConsts);
 
-template <bool BF16, bool TABLES>
+template <bool BF16, bool GENERAL>
 MtKernel pick_mt(int n) {
     switch (n) {
-        case 1: return mt_step_kernel<1, BF16, TABLES>;
-        case 2: return mt_step_kernel<2, BF16, TABLES>;
-        case 4: return mt_step_kernel<4, BF16, TABLES>;
-        case 8: return mt_step_kernel<8, BF16, TABLES>;
-        default: return mt_step_kernel<0, BF16, TABLES>;
+        case 1: return mt_step_kernel<1, BF16, GENERAL>;
+        case 2: return mt_step_kernel<2, BF16, GENERAL>;
+        case 4: return mt_step_kernel<4, BF16, GENERAL>;
+        case 8: return mt_step_kernel<8, BF16, GENERAL>;
+        default: return mt_step_kernel<0, BF16, GENERAL>;
     }
 }
 
-MtKernel pick_mt(int dtype, int n, bool tables) {
-    if (dtype == FSDP_DT_BF16) return tables ? pick_mt<true, true>(n) : pick_mt<true, false>(n);
-    return tables ? pick_mt<false, true>(n) : pick_mt<false, false>(n);
+MtKernel pick_mt(int dtype, int n, bool general) {
+    if (dtype == FSDP_DT_BF16) return general ? pick_mt<true, true>(n) : pick_mt<true, false>(n);
+    return general ? pick_mt<false, true>(n) : pick_mt<false, false>(n);
 }
 
 using ReduceStoreKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, int32_t, double*);
 
-template <bool BF16, bool SQ, bool TABLES>
+template <bool BF16, bool SQ, bool GENERAL>
 ReduceStoreKernel pick_reduce_store(int n) {
     switch (n) {
-        case 1: return mt_reduce_store_kernel<1, BF16, SQ, TABLES>;
-        case 2: return mt_reduce_store_kernel<2, BF16, SQ, TABLES>;
-        case 4: return mt_reduce_store_kernel<4, BF16, SQ, TABLES>;
-        case 8: return mt_reduce_store_kernel<8, BF16, SQ, TABLES>;
-        default: return mt_reduce_store_kernel<0, BF16, SQ, TABLES>;
+        case 1: return mt_reduce_store_kernel<1, BF16, SQ, GENERAL>;
+        case 2: return mt_reduce_store_kernel<2, BF16, SQ, GENERAL>;
+        case 4: return mt_reduce_store_kernel<4, BF16, SQ, GENERAL>;
+        case 8: return mt_reduce_store_kernel<8, BF16, SQ, GENERAL>;
+        default: return mt_reduce_store_kernel<0, BF16, SQ, GENERAL>;
     }
 }
 
-template <bool TABLES>
+template <bool GENERAL>
 ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq) {
     if (dtype == FSDP_DT_BF16)
-        return sq ? pick_reduce_store<true, true, TABLES>(n) : pick_reduce_store<true, false, TABLES>(n);
-    return sq ? pick_reduce_store<false, true, TABLES>(n) : pick_reduce_store<false, false, TABLES>(n);
+        return sq ? pick_reduce_store<true, true, GENERAL>(n) : pick_reduce_store<true, false, GENERAL>(n);
+    return sq ? pick_reduce_store<false, true, GENERAL>(n) : pick_reduce_store<false, false, GENERAL>(n);
 }
 
-ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq, bool tables) {
-    return tables ? pick_reduce_store<true>(dtype, n, sq) : pick_reduce_store<false>(dtype, n, sq);
+ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq, bool general) {
+    return general ? pick_reduce_store<true>(dtype, n, sq) : pick_reduce_store<false>(dtype, n, sq);
 }
 
 using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, uint32_t*);
 
-template <bool BF16, bool TABLES>
+template <bool BF16, bool GENERAL>
 AmaxKernel pick_amax(int n) {
     switch (n) {
-        case 1: return mt_step_amax_kernel<1, BF16, TABLES>;
-        case 2: return mt_step_amax_kernel<2, BF16, TABLES>;
-        case 4: return mt_step_amax_kernel<4, BF16, TABLES>;
-        case 8: return mt_step_amax_kernel<8, BF16, TABLES>;
-        default: return mt_step_amax_kernel<0, BF16, TABLES>;
+        case 1: return mt_step_amax_kernel<1, BF16, GENERAL>;
+        case 2: return mt_step_amax_kernel<2, BF16, GENERAL>;
+        case 4: return mt_step_amax_kernel<4, BF16, GENERAL>;
+        case 8: return mt_step_amax_kernel<8, BF16, GENERAL>;
+        default: return mt_step_amax_kernel<0, BF16, GENERAL>;
     }
 }
 
-AmaxKernel pick_amax(int dtype, int n, bool tables) {
-    if (dtype == FSDP_DT_BF16) return tables ? pick_amax<true, true>(n) : pick_amax<true, false>(n);
-    return tables ? pick_amax<false, true>(n) : pick_amax<false, false>(n);
+AmaxKernel pick_amax(int dtype, int n, bool general) {
+    if (dtype == FSDP_DT_BF16) return general ? pick_amax<true, true>(n) : pick_amax<true, false>(n);
+    return general ? pick_amax<false, true>(n) : pick_amax<false, false>(n);
 }
 
 using Fp8StepKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const float*,
                                uint32_t*);
 
-template <bool BF16, bool TABLES>
+template <bool BF16, bool GENERAL>
 Fp8StepKernel pick_fp8_step(int n) {
     switch (n) {
-        case 1: return mt_step_fp8_kernel<1, BF16, TABLES>;
-        case 2: return mt_step_fp8_kernel<2, BF16, TABLES>;
-        case 4: return mt_step_fp8_kernel<4, BF16, TABLES>;
-        case 8: return mt_step_fp8_kernel<8, BF16, TABLES>;
-        default: return mt_step_fp8_kernel<0, BF16, TABLES>;
+        case 1: return mt_step_fp8_kernel<1, BF16, GENERAL>;
+        case 2: return mt_step_fp8_kernel<2, BF16, GENERAL>;
+        case 4: return mt_step_fp8_kernel<4, BF16, GENERAL>;
+        case 8: return mt_step_fp8_kernel<8, BF16, GENERAL>;
+        default: return mt_step_fp8_kernel<0, BF16, GENERAL>;
     }
 }
 
-Fp8StepKernel pick_fp8_step(int dtype, int n, bool tables) {
-    if (dtype == FSDP_DT_BF16) return tables ? pick_fp8_step<true, true>(n) : pick_fp8_step<true, false>(n);
-    return tables ? pick_fp8_step<false, true>(n) : pick_fp8_step<false, false>(n);
+Fp8StepKernel pick_fp8_step(int dtype, int n, bool general) {
+    if (dtype == FSDP_DT_BF16) return general ? pick_fp8_step<true, true>(n) : pick_fp8_step<true, false>(n);
+    return general ? pick_fp8_step<false, true>(n) : pick_fp8_step<false, false>(n);
 }
 
 template <bool BF16>
@@ -1166,33 +1282,37 @@ bool slice_table_vec_ok(const void* const* ptrs, int32_t slice_dtype, int32_t n_
     return true;
 }
 
-// How many elements past a vector boundary every buffer of shard d starts
-// (0-3), or -1 when its buffers disagree (then no split aligns them all).
-// The slices count only when the shard has data to read.
-int element_phase(const TensorDesc& d, int32_t slice_dtype, int32_t n_slices,
-                  const void* const* table) {
+// In a plan, the vector path needs the fp32 buffers it reads and writes
+// back (param, moments, stored gradient) 16-byte aligned; the slices and the
+// low-precision copies may start at any element (they are read as two
+// aligned vectors and a byte shift, or stored in narrower pieces).
+bool plan_vec_ok(const TensorDesc& d) {
+    return aligned(d.param, kF32Vec) && aligned(d.m, kF32Vec) && aligned(d.v, kF32Vec) &&
+           (!d.grad_out || aligned(d.grad_out, kF32Vec));
+}
+
+// Whether a shard on the vector path has a slice or a low-precision copy that
+// is not vector-aligned (it then takes the kernels' any-alignment form).
+bool plan_needs_gen(const TensorDesc& d, int32_t slice_dtype, int32_t n_slices,
+                    const void* const* table) {
+    const bool slices_ok = d.valid == 0 ||
+                           (table ? slice_table_vec_ok(table, slice_dtype, n_slices)
+                                  : slices_vec_ok(d.slices, slice_dtype, d.slice_stride, n_slices));
+    return !slices_ok || (d.out_bf16 && !aligned(d.out_bf16, kBf16Vec)) ||
+           (d.out_fp8 && !aligned(d.out_fp8, kFp8Vec));
+}
+
+// How many elements past a vector boundary the fp32 buffers of shard d
+// start (0-3), or -1 when they disagree (then no split aligns them all).
+int element_phase(const TensorDesc& d) {
     int phase = -1;
     bool agree = true;
-    const auto take = [&](const void* p, int64_t esize) {
-        if (!p) return;
-        const int ph = static_cast<int>((reinterpret_cast<uintptr_t>(p) / esize) & 3);
+    const float* const fp32_bufs[4] = {d.param, d.m, d.v, d.grad_out};
+    for (const float* p : fp32_bufs) {
+        if (!p) continue;
+        const int ph = static_cast<int>((reinterpret_cast<uintptr_t>(p) / 4) & 3);
         if (phase < 0) phase = ph;
         else if (ph != phase) agree = false;
-    };
-    take(d.param, 4);
-    take(d.m, 4);
-    take(d.v, 4);
-    take(d.grad_out, 4);
-    take(d.out_bf16, 2);
-    take(d.out_fp8, 1);
-    if (d.valid > 0) {
-        const int64_t es = dtype_bytes(slice_dtype);
-        if (table) {
-            for (int32_t q = 0; q < n_slices; ++q) take(table[q], es);
-        } else {
-            take(d.slices, es);
-            if (n_slices > 1 && (d.slice_stride & 3) != 0) agree = false;
-        }
     }
     return agree ? phase : -1;
 }
@@ -1235,7 +1355,8 @@ struct fsdp_mt_plan {
     bool all_fp8 = false;            // every non-empty shard has one
     bool any_bf16 = false;           // some shard has a bf16 copy
     bool any_grad_out = false;       // some shard stores its reduced gradient
-    bool any_table = false;          // some shard reads its slices through a table of pointers
+    bool any_general = false;        // some shard reads its slices through a table of pointers,
+                                     // or has a slice or copy that is not vector-aligned
     uint32_t* d_tile_amax = nullptr;      // fp8: largest |p'| per workgroup
     ShardTiles* d_shard_tiles = nullptr;  // fp8: each input shard's run of workgroups
     TensorDesc* d_tensors = nullptr;
@@ -1465,16 +1586,16 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
         d.slice_stride = table ? 0 : t.slice_stride;
         d.shard_numel = t.shard_numel;
         d.valid = t.valid;
-        d.vec_ok = vec_ok(d, slice_dtype, n_slices) &&
-                   (!table || slice_table_vec_ok(t.grad_slice_ptrs, slice_dtype, n_slices));
-        // A shard whose buffers all start the same 1-3 elements before a
+        const void* const* tab = table ? t.grad_slice_ptrs : nullptr;
+        d.vec_ok = plan_vec_ok(d);
+        d.gen = d.vec_ok && plan_needs_gen(d, slice_dtype, n_slices, tab);
+        // A shard whose fp32 buffers all start the same 1-3 elements past a
         // vector boundary (shards packed back to back after one whose size is
         // not a multiple of 4) is split in two under its index: a head of
         // those elements, which takes the element path, and the aligned rest,
         // which streams in vectors.  Their chunk entries are adjacent, so the
         // shard's workgroups stay one run.
-        const int phase = d.vec_ok ? 0 : element_phase(d, slice_dtype, n_slices,
-                                                        table ? t.grad_slice_ptrs : nullptr);
+        const int phase = d.vec_ok ? 0 : element_phase(d);
         const int64_t head = phase > 0 ? 4 - phase : 0;
         if (head > 0 && d.valid >= head + kGroup) {
             const int64_t es = dtype_bytes(slice_dtype);
@@ -1491,15 +1612,17 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
             d.shard_numel = head;
             d.valid = head;
             d.vec_ok = 0;
+            d.gen = 0;
+            b.vec_ok = plan_vec_ok(b);
             if (table) {
                 table_off.push_back(static_cast<int64_t>(table_host.size()));
                 for (int32_t q = 0; q < n_slices; ++q)
                     table_host.push_back(static_cast<const char*>(t.grad_slice_ptrs[q]) + head * es);
-                b.vec_ok = vec_ok(b, slice_dtype, n_slices) &&
-                           slice_table_vec_ok(table_host.data() + table_off.back(), slice_dtype, n_slices);
+                b.gen = b.vec_ok && plan_needs_gen(b, slice_dtype, n_slices,
+                                                   table_host.data() + table_off.back());
             } else {
                 table_off.push_back(-1);
-                b.vec_ok = vec_ok(b, slice_dtype, n_slices);
+                b.gen = b.vec_ok && plan_needs_gen(b, slice_dtype, n_slices, nullptr);
             }
             descs.push_back(d);
             descs.push_back(b);
@@ -1559,7 +1682,8 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
     plan->all_fp8 = all_fp8;
     plan->any_bf16 = any_bf16;
     plan->any_grad_out = any_grad_out;
-    plan->any_table = !table_host.empty();
+    plan->any_general = !table_host.empty() ||
+                        std::any_of(descs.begin(), descs.end(), [](const TensorDesc& x) { return x.gen != 0; });
     plan->footprint = std::move(footprint);
     hipError_t e = hipGetDevice(&plan->device);
     if (e == hipSuccess && any_fp8 && n_tensors > 0) {
@@ -1614,7 +1738,7 @@ extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
-    const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_table);
+    const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_general);
     hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                        lds_reserve(step_bytes(plan)), stream, plan->d_tensors, plan->d_chunks, c);
     return launch_status(who);
@@ -1638,7 +1762,7 @@ extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumul
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(nullptr, plan->n_slices);
         const ReduceStoreKernel k = pick_reduce_store(plan->slice_dtype, plan->n_slices, sq,
-                                                      plan->any_table);
+                                                      plan->any_general);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(slice_bytes(plan) + 4 + 4 * accumulate,
                                        accumulate ? RS_INFLIGHT_KB_ACC : RS_INFLIGHT_KB), stream,
@@ -1737,7 +1861,8 @@ extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hpa
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
-    hipLaunchKernelGGL(mt_scaled_step_kernel, dim3(static_cast<uint32_t>(plan->n_blocks)),
+    hipLaunchKernelGGL(plan->any_general ? mt_scaled_step_kernel<true> : mt_scaled_step_kernel<false>,
+                       dim3(static_cast<uint32_t>(plan->n_blocks)),
                        dim3(kBlock), lds_reserve(4 + 24 + 2 * plan->any_bf16), stream,
                        plan->d_tensors, plan->d_chunks,
                        c, grad_scale);
@@ -1759,7 +1884,7 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(hp, plan->n_slices);
-        const AmaxKernel k = pick_amax(plan->slice_dtype, plan->n_slices, plan->any_table);
+        const AmaxKernel k = pick_amax(plan->slice_dtype, plan->n_slices, plan->any_general);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(step_bytes(plan), RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
                            plan->d_chunks, c, plan->d_tile_amax);
@@ -1796,7 +1921,7 @@ static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int
         return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
-    hipLaunchKernelGGL(mt_cast_fp8_kernel,
+    hipLaunchKernelGGL(plan->any_general ? mt_cast_fp8_kernel<true> : mt_cast_fp8_kernel<false>,
                        dim3(static_cast<uint32_t>(plan->n_chunks * (kTilesPerChunk / RS_CAST_TILES))),
                        dim3(kBlock), 0, stream, plan->d_tensors,
                        plan->d_chunks, amax_ranks, n_ranks, plan->n_tensors, scale_out);
@@ -1826,7 +1951,7 @@ static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(hp, plan->n_slices);
-        const Fp8StepKernel k = pick_fp8_step(plan->slice_dtype, plan->n_slices, plan->any_table);
+        const Fp8StepKernel k = pick_fp8_step(plan->slice_dtype, plan->n_slices, plan->any_general);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(step_bytes(plan) + 1, RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
                            plan->d_chunks, c, scale_in, plan->d_tile_amax);

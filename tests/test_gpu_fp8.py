@@ -262,3 +262,55 @@ def test_delayed_scaling_two_steps(gpu):
         bf = PR.bf16_bits(st.ag_slot[off:off + held])
         assert np.array_equal(bf, O.bf16_rne(p.astype(np.float64))), i
     st.close()
+
+
+@pytest.mark.parametrize("f8_off", [1, 2, 3])
+def test_fp8_codes_at_any_byte_alignment(gpu, f8_off):
+    """fp8 copies 1-3 bytes past a 4-byte boundary, the fp32 state aligned:
+    the code pass and the one-pass fp8 step store them in narrower pieces.
+    Codes equal the oracle's quantisation of the GPU's own p', the padding
+    codes are 0 and the bytes around every copy are untouched."""
+    N, sdt = 3, "bf16"
+    sizes = [(2048 * 3 + 1100, 2048 * 3 + 1093), (1025, 1021), (37, 37)]
+    g = torch.Generator(device=gpu)
+    g.manual_seed(90 + f8_off)
+    shards = []
+    for S, valid in sizes:
+        p = torch.zeros(S, dtype=torch.float32, device=gpu)
+        p[:valid] = torch.randn(valid, generator=g, device=gpu) * 0.02
+        m, v = torch.zeros_like(p), torch.zeros_like(p)
+        sl = (torch.randn(N * S, generator=g, device=gpu) * 1e-2).to(torch.bfloat16)
+        raw = torch.full((S + 16,), 0xAB, dtype=torch.uint8, device=gpu)
+        shards.append(dict(p=p, m=m, v=v, sl=sl, raw=raw, f8=raw[8 + f8_off:8 + f8_off + S],
+                           S=S, valid=valid))
+    plan = B.MtPlan([{"param_fp32": s["p"], "exp_avg": s["m"], "exp_avg_sq": s["v"],
+                      "grad_slices": s["sl"], "slice_stride": s["S"], "shard_numel": s["S"],
+                      "valid": s["valid"], "unshard_fp8_out": s["f8"]} for s in shards], N, sdt)
+    n = len(shards)
+
+    def check(name, scales):
+        for i, s in enumerate(shards):
+            p = s["p"].cpu().numpy()
+            codes = _codes(s["f8"])
+            _check_codes(f"{name} shard {i}", p[:s["valid"]], codes[:s["valid"]], scales[i])
+            assert np.all(codes[s["valid"]:] == 0), f"{name} shard {i}: pad codes not 0"
+            raw = _codes(s["raw"])
+            lo, hi = 8 + f8_off, 8 + f8_off + s["S"]
+            assert np.all(raw[:lo] == 0xAB) and np.all(raw[hi:] == 0xAB), f"{name} shard {i}: guard bytes"
+
+    # dynamic scaling: the step with amax, then the code pass
+    amax = torch.full((n,), -1.0, dtype=torch.float32, device=gpu)
+    scale = torch.zeros(n, dtype=torch.float32, device=gpu)
+    plan.step_amax(HPARAMS, 1, amax)
+    plan.cast_fp8(amax, 1, scale)
+    torch.cuda.synchronize()
+    am = amax.cpu().numpy()
+    for i, s in enumerate(shards):
+        assert am[i] == np.float32(F.amax(s["p"].cpu().numpy()[:s["valid"]])), i
+    check("code pass", [F.scale_of(a) for a in am])
+    # the one-pass step with given scales
+    scales = np.array([448.0 / 0.05, 3.0e4, 0.5], dtype=np.float32)
+    plan.step_fp8(HPARAMS, 2, torch.from_numpy(scales).to(gpu), amax)
+    torch.cuda.synchronize()
+    check("one-pass step", scales)
+    plan.close()

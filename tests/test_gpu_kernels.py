@@ -54,28 +54,32 @@ class Buf:
 
 
 class Shard:
+    """One shard's buffers.  ``offset``: element offset of every buffer, or a
+    dict of per-buffer offsets (keys p, m, v, sl, out, gout; default 0)."""
+
     def __init__(self, S, valid, N, sdt, device, seed, offset=0, stride_extra=0, bf16=True,
                  gout=True):
         g = torch.Generator(device=device)
         g.manual_seed(seed)
         f32 = torch.float32
+        off = (lambda k: offset.get(k, 0)) if isinstance(offset, dict) else (lambda k: offset)
         self.S, self.valid, self.N, self.sdt = S, valid, N, sdt
-        self.p = Buf(S, f32, device, fill=1.0e30, offset=offset)
-        self.m = Buf(S, f32, device, fill=float("nan"), offset=offset)
-        self.v = Buf(S, f32, device, fill=float("inf"), offset=offset)
+        self.p = Buf(S, f32, device, fill=1.0e30, offset=off("p"))
+        self.m = Buf(S, f32, device, fill=float("nan"), offset=off("m"))
+        self.v = Buf(S, f32, device, fill=float("inf"), offset=off("v"))
         if valid:
             self.p.t[:valid] = torch.randn(valid, generator=g, device=device) * 0.02
             self.m.t[:valid] = torch.randn(valid, generator=g, device=device) * 1e-3
             self.v.t[:valid] = torch.randn(valid, generator=g, device=device).square() * 1e-6
         self.stride = S + stride_extra
         sd = torch.float32 if sdt == "f32" else torch.bfloat16
-        self.sl = Buf(N * self.stride, sd, device, fill=float("nan"), offset=offset)
+        self.sl = Buf(N * self.stride, sd, device, fill=float("nan"), offset=off("sl"))
         x = torch.randn(N, S, generator=g, device=device) * 1e-2
         self.sl.t.view(N, self.stride)[:, :S] = x.to(sd)
         if valid < S:
             self.sl.t.view(N, self.stride)[:, valid:S] = float("nan")   # pad garbage
-        self.out = Buf(S, torch.bfloat16, device, fill=1.5, offset=offset) if bf16 else None
-        self.gout = Buf(S, f32, device, fill=float("nan"), offset=offset) if gout else None
+        self.out = Buf(S, torch.bfloat16, device, fill=1.5, offset=off("out")) if bf16 else None
+        self.gout = Buf(S, f32, device, fill=float("nan"), offset=off("gout")) if gout else None
         for b in self.bufs():
             b.seal()
 
@@ -392,28 +396,85 @@ def test_fp32_replica_bit_exact(gpu, sdt, N):
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
 @pytest.mark.parametrize("off,head", [(1, 3), (2, 2), (3, 1)])
 def test_misaligned_shard_split_equals_element_path(gpu, sdt, off, head):
-    """A shard whose buffers all start `off` elements past a vector boundary is
-    split into a head of 4 - off elements and an aligned body (one more chunk
-    entry); the same data with one slice stride out of phase cannot be split
-    and runs element by element.  Both give identical bits."""
+    """A shard whose fp32 buffers all start `off` elements past a vector
+    boundary is split into a head of 4 - off elements and an aligned body
+    (one more chunk entry): (a) with the slices in phase after the split,
+    (b) with a slice stride that leaves them out of phase (the body reads them
+    as shifted vectors).  (c) The same data with one moment buffer in another
+    phase cannot be split and runs element by element.  All give identical
+    bits."""
     N, S, va = 3, 5013, 5009
     a = Shard(S, va, N, sdt, gpu, seed=8100 + off, offset=off, stride_extra=3)   # stride % 4 == 0
     b = Shard(S, va, N, sdt, gpu, seed=8100 + off, offset=off, stride_extra=1)   # stride % 4 == 2
-    pa, pb = B.MtPlan([a.mt()], N, sdt), B.MtPlan([b.mt()], N, sdt)
-    assert pa.info()["n_chunks"] == 1 + -(-(S - head) // 2048)
-    assert pb.info()["n_chunks"] == -(-S // 2048)
+    c = Shard(S, va, N, sdt, gpu, seed=8100 + off, stride_extra=3,
+              offset={"p": off, "m": (off + 1) % 4, "v": off, "sl": off, "out": off, "gout": off})
+    plans = [B.MtPlan([x.mt()], N, sdt) for x in (a, b, c)]
+    split = 1 + -(-(S - head) // 2048)
+    assert [pl.info()["n_chunks"] for pl in plans] == [split, split, -(-S // 2048)]
     for t in (1, 2):
         snap = a.snapshot()
-        pa.step(HP, t)
-        pb.step(HP, t)
+        for pl in plans:
+            pl.step(HP, t)
         torch.cuda.synchronize()
         a.check(f"split off={off} {sdt} t={t}", snap, t)
-        for nm in ("p", "m", "v", "gout"):
-            x, y = getattr(a, nm).t, getattr(b, nm).t
-            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (nm, t)
-        assert torch.equal(a.out.t.view(torch.int16), b.out.t.view(torch.int16)), t
-    pa.close()
-    pb.close()
+        for y in (b, c):
+            for nm in ("p", "m", "v", "gout"):
+                assert torch.equal(getattr(a, nm).t.view(torch.int32), getattr(y, nm).t.view(torch.int32)), (nm, t)
+            assert torch.equal(a.out.t.view(torch.int16), y.out.t.view(torch.int16)), t
+        for x in (a, b, c):
+            for bf in x.bufs():
+                bf.check_guards(f"split off={off}")
+    for pl in plans:
+        pl.close()
+
+
+# slices (per-slice phases through the stride) and bf16 copies at every
+# element phase, with the fp32 state aligned: the vector path reads the
+# slices as shifted vectors and stores the copies in narrower pieces
+PLACEMENTS = [
+    {"sl": 1, "out": 1}, {"sl": 2, "out": 2}, {"sl": 3, "out": 3},
+    {"sl": 0, "out": 1}, {"sl": 1, "out": 0}, {"sl": 2, "out": 3},
+]
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 3, 8])
+def test_misaligned_slices_and_copies_equal_aligned(gpu, N, sdt):
+    """The same data with every buffer aligned, and with the slices and the
+    bf16 copy at other element phases (strides in and out of phase): the
+    fused step and the clipped step give identical bits, guards intact."""
+    specs = [(2048 * 3 + 517, 2048 * 3 + 510, x) for x in (0, 1, 2, 3)] + [(300, 297, 2), (9, 9, 1)]
+    # the reference: every buffer aligned, strides keeping every slice aligned
+    mk = lambda pl, aligned: [Shard(S, va, N, sdt, gpu, seed=8300 + 10 * i + N, offset=pl,
+                                    stride_extra=(-S) % 4 if aligned else x)
+                              for i, (S, va, x) in enumerate(specs)]
+    for pl in PLACEMENTS:
+        a, b = mk({}, True), mk(pl, False)
+        plan_a = B.MtPlan([s.mt() for s in a], N, sdt)
+        plan_b = B.MtPlan([s.mt() for s in b], N, sdt)
+        sq = [torch.zeros(1, dtype=torch.float64, device=gpu) for _ in range(2)]
+        coef = [torch.zeros(1, dtype=torch.float32, device=gpu) for _ in range(2)]
+        snaps = [s.snapshot() for s in b]
+        for k, plan in enumerate((plan_a, plan_b)):
+            plan.step(HP, 1)
+        torch.cuda.synchronize()
+        for i, (s, snap) in enumerate(zip(b, snaps)):
+            s.check(f"placement {pl} N={N} {sdt} shard {i}", snap, 1)
+        for k, plan in enumerate((plan_a, plan_b)):
+            plan.reduce_sqnorm(sq[k])
+            B.fsdp_clip_coef(coef[k], None, sq[k], 1, 0.05)
+            plan.step_clipped(HP, 2, coef[k])
+        torch.cuda.synchronize()
+        assert sq[0].view(torch.int64).item() == sq[1].view(torch.int64).item()
+        for i, (x, y) in enumerate(zip(a, b)):
+            for nm in ("p", "m", "v", "gout"):
+                assert torch.equal(getattr(x, nm).t.view(torch.int32), getattr(y, nm).t.view(torch.int32)), \
+                    (pl, i, nm)
+            assert torch.equal(x.out.t.view(torch.int16), y.out.t.view(torch.int16)), (pl, i)
+            for bf in y.bufs():
+                bf.check_guards(f"placement {pl} shard {i}")
+        plan_a.close()
+        plan_b.close()
 
 
 # the largest slice count the ABI accepts, and one short of it (a partial
