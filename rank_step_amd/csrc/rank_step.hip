@@ -162,8 +162,11 @@ struct TensorDesc {
     int64_t valid;
     int64_t vec_ok;      // the buffers the vector path needs aligned are aligned
     int64_t index;       // position of the shard in the plan's input list
-    int64_t gen;         // some slice or low-precision copy is not vector-aligned
+    int64_t gen;         // kGenStore | kGenLoad: a low-precision copy / a slice is not
+                         // vector-aligned (then the any-alignment forms run)
 };
+
+constexpr int64_t kGenStore = 1, kGenLoad = 2;
 
 // One entry of the chunk-descriptor table: elements [begin, begin+count) of a shard.
 struct ChunkDesc {
@@ -331,7 +334,7 @@ template <bool BF16>
 __device__ __forceinline__ SliceVec<BF16> join_shifted(const SliceVec<BF16>& A, const SliceVec<BF16>& B,
                                                        uint32_t sh) {
     if constexpr (BF16) {
-        // sh = 2, 4 or 6: dword offset w, byte offset b within it
+        // sh = 0, 2, 4 or 6: dword offset w, byte offset b within it
         const bool w = sh >= 4;
         const uint32_t b = sh & 3u;
         const uint32_t x0 = w ? A[1] : A[0];
@@ -339,36 +342,57 @@ __device__ __forceinline__ SliceVec<BF16> join_shifted(const SliceVec<BF16>& A, 
         const uint32_t x2 = w ? B[1] : B[0];
         return u32x2{__builtin_amdgcn_alignbyte(x1, x0, b), __builtin_amdgcn_alignbyte(x2, x1, b)};
     } else {
-        // sh = 4, 8 or 12: whole dwords
-        const bool d1 = sh == 4, d2 = sh == 8;
-        return u32x4{d1 ? A[1] : (d2 ? A[2] : A[3]), d1 ? A[2] : (d2 ? A[3] : B[0]),
-                     d1 ? A[3] : (d2 ? B[0] : B[1]), d1 ? B[0] : (d2 ? B[1] : B[2])};
+        // sh = 0, 4, 8 or 12: whole dwords
+        const bool d0 = sh == 0, d1 = sh == 4, d2 = sh == 8;
+        return u32x4{d0 ? A[0] : (d1 ? A[1] : (d2 ? A[2] : A[3])),
+                     d0 ? A[1] : (d1 ? A[2] : (d2 ? A[3] : B[0])),
+                     d0 ? A[2] : (d1 ? A[3] : (d2 ? B[0] : B[1])),
+                     d0 ? A[3] : (d1 ? B[0] : (d2 ? B[1] : B[2]))};
     }
 }
 
-// Group i of a slice that starts at any element alignment.  Every group of
-// the slice starts `sh` bytes past a vector boundary, sh taken from the
-// slice's base (uniform, so the test is a scalar branch).  sh == 0: one
-// vector load.  Otherwise the two aligned vectors that hold the group,
-// joined: each holds bytes of the group, so neither reaches past the page
-// (or the allocation) the group lies in.
+// The parts of a group load at any element alignment.  `lo` is the aligned
+// vector at or before the group (the group itself when aligned), `hi` the
+// address of the next vector when the group spans two (else lo again, so
+// that no load leaves the group's vectors), and `sh` the group's offset in
+// bytes past `lo`.
 template <bool BF16>
-__device__ __forceinline__ SliceVec<BF16> load_group_any(const void* base, int64_t i) {
-    using V = SliceVec<BF16>;
-    constexpr uintptr_t W = sizeof(V);
+struct AnyGroup {
+    uintptr_t lo, hi;
+    uint32_t sh;
+};
+
+template <bool BF16>
+__device__ __forceinline__ AnyGroup<BF16> any_group(const void* base, int64_t i) {
+    constexpr uintptr_t W = sizeof(SliceVec<BF16>);
     const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base) & (W - 1));
-    const uintptr_t a = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(i) * (W / kGroup);
-    if (sh == 0) return ld_slice(reinterpret_cast<const V*>(a));
-    const V A = ld_slice(reinterpret_cast<const V*>(a - sh));
-    const V B = ld_slice(reinterpret_cast<const V*>(a - sh + W));
-    return join_shifted<BF16>(A, B, sh);
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(i) * (W / kGroup) - sh;
+    return AnyGroup<BF16>{lo, sh ? lo + W : lo, sh};
 }
 
-// GEN: the slice may start at any element alignment.
-template <bool BF16, bool GEN>
-__device__ __forceinline__ SliceVec<BF16> load_slice_group(const void* base, int64_t i) {
-    if constexpr (GEN) return load_group_any<BF16>(base, i);
-    else return load_group<BF16>(base, i);
+// Groups at element e of the slices j < min(K, n), each slice at any element
+// alignment (base(j) gives slice j's start), into w[].  Every lane loads the
+// two aligned vectors that hold its group (the group's own vector twice
+// when it is aligned), all loads before the first join: no test on a
+// slice's alignment sits between them.  Each vector loaded holds bytes of
+// the group, so none reaches past the page (or the allocation) the slice
+// lies in.
+template <int K, bool BF16, typename Base>
+__device__ __forceinline__ void load_any(SliceVec<BF16> w[K], Base&& base, int n, int64_t e) {
+    using V = SliceVec<BF16>;
+    AnyGroup<BF16> g[K];
+    V A[K], B[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        if (j < n) {
+            g[j] = any_group<BF16>(base(j), e);
+            A[j] = ld_slice(reinterpret_cast<const V*>(g[j].lo));
+            B[j] = ld_slice(reinterpret_cast<const V*>(g[j].hi));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        if (j < n) w[j] = join_shifted<BF16>(A[j], B[j], g[j].sh);
 }
 
 template <bool BF16>
@@ -409,12 +433,17 @@ __device__ __forceinline__ const void* slice_base(const TensorDesc& T, int q) {
     }
 }
 
+// GEN: the slices may start at any element alignment.
 template <int NS, bool BF16, bool TABLE, bool GEN = false>
 __device__ __forceinline__ void load_slices(SliceRegs<NS, BF16>& r, const TensorDesc& T,
                                             int64_t e) {
     static_assert(NS > 0, "compile-time slice count");
+    if constexpr (GEN) {
+        load_any<NS, BF16>(r.w, [&](int q) { return slice_base<BF16, TABLE>(T, q); }, NS, e);
+    } else {
 #pragma unroll
-    for (int q = 0; q < NS; ++q) r.w[q] = load_slice_group<BF16, GEN>(slice_base<BF16, TABLE>(T, q), e);
+        for (int q = 0; q < NS; ++q) r.w[q] = load_group<BF16>(slice_base<BF16, TABLE>(T, q), e);
+    }
 }
 
 template <int NS, bool BF16>
@@ -448,9 +477,13 @@ __device__ __forceinline__ void reduce_runtime(const TensorDesc& T, int64_t e, f
     constexpr int KB = rt_batch<BF16>();
     for (int q0 = 0; q0 < c.n; q0 += KB) {
         SliceVec<BF16> w[KB];
+        if constexpr (GEN) {
+            load_any<KB, BF16>(w, [&](int j) { return slice_base<BF16, TABLE>(T, q0 + j); }, c.n - q0, e);
+        } else {
 #pragma unroll
-        for (int j = 0; j < KB; ++j)
-            if (q0 + j < c.n) w[j] = load_slice_group<BF16, GEN>(slice_base<BF16, TABLE>(T, q0 + j), e);
+            for (int j = 0; j < KB; ++j)
+                if (q0 + j < c.n) w[j] = load_group<BF16>(slice_base<BF16, TABLE>(T, q0 + j), e);
+        }
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
             if (q0 + j < c.n) {
@@ -643,10 +676,10 @@ __device__ __forceinline__ int64_t vector_end(const TensorDesc& T, int64_t begin
 }
 
 // The fused step on elements [begin, end) of shard T; `begin` is a multiple of
-// kGroup.  AMAX, FP8 and GEN as in update_store; TABLE as in slice_base;
-// GEN also lets the slices start at any element alignment.
+// kGroup.  AMAX and FP8 as in update_store, GEN_ST as its GEN; TABLE as in
+// slice_base; GEN_LD: the slices may start at any element alignment.
 template <int NS, bool BF16, bool AMAX = false, bool FP8 = false, bool TABLE = false,
-          bool GEN = false>
+          bool GEN_LD = false, bool GEN_ST = false>
 __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, int64_t end,
                                             const StepConsts& c, uint32_t* amax = nullptr,
                                             float fp8_scale = 0.0f) {
@@ -656,16 +689,16 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
         if constexpr (NS > 0) {
             // every load of the group before the first arithmetic
             SliceRegs<NS, BF16> sr;
-            load_slices<NS, BF16, TABLE, GEN>(sr, T, e);
+            load_slices<NS, BF16, TABLE, GEN_LD>(sr, T, e);
             load_state(s, T, e);
             float g[kGroup];
             reduce_regs<NS, BF16>(sr, g, c);
-            update_store<true, AMAX, FP8, GEN>(s, g, T, e, c, amax, fp8_scale);
+            update_store<true, AMAX, FP8, GEN_ST>(s, g, T, e, c, amax, fp8_scale);
         } else {
             load_state(s, T, e);
             float g[kGroup];
-            reduce_runtime<BF16, TABLE, GEN>(T, e, g, c);
-            update_store<true, AMAX, FP8, GEN>(s, g, T, e, c, amax, fp8_scale);
+            reduce_runtime<BF16, TABLE, GEN_LD>(T, e, g, c);
+            update_store<true, AMAX, FP8, GEN_ST>(s, g, T, e, c, amax, fp8_scale);
         }
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
@@ -839,12 +872,17 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& T, int64_t b, int64
                                            uint32_t* amax = nullptr, float fp8_scale = 0.0f) {
     if constexpr (GENERAL) {
         if (T.slice_ptrs) {
-            if (T.gen) fused_range<NS, BF16, AMAX, FP8, true, true>(T, b, e, c, amax, fp8_scale);
-            else fused_range<NS, BF16, AMAX, FP8, true, false>(T, b, e, c, amax, fp8_scale);
+            if (T.gen & kGenLoad) fused_range<NS, BF16, AMAX, FP8, true, true, true>(T, b, e, c, amax, fp8_scale);
+            else if (T.gen) fused_range<NS, BF16, AMAX, FP8, true, false, true>(T, b, e, c, amax, fp8_scale);
+            else fused_range<NS, BF16, AMAX, FP8, true>(T, b, e, c, amax, fp8_scale);
+            return;
+        }
+        if (T.gen & kGenLoad) {
+            fused_range<NS, BF16, AMAX, FP8, false, true, true>(T, b, e, c, amax, fp8_scale);
             return;
         }
         if (T.gen) {
-            fused_range<NS, BF16, AMAX, FP8, false, true>(T, b, e, c, amax, fp8_scale);
+            fused_range<NS, BF16, AMAX, FP8, false, false, true>(T, b, e, c, amax, fp8_scale);
             return;
         }
     }
@@ -872,9 +910,9 @@ __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDes
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         const bool a = acc != 0;
         if (GENERAL && T.slice_ptrs)
-            sq = T.gen ? reduce_store_range<NS, BF16, SQ, true, true>(T, b, e, c, a)
-                       : reduce_store_range<NS, BF16, SQ, true>(T, b, e, c, a);
-        else if (GENERAL && T.gen)
+            sq = T.gen & kGenLoad ? reduce_store_range<NS, BF16, SQ, true, true>(T, b, e, c, a)
+                                  : reduce_store_range<NS, BF16, SQ, true>(T, b, e, c, a);
+        else if (GENERAL && (T.gen & kGenLoad))
             sq = reduce_store_range<NS, BF16, SQ, false, true>(T, b, e, c, a);
         else
             sq = reduce_store_range<NS, BF16, SQ>(T, b, e, c, a);
@@ -900,7 +938,7 @@ __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc
                                                                 StepConsts c, const float* scale) {
     const float k = *scale;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        if (GENERAL && T.gen) scaled_range<true>(T, b, e, k, c);
+        if (GENERAL && (T.gen & kGenStore)) scaled_range<true>(T, b, e, k, c);
         else scaled_range(T, b, e, k, c);
     });
 }
@@ -994,7 +1032,7 @@ __global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* _
         const float den = (amax > 1e-12f || amax != amax) ? amax : 1e-12f;
         const float scale = 448.0f / den;
         if (b == 0 && scale_out && threadIdx.x == 0) st(scale_out + T.index, scale);
-        if (GENERAL && T.gen) fp8_range<RS_CAST_TILES, true>(T, b, e, scale);
+        if (GENERAL && (T.gen & kGenStore)) fp8_range<RS_CAST_TILES, true>(T, b, e, scale);
         else fp8_range<RS_CAST_TILES>(T, b, e, scale);
     });
 }
@@ -1291,15 +1329,17 @@ bool plan_vec_ok(const TensorDesc& d) {
            (!d.grad_out || aligned(d.grad_out, kF32Vec));
 }
 
-// Whether a shard on the vector path has a slice or a low-precision copy that
-// is not vector-aligned (it then takes the kernels' any-alignment form).
-bool plan_needs_gen(const TensorDesc& d, int32_t slice_dtype, int32_t n_slices,
-                    const void* const* table) {
+// The any-alignment forms a shard on the vector path needs: kGenLoad when a
+// slice is not vector-aligned, kGenStore when a low-precision copy is not
+// (or when its slices are not: that form stores at any alignment too).
+int64_t plan_gen(const TensorDesc& d, int32_t slice_dtype, int32_t n_slices,
+                 const void* const* table) {
     const bool slices_ok = d.valid == 0 ||
                            (table ? slice_table_vec_ok(table, slice_dtype, n_slices)
                                   : slices_vec_ok(d.slices, slice_dtype, d.slice_stride, n_slices));
-    return !slices_ok || (d.out_bf16 && !aligned(d.out_bf16, kBf16Vec)) ||
-           (d.out_fp8 && !aligned(d.out_fp8, kFp8Vec));
+    const bool copies_ok = (!d.out_bf16 || aligned(d.out_bf16, kBf16Vec)) &&
+                           (!d.out_fp8 || aligned(d.out_fp8, kFp8Vec));
+    return (slices_ok ? 0 : kGenLoad | kGenStore) | (copies_ok ? 0 : kGenStore);
 }
 
 // How many elements past a vector boundary the fp32 buffers of shard d
@@ -1588,7 +1628,7 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
         d.valid = t.valid;
         const void* const* tab = table ? t.grad_slice_ptrs : nullptr;
         d.vec_ok = plan_vec_ok(d);
-        d.gen = d.vec_ok && plan_needs_gen(d, slice_dtype, n_slices, tab);
+        d.gen = d.vec_ok ? plan_gen(d, slice_dtype, n_slices, tab) : 0;
         // A shard whose fp32 buffers all start the same 1-3 elements past a
         // vector boundary (shards packed back to back after one whose size is
         // not a multiple of 4) is split in two under its index: a head of
@@ -1618,11 +1658,11 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
                 table_off.push_back(static_cast<int64_t>(table_host.size()));
                 for (int32_t q = 0; q < n_slices; ++q)
                     table_host.push_back(static_cast<const char*>(t.grad_slice_ptrs[q]) + head * es);
-                b.gen = b.vec_ok && plan_needs_gen(b, slice_dtype, n_slices,
-                                                   table_host.data() + table_off.back());
+                b.gen = b.vec_ok ? plan_gen(b, slice_dtype, n_slices, table_host.data() + table_off.back())
+                                 : 0;
             } else {
                 table_off.push_back(-1);
-                b.gen = b.vec_ok && plan_needs_gen(b, slice_dtype, n_slices, nullptr);
+                b.gen = b.vec_ok ? plan_gen(b, slice_dtype, n_slices, nullptr) : 0;
             }
             descs.push_back(d);
             descs.push_back(b);
