@@ -705,14 +705,15 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
         fused_elem<BF16, AMAX, FP8, TABLE>(T, k, c, amax, fp8_scale);
 }
 
-// Reduce only: grad_out = mean of the slices on [begin, end).
-template <int NS, bool BF16>
+// Reduce only: grad_out = mean of the slices on [begin, end); GEN: the
+// slices may start at any element alignment.
+template <int NS, bool BF16, bool GEN = false>
 __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin, int64_t end,
                                              const StepConsts& c) {
     const int64_t vend = vector_end(T, begin, end);
     for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         float g[kGroup];
-        reduce_group<NS, BF16>(T, e, g, c);
+        reduce_group<NS, BF16, false, GEN>(T, e, g, c);
         st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
@@ -822,12 +823,15 @@ __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, in
                                       : uint8_t(0));
 }
 
-// Cast only: out_bf16 = RNE(param) on [begin, end).
+// Cast only: out_bf16 = RNE(param) on [begin, end); GEN: the copy may start
+// at any element alignment.
+template <bool GEN = false>
 __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, int64_t end) {
     const int64_t vend = vector_end(T, begin, end);
     for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         const f32x4 a = ld_s<RS_NT_CAST_LD>(reinterpret_cast<const f32x4*>(T.param + e));
-        st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(a));
+        if constexpr (GEN) store_bf16_any(T.out_bf16 + e, pack_bf16(a), misalign(T.out_bf16, 8));
+        else st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(a));
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.out_bf16 + k, k < T.valid ? static_cast<uint16_t>(bf16_rne(ld(T.param + k))) : uint16_t(0));
@@ -1077,21 +1081,25 @@ __global__ void clip_coef_kernel(float* coef_out, double* norm_out, const double
 }
 
 // Single-shard kernels: workgroup b covers elements [b*kTile, (b+1)*kTile).
-template <int NS, bool BF16>
+// GEN: the slices (the gradient, for AdamW alone) or the bf16 copy start off
+// a vector boundary, the fp32 buffers on it.
+template <int NS, bool BF16, bool GEN = false>
 __global__ __launch_bounds__(kBlock) void fused_single_kernel(TensorDesc T, StepConsts c) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
-    fused_range<NS, BF16>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
+    fused_range<NS, BF16, false, false, false, GEN>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel),
+                                                   c);
 }
 
-template <int NS, bool BF16>
+template <int NS, bool BF16, bool GEN = false>
 __global__ __launch_bounds__(kBlock) void reduce_single_kernel(TensorDesc T, StepConsts c) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
-    reduce_range<NS, BF16>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
+    reduce_range<NS, BF16, GEN>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
 }
 
+template <bool GEN = false>
 __global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
-    cast_range(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel));
+    cast_range<GEN>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel));
 }
 
 // ---------------------------------------------------------------- kernel selection
@@ -1176,15 +1184,20 @@ Fp8StepKernel pick_fp8_step(int dtype, int n, bool general) {
     return general ? pick_fp8_step<false, true>(n) : pick_fp8_step<false, false>(n);
 }
 
-template <bool BF16>
+template <bool BF16, bool GEN>
 ReduceKernel pick_reduce(int n) {
     switch (n) {
-        case 1: return reduce_single_kernel<1, BF16>;
-        case 2: return reduce_single_kernel<2, BF16>;
-        case 4: return reduce_single_kernel<4, BF16>;
-        case 8: return reduce_single_kernel<8, BF16>;
-        default: return reduce_single_kernel<0, BF16>;
+        case 1: return reduce_single_kernel<1, BF16, GEN>;
+        case 2: return reduce_single_kernel<2, BF16, GEN>;
+        case 4: return reduce_single_kernel<4, BF16, GEN>;
+        case 8: return reduce_single_kernel<8, BF16, GEN>;
+        default: return reduce_single_kernel<0, BF16, GEN>;
     }
+}
+
+ReduceKernel pick_reduce(int dtype, int n, bool gen) {
+    if (dtype == FSDP_DT_BF16) return gen ? pick_reduce<true, true>(n) : pick_reduce<true, false>(n);
+    return gen ? pick_reduce<false, true>(n) : pick_reduce<false, false>(n);
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -1236,15 +1249,6 @@ bool slices_vec_ok(const void* slices, int32_t slice_dtype, int64_t stride, int3
     const uintptr_t a = slice_dtype == FSDP_DT_BF16 ? kBf16Vec : kF32Vec;
     if (slices && !aligned(slices, a)) return false;
     return n_slices == 1 || (stride * dtype_bytes(slice_dtype)) % static_cast<int64_t>(a) == 0;
-}
-
-bool vec_ok(const TensorDesc& T, int32_t slice_dtype, int32_t n_slices) {
-    if (!aligned(T.param, kF32Vec) || !aligned(T.m, kF32Vec) || !aligned(T.v, kF32Vec)) return false;
-    if (!slices_vec_ok(T.slices, slice_dtype, T.slice_stride, n_slices)) return false;
-    if (T.out_bf16 && !aligned(T.out_bf16, kBf16Vec)) return false;
-    if (T.grad_out && !aligned(T.grad_out, kF32Vec)) return false;
-    if (T.out_fp8 && !aligned(T.out_fp8, kFp8Vec)) return false;
-    return true;
 }
 
 int64_t tiles_for(int64_t S) { return (S + kTile - 1) / kTile; }
@@ -1320,11 +1324,11 @@ bool slice_table_vec_ok(const void* const* ptrs, int32_t slice_dtype, int32_t n_
     return true;
 }
 
-// In a plan, the vector path needs the fp32 buffers it reads and writes
-// back (param, moments, stored gradient) 16-byte aligned; the slices and the
+// The vector path needs the fp32 buffers it reads and writes back (param,
+// moments, stored gradient) 16-byte aligned; the slices and the
 // low-precision copies may start at any element (they are read as two
 // aligned vectors and a byte shift, or stored in narrower pieces).
-bool plan_vec_ok(const TensorDesc& d) {
+bool state_vec_ok(const TensorDesc& d) {
     return aligned(d.param, kF32Vec) && aligned(d.m, kF32Vec) && aligned(d.v, kF32Vec) &&
            (!d.grad_out || aligned(d.grad_out, kF32Vec));
 }
@@ -1470,12 +1474,13 @@ static int32_t reduce_grad_shard_impl(float* grad_shard_out, const void* grad_sl
     T.slice_stride = slice_stride;
     T.shard_numel = shard_numel;
     T.valid = valid;
-    T.vec_ok = aligned(grad_shard_out, kF32Vec) &&
-               slices_vec_ok(grad_slices, slice_dtype, slice_stride, n_slices);
+    // the vector path needs the output aligned; slices off a vector
+    // boundary take the shifted loads
+    T.vec_ok = aligned(grad_shard_out, kF32Vec);
+    const bool gen = T.vec_ok && !slices_vec_ok(grad_slices, slice_dtype, slice_stride, n_slices);
     const StepConsts c = make_consts(nullptr, n_slices);
     if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
-    const ReduceKernel k = slice_dtype == FSDP_DT_BF16 ? pick_reduce<true>(n_slices)
-                                                       : pick_reduce<false>(n_slices);
+    const ReduceKernel k = pick_reduce(slice_dtype, n_slices, gen);
     hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(tiles_for(shard_numel))), dim3(kBlock),
                        lds_reserve(dtype_bytes(slice_dtype) * inflight_slices(n_slices, slice_dtype) + 4),
                        stream, T, c);
@@ -1511,10 +1516,14 @@ static int32_t adamw_shard_step_impl(float* param_fp32, float* exp_avg, float* e
     T.slice_stride = shard_numel;
     T.shard_numel = shard_numel;
     T.valid = valid;
-    T.vec_ok = vec_ok(T, FSDP_DT_F32, 1);
+    // the vector path needs the state aligned; a gradient off a vector
+    // boundary takes the shifted loads
+    T.vec_ok = state_vec_ok(T);
+    const bool gen = T.vec_ok && !aligned(grad_shard, kF32Vec);
     const StepConsts c = make_consts(hp, 1);
     if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
-    hipLaunchKernelGGL((fused_single_kernel<1, false>), dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
+    const ReduceKernel k = gen ? fused_single_kernel<1, false, true> : fused_single_kernel<1, false, false>;
+    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
                        dim3(kBlock), lds_reserve(4 + 24), stream, T, c);
     return launch_status(who);
 }
@@ -1538,9 +1547,13 @@ static int32_t cast_unshard_bf16_impl(uint16_t* unshard_bf16_out, const float* p
     T.out_bf16 = unshard_bf16_out;
     T.shard_numel = shard_numel;
     T.valid = valid;
-    T.vec_ok = aligned(unshard_bf16_out, kBf16Vec) && aligned(param_fp32, kF32Vec);
+    // the vector path needs the parameter aligned; a copy off a vector
+    // boundary is stored in narrower pieces
+    T.vec_ok = aligned(param_fp32, kF32Vec);
+    const bool gen = T.vec_ok && !aligned(unshard_bf16_out, kBf16Vec);
     if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
-    hipLaunchKernelGGL(cast_single_kernel, dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
+    hipLaunchKernelGGL(gen ? cast_single_kernel<true> : cast_single_kernel<false>,
+                       dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
                        dim3(kBlock), lds_reserve(4 + 2), stream, T);
     return launch_status(who);
 }
@@ -1627,7 +1640,7 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
         d.shard_numel = t.shard_numel;
         d.valid = t.valid;
         const void* const* tab = table ? t.grad_slice_ptrs : nullptr;
-        d.vec_ok = plan_vec_ok(d);
+        d.vec_ok = state_vec_ok(d);
         d.gen = d.vec_ok ? plan_gen(d, slice_dtype, n_slices, tab) : 0;
         // A shard whose fp32 buffers all start the same 1-3 elements past a
         // vector boundary (shards packed back to back after one whose size is
@@ -1653,7 +1666,7 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
             d.valid = head;
             d.vec_ok = 0;
             d.gen = 0;
-            b.vec_ok = plan_vec_ok(b);
+            b.vec_ok = state_vec_ok(b);
             if (table) {
                 table_off.push_back(static_cast<int64_t>(table_host.size()));
                 for (int32_t q = 0; q < n_slices; ++q)

@@ -477,6 +477,34 @@ def test_misaligned_slices_and_copies_equal_aligned(gpu, N, sdt):
         plan_b.close()
 
 
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_single_calls_at_any_alignment_equal_aligned(gpu, sdt):
+    """The three single-shard calls with the slices, the gradient the AdamW
+    call reads and the bf16 copy off their vector boundaries (the fp32 state
+    and the reduce's output aligned): identical bits to the all-aligned
+    placement, guards intact."""
+    N = 3
+    S, va = 2048 * 2 + 333, 2048 * 2 + 330
+    for pl in PLACEMENTS:
+        a = Shard(S, va, N, sdt, gpu, seed=8500, stride_extra=(-S) % 4)
+        b = Shard(S, va, N, sdt, gpu, seed=8500, offset=pl, stride_extra=1)
+        grads = []
+        for s, off in ((a, 0), (b, pl["sl"] or 1)):
+            B.fsdp_reduce_grad_shard(s.gout.t, s.sl.t, sdt, s.stride, N, S, va)
+            g = Buf(S, torch.float32, gpu, fill=float("nan"), offset=off)  # the gradient elsewhere
+            g.t.copy_(s.gout.t)
+            g.seal()
+            grads.append(g)
+            B.fsdp_adamw_shard_step(s.p.t, s.m.t, s.v.t, g.t, S, va, HP, 1)
+            B.fsdp_cast_unshard_bf16(s.out.t, s.p.t, S, va)
+        torch.cuda.synchronize()
+        for nm in ("p", "m", "v", "gout"):
+            assert torch.equal(getattr(a, nm).t.view(torch.int32), getattr(b, nm).t.view(torch.int32)), (pl, nm)
+        assert torch.equal(a.out.t.view(torch.int16), b.out.t.view(torch.int16)), pl
+        for bf in b.bufs() + grads:
+            bf.check_guards(f"single calls {pl}")
+
+
 # the largest slice count the ABI accepts, and one short of it (a partial
 # last batch), on small ragged shards
 MAX_N_SPECS = [(2048 + 300, 2048 + 297, 0, 0), (1001, 1001, 0, 3), (255, 250, 4, 1), (37, 37, 1, 3)]
