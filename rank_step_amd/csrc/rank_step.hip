@@ -760,13 +760,16 @@ __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_
 
 // In-place accumulation of one micro-batch's unsharded gradient, elements
 // [begin, end): acc = acc + x (fp32 add), or acc = x exactly for the first.
-template <bool BF16>
+// GEN: x may start at any element alignment (acc is aligned).
+template <bool BF16, bool GEN = false>
 __device__ __forceinline__ void accumulate_range(float* a, const void* x, int64_t begin,
                                                  int64_t end, bool accum, bool vec) {
     const int64_t vend = vec ? std::max(begin, end & ~int64_t(kGroup - 1)) : begin;
     for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         f32x4* ap = reinterpret_cast<f32x4*>(a + e);
-        const SliceVec<BF16> w = load_group<BF16>(x, e);
+        SliceVec<BF16> w;
+        if constexpr (GEN) load_any<1, BF16>(&w, [&](int) { return x; }, 1, e);
+        else w = load_group<BF16>(x, e);
         f32x4 av = {0.f, 0.f, 0.f, 0.f};
         if (accum) av = ld_state(ap);
         float xv[kGroup];
@@ -928,11 +931,11 @@ __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDes
 }
 
 // Workgroup b accumulates elements [b*kTile, (b+1)*kTile) of one buffer.
-template <bool BF16>
+template <bool BF16, bool GEN = false>
 __global__ __launch_bounds__(kBlock) void accumulate_kernel(float* a, const void* x, int64_t n,
                                                             int32_t accum, int32_t vec) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
-    accumulate_range<BF16>(a, x, begin, std::min(begin + kTile, n), accum != 0, vec != 0);
+    accumulate_range<BF16, GEN>(a, x, begin, std::min(begin + kTile, n), accum != 0, vec != 0);
 }
 
 // Pass 2 of a clipped step: AdamW and cast from grad_shard_out times *scale.
@@ -1867,16 +1870,17 @@ static int32_t grad_accumulate_impl(float* acc, const void* micro, int32_t micro
     if ((st = fsdp::check_aliases(rs)) != FSDP_OK) return st;
     const int64_t blocks = tiles_for(numel);
     if ((st = check_grid(blocks, who)) != FSDP_OK) return st;
-    const int32_t vec = aligned(acc, kF32Vec) &&
-                        aligned(micro, micro_dtype == FSDP_DT_BF16 ? kBf16Vec : kF32Vec);
-    if (micro_dtype == FSDP_DT_BF16)
-        hipLaunchKernelGGL(accumulate_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
-                           lds_reserve(dtype_bytes(micro_dtype) + 4 + 4 * accumulate), stream, acc,
-                           micro, numel, accumulate, vec);
-    else
-        hipLaunchKernelGGL(accumulate_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
-                           lds_reserve(dtype_bytes(micro_dtype) + 4 + 4 * accumulate), stream, acc,
-                           micro, numel, accumulate, vec);
+    // the vector path needs the accumulator aligned; a micro-batch gradient
+    // off a vector boundary takes the shifted loads
+    const int32_t vec = aligned(acc, kF32Vec);
+    const bool gen = vec && !aligned(micro, micro_dtype == FSDP_DT_BF16 ? kBf16Vec : kF32Vec);
+    using AccKernel = void (*)(float*, const void*, int64_t, int32_t, int32_t);
+    const AccKernel k = micro_dtype == FSDP_DT_BF16
+                            ? (gen ? accumulate_kernel<true, true> : accumulate_kernel<true, false>)
+                            : (gen ? accumulate_kernel<false, true> : accumulate_kernel<false, false>);
+    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
+                       lds_reserve(dtype_bytes(micro_dtype) + 4 + 4 * accumulate), stream, acc, micro,
+                       numel, accumulate, vec);
     return launch_status(who);
 }
 

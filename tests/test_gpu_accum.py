@@ -24,11 +24,15 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("n,off", [(0, 0), (1, 0), (7, 0), (8, 0), (2048 * 3 + 517, 0), (70001, 1),
-                                   (4096 + 257, 2), (4096 + 257, 4)])
-def test_grad_accumulate(gpu, dt, n, off):
+# off: element offset of the accumulator; xoff: of the micro-batch gradient
+# (the accumulator aligned and the gradient 1-3 elements past a vector
+# boundary takes the shifted loads)
+@pytest.mark.parametrize("n,off,xoff", [(0, 0, 0), (1, 0, 0), (7, 0, 0), (8, 0, 0), (2048 * 3 + 517, 0, 0),
+                                        (70001, 1, 1), (4096 + 257, 2, 2), (4096 + 257, 4, 4),
+                                        (4096 + 257, 0, 1), (4096 + 257, 0, 2), (70001, 0, 3)])
+def test_grad_accumulate(gpu, dt, n, off, xoff):
     g = torch.Generator(device=gpu)
-    g.manual_seed(n + off)
+    g.manual_seed(n + off + 10 * xoff)
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     acc_full = torch.full((n + off + 8,), float("nan"), dtype=torch.float32, device=gpu)
     acc = acc_full[off:off + n]
@@ -38,7 +42,7 @@ def test_grad_accumulate(gpu, dt, n, off):
         x = (torch.randn(n, generator=g, device=gpu) * 10.0 ** (k - 2)).to(tdt)
         if n:
             x[0] = -0.0 if k == 0 else x[0]
-        xs = torch.zeros(n + off, dtype=tdt, device=gpu)[off:]
+        xs = torch.zeros(n + xoff, dtype=tdt, device=gpu)[xoff:]
         xs.copy_(x)
         B.fsdp_grad_accumulate(acc, xs, dt, n, k > 0)
         torch.cuda.synchronize()
