@@ -2,8 +2,9 @@
 
 Each plan draws its own shard table: the number of shards, their sizes
 (empty, a few elements, several 2048-element chunk entries), how much of each
-is padding, buffer offsets that keep or break the vector alignments, slice
-strides wider than the shard, the slice count N and dtype, which shards write
+is padding, buffer offsets (one for the whole shard, or one per buffer, so
+that shards split, read shifted slices, store copies in pieces or run
+element by element), slice strides wider than the shard, the slice count N and dtype, which shards write
 the bf16 copy and the reduced gradient, and the AdamW hyperparameters and step.
 Every shard is checked against the float64 oracle (per-step resync) with guard
 words around every buffer, over two consecutive steps.  The same random tables
@@ -49,7 +50,15 @@ def _draw_plan(rng):
         else:
             S = int(rng.integers(6000, 40000))
         valid = S if rng.random() < 0.6 else int(rng.integers(0, S + 1))
-        offset = int(rng.choice([0, 0, 0, 1, 2, 4]))
+        kind = rng.random()
+        if kind < 0.6:      # every buffer at one offset
+            offset = int(rng.choice([0, 0, 0, 1, 2, 4]))
+        elif kind < 0.85:   # fp32 buffers in one phase, slices and copy anywhere
+            co = int(rng.integers(0, 4))
+            offset = {"p": co, "m": co, "v": co, "gout": co,
+                      "sl": int(rng.integers(0, 4)), "out": int(rng.integers(0, 4))}
+        else:               # every buffer anywhere (fp32 phases may disagree)
+            offset = {k: int(rng.integers(0, 4)) for k in ("p", "m", "v", "gout", "sl", "out")}
         stride_extra = int(rng.choice([0, 0, 0, 1, 2, 4, 37]))
         specs.append((S, valid, offset, stride_extra, bool(rng.random() < 0.7),
                       bool(rng.random() < 0.5)))
