@@ -9,6 +9,9 @@ benchmark times (one multi-tensor plan over the rank's packed shards).
 * 7B rank shard (291 shards) and 70B rank shard (723 shards): full size, a
   sample of elements (random plus the first and last elements of every shard)
   that the oracle computes one by one from the GPU's state before each step.
+* Units of odd sizes (FLAT N=4, Shard(0) N=8), every rank and element: shard
+  sizes that are not multiples of 4, so slices sit at odd strides, all-gather
+  slots and packed shards start off vector boundaries.
 """
 
 import numpy as np
@@ -18,7 +21,7 @@ import torch
 from oracle import layout as OL
 from oracle import step as O
 from rank_step_amd.state import RankState
-from rank_step_amd.workloads import WORKLOADS, shapes_of
+from rank_step_amd.workloads import WORKLOADS, Param, Workload, shapes_of
 from tests import parity as PR
 
 pytestmark = pytest.mark.gpu
@@ -196,3 +199,46 @@ def test_llama70b_rank_shard(gpu):
     assert st.total == 2_204_803_328 and len(st.segments) == 723
     del st
     torch.cuda.empty_cache()
+
+
+# odd sizes: FLAT with P = 590,081 (S = 147,521, 3 padding elements), and
+# Shard(0) with rows and dim-0 sizes that leave every packed shard, its
+# slices and its all-gather slot at varying element phases
+ODD = {
+    "flat": Workload(91, "odd_flat_n4", "flat", 4,
+                     (Param("W1", (256, 256), "f32"), Param("b1", (257,), "f32"),
+                      Param("W2", (1024, 256), "f32"), Param("W3", (256, 1024), "f32")),
+                     "f32", 4, False, True, 2, 1e-2),
+    "shard0": Workload(92, "odd_shard0_n8", "shard0", 8,
+                       (Param("emb", (1001, 3), "bf16"), Param("w1", (257, 129), "bf16"),
+                        Param("n1", (129,), "bf16", True), Param("w2", (77, 61), "bf16"),
+                        Param("b2", (61,), "bf16"), Param("w3", (4099, 17), "bf16")),
+                     "bf16", 8, True, True, 2, 1e-3),
+}
+
+
+@pytest.mark.parametrize("kind", ["flat", "shard0"])
+def test_odd_sizes_every_rank(gpu, kind):
+    w = ODD[kind]
+    for r in range(w.world_size):
+        st = RankState(w, r, gpu, bf16_out=True, grad_out=True, ag_full=True, garbage_pad=True)
+        _layout_matches_oracle(st)
+        plan = st.make_plan()
+        if kind == "shard0":
+            # packed shards that start off a vector boundary are split
+            phases = [off % 4 for off, length, held, _ in st.segments]
+            assert any(phases), "the sizes should put some shards off a vector boundary"
+            entries = sum(-(-length // 2048) for _, length, _, _ in st.segments)
+            assert plan.info()["n_chunks"] > entries
+        for t in range(1, w.steps + 1):
+            st.load_grads(t)
+            snap = _snapshot(st)
+            st.step(t)
+            torch.cuda.synchronize()
+            _check_full(st, snap, t, f"{w.name} rank {r} t={t}", check_g=True)
+        ag = PR.bf16_bits(st.ag)
+        S = st.total
+        mask = np.ones(ag.size, dtype=bool)
+        mask[r * S:(r + 1) * S] = False
+        assert np.all(ag[mask] == 0), f"{w.name} rank {r}: another rank's slot written"
+        st.close()
