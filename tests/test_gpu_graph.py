@@ -167,3 +167,32 @@ def test_slice_table_steps_graph(gpu):
         st.plan.step_clipped(w.hparams, 4, bufs["coef"])
 
     _run(w, a, b, gpu, calls, extra=(("sq", (1, torch.float64)), ("coef", (1, torch.float32))))
+
+
+def test_general_plan_graph(gpu):
+    """A plan whose shards need the any-alignment forms (odd sizes: split
+    shards, slices at an odd stride, the bf16 copy in an all-gather slot off
+    a vector boundary) runs the general kernel variants: the fused, clipped
+    and one-pass fp8 steps captured and replayed."""
+    from tests.test_gpu_workloads import ODD
+    w = ODD["shard0"]
+    kw = dict(bf16_out=True, grad_out=True, ag_full=True, fp8_out=True)
+    a, b = RankState(w, 1, gpu, **kw), RankState(w, 1, gpu, **kw)
+    assert (a.total * 1) % 4 != 0, "rank 1's all-gather slot should start off a vector boundary"
+    a.make_plan()
+    b.make_plan()
+    n = len(a.segments)
+
+    def calls(st, bufs):
+        st.plan.step(w.hparams, 3)
+        st.plan.reduce_sqnorm(bufs["sq"])
+        B.fsdp_clip_coef(bufs["coef"], None, bufs["sq"], 1, 0.05)
+        st.plan.step_clipped(w.hparams, 4, bufs["coef"])
+        st.plan.step_fp8(w.hparams, 5, bufs["scale"], bufs["amax"])
+
+    _run(w, a, b, gpu, calls,
+         extra=(("sq", (1, torch.float64)), ("coef", (1, torch.float32)),
+                ("scale", (n, torch.float32)), ("amax", (n, torch.float32))),
+         init={"scale": 448.0 / 0.05})
+    a.close()
+    b.close()
