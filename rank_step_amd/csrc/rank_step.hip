@@ -328,8 +328,9 @@ __device__ __forceinline__ SliceVec<BF16> load_group(const void* base, int64_t i
     else return ld_slice(reinterpret_cast<const V*>(static_cast<const float*>(base) + i));
 }
 
-// The group starting `sh` bytes into A (0 < sh < sizeof A, a multiple of
-// the element size), given A and the vector B that follows it.
+// The group starting `sh` bytes into A (0 <= sh < sizeof A, a multiple of
+// the element size), given A and the vector B that follows it; A itself
+// when sh is 0.
 template <bool BF16>
 __device__ __forceinline__ SliceVec<BF16> join_shifted(const SliceVec<BF16>& A, const SliceVec<BF16>& B,
                                                        uint32_t sh) {
@@ -356,18 +357,17 @@ __device__ __forceinline__ SliceVec<BF16> join_shifted(const SliceVec<BF16>& A, 
 // address of the next vector when the group spans two (else lo again, so
 // that no load leaves the group's vectors), and `sh` the group's offset in
 // bytes past `lo`.
-template <bool BF16>
 struct AnyGroup {
     uintptr_t lo, hi;
     uint32_t sh;
 };
 
 template <bool BF16>
-__device__ __forceinline__ AnyGroup<BF16> any_group(const void* base, int64_t i) {
+__device__ __forceinline__ AnyGroup any_group(const void* base, int64_t i) {
     constexpr uintptr_t W = sizeof(SliceVec<BF16>);
     const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base) & (W - 1));
     const uintptr_t lo = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(i) * (W / kGroup) - sh;
-    return AnyGroup<BF16>{lo, sh ? lo + W : lo, sh};
+    return AnyGroup{lo, sh ? lo + W : lo, sh};
 }
 
 // Groups at element e of the slices j < min(K, n), each slice at any element
@@ -380,7 +380,7 @@ __device__ __forceinline__ AnyGroup<BF16> any_group(const void* base, int64_t i)
 template <int K, bool BF16, typename Base>
 __device__ __forceinline__ void load_any(SliceVec<BF16> w[K], Base&& base, int n, int64_t e) {
     using V = SliceVec<BF16>;
-    AnyGroup<BF16> g[K];
+    AnyGroup g[K];
     V A[K], B[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
