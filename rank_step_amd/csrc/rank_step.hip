@@ -12,8 +12,12 @@
 // elements per access (one 16-byte load per fp32 array, one 8-byte load per
 // bf16 slice), and every load of the tile is issued before its first use.
 // Gradient slices and the low-precision copies are touched once and use
-// non-temporal accesses.  Shards whose buffers are not aligned for those
-// vectors take an element-by-element path with the same arithmetic
+// non-temporal accesses.  The vector path needs a shard's fp32 buffers
+// 16-byte aligned; its slices and copies may start at any element (shifted
+// loads, stores in narrower pieces), and a plan splits a shard whose fp32
+// buffers all start off a boundary into a short head and an aligned rest.
+// What is left (shards whose fp32 buffers disagree, partial groups, the
+// padding) goes element by element with the same arithmetic
 // (bit-identical results).
 //
 // Residency is capped on purpose: each streaming launch reserves enough LDS
@@ -668,8 +672,9 @@ __device__ __forceinline__ void scaled_elem(const TensorDesc& T, int64_t k, floa
 // ---------------------------------------------------------------- ranges of a shard
 
 // End of the vector part of [begin, end): whole groups below `valid` when the
-// shard's buffers allow vector accesses; the rest (the partial group at
-// `valid`, the padding, misaligned shards) goes element by element.
+// shard's fp32 buffers are aligned for vectors; the rest (the partial group
+// at `valid`, the padding, shards whose fp32 buffers are not) goes element
+// by element.
 __device__ __forceinline__ int64_t vector_end(const TensorDesc& T, int64_t begin, int64_t end) {
     const int64_t vend = T.vec_ok ? std::min(end, T.valid & ~int64_t(kGroup - 1)) : begin;
     return std::max(vend, begin);
