@@ -35,6 +35,10 @@
  *     Inf in inputs are not errors: they propagate per IEEE 754.
  *   - Floating point: fp32 with IEEE-correct division and square root, no
  *     flush of denormals.  Results are deterministic run to run (no atomics).
+ *   - Speed, not correctness: every call streams in 16-byte vectors when the
+ *     fp32 buffers it writes back in place are 16-byte aligned; gradient
+ *     slices and bf16/fp8 copies may start at any element (see also
+ *     fsdp_mt_tensor).  Otherwise it runs element by element, bit-identical.
  *   - Resources: the streaming kernels run one wave64 per workgroup and,
  *     except the fp8 code pass, reserve up to 36 KB of LDS per workgroup that
  *     they never touch.  The reservation caps how many of their workgroups
