@@ -454,6 +454,41 @@ int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_
 int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, const float* scale_in,
                          float* amax_out, hipStream_t stream);
 
+/* ------------------------------------------------------------------ no device allocation */
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  A plan's
+ * tables and its per-workgroup partial sums are allocated when the plan is
+ * made; this call needs no plan and allocates nothing.
+ *
+ * Pass 1 of a clipped step for one shard: the reduced gradient, exactly as
+ * fsdp_reduce_grad_shard writes it, to grad_shard_out, and the sum of its
+ * squares to sqnorm_out (device, one fp64).  Its results are bit-identical
+ * to fsdp_mt_reduce_sqnorm's on a plan holding this one shard (same kernel
+ * body, same per-workgroup partials, same fixed summation order) when the
+ * shard's fp32 buffers of that plan are 16-byte aligned.
+ *   grad_shard_out  device fp32 [shard_numel], written (+0 in the padding)
+ *   sqnorm_out      device fp64 [1], written (0 for shard_numel = 0)
+ *   the slices      as in fsdp_reduce_grad_shard
+ * The per-workgroup partial sums live in one fixed device array of the
+ * library, FSDP_NOALLOC_SCRATCH_BYTES (1 MiB) on each device, held until the
+ * process ends, so shard_numel is at most FSDP_NOALLOC_MAX_NUMEL (else
+ * FSDP_E_CAPACITY, nothing queued).  Every call on a device shares that
+ * device's array: calls that overlap on one device (different streams
+ * without ordering between them, or different host threads) race.  Each
+ * call writes every partial it reads, so nothing is cleared between calls.
+ * No hipMalloc, hipFree or other allocating call is made; the array's device
+ * address is looked up once per device, on the first call there.  Errors:
+ * as fsdp_reduce_grad_shard; FSDP_E_ARG for a null sqnorm_out, FSDP_E_ALIGN
+ * if it is not 8-byte aligned, FSDP_E_ALIAS if it overlaps the gradient or
+ * the slices. */
+#define FSDP_NOALLOC_SCRATCH_BYTES (1 << 20)
+#define FSDP_NOALLOC_MAX_NUMEL ((int64_t)33292288) /* 16,256 chunk entries of 2048 */
+int32_t fsdp_reduce_sqnorm_noalloc(float* grad_shard_out, double* sqnorm_out,
+                                   const void* grad_slices, int32_t slice_dtype,
+                                   int64_t slice_stride, int32_t n_slices, int64_t shard_numel,
+                                   int64_t valid, hipStream_t stream);
+
 /* Sizes of a plan (host only). */
 int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info_out);
 

@@ -32,7 +32,10 @@ EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
            "fsdp_mt_step", "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy",
            "fsdp_mt_reduce_sqnorm", "fsdp_clip_coef", "fsdp_mt_step_clipped",
            "fsdp_mt_step_amax", "fsdp_mt_cast_fp8", "fsdp_mt_step_fp8",
-           "fsdp_mt_reduce_accumulate", "fsdp_grad_accumulate")
+           "fsdp_mt_reduce_accumulate", "fsdp_grad_accumulate", "fsdp_reduce_sqnorm_noalloc")
+
+# fsdp_reduce_sqnorm_noalloc's limit (FSDP_NOALLOC_MAX_NUMEL in the header)
+NOALLOC_MAX_NUMEL = 33_292_288
 
 
 class FsdpError(RuntimeError):
@@ -118,6 +121,7 @@ def lib():
             "fsdp_mt_step_fp8": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp],
             "fsdp_mt_reduce_accumulate": [vp, i32, vp, vp],
             "fsdp_grad_accumulate": [vp, vp, i32, i64, i32, vp],
+            "fsdp_reduce_sqnorm_noalloc": [vp, vp, vp, i32, i64, i32, i64, i64, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -273,6 +277,13 @@ def fsdp_mt_reduce_accumulate(plan, accumulate, sqnorm_out=None, stream=None):
 def fsdp_grad_accumulate(acc, micro, micro_dtype, numel, accumulate, stream=None):
     _check(lib().fsdp_grad_accumulate(_ptr(acc), _ptr(micro), _dtype(micro_dtype), int(numel),
                                       int(bool(accumulate)), _stream(stream)))
+
+
+def fsdp_reduce_sqnorm_noalloc(grad_shard_out, sqnorm_out, grad_slices, slice_dtype, slice_stride,
+                               n_slices, shard_numel, valid, stream=None):
+    _check(lib().fsdp_reduce_sqnorm_noalloc(_ptr(grad_shard_out), _ptr(sqnorm_out), _ptr(grad_slices),
+                                            _dtype(slice_dtype), int(slice_stride), int(n_slices),
+                                            int(shard_numel), int(valid), _stream(stream)))
 
 
 class MtPlan:

@@ -40,6 +40,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <type_traits>
 #include <vector>
@@ -1110,6 +1111,21 @@ __global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T) {
     cast_range<GEN>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel));
 }
 
+// Reduce one shard into grad_out and write each workgroup's sum of squares to
+// its partials slot.  The grid is whole chunk entries (a multiple of 8), as a
+// plan holding this one shard launches it: workgroup b covers elements
+// [b*kTile, (b+1)*kTile), the same tile as the plan's tile b % 8 of entry
+// b / 8, and the workgroups past the shard's end store a zero partial.
+template <int NS, bool BF16, bool GEN = false>
+__global__ __launch_bounds__(kBlock) void reduce_sqnorm_single_kernel(TensorDesc T, StepConsts c,
+                                                                      double* partials) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
+    const int64_t end = std::max(begin, std::min<int64_t>(begin + kTile, T.shard_numel));
+    const double sq = reduce_store_range<NS, BF16, true, false, GEN>(T, begin, end, c, false);
+    const double total = wave_sum(sq);
+    if (threadIdx.x == 0) st(partials + xcd_slot(blockIdx.x, gridDim.x), total);
+}
+
 // ---------------------------------------------------------------- kernel selection
 
 using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts);
@@ -1206,6 +1222,24 @@ ReduceKernel pick_reduce(int n) {
 ReduceKernel pick_reduce(int dtype, int n, bool gen) {
     if (dtype == FSDP_DT_BF16) return gen ? pick_reduce<true, true>(n) : pick_reduce<true, false>(n);
     return gen ? pick_reduce<false, true>(n) : pick_reduce<false, false>(n);
+}
+
+using SqnormSingleKernel = void (*)(TensorDesc, StepConsts, double*);
+
+template <bool BF16, bool GEN>
+SqnormSingleKernel pick_sqnorm_single(int n) {
+    switch (n) {
+        case 1: return reduce_sqnorm_single_kernel<1, BF16, GEN>;
+        case 2: return reduce_sqnorm_single_kernel<2, BF16, GEN>;
+        case 4: return reduce_sqnorm_single_kernel<4, BF16, GEN>;
+        case 8: return reduce_sqnorm_single_kernel<8, BF16, GEN>;
+        default: return reduce_sqnorm_single_kernel<0, BF16, GEN>;
+    }
+}
+
+SqnormSingleKernel pick_sqnorm_single(int dtype, int n, bool gen) {
+    if (dtype == FSDP_DT_BF16) return gen ? pick_sqnorm_single<true, true>(n) : pick_sqnorm_single<true, false>(n);
+    return gen ? pick_sqnorm_single<false, true>(n) : pick_sqnorm_single<false, false>(n);
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -2023,6 +2057,125 @@ static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
                        0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
                        static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds,
                        amax_out);
+    return launch_status(who);
+}
+
+// ---------------------------------------------------------------- no device allocation
+
+// Per-workgroup partial sums of fsdp_reduce_sqnorm_noalloc, then its
+// kSumBlocks second-stage sums.  Device code never names this array: host
+// code looks up its address on each device (hipGetSymbolAddress) and passes
+// that address to the kernels, as a plan passes its own partials.
+constexpr int64_t kScratchDoubles = FSDP_NOALLOC_SCRATCH_BYTES / sizeof(double);
+static __device__ __align__(256) double scratch[kScratchDoubles];
+
+namespace {
+
+// The largest shard whose partials and second-stage sums fit the array, in
+// whole chunk entries.
+constexpr int64_t kNoAllocMaxBlocks = (kScratchDoubles - kSumBlocks) / kTilesPerChunk * kTilesPerChunk;
+static_assert(FSDP_NOALLOC_MAX_NUMEL == kNoAllocMaxBlocks / kTilesPerChunk * kChunk,
+              "the header's size limit is what the scratch array holds");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_dev[kMaxDevices] = {};  // the array's address on each device, once looked up
+
+// The scratch array's address on the current device, looked up on the first
+// call there with that device current.
+int32_t scratch_on_current_device(double** out, const char* who) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FSDP_E_HIP, "%s: %s", who, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(FSDP_E_STATE, "%s: device %d beyond the %d this library tracks", who, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(FSDP_E_HIP, "%s: address of the scratch array on device %d: %s", who, dev,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = static_cast<double*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return FSDP_OK;
+}
+
+bool overlaps(uintptr_t a_lo, uintptr_t a_hi, uintptr_t b_lo, uintptr_t b_hi) {
+    return a_lo < a_hi && b_lo < b_hi && a_lo < b_hi && b_lo < a_hi;
+}
+
+}  // namespace
+
+extern "C" int32_t fsdp_reduce_sqnorm_noalloc(float* grad_shard_out, double* sqnorm_out,
+                                              const void* grad_slices, int32_t slice_dtype,
+                                              int64_t slice_stride, int32_t n_slices,
+                                              int64_t shard_numel, int64_t valid, hipStream_t stream) {
+    const char* who = "fsdp_reduce_sqnorm_noalloc";
+    int32_t st;
+    if ((st = check_sizes(shard_numel, valid, who)) != FSDP_OK) return st;
+    if ((st = check_slices(grad_slices, slice_dtype, slice_stride, n_slices, shard_numel, valid,
+                           who)) != FSDP_OK)
+        return st;
+    if (shard_numel > FSDP_NOALLOC_MAX_NUMEL)
+        return fail(FSDP_E_CAPACITY, "%s: shard_numel %lld exceeds FSDP_NOALLOC_MAX_NUMEL (%lld): "
+                    "the partial sums would not fit the library's %d-byte scratch array", who,
+                    static_cast<long long>(shard_numel), static_cast<long long>(FSDP_NOALLOC_MAX_NUMEL),
+                    FSDP_NOALLOC_SCRATCH_BYTES);
+    if (!sqnorm_out) return fail(FSDP_E_ARG, "%s: null sqnorm_out", who);
+    if (!aligned(sqnorm_out, 8)) return fail(FSDP_E_ALIGN, "%s: sqnorm_out not 8-byte aligned", who);
+    if (shard_numel > 0 && !grad_shard_out) return fail(FSDP_E_ARG, "%s: null grad_shard_out", who);
+    if (!aligned(grad_shard_out, 4)) return fail(FSDP_E_ALIGN, "%s: grad_shard_out misaligned", who);
+    // overlaps, checked pairwise (nothing allocated): the two outputs against
+    // each other and against every slice
+    const uintptr_t g_lo = reinterpret_cast<uintptr_t>(grad_shard_out);
+    const uintptr_t g_hi = g_lo + static_cast<uintptr_t>(shard_numel) * 4;
+    const uintptr_t s_lo = reinterpret_cast<uintptr_t>(sqnorm_out), s_hi = s_lo + 8;
+    if (overlaps(g_lo, g_hi, s_lo, s_hi))
+        return fail(FSDP_E_ALIAS, "%s: sqnorm_out overlaps grad_shard_out", who);
+    if (valid > 0) {
+        const int64_t es = dtype_bytes(slice_dtype);
+        for (int32_t q = 0; q < n_slices; ++q) {
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(grad_slices) +
+                                 static_cast<uintptr_t>(q * slice_stride * es);
+            const uintptr_t hi = lo + static_cast<uintptr_t>(valid * es);
+            if (overlaps(g_lo, g_hi, lo, hi) || overlaps(s_lo, s_hi, lo, hi))
+                return fail(FSDP_E_ALIAS, "%s: an output overlaps gradient slice %d", who, q);
+        }
+    }
+    double* partials = nullptr;
+    if ((st = scratch_on_current_device(&partials, who)) != FSDP_OK) return st;
+    if (shard_numel == 0) {
+        // nothing to sum: one workgroup over an empty range writes 0
+        hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
+                           static_cast<const double*>(nullptr), int64_t(0), int64_t(0), sqnorm_out);
+        return launch_status(who);
+    }
+    TensorDesc T{};
+    T.slices = grad_slices;
+    T.grad_out = grad_shard_out;
+    T.slice_stride = slice_stride;
+    T.shard_numel = shard_numel;
+    T.valid = valid;
+    T.vec_ok = aligned(grad_shard_out, kF32Vec);
+    const bool gen = T.vec_ok && !slices_vec_ok(grad_slices, slice_dtype, slice_stride, n_slices);
+    const StepConsts c = make_consts(nullptr, n_slices);
+    const int64_t n = (shard_numel + kChunk - 1) / kChunk * kTilesPerChunk;
+    const int64_t in_flight = dtype_bytes(slice_dtype) * inflight_slices(n_slices, slice_dtype);
+    hipLaunchKernelGGL(pick_sqnorm_single(slice_dtype, n_slices, gen), dim3(static_cast<uint32_t>(n)),
+                       dim3(kBlock), lds_reserve(in_flight + 4), stream, T, c, partials);
+    if ((st = launch_status(who)) != FSDP_OK) return st;
+    // the same two fixed-order stages as a plan's: n partials -> up to
+    // kSumBlocks -> one
+    const int64_t per = (n + kSumBlocks - 1) / kSumBlocks;
+    const int64_t stage = (n + per - 1) / per;
+    double* second = partials + n;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(static_cast<uint32_t>(stage)), dim3(kBlock), 0, stream,
+                       static_cast<const double*>(partials), n, per, second);
+    if ((st = launch_status(who)) != FSDP_OK) return st;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
+                       static_cast<const double*>(second), stage, stage, sqnorm_out);
     return launch_status(who);
 }
 
