@@ -26,7 +26,8 @@
  *   - All arguments are checked on the host before any device work is queued.
  *   - Device pointers are plain HIP device addresses on the current device.
  *     The caller owns every buffer it passes; the library never allocates or
- *     frees them (a plan allocates only its own tables, see fsdp_mt_plan_create).
+ *     frees them (a plan allocates only its own tables, from the
+ *     stream-ordered allocator, see fsdp_mt_plan_create).
  *   - Work is queued on the caller's stream (NULL = the null stream) and is
  *     asynchronous; no call synchronises the host except fsdp_mt_plan_create.
  *   - Sizes and offsets are in elements unless a name says bytes.
@@ -36,9 +37,14 @@
  *   - Floating point: fp32 with IEEE-correct division and square root, no
  *     flush of denormals.  Results are deterministic run to run (no atomics).
  *   - Speed, not correctness: every call streams in 16-byte vectors when the
- *     fp32 buffers it writes back in place are 16-byte aligned; gradient
- *     slices and bf16/fp8 copies may start at any element (see also
- *     fsdp_mt_tensor).  Otherwise it runs element by element, bit-identical.
+ *     fp32 buffers it streams are 16-byte aligned: grad_shard_out for
+ *     fsdp_reduce_grad_shard and fsdp_reduce_sqnorm_noalloc; param_fp32,
+ *     exp_avg and exp_avg_sq for fsdp_adamw_shard_step; param_fp32 for
+ *     fsdp_cast_unshard_bf16; acc for fsdp_grad_accumulate; for a plan, the
+ *     rule given at fsdp_mt_tensor.  Gradient slices, the gradient read by
+ *     fsdp_adamw_shard_step, micro-batch gradients and bf16/fp8 copies may
+ *     start at any element.  Otherwise the call runs element by element,
+ *     bit-identical.
  *   - Resources: the streaming kernels run one wave64 per workgroup and,
  *     except the fp8 code pass, reserve up to 36 KB of LDS per workgroup that
  *     they never touch.  The reservation caps how many of their workgroups
@@ -170,7 +176,14 @@ int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t rank,
  * Required: all finite, lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps >= 0,
  * weight_decay >= 0, step >= 1 (else FSDP_E_ARG).  Derived scalars
  * (1 - lr*wd, lr/(1 - beta1^step), 1/sqrt(1 - beta2^step)) are computed on
- * the host in double and rounded to fp32. */
+ * the host in double and rounded to fp32, and reach the kernel by value.
+ * A launch captured into a HIP graph therefore keeps them as they were at
+ * capture: every replay applies the captured step's bias corrections and
+ * learning rate (a graph captured at step 3 and replayed at step 1000 steps
+ * 3.7x too far, with 1/sqrt(1 - beta2^3) = 18.3 where 1.0 is due), and
+ * nothing reports it.  To step a graph through t = 1, 2, ..., capture one
+ * graph per step value (the bias corrections settle after a few thousand
+ * steps) or make the step calls eagerly. */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
     int64_t step;
@@ -318,7 +331,9 @@ int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tenso
 /* One step over every shard of the plan: exactly one kernel launch on
  * `stream` (none for an empty plan), no host synchronisation.  The plan must
  * be used on the device it was made on (FSDP_E_STATE).  Two steps of one
- * plan on different streams without ordering between them race. */
+ * plan on different streams without ordering between them race.  Under HIP
+ * graph capture the launch is recorded with hp's derived scalars fixed (see
+ * fsdp_adamw_hparams). */
 int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, hipStream_t stream);
 
 /* ------------------------------------------------------------------ clipping */
@@ -492,8 +507,14 @@ int32_t fsdp_reduce_sqnorm_noalloc(float* grad_shard_out, double* sqnorm_out,
 /* Sizes of a plan (host only). */
 int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_info* info_out);
 
-/* Free a plan's device tables; waits for device work that may still read
- * them.  NULL is a no-op. */
+/* Free a plan's device tables.  Waits until the plan's last launch made
+ * outside a HIP graph capture has finished (its completion event is bound to
+ * that kernel), and for nothing else on the device: no device-wide
+ * synchronisation.  The tables come from the stream-ordered allocator and
+ * are freed in stream order after that wait.  Calls on one plan are ordered
+ * (they race otherwise), so the last launch finishing means all have.  A HIP
+ * graph holding launches of the plan must not be replayed once the plan is
+ * destroyed.  NULL is a no-op. */
 int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan);
 
 #ifdef __cplusplus

@@ -34,6 +34,7 @@
 // Floating point: fp32, FMA only where written (built with -ffp-contract=off),
 // IEEE-correct division and square root, denormals kept.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -120,6 +121,7 @@ constexpr int kTile = kBlock * kGroup;  // elements per workgroup
 constexpr int kTilesPerChunk = 8;
 constexpr int64_t kChunk = int64_t(kTilesPerChunk) * kTile;  // elements per chunk entry
 constexpr int kMaxSlices = 1024;
+constexpr int kMaxDevices = 64;         // devices whose per-device library state is tracked
 constexpr int kLdsPerCu = 160 * 1024;   // gfx950
 
 // Dynamic LDS that leaves room for `occ` workgroups per CU but not occ + 1.
@@ -1451,9 +1453,61 @@ struct fsdp_mt_plan {
     double* d_partials = nullptr;    // clipped steps: one sum of squares per workgroup,
                                      // then kSumBlocks second-stage sums
     fsdp::Footprint footprint;       // the shards' buffers, for checking the calls' other buffers
+    bool pooled = false;             // the device tables come from the stream-ordered allocator
+    hipEvent_t done = nullptr;       // completes with the plan's last launch outside a capture
 };
 
 namespace {
+
+// Whether work queued on `s` now would be captured into a HIP graph (or the
+// query fails, as it does for the null stream while another stream captures
+// globally: then it is treated as capturing).
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
+// Launch of a plan call.  The call's last launch carries the plan's
+// completion event, bound to the kernel's own completion (no further queue
+// entry), which fsdp_mt_plan_destroy waits on.  Launches that a HIP graph
+// captures carry none: the graph's replays are the caller's to order.
+template <typename K, typename... Args>
+void plan_launch(const fsdp_mt_plan* plan, bool last, K k, dim3 grid, dim3 block, size_t lds,
+                 hipStream_t stream, Args... args) {
+    if (last && plan->done && !capturing(stream))
+        hipExtLaunchKernelGGL(k, grid, block, static_cast<uint32_t>(lds), stream, nullptr, plan->done,
+                              0u, args...);
+    else
+        hipLaunchKernelGGL(k, grid, block, lds, stream, args...);
+}
+
+// A plan's device tables come from the stream-ordered allocator where the
+// device has one, so that destroying the plan frees them without the
+// device-wide synchronisation that hipFree performs.
+hipError_t plan_alloc(const fsdp_mt_plan* plan, void** p, size_t bytes, hipStream_t stream) {
+    return plan->pooled ? hipMallocAsync(p, bytes, stream) : hipMalloc(p, bytes);
+}
+
+// One non-blocking stream per device, made on the first plan destroyed there
+// and kept until the process ends: the stream-ordered frees go on it, after
+// the host has waited for the plan's last launch.
+std::mutex g_free_mu;
+hipStream_t g_free_stream[kMaxDevices] = {};
+
+hipError_t free_stream(int dev, hipStream_t* out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_free_mu);
+    if (!g_free_stream[dev]) {
+        const hipError_t e = hipStreamCreateWithFlags(&g_free_stream[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+    }
+    *out = g_free_stream[dev];
+    return hipSuccess;
+}
 
 // The plan exists and belongs to the current device.
 int32_t check_plan_device(const fsdp_mt_plan* plan, const char* who) {
@@ -1745,6 +1799,11 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
         const int32_t st = check_grid(n_chunks * kTilesPerChunk, who);
         if (st != FSDP_OK) return st;
     }
+    if (any_fp8) {
+        // the per-shard amax pass runs one kAmaxBlock-thread workgroup per shard
+        const int32_t st = check_grid(int64_t(n_tensors) * (kAmaxBlock / kBlock), who);
+        if (st != FSDP_OK) return st;
+    }
     std::vector<ChunkDesc> chunks;
     chunks.reserve(static_cast<size_t>(n_chunks));
     std::vector<ShardTiles> runs(static_cast<size_t>(n_tensors), ShardTiles{0, 0});
@@ -1781,19 +1840,25 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
                         std::any_of(descs.begin(), descs.end(), [](const TensorDesc& x) { return x.gen != 0; });
     plan->footprint = std::move(footprint);
     hipError_t e = hipGetDevice(&plan->device);
+    int pools = 0;
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&pools, hipDeviceAttributeMemoryPoolsSupported, plan->device);
+    plan->pooled = pools != 0;
+    if (e == hipSuccess && !chunks.empty()) e = hipEventCreateWithFlags(&plan->done, hipEventDisableTiming);
+    auto alloc = [&](auto** p, size_t bytes) {
+        return plan_alloc(plan, reinterpret_cast<void**>(p), bytes, stream);
+    };
     if (e == hipSuccess && any_fp8 && n_tensors > 0) {
-        e = hipMalloc(reinterpret_cast<void**>(&plan->d_shard_tiles), runs.size() * sizeof(ShardTiles));
+        e = alloc(&plan->d_shard_tiles, runs.size() * sizeof(ShardTiles));
         if (e == hipSuccess)
             e = hipMemcpyAsync(plan->d_shard_tiles, runs.data(), runs.size() * sizeof(ShardTiles),
                                hipMemcpyHostToDevice, stream);
         if (e == hipSuccess && !chunks.empty())
-            e = hipMalloc(reinterpret_cast<void**>(&plan->d_tile_amax),
-                          static_cast<size_t>(plan->n_blocks) * sizeof(uint32_t));
+            e = alloc(&plan->d_tile_amax, static_cast<size_t>(plan->n_blocks) * sizeof(uint32_t));
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
     }
     if (e == hipSuccess && !chunks.empty() && !table_host.empty()) {
-        e = hipMalloc(reinterpret_cast<void**>(&plan->d_slice_ptrs),
-                      table_host.size() * sizeof(const void*));
+        e = alloc(&plan->d_slice_ptrs, table_host.size() * sizeof(const void*));
         if (e == hipSuccess)
             e = hipMemcpyAsync(plan->d_slice_ptrs, table_host.data(),
                                table_host.size() * sizeof(const void*), hipMemcpyHostToDevice,
@@ -1802,12 +1867,10 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
             if (table_off[k] >= 0) descs[k].slice_ptrs = plan->d_slice_ptrs + table_off[k];
     }
     if (e == hipSuccess && !chunks.empty()) {
-        e = hipMalloc(reinterpret_cast<void**>(&plan->d_tensors), descs.size() * sizeof(TensorDesc));
-        if (e == hipSuccess)
-            e = hipMalloc(reinterpret_cast<void**>(&plan->d_chunks), chunks.size() * sizeof(ChunkDesc));
+        e = alloc(&plan->d_tensors, descs.size() * sizeof(TensorDesc));
+        if (e == hipSuccess) e = alloc(&plan->d_chunks, chunks.size() * sizeof(ChunkDesc));
         if (e == hipSuccess && all_grad_out)
-            e = hipMalloc(reinterpret_cast<void**>(&plan->d_partials),
-                          static_cast<size_t>(plan->n_blocks + kSumBlocks) * sizeof(double));
+            e = alloc(&plan->d_partials, static_cast<size_t>(plan->n_blocks + kSumBlocks) * sizeof(double));
         if (e == hipSuccess)
             e = hipMemcpyAsync(plan->d_tensors, descs.data(), descs.size() * sizeof(TensorDesc),
                                hipMemcpyHostToDevice, stream);
@@ -1817,6 +1880,9 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
     }
     if (e != hipSuccess) {
+        // uploads queued before the failure finish before their tables are freed
+        (void)hipStreamSynchronize(stream);
+        (void)hipGetLastError();
         fsdp_mt_plan_destroy(plan);
         return fail(FSDP_E_HIP, "%s: %s", who, hipGetErrorString(e));
     }
@@ -1834,8 +1900,8 @@ extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
     const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_general);
-    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
-                       lds_reserve(step_bytes(plan)), stream, plan->d_tensors, plan->d_chunks, c);
+    plan_launch(plan, true, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+                lds_reserve(step_bytes(plan)), stream, plan->d_tensors, plan->d_chunks, c);
     return launch_status(who);
 }
 
@@ -1858,18 +1924,17 @@ extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumul
         const StepConsts c = make_consts(nullptr, plan->n_slices);
         const ReduceStoreKernel k = pick_reduce_store(plan->slice_dtype, plan->n_slices, sq,
                                                       plan->any_general);
-        hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
-                           lds_reserve(slice_bytes(plan) + 4 + 4 * accumulate,
-                                       accumulate ? RS_INFLIGHT_KB_ACC : RS_INFLIGHT_KB), stream,
-                           plan->d_tensors, plan->d_chunks, c,
-                           accumulate, plan->d_partials);
+        plan_launch(plan, !sq, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+                    lds_reserve(slice_bytes(plan) + 4 + 4 * accumulate,
+                                accumulate ? RS_INFLIGHT_KB_ACC : RS_INFLIGHT_KB), stream,
+                    plan->d_tensors, plan->d_chunks, c, accumulate, plan->d_partials);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
     if (!sq) return FSDP_OK;
     if (plan->n_chunks == 0) {
         // nothing to sum: one workgroup over an empty range writes 0
-        hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
-                           static_cast<const double*>(nullptr), int64_t(0), int64_t(0), sqnorm_out);
+        plan_launch(plan, true, sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
+                    static_cast<const double*>(nullptr), int64_t(0), int64_t(0), sqnorm_out);
         return launch_status(who);
     }
     // two fixed-order stages: n_blocks partials -> up to kSumBlocks -> one
@@ -1880,8 +1945,8 @@ extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumul
     hipLaunchKernelGGL(sum_partials_kernel, dim3(static_cast<uint32_t>(stage)), dim3(kBlock), 0,
                        stream, static_cast<const double*>(plan->d_partials), n, per, second);
     if ((st = launch_status(who)) != FSDP_OK) return st;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
-                       static_cast<const double*>(second), stage, stage, sqnorm_out);
+    plan_launch(plan, true, sum_partials_kernel, dim3(1), dim3(kBlock), 0, stream,
+                static_cast<const double*>(second), stage, stage, sqnorm_out);
     return launch_status(who);
 }
 
@@ -1957,11 +2022,10 @@ extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hpa
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
-    hipLaunchKernelGGL(plan->any_general ? mt_scaled_step_kernel<true> : mt_scaled_step_kernel<false>,
-                       dim3(static_cast<uint32_t>(plan->n_blocks)),
-                       dim3(kBlock), lds_reserve(4 + 24 + 2 * plan->any_bf16), stream,
-                       plan->d_tensors, plan->d_chunks,
-                       c, grad_scale);
+    plan_launch(plan, true, plan->any_general ? mt_scaled_step_kernel<true> : mt_scaled_step_kernel<false>,
+                dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+                lds_reserve(4 + 24 + 2 * plan->any_bf16), stream, plan->d_tensors, plan->d_chunks, c,
+                grad_scale);
     return launch_status(who);
 }
 
@@ -1986,10 +2050,9 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
                            plan->d_chunks, c, plan->d_tile_amax);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
-    hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kAmaxBlock),
-                       0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
-                       static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds,
-                       amax_out);
+    plan_launch(plan, true, shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)),
+                dim3(kAmaxBlock), 0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
+                static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds, amax_out);
     return launch_status(who);
 }
 
@@ -2017,10 +2080,10 @@ static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int
         return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
-    hipLaunchKernelGGL(plan->any_general ? mt_cast_fp8_kernel<true> : mt_cast_fp8_kernel<false>,
-                       dim3(static_cast<uint32_t>(plan->n_chunks * (kTilesPerChunk / RS_CAST_TILES))),
-                       dim3(kBlock), 0, stream, plan->d_tensors,
-                       plan->d_chunks, amax_ranks, n_ranks, plan->n_tensors, scale_out);
+    plan_launch(plan, true, plan->any_general ? mt_cast_fp8_kernel<true> : mt_cast_fp8_kernel<false>,
+                dim3(static_cast<uint32_t>(plan->n_chunks * (kTilesPerChunk / RS_CAST_TILES))),
+                dim3(kBlock), 0, stream, plan->d_tensors, plan->d_chunks, amax_ranks, n_ranks,
+                plan->n_tensors, scale_out);
     return launch_status(who);
 }
 
@@ -2053,10 +2116,9 @@ static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
                            plan->d_chunks, c, scale_in, plan->d_tile_amax);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
-    hipLaunchKernelGGL(shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)), dim3(kAmaxBlock),
-                       0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
-                       static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds,
-                       amax_out);
+    plan_launch(plan, true, shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)),
+                dim3(kAmaxBlock), 0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
+                static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds, amax_out);
     return launch_status(who);
 }
 
@@ -2077,7 +2139,6 @@ constexpr int64_t kNoAllocMaxBlocks = (kScratchDoubles - kSumBlocks) / kTilesPer
 static_assert(FSDP_NOALLOC_MAX_NUMEL == kNoAllocMaxBlocks / kTilesPerChunk * kChunk,
               "the header's size limit is what the scratch array holds");
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 double* g_scratch_dev[kMaxDevices] = {};  // the array's address on each device, once looked up
 
@@ -2261,15 +2322,30 @@ extern "C" int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_
 extern "C" int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan) {
     if (!plan) return FSDP_OK;
     hipError_t e = hipSuccess;
-    if (plan->d_tensors || plan->d_chunks || plan->d_partials || plan->d_tile_amax ||
-        plan->d_shard_tiles || plan->d_slice_ptrs) {
-        e = hipDeviceSynchronize();
-        if (plan->d_slice_ptrs) (void)hipFree(plan->d_slice_ptrs);
-        if (plan->d_tensors) (void)hipFree(plan->d_tensors);
-        if (plan->d_chunks) (void)hipFree(plan->d_chunks);
-        if (plan->d_partials) (void)hipFree(plan->d_partials);
-        if (plan->d_tile_amax) (void)hipFree(plan->d_tile_amax);
-        if (plan->d_shard_tiles) (void)hipFree(plan->d_shard_tiles);
+    // the plan's last launch (outside a graph capture) has finished; other
+    // work on the device is not waited for
+    if (plan->done) {
+        e = hipEventSynchronize(plan->done);
+        const hipError_t d = hipEventDestroy(plan->done);
+        if (e == hipSuccess) e = d;
+    }
+    void* const bufs[] = {plan->d_slice_ptrs, plan->d_tensors, plan->d_chunks, plan->d_partials,
+                          plan->d_tile_amax, plan->d_shard_tiles};
+    const bool any = std::any_of(std::begin(bufs), std::end(bufs), [](void* b) { return b != nullptr; });
+    if (any && plan->pooled) {
+        // stream-ordered frees on the plan's device, which wait for nothing
+        int cur = -1;
+        hipError_t d = hipGetDevice(&cur);
+        if (d == hipSuccess && cur != plan->device) d = hipSetDevice(plan->device);
+        hipStream_t fs = nullptr;
+        if (d == hipSuccess) d = free_stream(plan->device, &fs);
+        for (void* b : bufs)
+            if (b && d == hipSuccess) d = hipFreeAsync(b, fs);
+        if (cur >= 0 && cur != plan->device) (void)hipSetDevice(cur);
+        if (e == hipSuccess) e = d;
+    } else if (any) {
+        for (void* b : bufs)
+            if (b) (void)hipFree(b);
     }
     delete plan;
     if (e != hipSuccess) return fail(FSDP_E_HIP, "fsdp_mt_plan_destroy: %s", hipGetErrorString(e));

@@ -13,6 +13,11 @@ Each graph is replayed several times, with eager work (fresh gradients) and
 synchronisations between the replays.  After every replay, the state and
 outputs must equal a twin state driven by the same calls made eagerly.  The
 eager calls are themselves checked against the oracle in the other GPU tests.
+
+The step count and learning rate reach the kernels by value, so a captured
+step keeps the ones it was captured with: every replay equals an eager step
+at the captured count, and differs from one at the advancing count (the
+limitation the header states at fsdp_adamw_hparams).
 """
 
 import pytest
@@ -196,3 +201,33 @@ def test_general_plan_graph(gpu):
          init={"scale": 448.0 / 0.05})
     a.close()
     b.close()
+
+
+def test_graph_replays_keep_the_captured_step_count(gpu):
+    """Captured at t=3 and replayed four times: each replay equals an eager
+    step at t=3, not one at t = 3, 4, 5, 6 -- the bias corrections and the
+    learning rate are fixed at capture."""
+    w = WORKLOADS[3]
+    kw = dict(bf16_out=True)
+    fixed, graphed, advancing = (RankState(w, 0, gpu, **kw) for _ in range(3))
+    for st in (fixed, graphed, advancing):
+        st.make_plan(with_grad_out=False)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.plan.step(w.hparams, 3)
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        for st in (fixed, graphed, advancing):
+            st.load_grads(rep + 1)
+        fixed.plan.step(w.hparams, 3)
+        advancing.plan.step(w.hparams, 3 + rep)
+        g.replay()
+        torch.cuda.synchronize()
+        _same(fixed, graphed, f"replay {rep} against eager t=3")
+        if rep > 0:
+            assert not torch.equal(_bits(advancing.master), _bits(graphed.master)), \
+                f"replay {rep} should not equal an eager step at t={3 + rep}"
+    del g
+    for st in (fixed, graphed, advancing):
+        st.close()

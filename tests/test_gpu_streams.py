@@ -86,3 +86,45 @@ def test_two_plans_on_two_streams(gpu):
             assert np.array_equal(x, y), f"{name}: output {i} differs from the sequential run"
     a.close()
     b.close()
+
+
+def _sleep_cycles_per_ms(gpu):
+    """Rate of torch.cuda._sleep's counter, measured (its clock is the
+    device's, not fixed)."""
+    s = torch.cuda.current_stream(gpu)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)          # first launch outside the measurement
+    e0.record(s)
+    torch.cuda._sleep(1_000_000)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+
+
+def test_destroy_waits_for_its_plan_only(gpu):
+    """fsdp_mt_plan_destroy returns once the plan's last launch has finished
+    and waits for nothing else: a step queued on one stream behind a 100 ms
+    delay has finished when destroy returns, while a 1.5 s delay on another
+    stream, queued first, is still running."""
+    import time
+
+    rate = _sleep_cycles_per_ms(gpu)
+    a = PlanSet(gpu, 300)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(device=gpu), torch.cuda.Stream(device=gpu)
+    e_step, e_other = torch.cuda.Event(), torch.cuda.Event()
+    with torch.cuda.stream(s2):
+        torch.cuda._sleep(int(1500 * rate))
+        e_other.record(s2)
+    with torch.cuda.stream(s1):
+        torch.cuda._sleep(int(100 * rate))
+    a.plan.step(HPARAMS, 1, s1.cuda_stream)
+    e_step.record(s1)
+    t0 = time.perf_counter()
+    a.close()
+    waited = time.perf_counter() - t0
+    step_done, other_done = e_step.query(), e_other.query()
+    torch.cuda.synchronize()
+    assert step_done, "destroy returned before the plan's step had finished"
+    assert not other_done, f"destroy waited for another stream's work ({waited:.3f} s)"
+    assert waited < 1.2, waited
