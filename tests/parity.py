@@ -12,12 +12,13 @@ where s_x is the magnitude of the terms that form x, so that cancellation
     s_v = beta2*v + (1-beta2)*s_G^2                  second moment
     s_p = |p|*(1-lr*wd) + lr*(s_m/bc1)/(sqrt(vhat)+eps) + d_p   parameter
 
-d_p carries the allowed error of G through the denominator: G's allowance
-moves vhat by dvhat = (1-beta2)*2*|G|*s_G/bc2, and the update
-lr*mhat/(sqrt(vhat)+eps) by lr*|mhat|*dvhat / (2*sqrt(vhat)*(sqrt(vhat)+eps)^2)
-(first order).  It matters only where G cancels and v is tiny beside m, so
-that the update hangs on a few bits of G; elsewhere it is about one more
-update's worth.
+d_p (only with ``widen=True``) carries the allowed error of G through the
+denominator: G's allowance moves vhat by dvhat = (1-beta2)*2*|G|*s_G/bc2, and
+the update lr*mhat/(sqrt(vhat)+eps) by
+lr*|mhat|*dvhat / (2*sqrt(vhat)*(sqrt(vhat)+eps)^2) (first order).  It
+matters where G cancels across many slices and v is tiny beside m, so that
+the update hangs on a few bits of G: the tests that draw N = 33 slices or a
+random N widen the floor with it; every other case is judged without it.
 
 The inputs of the oracle are the GPU's own state before the step, widened
 exactly (per-step resynchronisation), so one step's rounding is judged.
@@ -65,7 +66,7 @@ def _denominator_term(ref, sl, sG, hp, t):
     return np.where(sq > 0, d, 0.0)
 
 
-def floors(p, m, v, sl, ref, hp, t):
+def floors(p, m, v, sl, ref, hp, t, widen=False):
     lr, b1, b2, eps, wd = hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"]
     sG = np.mean(np.abs(sl), axis=0) if sl.shape[0] else np.zeros(0)
     s_m = b1 * np.abs(m) + (1 - b1) * sG
@@ -73,12 +74,13 @@ def floors(p, m, v, sl, ref, hp, t):
     bc1 = 1 - b1 ** t
     bc2 = 1 - b2 ** t
     vhat = ref["v"] / bc2
-    s_p = (np.abs(p) * (1 - lr * wd) + lr * (s_m / bc1) / (np.sqrt(vhat) + eps)
-           + _denominator_term(ref, sl, sG, hp, t))
+    s_p = np.abs(p) * (1 - lr * wd) + lr * (s_m / bc1) / (np.sqrt(vhat) + eps)
+    if widen:
+        s_p = s_p + _denominator_term(ref, sl, sG, hp, t)
     return {"g": sG, "m": s_m, "v": s_v, "p": s_p}
 
 
-def free_floors(prev, sl, ref, hp, t):
+def free_floors(prev, sl, ref, hp, t, widen=False):
     """Floors for a free-running comparison: the term magnitudes carried along
     the whole trajectory, so that slack allowed at an earlier step (e.g. an
     element whose mean gradient cancelled to about eps) is still allowed.
@@ -88,8 +90,9 @@ def free_floors(prev, sl, ref, hp, t):
     s_m = b1 * prev["m"] + (1 - b1) * sG
     s_v = b2 * prev["v"] + (1 - b2) * sG * sG
     vhat = ref["v"] / (1 - b2 ** t)
-    s_p = (prev["p"] * (1 - lr * wd) + lr * (s_m / (1 - b1 ** t)) / (np.sqrt(vhat) + eps)
-           + _denominator_term(ref, sl, sG, hp, t))
+    s_p = prev["p"] * (1 - lr * wd) + lr * (s_m / (1 - b1 ** t)) / (np.sqrt(vhat) + eps)
+    if widen:
+        s_p = s_p + _denominator_term(ref, sl, sG, hp, t)
     return {"g": sG, "m": s_m, "v": s_v, "p": s_p}
 
 
@@ -116,6 +119,30 @@ def assert_close(name, got, ref, floor, tol=TOL, abs_tol=0.0):
     big = np.abs(ref[ok]) >= 1e-3 * floor[ok]
     rel = err[big] / np.maximum(np.abs(ref[ok][big]), 1e-300)
     return float(rel.max()) if rel.size else 0.0
+
+
+def mixed_ratio(got, ref, floor, tol=TOL):
+    """Largest err / (tol * max(|ref|, floor)) over the finite results: the
+    share of the mixed allowance the worst element uses (<= 1 passes)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    ok = np.isfinite(ref) & np.isfinite(got)
+    if not ok.any():
+        return 0.0
+    lim = tol * np.maximum(np.abs(ref[ok]), floor[ok])
+    err = np.abs(got[ok] - ref[ok])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(lim > 0, err / lim, np.where(err > 0, np.inf, 0.0))
+    return float(r.max())
+
+
+def literal_count(got, ref, tol=TOL):
+    """Finite results outside the literal relative bound |err| <= tol*|ref|
+    (those the mixed criterion admits through its floor)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    ok = np.isfinite(ref)
+    return int(np.count_nonzero(np.abs(got[ok] - ref[ok]) > tol * np.abs(ref[ok])))
 
 
 def check_bf16(name, got_bits, gpu_p, ref_p, floor_p, tol=TOL):
