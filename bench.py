@@ -13,7 +13,10 @@ Default workload: the 7B model's rank shard at N=8 (291 Shard(0) shards,
 
 Prints ONE JSON line: params/s as ``value``, HBM GB/s, the roofline fraction
 of the fused kernel against the 8 TB/s HBM3E peak (kernel time from HIP events
-on the launch stream), and the CPU oracle timed on a bounded sample of the
+on the launch stream), the other paths on the same state (clipped step, fp8
+copy, gradient accumulation, slice tables, the unfused chain), the other
+workloads timed the same way (``configs``: the 128 MiB unit, the Llama-7B
+block and the 70B shard), and the CPU oracle timed on one full step of the
 same workload on this host's cores.
 """
 
@@ -71,58 +74,136 @@ def measured_traffic(workload, launches_numel):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(st, t, min_seconds=10.0):
-    """The oracle (float64 NumPy), as it stands, on a bounded sample of the
-    workload: the rank's first shard(s), about 16M params, split across this
-    host's cores with a thread pool (NumPy releases the GIL inside its array
-    loops).  Consecutive steps run on the sample until at least
-    ``min_seconds`` of wall time have passed."""
+def host_cores():
+    """Cores this process may use: the affinity mask, bounded by the cgroup's
+    CPU quota where one is set (a one-GPU machine grants 16)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()
+        if quota != "max":
+            n = min(n, max(1, int(quota) // int(period)))
+    except (OSError, ValueError):
+        pass
+    return max(1, n)
+
+
+def _cpu_inputs(rng, n, w):
+    """One shard's oracle inputs on the host, drawn with the workload's
+    distributions: fp32 state (master ~ N(0, 0.02), moments of a running
+    optimizer) widened to float64, and N slices as raw bf16 bits (the top
+    half of each fp32 draw) or fp32."""
     import numpy as np
-    import torch
-    from concurrent.futures import ThreadPoolExecutor
+    p = (rng.standard_normal(n, dtype=np.float32) * np.float32(0.02)).astype(np.float64)
+    m = (rng.standard_normal(n, dtype=np.float32) * np.float32(1e-4)).astype(np.float64)
+    v = (rng.standard_normal(n, dtype=np.float32) ** 2 * np.float32(1e-8)).astype(np.float64)
+    x = rng.standard_normal((w["n_slices"], n), dtype=np.float32) * np.float32(w["sigma"])
+    if w["outlier_frac"] > 0:
+        x = np.where(rng.random((w["n_slices"], n), dtype=np.float32) < w["outlier_frac"],
+                     x * np.float32(w["outlier_scale"]), x)
+    raw = (x.view(np.uint32) >> 16).astype(np.uint16) if w["bf16"] else x
+    return p, m, v, raw
 
+
+def _cpu_oracle_step(inputs, w, t):
+    """The oracle as the parity tests call it: the slices widened exactly,
+    then oracle.step.rank_step over the shard."""
     from oracle import step as O
+    p, m, v, raw = inputs
+    sl = O.widen_bf16_bits(raw) if w["bf16"] else O.widen_f32(raw)
+    O.rank_step(p, m, v, sl, p.size, t, w["hparams"])
+    return p.size
 
-    w = st.w
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    n = 0
-    names = []
-    for (off, length, held, _), p in zip(st.segments, w.params):
-        if n + length > 16_500_000 and n > 0:
-            break
-        n += length
-        names.append(p.name)
-    p = st.master[:n].double().cpu().numpy()
-    m = st.exp_avg[:n].double().cpu().numpy()
-    v = st.exp_avg_sq[:n].double().cpu().numpy()
-    if w.slice_dtype == "bf16":
-        raw = st.slices[:, :n].view(torch.int16).cpu().numpy().view(np.uint16)
-    else:
-        raw = st.slices[:, :n].cpu().numpy()
-    bounds = np.linspace(0, n, cores + 1).astype(np.int64)
-    state = [(p[a:b], m[a:b], v[a:b]) for a, b in zip(bounds[:-1], bounds[1:])]
 
-    def work(i, step):
-        a, b = bounds[i], bounds[i + 1]
-        sl = O.widen_bf16_bits(raw[:, a:b]) if w.slice_dtype == "bf16" else O.widen_f32(raw[:, a:b])
-        r = O.rank_step(*state[i], sl, b - a, step, w.hparams)
-        state[i] = (r["p"], r["m"], r["v"])
-        return b - a
+def _cpu_worker(shards, w, t, seed, ready, go, out):
+    """One process of the CPU baseline: draws its shards' inputs (untimed),
+    says so, waits for the start, then runs the oracle over its shards and
+    reports the parameters done."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    inputs = [_cpu_inputs(rng, n, w) for n in shards]
+    ready.put(1)
+    go.wait()
+    done = sum(_cpu_oracle_step(x, w, t) for x in inputs)
+    out.put(done)
 
-    done = 0
-    steps = 0
-    with ThreadPoolExecutor(max_workers=cores) as ex:
+
+def _collect(q, n, procs, limit_s):
+    """n items from q, failing early if a worker process has died."""
+    import queue
+    got, deadline = [], time.time() + limit_s
+    while len(got) < n:
+        try:
+            got.append(q.get(timeout=2))
+        except queue.Empty:
+            dead = [p.exitcode for p in procs if p.exitcode not in (None, 0)]
+            if dead or time.time() > deadline:
+                raise RuntimeError(f"cpu baseline: worker exit codes {dead}" if dead else
+                                   "cpu baseline: timed out")
+    return got
+
+
+def _workload_spec(w):
+    return {"n_slices": w.n_slices, "bf16": w.slice_dtype == "bf16", "sigma": w.grad_sigma,
+            "outlier_frac": w.outlier_frac, "outlier_scale": w.outlier_scale, "hparams": dict(w.hparams)}
+
+
+def cpu_baseline(w, segments, total, t):
+    """The oracle (float64 NumPy), as it stands, timed on this host:
+    one full step of the rank's workload, every shard, chunked by shard
+    over one spawned process per core (largest shards first, each to the
+    least-loaded process), wall time from the moment every process holds its
+    inputs to the last one's finish; and one step of the Llama-7B block on a
+    single core, for a per-core figure."""
+    import multiprocessing as mp
+
+    from rank_step_amd.workloads import WORKLOADS
+
+    cores = host_cores()
+    sizes = sorted((length for length, _ in segments), reverse=True)
+    share = [[] for _ in range(cores)]
+    load = [0] * cores
+    for n in sizes:
+        i = load.index(min(load))
+        share[i].append(n)
+        load[i] += n
+    spec = _workload_spec(w)
+    ctx = mp.get_context("spawn")          # fresh interpreters: nothing of this process's GPU state
+    ready, go, out = ctx.Queue(), ctx.Event(), ctx.Queue()
+    procs = [ctx.Process(target=_cpu_worker, args=(share[i], spec, t, 1000 + i, ready, go, out))
+             for i in range(cores)]
+    for p in procs:
+        p.start()
+    try:
+        _collect(ready, cores, procs, 600)     # every process holds its inputs
         t0 = time.perf_counter()
-        while True:
-            done += sum(ex.map(lambda i: work(i, t + steps), range(cores)))
-            steps += 1
-            dt = time.perf_counter() - t0
-            if dt >= min_seconds:
-                break
-    return {"value": done / dt, "unit": "params/s", "cores": cores, "kind": "oracle",
-            "sample": f"{steps} consecutive steps of the float64 oracle on the rank's first "
-                      f"{len(names)} shard(s) ({', '.join(names)}: {n:,} params, {w.n_slices} "
-                      f"{w.slice_dtype} gradient slices each), {dt:.1f} s wall on {cores} threads"}
+        go.set()
+        done = sum(_collect(out, cores, procs, 900))
+        wall = time.perf_counter() - t0
+    finally:
+        for p in procs:
+            p.join(timeout=60)
+            if p.is_alive():
+                p.kill()
+    assert done == total, (done, total)
+    # one core: the Llama-7B block's step (every dim 0 divides by its N = 8)
+    import numpy as np
+    wb = WORKLOADS[3]
+    rng = np.random.default_rng(7)
+    block_shards = [p.numel // wb.world_size for p in wb.params]
+    inputs = [_cpu_inputs(rng, n, _workload_spec(wb)) for n in block_shards]
+    t1 = time.perf_counter()
+    n1 = sum(_cpu_oracle_step(x, _workload_spec(wb), t) for x in inputs)
+    one = time.perf_counter() - t1
+    return {"value": total / wall, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "sample": f"one full step of the {w.name} rank shard: all {len(sizes)} shards, "
+                      f"{total:,} params, {w.n_slices} {w.slice_dtype} gradient slices each, "
+                      f"chunked by shard over {cores} spawned processes (one per core of this "
+                      f"host's {len(os.sched_getaffinity(0))}-core affinity mask); inputs drawn on "
+                      f"the host with the workload's distributions; {wall:.1f} s wall",
+            "seconds": wall,
+            "single_core": {"workload": wb.name, "params": n1, "seconds": one,
+                            "params_per_s": n1 / one}}
 
 
 def clipped_step(st, stream, args, t0):
@@ -381,67 +462,18 @@ def unfused_chain(st, stream, args, t0):
                                         "hbm_gb_s": bpp * st.total / ms_whole / 1e6}}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama7b_full_n8", choices=sorted(WORKLOAD_BY_NAME))
-    ap.add_argument("--no-cpu-baseline", action="store_true",
-                    help="skip the CPU oracle timing (e.g. under a profiler)")
-    ap.add_argument("--clip", type=float, default=1.0, metavar="MAX_NORM",
-                    help="also time the clipped step (global grad-norm clipping) with this max_norm")
-    ap.add_argument("--no-clip", dest="clip", action="store_const", const=None,
-                    help="do not time the clipped step")
-    ap.add_argument("--no-chain", action="store_true",
-                    help="do not time the unfused three-call chain")
-    ap.add_argument("--no-table", action="store_true",
-                    help="do not time the step with slices read through tables of pointers")
-    ap.add_argument("--no-fp8", action="store_true",
-                    help="do not time the step with the fp8 all-gather copy")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="instead of the step, run torch copies of MIB MiB (counter calibration)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
-              "(each rank's step is independent of the others; one GPU shows one rank's share)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def time_fused(w, dev, stream, args, keep=False, **state_kw):
+    """Plan the rank's shards of workload ``w`` and time K fused steps
+    (``fsdp_mt_step``, one launch each) back to back between two events on
+    the launch stream, after W warm-up steps; then K more with an event
+    between consecutive steps for the spread.  Workloads whose step moves
+    less than ROTATE_BYTES rotate through copies of the rank's state.  With
+    ``keep`` the first copy stays open for the other legs."""
     import torch
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
-
-    if args.calibrate_copy:
-        n = args.calibrate_copy * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        for _ in range(args.warmup):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            b.copy_(a)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
-                          "ms_per_copy": ms, "gb_s": 8 * n / ms / 1e6}), flush=True)
-        return
-
     from rank_step_amd.state import RankState
-    from rank_step_amd.workloads import WORKLOADS
 
-    w = WORKLOADS[WORKLOAD_BY_NAME[args.workload]]
-    bf16_out = w.bf16_out
-    st = RankState(w, 0, dev, bf16_out=bf16_out, grad_out=args.clip is not None,
-                   fp8_out=not args.no_fp8)
+    st = RankState(w, 0, dev, bf16_out=w.bf16_out, **state_kw)
     st.load_grads(1)
     # plan creation: once per wrap, on the host (layout of the chunk and
     # descriptor tables, argument and alias checks, one upload)
@@ -449,20 +481,19 @@ def main():
     p0 = time.perf_counter()
     st.make_plan(stream, with_grad_out=False, with_fp8=False)
     plan_s = time.perf_counter() - p0
-    info = st.plan.info()
     total = st.total
-    bpp = bytes_per_param(w, bf16_out)
-
-    t = 0
+    bpp = bytes_per_param(w, w.bf16_out)
     # copies of the state to rotate through (1: the workload is large enough)
     n_copies = min(MAX_COPIES, max(1, -(-ROTATE_BYTES // (bpp * total)) + 1)) \
         if bpp * total < ROTATE_BYTES else 1
     copies = [st]
     for _ in range(n_copies - 1):
-        c = RankState(w, 0, dev, bf16_out=bf16_out)
+        c = RankState(w, 0, dev, bf16_out=w.bf16_out)
         c.load_grads(1)
         c.make_plan(stream, with_grad_out=False, with_fp8=False)
         copies.append(c)
+    torch.cuda.synchronize()
+    t = 0
     # warm-up: W steps, and at least one on every copy
     for i in range(max(args.warmup, n_copies) if n_copies > 1 else args.warmup):
         t += 1
@@ -491,22 +522,116 @@ def main():
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    for c in copies[1:]:
+    info = st.plan.info()
+    for c in copies[0 if not keep else 1:]:
         c.close()
-    del copies[1:]
-    sec = ms / 1e3
-    params_s = total / sec
-    gbs = bpp * total / sec / 1e9
+    gbs = bpp * total / (ms / 1e3) / 1e9
+    return {
+        "state": st if keep else None,
+        "t": t,
+        "ms_per_step": ms,
+        "params_per_s": total / (ms / 1e3),
+        "hbm_gb_s": gbs,
+        "frac": gbs / HBM_PEAK_GBS,
+        "bytes_per_param": bpp,
+        "local_params": total,
+        "shards": info["n_tensors"],
+        "launch": {"workgroups": info["n_blocks"], "chunks": info["n_chunks"],
+                   "chunk_numel": info["chunk_numel"]},
+        "per_step_ms": {"median": per_step[len(per_step) // 2],
+                        "p95": per_step[min(len(per_step) - 1, (95 * len(per_step)) // 100)],
+                        "min": per_step[0], "max": per_step[-1],
+                        "from": "a second pass of K steps with an event between consecutive steps"},
+        "host_wall_s_timed": wall,
+        "plan_create_ms": plan_s * 1e3,
+        "timing": ("steps back to back" if n_copies == 1 else
+                   f"steps back to back, rotating through {n_copies} copies of the rank's "
+                   f"state ({n_copies * bpp * total / 1e9:.2f} GB) so that none finds its "
+                   f"data in the {INFINITY_CACHE_BYTES >> 20} MB Infinity Cache"),
+    }
 
-    traffic = measured_traffic(w.name, total)
+
+# the other workloads timed in the same run (their own plans, one after
+# another once the headline's buffers are freed)
+OTHER_CONFIGS = ("mlp128m_flat_n4", "llama7b_block_n8", "llama70b_full_n32")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_full_n8", choices=sorted(WORKLOAD_BY_NAME))
+    ap.add_argument("--configs", default=",".join(OTHER_CONFIGS),
+                    help="comma-separated other workloads to time after the headline ('' for none)")
+    ap.add_argument("--stream", choices=("default", "own"), default="default",
+                    help="launch on torch's default stream or on a stream of its own")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle timing (e.g. under a profiler)")
+    ap.add_argument("--clip", type=float, default=1.0, metavar="MAX_NORM",
+                    help="also time the clipped step (global grad-norm clipping) with this max_norm")
+    ap.add_argument("--no-clip", dest="clip", action="store_const", const=None,
+                    help="do not time the clipped step")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="do not time the unfused three-call chain")
+    ap.add_argument("--no-table", action="store_true",
+                    help="do not time the step with slices read through tables of pointers")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="do not time the step with the fp8 all-gather copy")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the step, run torch copies of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
+              "(each rank's step is independent of the others; one GPU shows one rank's share)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.stream == "own":
+        torch.cuda.set_stream(torch.cuda.Stream(dev))
+    stream = torch.cuda.current_stream(dev)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(args.warmup):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                          "ms_per_copy": ms, "gb_s": 8 * n / ms / 1e6}), flush=True)
+        return
+
+    from rank_step_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[WORKLOAD_BY_NAME[args.workload]]
+    r = time_fused(w, dev, stream, args, keep=True, grad_out=args.clip is not None,
+                   fp8_out=not args.no_fp8)
+    st = r.pop("state")
+    t = r["t"]
+    traffic = measured_traffic(w.name, st.total)
     out = {
         "metric": METRIC,
-        "value": params_s,
+        "value": r["params_per_s"],
         "unit": "params/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -517,33 +642,27 @@ def main():
             "layout": w.mode,
             "world_size": w.world_size,
             "rank": 0,
-            "local_params": total,
-            "shards": info["n_tensors"],
+            "local_params": st.total,
+            "shards": r["shards"],
             "grad_slices": f"{w.n_slices} x {w.slice_dtype}",
             "state": "fp32 master + exp_avg + exp_avg_sq" if w.has_master else "fp32 param + exp_avg + exp_avg_sq",
-            "bf16_out": bf16_out,
-            "bytes_per_param": bpp,
-            "launch": {"workgroups": info["n_blocks"], "chunks": info["n_chunks"],
-                       "chunk_numel": info["chunk_numel"]},
-            "timing": ("steps back to back" if n_copies == 1 else
-                       f"steps back to back, rotating through {n_copies} copies of the rank's "
-                       f"state ({n_copies * bpp * total / 1e9:.2f} GB) so that none finds its "
-                       f"data in the {INFINITY_CACHE_BYTES >> 20} MB Infinity Cache"),
+            "bf16_out": w.bf16_out,
+            "bytes_per_param": r["bytes_per_param"],
+            "launch": r["launch"],
+            "stream": "torch's default stream" if args.stream == "default" else "a stream of its own",
+            "timing": r["timing"],
         },
-        "hbm_gb_s": gbs,
-        "hbm_frac_of_peak": gbs / HBM_PEAK_GBS,
-        "per_step_ms": {"median": per_step[len(per_step) // 2],
-                        "p95": per_step[min(len(per_step) - 1, (95 * len(per_step)) // 100)],
-                        "min": per_step[0], "max": per_step[-1],
-                        "from": "a second pass of K steps with an event between consecutive steps"},
-        "host_wall_s_timed": wall,
-        "plan_create_ms": plan_s * 1e3,
+        "hbm_gb_s": r["hbm_gb_s"],
+        "hbm_frac_of_peak": r["frac"],
+        "per_step_ms": r["per_step_ms"],
+        "host_wall_s_timed": r["host_wall_s_timed"],
+        "plan_create_ms": r["plan_create_ms"],
         "roofline": {
             "bound": "hbm",
-            "achieved": gbs,
+            "achieved": r["hbm_gb_s"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": gbs / HBM_PEAK_GBS,
+            "frac": r["frac"],
             "traffic": traffic,
         },
     }
@@ -557,9 +676,24 @@ def main():
         out["slice_table_step"] = slice_table_step(st, stream, args, t)
     if not args.no_chain:
         out["unfused_chain"] = unfused_chain(st, stream, args, t)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(st, t + 1)
+    segments = [(length, held) for _, length, held, _ in st.segments]
+    total = st.total
     st.close()
+    del st
+    torch.cuda.empty_cache()
+    others = [c for c in args.configs.split(",") if c and c != w.name]
+    if others:
+        out["configs"] = {}
+        for name in others:
+            if name not in WORKLOAD_BY_NAME:
+                raise SystemExit(f"bench.py: unknown workload {name!r} in --configs")
+            rc = time_fused(WORKLOADS[WORKLOAD_BY_NAME[name]], dev, stream, args)
+            rc.pop("state")
+            rc.pop("t")
+            out["configs"][name] = rc
+            torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, segments, total, t + 1)
     print(json.dumps(out), flush=True)
 
 
