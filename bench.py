@@ -39,6 +39,8 @@ HBM_PEAK_GBS = 8000.0
 INFINITY_CACHE_BYTES = 256 << 20
 ROTATE_BYTES = 16 * INFINITY_CACHE_BYTES
 MAX_COPIES = 64
+# The warm-up runs at least this long (seconds of steps)
+SETTLE_S = 0.3
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["rank_step_amd/csrc/rank_step.hip"]
 WORKLOAD_BY_NAME = {"llama7b_full_n8": 4, "llama7b_block_n8": 3, "mlp128m_flat_n4": 2,
@@ -360,7 +362,7 @@ def slice_table_step(st, stream, args, t0):
         d = dict(d)
         d.pop("grad_slices")
         d.pop("slice_stride")
-        d["grad_slice_ptrs"] = [base + es * (q * st.total + off) for q in range(w.n_slices)]
+        d["grad_slice_ptrs"] = [base + es * (q * st.slice_stride + off) for q in range(w.n_slices)]
         recs.append(d)
     plan = B.MtPlan(recs, w.n_slices, w.slice_dtype, stream)
     t = t0
@@ -438,7 +440,7 @@ def unfused_chain(st, stream, args, t0):
     n_all = st.total
 
     def whole(t):
-        B.fsdp_reduce_grad_shard(gp, d0["grad_slices"], w.slice_dtype, st.total, w.n_slices,
+        B.fsdp_reduce_grad_shard(gp, d0["grad_slices"], w.slice_dtype, st.slice_stride, w.n_slices,
                                  n_all, n_all, stream)
         B.fsdp_adamw_shard_step(d0["param_fp32"], d0["exp_avg"], d0["exp_avg_sq"], gp, n_all, n_all,
                                 w.hparams, t, stream)
@@ -494,11 +496,20 @@ def time_fused(w, dev, stream, args, keep=False, **state_kw):
         copies.append(c)
     torch.cuda.synchronize()
     t = 0
-    # warm-up: W steps, and at least one on every copy
-    for i in range(max(args.warmup, n_copies) if n_copies > 1 else args.warmup):
+    # warm-up: W steps, at least one on every copy, and at least SETTLE_S of
+    # steps, so that a GPU that was idle has reached its working clocks (a
+    # box's first few hundred milliseconds of work can run several % slower)
+    n_warm = max(args.warmup, n_copies) if n_copies > 1 else args.warmup
+    w0 = time.perf_counter()
+    i = 0
+    while i < n_warm or time.perf_counter() - w0 < SETTLE_S:
         t += 1
         copies[i % n_copies].step(t, stream)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()         # the elapsed time is the GPU's
     torch.cuda.synchronize()
+    warm_steps = i
     # the timed region: K steps between two events on the launch stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -544,6 +555,7 @@ def time_fused(w, dev, stream, args, keep=False, **state_kw):
                         "from": "a second pass of K steps with an event between consecutive steps"},
         "host_wall_s_timed": wall,
         "plan_create_ms": plan_s * 1e3,
+        "warmup_steps_run": warm_steps,
         "timing": ("steps back to back" if n_copies == 1 else
                    f"steps back to back, rotating through {n_copies} copies of the rank's "
                    f"state ({n_copies * bpp * total / 1e9:.2f} GB) so that none finds its "
@@ -657,6 +669,7 @@ def main():
         "per_step_ms": r["per_step_ms"],
         "host_wall_s_timed": r["host_wall_s_timed"],
         "plan_create_ms": r["plan_create_ms"],
+        "warmup_steps_run": r["warmup_steps_run"],
         "roofline": {
             "bound": "hbm",
             "achieved": r["hbm_gb_s"],

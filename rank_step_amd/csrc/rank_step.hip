@@ -12,7 +12,9 @@
 // elements per access (one 16-byte load per fp32 array, one 8-byte load per
 // bf16 slice), and every load of the tile is issued before its first use.
 // Gradient slices and the low-precision copies are touched once and use
-// non-temporal accesses.  The vector path needs a shard's fp32 buffers
+// non-temporal accesses.  The fused step writes the updated state and the
+// bf16 copy through to memory, so that a launch does not end with dirty lines
+// in L2 for its release to write back.  The vector path needs a shard's fp32 buffers
 // 16-byte aligned; its slices and copies may start at any element (shifted
 // loads, stores in narrower pieces), and a plan splits a shard whose fp32
 // buffers all start off a boundary into a short head and an aligned rest.
@@ -83,6 +85,16 @@ namespace {
 // longer for the same bytes, so they need more resident waves: their budget.
 #ifndef RS_INFLIGHT_KB_FP8
 #define RS_INFLIGHT_KB_FP8 105
+#endif
+// The fused step's budgets under its write-through store policies (see
+// StorePolicy): write-through keeps the general budget; non-temporal
+// write-through, whose writes are close to half the traffic, needs fewer
+// resident waves (the 70B shard: 10.09 against 10.27 ms at 100 KB).
+#ifndef RS_INFLIGHT_KB_WT
+#define RS_INFLIGHT_KB_WT RS_INFLIGHT_KB
+#endif
+#ifndef RS_INFLIGHT_KB_NTWT
+#define RS_INFLIGHT_KB_NTWT 80
 #endif
 // The synchronised accumulation pass (reduce, then add into the stored
 // gradient) ran 7 % slower at 16 resident workgroups per CU than at 15, which
@@ -321,7 +333,9 @@ template <typename T> __device__ __forceinline__ void st_out(T* p, T x) { st_s<R
 // step over a 25 M-param block runs 2.5 % faster and the 7B shard about 2 %.
 // Non-temporal write-through (nt and sc1): the same, streamed; the better of
 // the two where writes are close to half the traffic (the 70B shard's
-// 14 of 30 bytes per param).
+// 14 of 30 bytes per param).  Under either, the bf16 copy is written through
+// and streamed as well (another 1 % on the 25 M-param block and the 70B
+// shard).
 enum StorePolicy : int { kStPlain = 0, kStWriteThrough = 1, kStNtWriteThrough = 2 };
 
 // A wave-uniform copy of a pointer that every active lane holds alike.
@@ -349,6 +363,16 @@ __device__ __forceinline__ void st_state_pol(float* lane_ptr, const f32x4& x) {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r,
                                                static_cast<int>(threadIdx.x) * 16, 0, kAux);
     }
+}
+
+// This lane's 4 bf16 of the all-gather copy at `lane_ptr` (the group's base
+// plus 4 * threadIdx.x elements, 8-byte aligned), written through to memory
+// and streamed (nt and sc1): under a write-through state policy the copy
+// leaves no dirty lines either.
+__device__ __forceinline__ void st_bf16_wt(uint16_t* lane_ptr, const u32x2& x) {
+    uint16_t* base = uniform_ptr(lane_ptr - threadIdx.x * kGroup);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, static_cast<int>(threadIdx.x) * 8, 0, 16 | 2);
 }
 
 // Sums and maxima over the wave in a fixed order (xor-shuffle steps); every
@@ -640,6 +664,7 @@ __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup]
     st_state_pol<POL>(T.v + e, s.v);
     if (T.out_bf16) {
         if constexpr (GEN) store_bf16_any(T.out_bf16 + e, pack_bf16(s.p), misalign(T.out_bf16, 8));
+        else if constexpr (POL != kStPlain) st_bf16_wt(T.out_bf16 + e, pack_bf16(s.p));
         else st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(s.p));
     }
     if constexpr (FP8) {
@@ -1967,8 +1992,11 @@ extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
     const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_general, plan->store_pol);
+    const int64_t budget = plan->store_pol == kStWriteThrough     ? RS_INFLIGHT_KB_WT
+                           : plan->store_pol == kStNtWriteThrough ? RS_INFLIGHT_KB_NTWT
+                                                                  : RS_INFLIGHT_KB;
     plan_launch(plan, true, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
-                lds_reserve(step_bytes(plan)), stream, plan->d_tensors, plan->d_chunks, c);
+                lds_reserve(step_bytes(plan), budget), stream, plan->d_tensors, plan->d_chunks, c);
     return launch_status(who);
 }
 

@@ -314,3 +314,62 @@ def test_fp8_codes_at_any_byte_alignment(gpu, f8_off):
     torch.cuda.synchronize()
     check("one-pass step", scales)
     plan.close()
+
+
+def _monotone_e4m3(c):
+    c = c.astype(np.int32)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def test_codes_against_the_double_trajectory(gpu):
+    """The codes against the oracle taken wholly in double precision: the
+    updated parameter from the oracle's step (per-step resync), each tensor's
+    amax and scale 448 / max(amax, 1e-12) in double, and the code
+    RNE_e4m3(clamp(p' * scale)) in double.  The GPU decides the same code in
+    fp32 from its own p' and scale, so the two may differ by one code step
+    where p' * scale lies within its fp32 allowance of a rounding boundary:
+    wherever that allowance is below half an fp8 step, a code must be within
+    one step of the double one.  Reported: the codes that differ at all."""
+    w = WORKLOADS[3]
+    st = RankState(w, 0, gpu, bf16_out=True, fp8_out=True)
+    st.make_plan()
+    n = len(st.segments)
+    amax = torch.zeros(n, dtype=torch.float32, device=gpu)
+    scale = torch.zeros(n, dtype=torch.float32, device=gpu)
+    differ = 0
+    judged_total = 0
+    for t in (1, 2, 3):
+        st.load_grads(t)
+        snap = (PR.f64(st.master), PR.f64(st.exp_avg), PR.f64(st.exp_avg_sq),
+                PR.widen_slices(st.slices, w.slice_dtype))
+        st.plan.step_amax(w.hparams, t, amax)
+        st.plan.cast_fp8(amax, 1, scale)
+        torch.cuda.synchronize()
+        codes = _codes(st.fp8)
+        am = amax.cpu().numpy()
+        for i, (off, length, held, _) in enumerate(st.segments):
+            a, b = off, off + held
+            p0, m0, v0, sl = (x[..., a:b] for x in snap)
+            ref = O.rank_step(p0, m0, v0, sl, held, t, w.hparams)
+            fl = PR.floors(p0, m0, v0, sl, ref, w.hparams, t)
+            amax_ref = float(np.max(np.abs(ref["p"])))
+            assert abs(float(am[i]) - amax_ref) <= PR.TOL * amax_ref, (i, float(am[i]), amax_ref)
+            sc = F.E4M3_MAX / max(amax_ref, F.AMAX_FLOOR)
+            y = np.clip(ref["p"] * sc, -F.E4M3_MAX, F.E4M3_MAX)
+            q_ref = F.e4m3_rne(y)
+            got = codes[a:b]
+            ay = np.abs(y)
+            with np.errstate(divide="ignore"):
+                lead = np.floor(np.log2(np.where(ay > 0, ay, 1.0)))
+            half_step = np.where(ay >= 2.0 ** -6, 2.0 ** (lead - 4), 2.0 ** -10)
+            # the fp32 allowance of y: that of p', plus the scale's own rounding
+            allow = (PR.TOL * np.maximum(np.abs(ref["p"]), fl["p"]) + 2.0 ** -23 * np.abs(ref["p"])) * sc
+            judged = allow < half_step
+            far = judged & (np.abs(_monotone_e4m3(got) - _monotone_e4m3(q_ref)) > 1)
+            assert not far.any(), (f"tensor {i} t={t}: {far.sum()} codes more than one step from the "
+                                   f"double-precision code, first at {np.flatnonzero(far)[:5]}")
+            differ += int(np.count_nonzero(got != q_ref))
+            judged_total += int(judged.sum())
+    print(f"fp8 codes against the double trajectory: {differ} of {3 * st.total:,} differ "
+          f"({judged_total:,} judged), none by more than one step", flush=True)
+    st.close()

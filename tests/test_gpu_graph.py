@@ -152,7 +152,7 @@ def _table_plan(st):
         d = dict(d)
         d.pop("grad_slices")
         d.pop("slice_stride")
-        d["grad_slice_ptrs"] = [base + es * (q * st.total + off) for q in range(st.w.n_slices)]
+        d["grad_slice_ptrs"] = [base + es * (q * st.slice_stride + off) for q in range(st.w.n_slices)]
         recs.append(d)
     st.plan = B.MtPlan(recs, st.w.n_slices, st.w.slice_dtype)
 
