@@ -297,12 +297,16 @@ typedef struct fsdp_mt_plan fsdp_mt_plan; /* opaque */
 typedef struct {
     int64_t n_tensors;   /* shards in the plan */
     int64_t n_chunks;    /* entries of the chunk-descriptor table */
-    int64_t n_blocks;    /* workgroups of one fsdp_mt_step launch */
+    int64_t n_blocks;    /* workgroups of a launch through the chunk table (8 per entry; a
+                            one-range step launches ceil(total_numel / 256)) */
     int64_t total_numel; /* sum of shard_numel */
     int64_t total_valid; /* sum of valid */
     int64_t chunk_numel; /* elements per chunk (the last of a shard may be shorter) */
     int32_t n_slices;
     int32_t slice_dtype;
+    int32_t step_one_range; /* 1: fsdp_mt_step runs the shards as one range (see fsdp_mt_step) */
+    int32_t store_policy;   /* fsdp_mt_step's state stores: 0 plain, 1 write-through,
+                               2 non-temporal write-through */
 } fsdp_mt_plan_info;
 
 /* Build a plan over n_tensors shards sharing N = n_slices and slice_dtype
@@ -330,8 +334,15 @@ int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tenso
 
 /* One step over every shard of the plan: exactly one kernel launch on
  * `stream` (none for an empty plan), no host synchronisation.  The plan must
- * be used on the device it was made on (FSDP_E_STATE).  Two steps of one
- * plan on different streams without ordering between them race.  Under HIP
+ * be used on the device it was made on (FSDP_E_STATE).  When the shards lie
+ * back to back in every buffer (state, copies, stored gradient, slices with
+ * one stride), all but the last unpadded, and those that start off a
+ * chunk_numel boundary of the whole hold at most 1/256 of its elements, the
+ * launch takes them as one range from its arguments instead of through the
+ * chunk table (step_one_range in the plan's info).  The elements and their
+ * arithmetic are the same either way, so the results are bit-identical;
+ * only which workgroups run which tiles may differ, in those few shards.
+ * Two steps of one plan on different streams without ordering between them race.  Under HIP
  * graph capture the launch is recorded with hp's derived scalars fixed (see
  * fsdp_adamw_hparams). */
 int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, hipStream_t stream);

@@ -81,7 +81,8 @@ class MtTensor(ctypes.Structure):
 class MtPlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("n_tensors", "n_chunks", "n_blocks", "total_numel",
                                               "total_valid", "chunk_numel")] + [
-        ("n_slices", ctypes.c_int32), ("slice_dtype", ctypes.c_int32)]
+        ("n_slices", ctypes.c_int32), ("slice_dtype", ctypes.c_int32),
+        ("step_one_range", ctypes.c_int32), ("store_policy", ctypes.c_int32)]
 
 
 def lib_path():

@@ -127,6 +127,22 @@ namespace {
 #ifndef RS_RT_BATCH_BYTES
 #define RS_RT_BATCH_BYTES 32
 #endif
+// 1: a plan whose shards lie back to back in every buffer, and start on a
+// chunk-entry boundary of the whole but for a negligible share of its
+// elements, runs its fused step as one range described by the kernel's
+// arguments: the same tiles on the same XCDs as through the chunk table,
+// without the two dependent table loads before a workgroup's first access;
+// 0: every plan goes through its chunk table.
+#ifndef RS_RUN_STEP
+#define RS_RUN_STEP 1
+#endif
+// Budget of that one-range step under write-through stores: its waves stream
+// from their first instructions, so fewer resident waves keep the bytes in
+// flight (one Llama-7B block at N = 8: 162.5-163.0 us at 75 KB, 165.0 at
+// 100; the 128 MiB flat unit: 55.2 against 55.7).
+#ifndef RS_INFLIGHT_KB_RUN
+#define RS_INFLIGHT_KB_RUN 75
+#endif
 // A launch whose share of that budget would allow this many resident
 // workgroups per CU or more is left uncapped (light kernels want every wave).
 #ifndef RS_OCC_UNCAPPED
@@ -983,6 +999,17 @@ __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __res
     });
 }
 
+// The fused step on a plan whose shards lie back to back in every buffer,
+// as one range T: workgroup b covers elements [b*kTile, (b+1)*kTile).  The
+// elements and their arithmetic are those of mt_step_kernel; only the way a
+// workgroup finds its tile differs.
+template <int NS, bool BF16, int POL>
+__global__ __launch_bounds__(kBlock) void run_step_kernel(TensorDesc T, StepConsts c) {
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
+    fused_range<NS, BF16, false, false, false, false, false, POL>(
+        T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
+}
+
 // Reduce (or reduce and accumulate) into grad_shard_out; SQ: also write
 // this workgroup's sum of squares of the stored values to its partials slot.
 template <int NS, bool BF16, bool SQ, bool GENERAL>
@@ -1224,6 +1251,32 @@ MtKernel pick_mt(int dtype, int n, bool general, int pol) {
         case kStWriteThrough: return pick_mt<kStWriteThrough>(dtype, n, general);
         case kStNtWriteThrough: return pick_mt<kStNtWriteThrough>(dtype, n, general);
         default: return pick_mt<kStPlain>(dtype, n, general);
+    }
+}
+
+using RunKernel = void (*)(TensorDesc, StepConsts);
+
+template <bool BF16, int POL>
+RunKernel pick_run(int n) {
+    switch (n) {
+        case 1: return run_step_kernel<1, BF16, POL>;
+        case 2: return run_step_kernel<2, BF16, POL>;
+        case 4: return run_step_kernel<4, BF16, POL>;
+        case 8: return run_step_kernel<8, BF16, POL>;
+        default: return run_step_kernel<0, BF16, POL>;
+    }
+}
+
+template <int POL>
+RunKernel pick_run(int dtype, int n) {
+    return dtype == FSDP_DT_BF16 ? pick_run<true, POL>(n) : pick_run<false, POL>(n);
+}
+
+RunKernel pick_run(int dtype, int n, int pol) {
+    switch (pol) {
+        case kStWriteThrough: return pick_run<kStWriteThrough>(dtype, n);
+        case kStNtWriteThrough: return pick_run<kStNtWriteThrough>(dtype, n);
+        default: return pick_run<kStPlain>(dtype, n);
     }
 }
 
@@ -1532,6 +1585,8 @@ struct fsdp_mt_plan {
                                      // then kSumBlocks second-stage sums
     fsdp::Footprint footprint;       // the shards' buffers, for checking the calls' other buffers
     int store_pol = kStPlain;        // how the fused step stores the updated state
+    bool has_run = false;            // the shards lie back to back in every buffer:
+    TensorDesc run{};                // then this one range covers them all
     bool pooled = false;             // the device tables come from the stream-ordered allocator
     hipEvent_t done = nullptr;       // completes with the plan's last launch outside a capture
 };
@@ -1622,6 +1677,57 @@ int64_t slice_bytes(const fsdp_mt_plan* plan) {
 }
 int64_t step_bytes(const fsdp_mt_plan* plan) {
     return slice_bytes(plan) + 24 + 2 * plan->any_bf16 + 4 * plan->any_grad_out;
+}
+
+// Whether the shards descs[0..) lie back to back in every buffer, so that
+// one range covers them: each starts where the one before it ends in the
+// state, the stored gradient, the copies and the slices (one stride for all),
+// every shard but the last has no padding, and all take the plain vector
+// path.  The range is written to *run.
+//
+// The range deals its tile j to workgroup j, hence to XCD j % 8; the chunk
+// table restarts the deal at every shard, giving a shard's tile j to XCD
+// j % 8.  The two agree on a shard that starts on a chunk-entry boundary of
+// the range.  The deal alone moves a step by several per cent either way
+// (it decides which HBM channels each XCD's L2 streams from), so the range
+// is taken only where the shards off such a boundary hold at most
+// 1/kRedealShare of the elements: a Llama block's last norm weight (2 of
+// 98,820 tiles), but not a whole model's shard, whose 512-element norm
+// weights shift every other layer's deal by four XCDs.
+constexpr int64_t kRedealShare = 256;
+
+bool merge_run(const std::vector<TensorDesc>& descs, int32_t slice_dtype, int32_t n_slices,
+               TensorDesc* run) {
+    if (descs.empty()) return false;
+    const int64_t es = dtype_bytes(slice_dtype);
+    int64_t redealt = 0;  // elements of shards that start off a chunk-entry boundary
+    TensorDesc r = descs[0];
+    for (size_t i = 0; i < descs.size(); ++i) {
+        const TensorDesc& d = descs[i];
+        if (d.slice_ptrs || !d.vec_ok || d.gen) return false;
+        if (i == 0) continue;
+        const TensorDesc& a = descs[i - 1];
+        const int64_t n = a.shard_numel;
+        if (a.valid != n) return false;
+        if (d.param != a.param + n || d.m != a.m + n || d.v != a.v + n) return false;
+        if ((a.grad_out == nullptr) != (d.grad_out == nullptr) || (d.grad_out && d.grad_out != a.grad_out + n))
+            return false;
+        if ((a.out_bf16 == nullptr) != (d.out_bf16 == nullptr) || (d.out_bf16 && d.out_bf16 != a.out_bf16 + n))
+            return false;
+        if ((a.out_fp8 == nullptr) != (d.out_fp8 == nullptr) || (d.out_fp8 && d.out_fp8 != a.out_fp8 + n))
+            return false;
+        if (d.valid > 0) {
+            if (d.slices != static_cast<const char*>(a.slices) + n * es) return false;
+            if (n_slices > 1 && d.slice_stride != a.slice_stride) return false;
+        }
+        if (r.shard_numel % kChunk != 0) redealt += d.shard_numel;
+        r.shard_numel += d.shard_numel;
+    }
+    if (redealt > r.shard_numel / kRedealShare) return false;
+    r.valid = r.shard_numel - (descs.back().shard_numel - descs.back().valid);
+    r.index = 0;
+    *run = r;
+    return true;
 }
 
 // The fused step's store policy for a plan: write-through where the step
@@ -1931,6 +2037,7 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
                         std::any_of(descs.begin(), descs.end(), [](const TensorDesc& x) { return x.gen != 0; });
     plan->footprint = std::move(footprint);
     plan->store_pol = store_policy(plan);
+    plan->has_run = RS_RUN_STEP && merge_run(descs, slice_dtype, n_slices, &plan->run);
     hipError_t e = hipGetDevice(&plan->device);
     int pools = 0;
     if (e == hipSuccess)
@@ -1991,12 +2098,20 @@ extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
-    const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_general, plan->store_pol);
     const int64_t budget = plan->store_pol == kStWriteThrough     ? RS_INFLIGHT_KB_WT
                            : plan->store_pol == kStNtWriteThrough ? RS_INFLIGHT_KB_NTWT
                                                                   : RS_INFLIGHT_KB;
-    plan_launch(plan, true, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
-                lds_reserve(step_bytes(plan), budget), stream, plan->d_tensors, plan->d_chunks, c);
+    if (plan->has_run) {
+        const RunKernel k = pick_run(plan->slice_dtype, plan->n_slices, plan->store_pol);
+        const int64_t run_budget = plan->store_pol == kStWriteThrough ? RS_INFLIGHT_KB_RUN : budget;
+        plan_launch(plan, true, k, dim3(static_cast<uint32_t>(tiles_for(plan->run.shard_numel))),
+                    dim3(kBlock), lds_reserve(step_bytes(plan), run_budget), stream, plan->run, c);
+        return launch_status(who);
+    }
+    const size_t lds = lds_reserve(step_bytes(plan), budget);
+    const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_general, plan->store_pol);
+    plan_launch(plan, true, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), lds, stream,
+                plan->d_tensors, plan->d_chunks, c);
     return launch_status(who);
 }
 
@@ -2411,6 +2526,8 @@ extern "C" int32_t fsdp_mt_plan_get_info(const fsdp_mt_plan* plan, fsdp_mt_plan_
     info->chunk_numel = plan->chunk_numel;
     info->n_slices = plan->n_slices;
     info->slice_dtype = plan->slice_dtype;
+    info->step_one_range = plan->has_run ? 1 : 0;
+    info->store_policy = plan->store_pol;
     return FSDP_OK;
 }
 

@@ -370,6 +370,6 @@ def test_codes_against_the_double_trajectory(gpu):
                                    f"double-precision code, first at {np.flatnonzero(far)[:5]}")
             differ += int(np.count_nonzero(got != q_ref))
             judged_total += int(judged.sum())
-    print(f"fp8 codes against the double trajectory: {differ} of {3 * st.total:,} differ "
-          f"({judged_total:,} judged), none by more than one step", flush=True)
+    print(f"fp8 codes against codes decided in double: {differ} of {3 * st.total:,} differ; "
+          f"none of the {judged_total:,} judged is more than one step away", flush=True)
     st.close()
