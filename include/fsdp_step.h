@@ -50,7 +50,10 @@
  *     they never touch.  The reservation caps how many of their workgroups
  *     share a compute unit (4 to 16, from the bytes the launch moves per
  *     element), which is where HBM serves their read/write mix best; kernels
- *     running concurrently on the same CUs have that much less LDS.
+ *     running concurrently on the same CUs have that much less LDS.  A
+ *     compute-bound kernel on another stream progresses at a small fraction
+ *     of its solo rate while a large step runs, with the cap or without it:
+ *     the step's waves hold the CUs either way.
  */
 #ifndef FSDP_STEP_H
 #define FSDP_STEP_H
