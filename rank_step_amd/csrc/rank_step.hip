@@ -75,6 +75,13 @@ namespace {
 #ifndef RS_ST_POLICY
 #define RS_ST_POLICY -1
 #endif
+// The same for the stores of the other streaming passes (the clipped update,
+// the fp8 steps and code pass, the reduce/accumulate pass, the no_sync
+// accumulation): -1 chooses per launch from the pass's own mix of reads and
+// writes, by the fused step's rule; 0/1/2 force one policy.
+#ifndef RS_ST_POLICY_PASSES
+#define RS_ST_POLICY_PASSES -1
+#endif
 // Bytes of HBM traffic (loads and stores) one CU should keep in flight: each
 // launch caps its resident workgroups at this divided by what one workgroup
 // moves, through its LDS reservation.
@@ -391,6 +398,14 @@ __device__ __forceinline__ void st_bf16_wt(uint16_t* lane_ptr, const u32x2& x) {
     __builtin_amdgcn_raw_buffer_store_b64(x, r, static_cast<int>(threadIdx.x) * 8, 0, 16 | 2);
 }
 
+// This lane's 4 fp8 codes at `lane_ptr` (the group's base plus 4 *
+// threadIdx.x bytes, 4-byte aligned), written through and streamed.
+__device__ __forceinline__ void st_fp8_wt(uint8_t* lane_ptr, uint32_t x) {
+    uint8_t* base = uniform_ptr(lane_ptr - threadIdx.x * kGroup);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b32(x, r, static_cast<int>(threadIdx.x) * 4, 0, 16 | 2);
+}
+
 // Sums and maxima over the wave in a fixed order (xor-shuffle steps); every
 // lane ends with the result.
 __device__ __forceinline__ double wave_sum(double x) {
@@ -686,11 +701,14 @@ __device__ __forceinline__ void update_store(StateRegs& s, const float g[kGroup]
     if constexpr (FP8) {
         if (T.out_fp8) {
             if constexpr (GEN) store_fp8_any(T.out_fp8 + e, pack_fp8(s.p, fp8_scale), misalign(T.out_fp8, 4));
+            else if constexpr (POL != kStPlain) st_fp8_wt(T.out_fp8 + e, pack_fp8(s.p, fp8_scale));
             else st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), pack_fp8(s.p, fp8_scale));
         }
     }
-    if (WRITE_G && T.grad_out)
-        st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
+    if (WRITE_G && T.grad_out) {
+        if constexpr (POL != kStPlain) st_state_pol<kStNtWriteThrough>(T.grad_out + e, f32x4{g[0], g[1], g[2], g[3]});
+        else st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
+    }
 }
 
 // ---------------------------------------------------------------- single elements
@@ -818,7 +836,7 @@ __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin,
 // accumulation over micro-batches), else it replaces it.  SQ: return this
 // lane's sum of the squares of the stored values, in fp64 (each fp32
 // square is exact in fp64).  The padding is +0 either way.
-template <int NS, bool BF16, bool SQ, bool TABLE = false, bool GEN = false>
+template <int NS, bool BF16, bool SQ, bool TABLE = false, bool GEN = false, int POL = kStPlain>
 __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_t begin,
                                                      int64_t end, const StepConsts& c, bool acc) {
     double sq = 0.0;
@@ -833,7 +851,8 @@ __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_
 #pragma unroll
             for (int j = 0; j < kGroup; ++j) g[j] = old[j] + g[j];
         }
-        st_out(go, f32x4{g[0], g[1], g[2], g[3]});
+        if constexpr (POL != kStPlain) st_state_pol<POL>(T.grad_out + e, f32x4{g[0], g[1], g[2], g[3]});
+        else st_out(go, f32x4{g[0], g[1], g[2], g[3]});
         if constexpr (SQ) {
 #pragma unroll
             for (int j = 0; j < kGroup; ++j) sq += static_cast<double>(g[j]) * static_cast<double>(g[j]);
@@ -854,7 +873,7 @@ __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_
 // In-place accumulation of one micro-batch's unsharded gradient, elements
 // [begin, end): acc = acc + x (fp32 add), or acc = x exactly for the first.
 // GEN: x may start at any element alignment (acc is aligned).
-template <bool BF16, bool GEN = false>
+template <bool BF16, bool GEN = false, int POL = kStPlain>
 __device__ __forceinline__ void accumulate_range(float* a, const void* x, int64_t begin,
                                                  int64_t end, bool accum, bool vec) {
     const int64_t vend = vec ? std::max(begin, end & ~int64_t(kGroup - 1)) : begin;
@@ -869,7 +888,8 @@ __device__ __forceinline__ void accumulate_range(float* a, const void* x, int64_
         widen<BF16>(w, xv);
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) av[j] = accum ? av[j] + xv[j] : xv[j];
-        st_state(ap, av);
+        if constexpr (POL != kStPlain) st_state_pol<POL>(a + e, av);
+        else st_state(ap, av);
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) {
         const float xk = slice_elem<BF16>(x, k);
@@ -878,7 +898,7 @@ __device__ __forceinline__ void accumulate_range(float* a, const void* x, int64_
 }
 
 // AdamW + cast on [begin, end) from the stored reduced gradient times `scale`.
-template <bool GEN = false>
+template <bool GEN = false, int POL = kStPlain>
 __device__ __forceinline__ void scaled_range(const TensorDesc& T, int64_t begin, int64_t end,
                                              float scale, const StepConsts& c) {
     const int64_t vend = vector_end(T, begin, end);
@@ -889,14 +909,14 @@ __device__ __forceinline__ void scaled_range(const TensorDesc& T, int64_t begin,
         float g[kGroup];
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) g[j] = gv[j] * scale;
-        update_store<false, false, false, GEN>(s, g, T, e, c);
+        update_store<false, false, false, GEN, POL>(s, g, T, e, c);
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock) scaled_elem(T, k, scale, c);
 }
 
 // fp8 copy of the updated shard on [begin, end), at most TILES tiles; codes 0
 // in the pad.  Each lane loads all of its groups before converting any.
-template <int TILES, bool GEN = false>
+template <int TILES, bool GEN = false, int POL = kStPlain>
 __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, int64_t end,
                                           float scale) {
     const int64_t vend = vector_end(T, begin, end);
@@ -911,6 +931,7 @@ __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, in
         const int64_t e = begin + (u * kBlock + threadIdx.x) * kGroup;
         if (e < vend) {
             if constexpr (GEN) store_fp8_any(T.out_fp8 + e, pack_fp8(a[u], scale), misalign(T.out_fp8, 4));
+            else if constexpr (POL != kStPlain) st_fp8_wt(T.out_fp8 + e, pack_fp8(a[u], scale));
             else st_out(reinterpret_cast<uint32_t*>(T.out_fp8 + e), pack_fp8(a[u], scale));
         }
     }
@@ -1012,7 +1033,7 @@ __global__ __launch_bounds__(kBlock) void run_step_kernel(TensorDesc T, StepCons
 
 // Reduce (or reduce and accumulate) into grad_shard_out; SQ: also write
 // this workgroup's sum of squares of the stored values to its partials slot.
-template <int NS, bool BF16, bool SQ, bool GENERAL>
+template <int NS, bool BF16, bool SQ, bool GENERAL, int POL>
 __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDesc* __restrict__ tensors,
                                                                  const ChunkDesc* __restrict__ chunks,
                                                                  StepConsts c, int32_t acc,
@@ -1021,12 +1042,12 @@ __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDes
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         const bool a = acc != 0;
         if (GENERAL && T.slice_ptrs)
-            sq = T.gen & kGenLoad ? reduce_store_range<NS, BF16, SQ, true, true>(T, b, e, c, a)
-                                  : reduce_store_range<NS, BF16, SQ, true>(T, b, e, c, a);
+            sq = T.gen & kGenLoad ? reduce_store_range<NS, BF16, SQ, true, true, POL>(T, b, e, c, a)
+                                  : reduce_store_range<NS, BF16, SQ, true, false, POL>(T, b, e, c, a);
         else if (GENERAL && (T.gen & kGenLoad))
-            sq = reduce_store_range<NS, BF16, SQ, false, true>(T, b, e, c, a);
+            sq = reduce_store_range<NS, BF16, SQ, false, true, POL>(T, b, e, c, a);
         else
-            sq = reduce_store_range<NS, BF16, SQ>(T, b, e, c, a);
+            sq = reduce_store_range<NS, BF16, SQ, false, false, POL>(T, b, e, c, a);
     });
     if constexpr (SQ) {
         const double total = wave_sum(sq);
@@ -1035,34 +1056,35 @@ __global__ __launch_bounds__(kBlock) void mt_reduce_store_kernel(const TensorDes
 }
 
 // Workgroup b accumulates elements [b*kTile, (b+1)*kTile) of one buffer.
-template <bool BF16, bool GEN = false>
+template <bool BF16, bool GEN, int POL>
 __global__ __launch_bounds__(kBlock) void accumulate_kernel(float* a, const void* x, int64_t n,
                                                             int32_t accum, int32_t vec) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
-    accumulate_range<BF16, GEN>(a, x, begin, std::min(begin + kTile, n), accum != 0, vec != 0);
+    accumulate_range<BF16, GEN, POL>(a, x, begin, std::min(begin + kTile, n), accum != 0,
+                                                     vec != 0);
 }
 
 // Pass 2 of a clipped step: AdamW and cast from grad_shard_out times *scale.
-template <bool GENERAL>
+template <bool GENERAL, int POL>
 __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc* __restrict__ tensors,
                                                                 const ChunkDesc* __restrict__ chunks,
                                                                 StepConsts c, const float* scale) {
     const float k = *scale;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        if (GENERAL && (T.gen & kGenStore)) scaled_range<true>(T, b, e, k, c);
-        else scaled_range(T, b, e, k, c);
+        if (GENERAL && (T.gen & kGenStore)) scaled_range<true, POL>(T, b, e, k, c);
+        else scaled_range<false, POL>(T, b, e, k, c);
     });
 }
 
 // The fused step that also records, per workgroup, the largest |p'| (as
 // fp32 bits, in the workgroup's slot) for the fp8 copy's per-tensor scale.
-template <int NS, bool BF16, bool GENERAL>
+template <int NS, bool BF16, bool GENERAL, int POL>
 __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* __restrict__ tensors,
                                                               const ChunkDesc* __restrict__ chunks,
                                                               StepConsts c, uint32_t* tile_amax) {
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
-        fused_tile<NS, BF16, true, false, GENERAL>(T, b, e, c, &am);
+        fused_tile<NS, BF16, true, false, GENERAL, POL>(T, b, e, c, &am);
     });
     const uint32_t wm = wave_max(am);
     if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
@@ -1071,7 +1093,7 @@ __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* 
 // The fused step that also writes the fp8 codes of p' with a per-tensor scale
 // given in advance (scale_in[index], e.g. from the previous step's amax) and
 // records this step's per-workgroup largest |p'|, all in the one pass.
-template <int NS, bool BF16, bool GENERAL>
+template <int NS, bool BF16, bool GENERAL, int POL>
 __global__ __launch_bounds__(kBlock) void mt_step_fp8_kernel(const TensorDesc* __restrict__ tensors,
                                                              const ChunkDesc* __restrict__ chunks,
                                                              StepConsts c, const float* scale_in,
@@ -1079,7 +1101,7 @@ __global__ __launch_bounds__(kBlock) void mt_step_fp8_kernel(const TensorDesc* _
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         const float scale = ld(scale_in + T.index);
-        fused_tile<NS, BF16, true, true, GENERAL>(T, b, e, c, &am, scale);
+        fused_tile<NS, BF16, true, true, GENERAL, POL>(T, b, e, c, &am, scale);
     });
     const uint32_t wm = wave_max(am);
     if (threadIdx.x == 0) st(tile_amax + xcd_slot(blockIdx.x, gridDim.x), wm);
@@ -1130,7 +1152,7 @@ __global__ __launch_bounds__(kAmaxBlock) void shard_amax_kernel(const ShardTiles
 // 448 / max(amax, 1e-12) in fp32.  The workgroup holding a shard's first
 // tile also stores the scale (both parts of a split shard store the same
 // value).  GENERAL: some shard's fp8 copy is not vector-aligned.
-template <bool GENERAL>
+template <bool GENERAL, int POL>
 __global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* __restrict__ tensors,
                                                              const ChunkDesc* __restrict__ chunks,
                                                              const float* amax_ranks, int32_t n_ranks,
@@ -1143,8 +1165,8 @@ __global__ __launch_bounds__(kBlock) void mt_cast_fp8_kernel(const TensorDesc* _
         const float den = (amax > 1e-12f || amax != amax) ? amax : 1e-12f;
         const float scale = 448.0f / den;
         if (b == 0 && scale_out && threadIdx.x == 0) st(scale_out + T.index, scale);
-        if (GENERAL && (T.gen & kGenStore)) fp8_range<RS_CAST_TILES, true>(T, b, e, scale);
-        else fp8_range<RS_CAST_TILES>(T, b, e, scale);
+        if (GENERAL && (T.gen & kGenStore)) fp8_range<RS_CAST_TILES, true, POL>(T, b, e, scale);
+        else fp8_range<RS_CAST_TILES, false, POL>(T, b, e, scale);
     });
 }
 
@@ -1280,65 +1302,108 @@ RunKernel pick_run(int dtype, int n, int pol) {
     }
 }
 
-using ReduceStoreKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, int32_t, double*);
-
-template <bool BF16, bool SQ, bool GENERAL>
-ReduceStoreKernel pick_reduce_store(int n) {
-    switch (n) {
-        case 1: return mt_reduce_store_kernel<1, BF16, SQ, GENERAL>;
-        case 2: return mt_reduce_store_kernel<2, BF16, SQ, GENERAL>;
-        case 4: return mt_reduce_store_kernel<4, BF16, SQ, GENERAL>;
-        case 8: return mt_reduce_store_kernel<8, BF16, SQ, GENERAL>;
-        default: return mt_reduce_store_kernel<0, BF16, SQ, GENERAL>;
+// The policy a pass's stores run under: the one chosen for the launch
+// (write-through or its non-temporal form), or the one forced at build time.
+template <typename Pick>
+auto by_policy(int pol, Pick pick) {
+    if constexpr (RS_ST_POLICY_PASSES >= 0) {
+        (void)pol;
+        return pick(std::integral_constant<int, RS_ST_POLICY_PASSES>{});
+    } else {
+        return pol == kStNtWriteThrough ? pick(std::integral_constant<int, kStNtWriteThrough>{})
+                                        : pick(std::integral_constant<int, kStWriteThrough>{});
     }
 }
 
-template <bool GENERAL>
-ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq) {
-    if (dtype == FSDP_DT_BF16)
-        return sq ? pick_reduce_store<true, true, GENERAL>(n) : pick_reduce_store<true, false, GENERAL>(n);
-    return sq ? pick_reduce_store<false, true, GENERAL>(n) : pick_reduce_store<false, false, GENERAL>(n);
+using ReduceStoreKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, int32_t, double*);
+
+template <bool BF16, bool SQ, bool GENERAL, int POL>
+ReduceStoreKernel pick_reduce_store(int n) {
+    switch (n) {
+        case 1: return mt_reduce_store_kernel<1, BF16, SQ, GENERAL, POL>;
+        case 2: return mt_reduce_store_kernel<2, BF16, SQ, GENERAL, POL>;
+        case 4: return mt_reduce_store_kernel<4, BF16, SQ, GENERAL, POL>;
+        case 8: return mt_reduce_store_kernel<8, BF16, SQ, GENERAL, POL>;
+        default: return mt_reduce_store_kernel<0, BF16, SQ, GENERAL, POL>;
+    }
 }
 
-ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq, bool general) {
-    return general ? pick_reduce_store<true>(dtype, n, sq) : pick_reduce_store<false>(dtype, n, sq);
+template <bool GENERAL, int POL>
+ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq) {
+    if (dtype == FSDP_DT_BF16)
+        return sq ? pick_reduce_store<true, true, GENERAL, POL>(n) : pick_reduce_store<true, false, GENERAL, POL>(n);
+    return sq ? pick_reduce_store<false, true, GENERAL, POL>(n) : pick_reduce_store<false, false, GENERAL, POL>(n);
+}
+
+ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq, bool general, int pol) {
+    return by_policy(pol, [&](auto P) {
+        constexpr int kPol = decltype(P)::value;
+        return general ? pick_reduce_store<true, kPol>(dtype, n, sq) : pick_reduce_store<false, kPol>(dtype, n, sq);
+    });
 }
 
 using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, uint32_t*);
 
-template <bool BF16, bool GENERAL>
+template <bool BF16, bool GENERAL, int POL>
 AmaxKernel pick_amax(int n) {
     switch (n) {
-        case 1: return mt_step_amax_kernel<1, BF16, GENERAL>;
-        case 2: return mt_step_amax_kernel<2, BF16, GENERAL>;
-        case 4: return mt_step_amax_kernel<4, BF16, GENERAL>;
-        case 8: return mt_step_amax_kernel<8, BF16, GENERAL>;
-        default: return mt_step_amax_kernel<0, BF16, GENERAL>;
+        case 1: return mt_step_amax_kernel<1, BF16, GENERAL, POL>;
+        case 2: return mt_step_amax_kernel<2, BF16, GENERAL, POL>;
+        case 4: return mt_step_amax_kernel<4, BF16, GENERAL, POL>;
+        case 8: return mt_step_amax_kernel<8, BF16, GENERAL, POL>;
+        default: return mt_step_amax_kernel<0, BF16, GENERAL, POL>;
     }
 }
 
-AmaxKernel pick_amax(int dtype, int n, bool general) {
-    if (dtype == FSDP_DT_BF16) return general ? pick_amax<true, true>(n) : pick_amax<true, false>(n);
-    return general ? pick_amax<false, true>(n) : pick_amax<false, false>(n);
+AmaxKernel pick_amax(int dtype, int n, bool general, int pol) {
+    return by_policy(pol, [&](auto P) {
+        constexpr int kPol = decltype(P)::value;
+        if (dtype == FSDP_DT_BF16)
+            return general ? pick_amax<true, true, kPol>(n) : pick_amax<true, false, kPol>(n);
+        return general ? pick_amax<false, true, kPol>(n) : pick_amax<false, false, kPol>(n);
+    });
 }
 
 using Fp8StepKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const float*,
                                uint32_t*);
 
-template <bool BF16, bool GENERAL>
+template <bool BF16, bool GENERAL, int POL>
 Fp8StepKernel pick_fp8_step(int n) {
     switch (n) {
-        case 1: return mt_step_fp8_kernel<1, BF16, GENERAL>;
-        case 2: return mt_step_fp8_kernel<2, BF16, GENERAL>;
-        case 4: return mt_step_fp8_kernel<4, BF16, GENERAL>;
-        case 8: return mt_step_fp8_kernel<8, BF16, GENERAL>;
-        default: return mt_step_fp8_kernel<0, BF16, GENERAL>;
+        case 1: return mt_step_fp8_kernel<1, BF16, GENERAL, POL>;
+        case 2: return mt_step_fp8_kernel<2, BF16, GENERAL, POL>;
+        case 4: return mt_step_fp8_kernel<4, BF16, GENERAL, POL>;
+        case 8: return mt_step_fp8_kernel<8, BF16, GENERAL, POL>;
+        default: return mt_step_fp8_kernel<0, BF16, GENERAL, POL>;
     }
 }
 
-Fp8StepKernel pick_fp8_step(int dtype, int n, bool general) {
-    if (dtype == FSDP_DT_BF16) return general ? pick_fp8_step<true, true>(n) : pick_fp8_step<true, false>(n);
-    return general ? pick_fp8_step<false, true>(n) : pick_fp8_step<false, false>(n);
+Fp8StepKernel pick_fp8_step(int dtype, int n, bool general, int pol) {
+    return by_policy(pol, [&](auto P) {
+        constexpr int kPol = decltype(P)::value;
+        if (dtype == FSDP_DT_BF16)
+            return general ? pick_fp8_step<true, true, kPol>(n) : pick_fp8_step<true, false, kPol>(n);
+        return general ? pick_fp8_step<false, true, kPol>(n) : pick_fp8_step<false, false, kPol>(n);
+    });
+}
+
+using AccumulateKernel = void (*)(float*, const void*, int64_t, int32_t, int32_t);
+
+AccumulateKernel pick_accumulate(bool bf16, bool gen, int pol) {
+    return by_policy(pol, [&](auto P) -> AccumulateKernel {
+        constexpr int kPol = decltype(P)::value;
+        if (bf16) return gen ? accumulate_kernel<true, true, kPol> : accumulate_kernel<true, false, kPol>;
+        return gen ? accumulate_kernel<false, true, kPol> : accumulate_kernel<false, false, kPol>;
+    });
+}
+
+using ScaledStepKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const float*);
+
+ScaledStepKernel pick_scaled_step(bool general, int pol) {
+    return by_policy(pol, [&](auto P) -> ScaledStepKernel {
+        constexpr int kPol = decltype(P)::value;
+        return general ? mt_scaled_step_kernel<true, kPol> : mt_scaled_step_kernel<false, kPol>;
+    });
 }
 
 template <bool BF16, bool GEN>
@@ -1730,16 +1795,31 @@ bool merge_run(const std::vector<TensorDesc>& descs, int32_t slice_dtype, int32_
     return true;
 }
 
-// The fused step's store policy for a plan: write-through where the step
-// reads at least half again as many bytes as it writes (N slices at 2 or 4
-// bytes and 12 bytes of state read against 12 of state, 2 of bf16 and 4 of
-// stored gradient written); non-temporal write-through where writes come
-// closer to half the traffic.
+// The store policy of a streaming pass that reads `reads` and writes
+// `writes` bytes per element: write-through where it reads more than half
+// again as many bytes as it writes; non-temporal write-through where writes
+// come closer to half the traffic.  Measured on the 7B shard's passes
+// (interleaved builds, 3 passes): the fused step at 28 : 14 and the fp8 steps
+// at 28 : 12-13 gain most from write-through (5.31 -> 5.21 ms for the
+// delayed-scaling step), the synchronised accumulation at 20 : 4 too (2.99 ->
+// 2.94 ms, 3.05 under the non-temporal form); the 70B shard's step at 16 : 14
+// and the no_sync accumulation at 6 : 4, the one tie, from the non-temporal
+// form (1.291 -> 1.244 ms, 1.265 under write-through alone).
+int write_policy(int64_t reads, int64_t writes) {
+    return 2 * reads > 3 * writes ? kStWriteThrough : kStNtWriteThrough;
+}
+
+// Bytes per element a plan's passes read in slices (all N) and write besides
+// the state.
+int64_t plan_slice_read(const fsdp_mt_plan* plan) { return dtype_bytes(plan->slice_dtype) * plan->n_slices; }
+int64_t plan_copy_write(const fsdp_mt_plan* plan) { return 2 * plan->any_bf16 + 4 * plan->any_grad_out; }
+
+// The fused step's store policy for a plan: N slices at 2 or 4 bytes and 12
+// bytes of state read against 12 of state, 2 of bf16 and 4 of stored
+// gradient written.
 int store_policy(const fsdp_mt_plan* plan) {
     if (RS_ST_POLICY >= 0) return RS_ST_POLICY;
-    const int64_t reads = dtype_bytes(plan->slice_dtype) * plan->n_slices + 12;
-    const int64_t writes = 12 + 2 * plan->any_bf16 + 4 * plan->any_grad_out;
-    return 2 * reads >= 3 * writes ? kStWriteThrough : kStNtWriteThrough;
+    return write_policy(plan_slice_read(plan) + 12, 12 + plan_copy_write(plan));
 }
 
 }  // namespace
@@ -2132,8 +2212,9 @@ extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumul
     const bool sq = sqnorm_out != nullptr;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(nullptr, plan->n_slices);
-        const ReduceStoreKernel k = pick_reduce_store(plan->slice_dtype, plan->n_slices, sq,
-                                                      plan->any_general);
+        const ReduceStoreKernel k =
+            pick_reduce_store(plan->slice_dtype, plan->n_slices, sq, plan->any_general,
+                              write_policy(plan_slice_read(plan) + 4 * accumulate, 4));
         plan_launch(plan, !sq, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                     lds_reserve(slice_bytes(plan) + 4 + 4 * accumulate,
                                 accumulate ? RS_INFLIGHT_KB_ACC : RS_INFLIGHT_KB), stream,
@@ -2188,10 +2269,9 @@ static int32_t grad_accumulate_impl(float* acc, const void* micro, int32_t micro
     // off a vector boundary takes the shifted loads
     const int32_t vec = aligned(acc, kF32Vec);
     const bool gen = vec && !aligned(micro, micro_dtype == FSDP_DT_BF16 ? kBf16Vec : kF32Vec);
-    using AccKernel = void (*)(float*, const void*, int64_t, int32_t, int32_t);
-    const AccKernel k = micro_dtype == FSDP_DT_BF16
-                            ? (gen ? accumulate_kernel<true, true> : accumulate_kernel<true, false>)
-                            : (gen ? accumulate_kernel<false, true> : accumulate_kernel<false, false>);
+    const AccumulateKernel k =
+        pick_accumulate(micro_dtype == FSDP_DT_BF16, gen,
+                        write_policy(dtype_bytes(micro_dtype) + 4 * accumulate, 4));
     hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
                        lds_reserve(dtype_bytes(micro_dtype) + 4 + 4 * accumulate), stream, acc, micro,
                        numel, accumulate, vec);
@@ -2232,8 +2312,8 @@ extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hpa
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const StepConsts c = make_consts(hp, plan->n_slices);
-    plan_launch(plan, true, plan->any_general ? mt_scaled_step_kernel<true> : mt_scaled_step_kernel<false>,
-                dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
+    const ScaledStepKernel k = pick_scaled_step(plan->any_general, write_policy(4 + 12, 12 + 2 * plan->any_bf16));
+    plan_launch(plan, true, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                 lds_reserve(4 + 24 + 2 * plan->any_bf16), stream, plan->d_tensors, plan->d_chunks, c,
                 grad_scale);
     return launch_status(who);
@@ -2254,7 +2334,8 @@ extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparam
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(hp, plan->n_slices);
-        const AmaxKernel k = pick_amax(plan->slice_dtype, plan->n_slices, plan->any_general);
+        const AmaxKernel k = pick_amax(plan->slice_dtype, plan->n_slices, plan->any_general,
+                                       write_policy(plan_slice_read(plan) + 12, 12 + plan_copy_write(plan)));
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(step_bytes(plan), RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
                            plan->d_chunks, c, plan->d_tile_amax);
@@ -2290,7 +2371,12 @@ static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int
         return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
-    plan_launch(plan, true, plan->any_general ? mt_cast_fp8_kernel<true> : mt_cast_fp8_kernel<false>,
+    // 4 bytes read per code written: write-through (the rule above)
+    const auto k = by_policy(write_policy(4, 1), [&](auto P) {
+        constexpr int kPol = decltype(P)::value;
+        return plan->any_general ? mt_cast_fp8_kernel<true, kPol> : mt_cast_fp8_kernel<false, kPol>;
+    });
+    plan_launch(plan, true, k,
                 dim3(static_cast<uint32_t>(plan->n_chunks * (kTilesPerChunk / RS_CAST_TILES))),
                 dim3(kBlock), 0, stream, plan->d_tensors, plan->d_chunks, amax_ranks, n_ranks,
                 plan->n_tensors, scale_out);
@@ -2320,7 +2406,9 @@ static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
         const StepConsts c = make_consts(hp, plan->n_slices);
-        const Fp8StepKernel k = pick_fp8_step(plan->slice_dtype, plan->n_slices, plan->any_general);
+        const Fp8StepKernel k =
+            pick_fp8_step(plan->slice_dtype, plan->n_slices, plan->any_general,
+                          write_policy(plan_slice_read(plan) + 12, 12 + plan_copy_write(plan) + plan->any_fp8));
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(step_bytes(plan) + 1, RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
                            plan->d_chunks, c, scale_in, plan->d_tile_amax);

@@ -155,8 +155,9 @@ CASES = {
                    8, "bf16", True, True, 1),
     "f32_n1_ntwt": ([(5 * CHUNK, 5 * CHUNK), (2 * CHUNK, 2 * CHUNK), (CHUNK + 516, CHUNK + 513)],
                     1, "f32", True, False, 2),
+    # 24 bytes read against 16 written: the tie, non-temporal write-through
     "f32_n3_runtime": ([(2 * CHUNK, 2 * CHUNK), (4 * CHUNK, 4 * CHUNK), (777, 777)],
-                       3, "f32", False, True, 1),
+                       3, "f32", False, True, 2),
     "bf16_n2_single": ([(6 * CHUNK + 260, 6 * CHUNK + 259)], 2, "bf16", True, False, 2),
     # a short shard whose successor starts off a chunk-entry boundary
     "bf16_n4_redealt": ([(256 * CHUNK, 256 * CHUNK), (512, 512), (508, 505)], 4, "bf16", True, True, 2),
