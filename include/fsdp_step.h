@@ -179,14 +179,15 @@ int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t rank,
  * Required: all finite, lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps >= 0,
  * weight_decay >= 0, step >= 1 (else FSDP_E_ARG).  Derived scalars
  * (1 - lr*wd, lr/(1 - beta1^step), 1/sqrt(1 - beta2^step)) are computed on
- * the host in double and rounded to fp32, and reach the kernel by value.
- * A launch captured into a HIP graph therefore keeps them as they were at
- * capture: every replay applies the captured step's bias corrections and
- * learning rate (a graph captured at step 3 and replayed at step 1000 steps
- * 3.7x too far, with 1/sqrt(1 - beta2^3) = 18.3 where 1.0 is due), and
- * nothing reports it.  To step a graph through t = 1, 2, ..., capture one
- * graph per step value (the bias corrections settle after a few thousand
- * steps) or make the step calls eagerly. */
+ * the host in double (beta^step by binary powering) and rounded to fp32, and
+ * reach the kernel by value.  A launch captured into a HIP graph therefore
+ * keeps them as they were at capture: every replay applies the captured
+ * step's bias corrections and learning rate (a graph captured at step 3 and
+ * replayed at step 1000 steps 3.7x too far, with 1/sqrt(1 - beta2^3) = 18.3
+ * where 1.0 is due), and nothing reports it.  To step a graph through
+ * t = 1, 2, ..., capture the _capturable forms of the step calls, which read
+ * the count from device memory (fsdp_mt_step_capturable), or make the calls
+ * eagerly. */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
     int64_t step;
@@ -350,6 +351,23 @@ int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tenso
  * fsdp_adamw_hparams). */
 int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, hipStream_t stream);
 
+/* fsdp_mt_step with the step count in device memory, for a HIP graph that
+ * replays the step (torch's "capturable" AdamW keeps its count on the device
+ * for the same reason).  step_dev: device int64 [1] holding the number of
+ * steps taken so far, 0 <= *step_dev < 2^62, not checked on the device.  The
+ * call first advances *step_dev by one, then steps with t = the new count:
+ * a one-lane launch derives t's scalars on the device, with the host's
+ * operations (so the results are bit-identical to fsdp_mt_step with
+ * hp->step = t), into a slot the plan owns, and the step launch reads them
+ * there.  hp->step is ignored; lr, betas, eps and weight_decay are taken at
+ * the call (a captured graph keeps them).  Two launches, no allocation, no
+ * host synchronisation; an empty plan advances the count only.  step_dev
+ * must not overlap the plan's buffers (FSDP_E_ALIAS); null is FSDP_E_ARG,
+ * misaligned FSDP_E_ALIGN.  Calls on one plan must not overlap (they share
+ * the slot). */
+int32_t fsdp_mt_step_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                int64_t* step_dev, hipStream_t stream);
+
 /* ------------------------------------------------------------------ clipping */
 
 /* Global gradient-norm clipping across the ranks' shards, [FSDP ch.18] §18.18:
@@ -392,6 +410,13 @@ int32_t fsdp_clip_coef(float* coef_out, double* norm_out, const double* sqnorms,
  * buffers are read, not written.  One kernel launch. */
 int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                              const float* grad_scale, hipStream_t stream);
+
+/* fsdp_mt_step_clipped with the step count in device memory, as
+ * fsdp_mt_step_capturable: advances *step_dev, then the scaled update at the
+ * new count.  step_dev must not overlap grad_scale either. */
+int32_t fsdp_mt_step_clipped_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                        int64_t* step_dev, const float* grad_scale,
+                                        hipStream_t stream);
 
 /* ------------------------------------------------------------------ gradient accumulation */
 

@@ -29,7 +29,8 @@ LAYOUTS = {"flat": 0, "shard0": 1, "owner": 2}
 # Every function the header declares; the CPU tests check each is exported.
 EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
            "fsdp_adamw_shard_step", "fsdp_cast_unshard_bf16", "fsdp_mt_plan_create",
-           "fsdp_mt_step", "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy",
+           "fsdp_mt_step", "fsdp_mt_step_capturable", "fsdp_mt_step_clipped_capturable",
+           "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy",
            "fsdp_mt_reduce_sqnorm", "fsdp_clip_coef", "fsdp_mt_step_clipped",
            "fsdp_mt_step_amax", "fsdp_mt_cast_fp8", "fsdp_mt_step_fp8",
            "fsdp_mt_reduce_accumulate", "fsdp_grad_accumulate", "fsdp_reduce_sqnorm_noalloc")
@@ -112,6 +113,8 @@ def lib():
             "fsdp_cast_unshard_bf16": [vp, vp, i64, i64, vp],
             "fsdp_mt_plan_create": [ctypes.POINTER(vp), ctypes.POINTER(MtTensor), i32, i32, i32, vp],
             "fsdp_mt_step": [vp, ctypes.POINTER(AdamWHparams), vp],
+            "fsdp_mt_step_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
+            "fsdp_mt_step_clipped_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp],
             "fsdp_mt_plan_get_info": [vp, ctypes.POINTER(MtPlanInfo)],
             "fsdp_mt_plan_destroy": [vp],
             "fsdp_mt_reduce_sqnorm": [vp, vp, vp],
@@ -254,6 +257,18 @@ def fsdp_mt_step_clipped(plan, hp, step, grad_scale, stream=None):
     _check(lib().fsdp_mt_step_clipped(plan, ctypes.byref(h), _ptr(grad_scale), _stream(stream)))
 
 
+def fsdp_mt_step_capturable(plan, hp, step_dev, stream=None):
+    """``step_dev``: device int64 [1], the steps taken so far (advanced by one)."""
+    h = _hparams(hp, 1)
+    _check(lib().fsdp_mt_step_capturable(plan, ctypes.byref(h), _ptr(step_dev), _stream(stream)))
+
+
+def fsdp_mt_step_clipped_capturable(plan, hp, step_dev, grad_scale, stream=None):
+    h = _hparams(hp, 1)
+    _check(lib().fsdp_mt_step_clipped_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(grad_scale),
+                                                  _stream(stream)))
+
+
 def fsdp_mt_step_amax(plan, hp, step, amax_out, stream=None):
     h = _hparams(hp, step)
     _check(lib().fsdp_mt_step_amax(plan, ctypes.byref(h), _ptr(amax_out), _stream(stream)))
@@ -298,6 +313,12 @@ class MtPlan:
 
     def step(self, hp, step, stream=None):
         fsdp_mt_step(self.handle, hp, step, stream)
+
+    def step_capturable(self, hp, step_dev, stream=None):
+        fsdp_mt_step_capturable(self.handle, hp, step_dev, stream)
+
+    def step_clipped_capturable(self, hp, step_dev, grad_scale, stream=None):
+        fsdp_mt_step_clipped_capturable(self.handle, hp, step_dev, grad_scale, stream)
 
     def info(self):
         return fsdp_mt_plan_get_info(self.handle)

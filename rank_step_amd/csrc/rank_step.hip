@@ -238,6 +238,28 @@ struct StepConsts {
     int32_t n_pow2;
 };
 
+// beta^t by binary exponentiation: the same IEEE double products on the host
+// and on the device, so that both derive bit-identical scalars from t.
+__host__ __device__ inline double pow_steps(double b, int64_t t) {
+    double r = 1.0, x = b;
+    for (; t > 0; t >>= 1) {
+        if (t & 1) r = r * x;
+        x = x * x;
+    }
+    return r;
+}
+
+// The step-count-dependent scalars of step t: lr / (1 - beta1^t) and
+// 1 / sqrt(1 - beta2^t), in double (correctly rounded division and square
+// root on the host and on the device alike), each rounded once to fp32.
+__host__ __device__ inline void count_scalars(StepConsts& c, double lr, double beta1, double beta2,
+                                              int64_t t) {
+    const double bc1 = 1.0 - pow_steps(beta1, t);
+    const double bc2 = 1.0 - pow_steps(beta2, t);
+    c.step_size = static_cast<float>(lr / bc1);
+    c.inv_sqrt_bc2 = static_cast<float>(1.0 / sqrt(bc2));
+}
+
 // ---------------------------------------------------------------- device math
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -1010,11 +1032,21 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& T, int64_t b, int64
     fused_range<NS, BF16, AMAX, FP8, false, false, false, POL>(T, b, e, c, amax, fp8_scale);
 }
 
+// The step's scalars: those passed by value, or (DEVC: a step whose count is
+// in device memory) those the count kernel derived at *cdev.  DEVC is a
+// template argument so that the by-value kernels carry no test of cdev.
+template <bool DEVC>
+__device__ __forceinline__ StepConsts step_consts(const StepConsts& c, const StepConsts* cdev) {
+    if constexpr (DEVC) return *cdev;
+    else return c;
+}
+
 // Multi-tensor fused step: reduce, AdamW and cast for every tile.
-template <int NS, bool BF16, bool GENERAL, int POL>
+template <int NS, bool BF16, bool GENERAL, int POL, bool DEVC>
 __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __restrict__ tensors,
                                                          const ChunkDesc* __restrict__ chunks,
-                                                         StepConsts c) {
+                                                         StepConsts c_arg, const StepConsts* cdev) {
+    const StepConsts c = step_consts<DEVC>(c_arg, cdev);
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         fused_tile<NS, BF16, false, false, GENERAL, POL>(T, b, e, c);
     });
@@ -1024,8 +1056,10 @@ __global__ __launch_bounds__(kBlock) void mt_step_kernel(const TensorDesc* __res
 // as one range T: workgroup b covers elements [b*kTile, (b+1)*kTile).  The
 // elements and their arithmetic are those of mt_step_kernel; only the way a
 // workgroup finds its tile differs.
-template <int NS, bool BF16, int POL>
-__global__ __launch_bounds__(kBlock) void run_step_kernel(TensorDesc T, StepConsts c) {
+template <int NS, bool BF16, int POL, bool DEVC>
+__global__ __launch_bounds__(kBlock) void run_step_kernel(TensorDesc T, StepConsts c_arg,
+                                                          const StepConsts* cdev) {
+    const StepConsts c = step_consts<DEVC>(c_arg, cdev);
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
     fused_range<NS, BF16, false, false, false, false, false, POL>(
         T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
@@ -1065,10 +1099,12 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(float* a, const void
 }
 
 // Pass 2 of a clipped step: AdamW and cast from grad_shard_out times *scale.
-template <bool GENERAL, int POL>
+template <bool GENERAL, int POL, bool DEVC>
 __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc* __restrict__ tensors,
                                                                 const ChunkDesc* __restrict__ chunks,
-                                                                StepConsts c, const float* scale) {
+                                                                StepConsts c_arg, const float* scale,
+                                                                const StepConsts* cdev) {
+    const StepConsts c = step_consts<DEVC>(c_arg, cdev);
     const float k = *scale;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         if (GENERAL && (T.gen & kGenStore)) scaled_range<true, POL>(T, b, e, k, c);
@@ -1209,6 +1245,24 @@ __global__ void clip_coef_kernel(float* coef_out, double* norm_out, const double
     if (norm_out) st(norm_out, norm);
 }
 
+// A step whose count lives in device memory: advance *step_dev by one and
+// derive that step's count-dependent scalars into *out (when out is not
+// null), the others coming from the host in `c`.  One lane does it all, with
+// vector memory accesses.
+__global__ __launch_bounds__(kBlock) void step_count_kernel(int64_t* step_dev, StepConsts c, double lr,
+                                                            double beta1, double beta2, StepConsts* out) {
+    if (threadIdx.x != 0) return;
+    const int64_t t = ld(step_dev) + 1;
+    st(step_dev, t);
+    if (!out) return;
+    count_scalars(c, lr, beta1, beta2, t);
+    static_assert(sizeof(StepConsts) % 4 == 0, "the scalars are stored as 32-bit words");
+    uint32_t w[sizeof(StepConsts) / 4];
+    __builtin_memcpy(w, &c, sizeof c);
+#pragma unroll
+    for (size_t i = 0; i < sizeof(StepConsts) / 4; ++i) st(reinterpret_cast<uint32_t*>(out) + i, w[i]);
+}
+
 // Single-shard kernels: workgroup b covers elements [b*kTile, (b+1)*kTile).
 // GEN: the slices (the gradient, for AdamW alone) or the bf16 copy start off
 // a vector boundary, the fp32 buffers on it.
@@ -1248,58 +1302,67 @@ __global__ __launch_bounds__(kBlock) void reduce_sqnorm_single_kernel(TensorDesc
 
 // ---------------------------------------------------------------- kernel selection
 
-using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts);
+using MtKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const StepConsts*);
 using ReduceKernel = void (*)(TensorDesc, StepConsts);
 
-template <bool BF16, bool GENERAL, int POL>
+template <bool BF16, bool GENERAL, int POL, bool DEVC>
 MtKernel pick_mt(int n) {
     switch (n) {
-        case 1: return mt_step_kernel<1, BF16, GENERAL, POL>;
-        case 2: return mt_step_kernel<2, BF16, GENERAL, POL>;
-        case 4: return mt_step_kernel<4, BF16, GENERAL, POL>;
-        case 8: return mt_step_kernel<8, BF16, GENERAL, POL>;
-        default: return mt_step_kernel<0, BF16, GENERAL, POL>;
+        case 1: return mt_step_kernel<1, BF16, GENERAL, POL, DEVC>;
+        case 2: return mt_step_kernel<2, BF16, GENERAL, POL, DEVC>;
+        case 4: return mt_step_kernel<4, BF16, GENERAL, POL, DEVC>;
+        case 8: return mt_step_kernel<8, BF16, GENERAL, POL, DEVC>;
+        default: return mt_step_kernel<0, BF16, GENERAL, POL, DEVC>;
     }
 }
 
-template <int POL>
-MtKernel pick_mt(int dtype, int n, bool general) {
-    if (dtype == FSDP_DT_BF16) return general ? pick_mt<true, true, POL>(n) : pick_mt<true, false, POL>(n);
-    return general ? pick_mt<false, true, POL>(n) : pick_mt<false, false, POL>(n);
-}
-
-MtKernel pick_mt(int dtype, int n, bool general, int pol) {
-    switch (pol) {
-        case kStWriteThrough: return pick_mt<kStWriteThrough>(dtype, n, general);
-        case kStNtWriteThrough: return pick_mt<kStNtWriteThrough>(dtype, n, general);
-        default: return pick_mt<kStPlain>(dtype, n, general);
+// The fused step's store policy as a compile-time constant: the one chosen
+// for the plan (write-through or its non-temporal form), or the one forced at
+// build time.
+template <typename Pick>
+auto by_step_policy(int pol, Pick pick) {
+    if constexpr (RS_ST_POLICY >= 0) {
+        (void)pol;
+        return pick(std::integral_constant<int, RS_ST_POLICY>{});
+    } else {
+        return pol == kStNtWriteThrough ? pick(std::integral_constant<int, kStNtWriteThrough>{})
+                                        : pick(std::integral_constant<int, kStWriteThrough>{});
     }
 }
 
-using RunKernel = void (*)(TensorDesc, StepConsts);
+MtKernel pick_mt(int dtype, int n, bool general, int pol, bool devc) {
+    return by_step_policy(pol, [&](auto P) {
+        constexpr int kPol = decltype(P)::value;
+        if (devc) {
+            if (dtype == FSDP_DT_BF16)
+                return general ? pick_mt<true, true, kPol, true>(n) : pick_mt<true, false, kPol, true>(n);
+            return general ? pick_mt<false, true, kPol, true>(n) : pick_mt<false, false, kPol, true>(n);
+        }
+        if (dtype == FSDP_DT_BF16)
+            return general ? pick_mt<true, true, kPol, false>(n) : pick_mt<true, false, kPol, false>(n);
+        return general ? pick_mt<false, true, kPol, false>(n) : pick_mt<false, false, kPol, false>(n);
+    });
+}
 
-template <bool BF16, int POL>
+using RunKernel = void (*)(TensorDesc, StepConsts, const StepConsts*);
+
+template <bool BF16, int POL, bool DEVC>
 RunKernel pick_run(int n) {
     switch (n) {
-        case 1: return run_step_kernel<1, BF16, POL>;
-        case 2: return run_step_kernel<2, BF16, POL>;
-        case 4: return run_step_kernel<4, BF16, POL>;
-        case 8: return run_step_kernel<8, BF16, POL>;
-        default: return run_step_kernel<0, BF16, POL>;
+        case 1: return run_step_kernel<1, BF16, POL, DEVC>;
+        case 2: return run_step_kernel<2, BF16, POL, DEVC>;
+        case 4: return run_step_kernel<4, BF16, POL, DEVC>;
+        case 8: return run_step_kernel<8, BF16, POL, DEVC>;
+        default: return run_step_kernel<0, BF16, POL, DEVC>;
     }
 }
 
-template <int POL>
-RunKernel pick_run(int dtype, int n) {
-    return dtype == FSDP_DT_BF16 ? pick_run<true, POL>(n) : pick_run<false, POL>(n);
-}
-
-RunKernel pick_run(int dtype, int n, int pol) {
-    switch (pol) {
-        case kStWriteThrough: return pick_run<kStWriteThrough>(dtype, n);
-        case kStNtWriteThrough: return pick_run<kStNtWriteThrough>(dtype, n);
-        default: return pick_run<kStPlain>(dtype, n);
-    }
+RunKernel pick_run(int dtype, int n, int pol, bool devc) {
+    return by_step_policy(pol, [&](auto P) {
+        constexpr int kPol = decltype(P)::value;
+        if (devc) return dtype == FSDP_DT_BF16 ? pick_run<true, kPol, true>(n) : pick_run<false, kPol, true>(n);
+        return dtype == FSDP_DT_BF16 ? pick_run<true, kPol, false>(n) : pick_run<false, kPol, false>(n);
+    });
 }
 
 // The policy a pass's stores run under: the one chosen for the launch
@@ -1397,12 +1460,14 @@ AccumulateKernel pick_accumulate(bool bf16, bool gen, int pol) {
     });
 }
 
-using ScaledStepKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const float*);
+using ScaledStepKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const float*,
+                                  const StepConsts*);
 
-ScaledStepKernel pick_scaled_step(bool general, int pol) {
+ScaledStepKernel pick_scaled_step(bool general, int pol, bool devc) {
     return by_policy(pol, [&](auto P) -> ScaledStepKernel {
         constexpr int kPol = decltype(P)::value;
-        return general ? mt_scaled_step_kernel<true, kPol> : mt_scaled_step_kernel<false, kPol>;
+        if (devc) return general ? mt_scaled_step_kernel<true, kPol, true> : mt_scaled_step_kernel<false, kPol, true>;
+        return general ? mt_scaled_step_kernel<true, kPol, false> : mt_scaled_step_kernel<false, kPol, false>;
     });
 }
 
@@ -1462,16 +1527,12 @@ int32_t check_hparams(const fsdp_adamw_hparams* hp) {
 StepConsts make_consts(const fsdp_adamw_hparams* hp, int32_t n) {
     StepConsts c{};
     if (hp) {
-        const double t = static_cast<double>(hp->step);
-        const double bc1 = 1.0 - std::pow(hp->beta1, t);
-        const double bc2 = 1.0 - std::pow(hp->beta2, t);
         c.decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
         c.beta1 = static_cast<float>(hp->beta1);
         c.omb1 = static_cast<float>(1.0 - hp->beta1);
         c.beta2 = static_cast<float>(hp->beta2);
         c.omb2 = static_cast<float>(1.0 - hp->beta2);
-        c.step_size = static_cast<float>(hp->lr / bc1);
-        c.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+        count_scalars(c, hp->lr, hp->beta1, hp->beta2, hp->step);
         c.eps = static_cast<float>(hp->eps);
     }
     c.n = n;
@@ -1648,6 +1709,7 @@ struct fsdp_mt_plan {
     const void** d_slice_ptrs = nullptr;  // the shards' tables of slice pointers, if any
     double* d_partials = nullptr;    // clipped steps: one sum of squares per workgroup,
                                      // then kSumBlocks second-stage sums
+    StepConsts* d_consts = nullptr;  // steps whose count is in device memory: that step's scalars
     fsdp::Footprint footprint;       // the shards' buffers, for checking the calls' other buffers
     int store_pol = kStPlain;        // how the fused step stores the updated state
     bool has_run = false;            // the shards lie back to back in every buffer:
@@ -2148,6 +2210,7 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
     if (e == hipSuccess && !chunks.empty()) {
         e = alloc(&plan->d_tensors, descs.size() * sizeof(TensorDesc));
         if (e == hipSuccess) e = alloc(&plan->d_chunks, chunks.size() * sizeof(ChunkDesc));
+        if (e == hipSuccess) e = alloc(&plan->d_consts, sizeof(StepConsts));
         if (e == hipSuccess && all_grad_out)
             e = alloc(&plan->d_partials, static_cast<size_t>(plan->n_blocks + kSumBlocks) * sizeof(double));
         if (e == hipSuccess)
@@ -2169,32 +2232,74 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
     return FSDP_OK;
 }
 
-extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                hipStream_t stream) {
-    const char* who = "fsdp_mt_step";
+// A step's scalars for a plan launch: from hp on the host, or, with a device
+// step count, advance the count and derive them on the device (a one-lane
+// launch queued first) into the plan's slot, which *cdev then names.  hp's
+// own step is not used then.
+static int32_t queue_step_consts(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, int64_t* step_dev,
+                          hipStream_t stream, StepConsts* c, const StepConsts** cdev, const char* who) {
+    *cdev = nullptr;
+    *c = make_consts(hp, plan->n_slices);
+    if (!step_dev) return FSDP_OK;
+    hipLaunchKernelGGL(step_count_kernel, dim3(1), dim3(kBlock), 0, stream, step_dev, *c, hp->lr,
+                       hp->beta1, hp->beta2, plan->n_chunks > 0 ? plan->d_consts : nullptr);
+    *cdev = plan->d_consts;
+    return launch_status(who);
+}
+
+// The hyperparameter and step-count checks of the calls that take a device
+// step count: hp as for a call (its step aside), and step_dev a device int64
+// that is no buffer of the plan's.
+static int32_t check_step_dev(const fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, const int64_t* step_dev,
+                       const char* who) {
+    if (!hp) return fail(FSDP_E_ARG, "%s: null hyperparameters", who);
+    fsdp_adamw_hparams h = *hp;
+    h.step = 1;
+    int32_t st;
+    if ((st = check_hparams(&h)) != FSDP_OK) return st;
+    if (!step_dev) return fail(FSDP_E_ARG, "%s: null step_dev", who);
+    if (!aligned(step_dev, 8)) return fail(FSDP_E_ALIGN, "%s: step_dev not 8-byte aligned", who);
+    return check_extra(plan, step_dev, 8, true, who, "step_dev");
+}
+
+// capturable: the count comes from step_dev (which must then be given).
+static int32_t mt_step_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bool capturable,
+                            int64_t* step_dev, hipStream_t stream, const char* who) {
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
-    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    if ((st = capturable ? check_step_dev(plan, hp, step_dev, who) : check_hparams(hp)) != FSDP_OK) return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    StepConsts c;
+    const StepConsts* cdev;
+    if ((st = queue_step_consts(plan, hp, step_dev, stream, &c, &cdev, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
-    const StepConsts c = make_consts(hp, plan->n_slices);
     const int64_t budget = plan->store_pol == kStWriteThrough     ? RS_INFLIGHT_KB_WT
                            : plan->store_pol == kStNtWriteThrough ? RS_INFLIGHT_KB_NTWT
                                                                   : RS_INFLIGHT_KB;
     if (plan->has_run) {
-        const RunKernel k = pick_run(plan->slice_dtype, plan->n_slices, plan->store_pol);
+        const RunKernel k = pick_run(plan->slice_dtype, plan->n_slices, plan->store_pol, cdev != nullptr);
         const int64_t run_budget = plan->store_pol == kStWriteThrough ? RS_INFLIGHT_KB_RUN : budget;
         plan_launch(plan, true, k, dim3(static_cast<uint32_t>(tiles_for(plan->run.shard_numel))),
-                    dim3(kBlock), lds_reserve(step_bytes(plan), run_budget), stream, plan->run, c);
+                    dim3(kBlock), lds_reserve(step_bytes(plan), run_budget), stream, plan->run, c, cdev);
         return launch_status(who);
     }
     const size_t lds = lds_reserve(step_bytes(plan), budget);
-    const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_general, plan->store_pol);
+    const MtKernel k = pick_mt(plan->slice_dtype, plan->n_slices, plan->any_general, plan->store_pol,
+                               cdev != nullptr);
     plan_launch(plan, true, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock), lds, stream,
-                plan->d_tensors, plan->d_chunks, c);
+                plan->d_tensors, plan->d_chunks, c, cdev);
     return launch_status(who);
 }
 
+extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                hipStream_t stream) {
+    return mt_step_impl(plan, hp, false, nullptr, stream, "fsdp_mt_step");
+}
+
+extern "C" int32_t fsdp_mt_step_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                           int64_t* step_dev, hipStream_t stream) {
+    return mt_step_impl(plan, hp, true, step_dev, stream, "fsdp_mt_step_capturable");
+}
 
 extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumulate,
                                              double* sqnorm_out, hipStream_t stream) {
@@ -2298,25 +2403,44 @@ static int32_t clip_coef_impl(float* coef_out, double* norm_out, const double* s
     return launch_status(who);
 }
 
-extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                        const float* grad_scale, hipStream_t stream) {
-    const char* who = "fsdp_mt_step_clipped";
+static int32_t mt_step_clipped_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bool capturable,
+                                    int64_t* step_dev, const float* grad_scale, hipStream_t stream,
+                                    const char* who) {
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
-    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    if ((st = capturable ? check_step_dev(plan, hp, step_dev, who) : check_hparams(hp)) != FSDP_OK) return st;
     if (!grad_scale) return fail(FSDP_E_ARG, "%s: null grad_scale", who);
     if (!aligned(grad_scale, 4)) return fail(FSDP_E_ALIGN, "%s: grad_scale misaligned", who);
     if (!plan->all_grad_out)
         return fail(FSDP_E_ARG, "%s: every shard of the plan needs a grad_shard_out", who);
     if ((st = check_extra(plan, grad_scale, 4, false, who, "grad_scale")) != FSDP_OK) return st;
+    if (step_dev) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(step_dev), b = reinterpret_cast<uintptr_t>(grad_scale);
+        if (a < b + 4 && b < a + 8)
+            return fail(FSDP_E_ALIAS, "%s: step_dev overlaps grad_scale", who);
+    }
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    StepConsts c;
+    const StepConsts* cdev;
+    if ((st = queue_step_consts(plan, hp, step_dev, stream, &c, &cdev, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
-    const StepConsts c = make_consts(hp, plan->n_slices);
-    const ScaledStepKernel k = pick_scaled_step(plan->any_general, write_policy(4 + 12, 12 + 2 * plan->any_bf16));
+    const ScaledStepKernel k =
+        pick_scaled_step(plan->any_general, write_policy(4 + 12, 12 + 2 * plan->any_bf16), cdev != nullptr);
     plan_launch(plan, true, k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                 lds_reserve(4 + 24 + 2 * plan->any_bf16), stream, plan->d_tensors, plan->d_chunks, c,
-                grad_scale);
+                grad_scale, cdev);
     return launch_status(who);
+}
+
+extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                        const float* grad_scale, hipStream_t stream) {
+    return mt_step_clipped_impl(plan, hp, false, nullptr, grad_scale, stream, "fsdp_mt_step_clipped");
+}
+
+extern "C" int32_t fsdp_mt_step_clipped_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                                   int64_t* step_dev, const float* grad_scale,
+                                                   hipStream_t stream) {
+    return mt_step_clipped_impl(plan, hp, true, step_dev, grad_scale, stream, "fsdp_mt_step_clipped_capturable");
 }
 
 extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
@@ -2630,7 +2754,7 @@ extern "C" int32_t fsdp_mt_plan_destroy(fsdp_mt_plan* plan) {
         if (e == hipSuccess) e = d;
     }
     void* const bufs[] = {plan->d_slice_ptrs, plan->d_tensors, plan->d_chunks, plan->d_partials,
-                          plan->d_tile_amax, plan->d_shard_tiles};
+                          plan->d_tile_amax, plan->d_shard_tiles, plan->d_consts};
     const bool any = std::any_of(std::begin(bufs), std::end(bufs), [](void* b) { return b != nullptr; });
     if (any && plan->pooled) {
         // stream-ordered frees on the plan's device, which wait for nothing

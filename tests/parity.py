@@ -175,6 +175,19 @@ def check_pad_zero(name, arr, valid):
             f"{name}: pad not +0"
 
 
+def pow_steps(b, t):
+    """b**t by binary powering in double, the library's own sequence of
+    products for the bias corrections (Python floats are IEEE doubles)."""
+    r, x = 1.0, float(b)
+    t = int(t)
+    while t > 0:
+        if t & 1:
+            r = r * x
+        x = x * x
+        t >>= 1
+    return r
+
+
 def fp32_replica_step(p, m, v, x, valid, t, hp, grad_scale=None):
     """The kernel's fp32 operation sequence, replayed in numpy (test-side
     only; the oracle stays float64).  Sum of the slices in slice order,
@@ -201,8 +214,8 @@ def fp32_replica_step(p, m, v, x, valid, t, hp, grad_scale=None):
     g = s.astype(f32)
     if grad_scale is not None:
         g = (g * f32(grad_scale)).astype(f32)
-    bc1 = 1.0 - hp["beta1"] ** t
-    bc2 = 1.0 - hp["beta2"] ** t
+    bc1 = 1.0 - pow_steps(hp["beta1"], t)
+    bc2 = 1.0 - pow_steps(hp["beta2"], t)
     decay = f32(1.0 - hp["lr"] * hp["weight_decay"])
     b1, omb1 = f32(hp["beta1"]), f32(1.0 - hp["beta1"])
     b2, omb2 = f32(hp["beta2"]), f32(1.0 - hp["beta2"])

@@ -1,0 +1,192 @@
+"""GPU: the capturable step calls, whose step count lives in device memory.
+
+fsdp_mt_step_capturable and fsdp_mt_step_clipped_capturable advance a device
+int64 count and step at the new count, deriving the count's scalars on the
+device with the host's operations.  So:
+  * eager calls equal fsdp_mt_step / fsdp_mt_step_clipped at t = 1, 2, ...
+    bit for bit (one-range and chunk-table plans, both store policies);
+  * one captured HIP graph, replayed with eager work and synchronisations
+    between replays, steps through t = 1, 2, ... and equals the eager
+    fixed-count calls at each t bit for bit, the count ending at the number
+    of replays;
+  * counts far out (t up to 10^6, where the bias corrections are 1) still
+    agree with the host's scalars;
+  * an empty plan advances the count only; bad arguments are refused before
+    any work is queued.
+The fixed-count calls are checked against the oracle in the other GPU tests.
+"""
+
+import pytest
+import torch
+
+from rank_step_amd import binding as B
+from rank_step_amd.state import RankState
+from rank_step_amd.workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+STEPS = 4
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def _same(a, b, what):
+    for name in ("master", "exp_avg", "exp_avg_sq", "grad_out", "ag_slot"):
+        x, y = getattr(a, name), getattr(b, name)
+        if x is None:
+            continue
+        assert torch.equal(_bits(x), _bits(y)), f"{what}: {name} differs"
+
+
+def _pair(cfg, gpu, **kw):
+    w = WORKLOADS[cfg]
+    return w, RankState(w, 0, gpu, **kw), RankState(w, 0, gpu, **kw)
+
+
+@pytest.mark.parametrize("cfg", [3, 2])
+def test_eager_capturable_equals_fixed_count(cfg, gpu):
+    """Config 3 (bf16 slices, one range) and config 2 (fp32 slices, one flat
+    shard); the table path is covered by the graph test below."""
+    w, a, b = _pair(cfg, gpu, bf16_out=w_bf16(cfg))
+    a.make_plan(with_grad_out=False)
+    b.make_plan(with_grad_out=False)
+    count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    for t in range(1, STEPS + 1):
+        a.load_grads(t)
+        b.load_grads(t)
+        a.plan.step(w.hparams, t)
+        b.plan.step_capturable(w.hparams, count)
+        torch.cuda.synchronize()
+        _same(a, b, f"{w.name} t={t}")
+        assert int(count.item()) == t
+    a.close()
+    b.close()
+
+
+def w_bf16(cfg):
+    return WORKLOADS[cfg].bf16_out
+
+
+def _table_order_plan(st, **kw):
+    """A plan over the rank's shards listed in reverse: not back to back in
+    list order, so its step goes through the chunk table."""
+    recs = st.mt_tensors(**kw)[::-1]
+    st.plan = B.MtPlan(recs, st.w.n_slices, st.w.slice_dtype)
+    assert st.plan.info()["step_one_range"] == 0
+    return st.plan
+
+
+@pytest.mark.parametrize("table", [False, True])
+def test_graph_replays_advance_the_count(table, gpu):
+    w, a, b = _pair(3, gpu, bf16_out=True)
+    if table:
+        _table_order_plan(a, with_grad_out=False, with_fp8=False)
+        _table_order_plan(b, with_grad_out=False, with_fp8=False)
+    else:
+        a.make_plan(with_grad_out=False)
+        b.make_plan(with_grad_out=False)
+    count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.plan.step_capturable(w.hparams, count)
+    torch.cuda.synchronize()
+    assert int(count.item()) == 0, "capture ran the launches"
+    for t in range(1, STEPS + 1):
+        a.load_grads(t)
+        b.load_grads(t)
+        a.plan.step(w.hparams, t)
+        g.replay()
+        torch.cuda.synchronize()
+        _same(a, b, f"replay {t}")
+        assert int(count.item()) == t
+    del g
+    a.close()
+    b.close()
+
+
+def test_clipped_graph_replays_advance_the_count(gpu):
+    w, a, b = _pair(3, gpu, bf16_out=True, grad_out=True)
+    a.make_plan()
+    b.make_plan()
+    mk = lambda n, dt: torch.zeros(n, dtype=dt, device=gpu)
+    sq_a, coef_a, norm_a = mk(1, torch.float64), mk(1, torch.float32), mk(1, torch.float64)
+    sq_b, coef_b, norm_b = mk(1, torch.float64), mk(1, torch.float32), mk(1, torch.float64)
+    count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.plan.reduce_sqnorm(sq_b)
+        B.fsdp_clip_coef(coef_b, norm_b, sq_b, 1, 0.05)
+        b.plan.step_clipped_capturable(w.hparams, count, coef_b)
+    torch.cuda.synchronize()
+    for t in range(1, STEPS + 1):
+        a.load_grads(t)
+        b.load_grads(t)
+        a.plan.reduce_sqnorm(sq_a)
+        B.fsdp_clip_coef(coef_a, norm_a, sq_a, 1, 0.05)
+        a.plan.step_clipped(w.hparams, t, coef_a)
+        g.replay()
+        torch.cuda.synchronize()
+        _same(a, b, f"clipped replay {t}")
+        assert torch.equal(coef_a, coef_b)
+        assert int(count.item()) == t
+    del g
+    a.close()
+    b.close()
+
+
+def test_far_counts_agree_with_the_host(gpu):
+    """Counts where beta2^t is far from 1 and where it has vanished: the
+    device-derived scalars step exactly as the host's."""
+    w, a, b = _pair(3, gpu, bf16_out=True)
+    a.make_plan(with_grad_out=False)
+    b.make_plan(with_grad_out=False)
+    count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    a.load_grads(1)
+    b.load_grads(1)
+    for t in (2, 3, 17, 999, 1000, 4097, 65536, 10 ** 6):
+        count.fill_(t - 1)
+        a.plan.step(w.hparams, t)
+        b.plan.step_capturable(w.hparams, count)
+        torch.cuda.synchronize()
+        _same(a, b, f"t={t}")
+        assert int(count.item()) == t
+    a.close()
+    b.close()
+
+
+def test_empty_plan_and_refusals(gpu):
+    w = WORKLOADS[3]
+    count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    empty = B.MtPlan([], 8, "bf16")
+    empty.step_capturable(w.hparams, count)
+    torch.cuda.synchronize()
+    assert int(count.item()) == 1
+    empty.close()
+
+    st = RankState(w, 0, gpu, bf16_out=True, grad_out=True)
+    st.make_plan()
+    before = [x.clone() for x in (st.master, st.exp_avg, st.exp_avg_sq)]
+    coef = torch.ones(1, dtype=torch.float32, device=gpu)
+    with pytest.raises(B.FsdpError, match="FSDP_E_ARG"):
+        st.plan.step_capturable(w.hparams, None)
+    with pytest.raises(B.FsdpError, match="FSDP_E_ARG"):
+        st.plan.step_clipped_capturable(w.hparams, None, coef)
+    wide = torch.zeros(3, dtype=torch.int64, device=gpu)
+    with pytest.raises(B.FsdpError, match="FSDP_E_ALIGN"):
+        B.fsdp_mt_step_capturable(st.plan.handle, w.hparams, wide.view(torch.int32)[1:].data_ptr())
+    with pytest.raises(B.FsdpError, match="FSDP_E_ALIAS"):
+        B.fsdp_mt_step_capturable(st.plan.handle, w.hparams, st.exp_avg.data_ptr())
+    with pytest.raises(B.FsdpError, match="FSDP_E_ALIAS"):
+        B.fsdp_mt_step_clipped_capturable(st.plan.handle, w.hparams, coef.data_ptr(), coef.data_ptr())
+    bad = dict(w.hparams, lr=-1.0)
+    with pytest.raises(B.FsdpError, match="FSDP_E_ARG"):
+        st.plan.step_capturable(bad, count)
+    torch.cuda.synchronize()
+    assert int(count.item()) == 1, "a refused call advanced the count"
+    for x, y in zip(before, (st.master, st.exp_avg, st.exp_avg_sq)):
+        assert torch.equal(_bits(x), _bits(y)), "a refused call changed the state"
+    st.close()
