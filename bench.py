@@ -464,6 +464,16 @@ def unfused_chain(st, stream, args, t0):
                                         "hbm_gb_s": bpp * st.total / ms_whole / 1e6}}
 
 
+def launch_info(info):
+    """The fused step's launch, from the plan's info: one range (workgroup b
+    on tile b of the whole) or through the chunk table (8 per entry)."""
+    if info["step_one_range"]:
+        return {"workgroups": -(-info["total_numel"] // 256), "form": "one range",
+                "chunks": info["n_chunks"], "chunk_numel": info["chunk_numel"]}
+    return {"workgroups": info["n_blocks"], "form": "chunk table", "chunks": info["n_chunks"],
+            "chunk_numel": info["chunk_numel"]}
+
+
 def time_fused(w, dev, stream, args, keep=False, **state_kw):
     """Plan the rank's shards of workload ``w`` and time K fused steps
     (``fsdp_mt_step``, one launch each) back to back between two events on
@@ -547,8 +557,7 @@ def time_fused(w, dev, stream, args, keep=False, **state_kw):
         "bytes_per_param": bpp,
         "local_params": total,
         "shards": info["n_tensors"],
-        "launch": {"workgroups": info["n_blocks"], "chunks": info["n_chunks"],
-                   "chunk_numel": info["chunk_numel"]},
+        "launch": launch_info(info),
         "per_step_ms": {"median": per_step[len(per_step) // 2],
                         "p95": per_step[min(len(per_step) - 1, (95 * len(per_step)) // 100)],
                         "min": per_step[0], "max": per_step[-1],
