@@ -361,7 +361,9 @@ int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, hipStream
  * hp->step = t), into a slot the plan owns, and the step launch reads them
  * there.  hp->step is ignored; lr, betas, eps and weight_decay are taken at
  * the call (a captured graph keeps them).  Two launches, no allocation, no
- * host synchronisation; an empty plan advances the count only.  step_dev
+ * host synchronisation; an empty plan advances the count only.  The step
+ * waits for the one-lane launch: about 6 us more per step than fsdp_mt_step
+ * (measured on MI355X), a share only small steps notice.  step_dev
  * must not overlap the plan's buffers (FSDP_E_ALIAS); null is FSDP_E_ARG,
  * misaligned FSDP_E_ALIGN.  Calls on one plan must not overlap (they share
  * the slot). */
