@@ -186,8 +186,8 @@ int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t rank,
  * replayed at step 1000 steps 3.7x too far, with 1/sqrt(1 - beta2^3) = 18.3
  * where 1.0 is due), and nothing reports it.  To step a graph through
  * t = 1, 2, ..., capture the _capturable forms of the step calls, which read
- * the count from device memory (fsdp_mt_step_capturable), or make the calls
- * eagerly. */
+ * the count from device memory (fsdp_mt_step_capturable and the clipped and
+ * fp8 forms), or make the calls eagerly. */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
     int64_t step;
@@ -483,6 +483,12 @@ int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t micro_dtype,
 int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, float* amax_out,
                           hipStream_t stream);
 
+/* fsdp_mt_step_amax with the step count in device memory, as
+ * fsdp_mt_step_capturable: advances *step_dev, then steps at the new count.
+ * step_dev must not overlap amax_out either. */
+int32_t fsdp_mt_step_amax_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                     int64_t* step_dev, float* amax_out, hipStream_t stream);
+
 /* Write every shard's fp8 codes from its updated fp32 parameter.  The amax
  * of shard i is the maximum over r of amax_ranks[r * n_tensors + i] (device
  * fp32 [n_ranks][n_tensors]: the ranks' fsdp_mt_step_amax outputs, or one
@@ -509,6 +515,13 @@ int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_
  * per-workgroup scratch: calls on one plan must not overlap. */
 int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, const float* scale_in,
                          float* amax_out, hipStream_t stream);
+
+/* fsdp_mt_step_fp8 with the step count in device memory, as
+ * fsdp_mt_step_capturable: advances *step_dev, then steps at the new count.
+ * step_dev must not overlap scale_in or amax_out either. */
+int32_t fsdp_mt_step_fp8_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                    int64_t* step_dev, const float* scale_in, float* amax_out,
+                                    hipStream_t stream);
 
 /* ------------------------------------------------------------------ no device allocation */
 

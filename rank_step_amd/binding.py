@@ -30,6 +30,7 @@ LAYOUTS = {"flat": 0, "shard0": 1, "owner": 2}
 EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
            "fsdp_adamw_shard_step", "fsdp_cast_unshard_bf16", "fsdp_mt_plan_create",
            "fsdp_mt_step", "fsdp_mt_step_capturable", "fsdp_mt_step_clipped_capturable",
+           "fsdp_mt_step_amax_capturable", "fsdp_mt_step_fp8_capturable",
            "fsdp_mt_plan_get_info", "fsdp_mt_plan_destroy",
            "fsdp_mt_reduce_sqnorm", "fsdp_clip_coef", "fsdp_mt_step_clipped",
            "fsdp_mt_step_amax", "fsdp_mt_cast_fp8", "fsdp_mt_step_fp8",
@@ -115,6 +116,8 @@ def lib():
             "fsdp_mt_step": [vp, ctypes.POINTER(AdamWHparams), vp],
             "fsdp_mt_step_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
             "fsdp_mt_step_clipped_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp],
+            "fsdp_mt_step_amax_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp],
+            "fsdp_mt_step_fp8_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp, vp],
             "fsdp_mt_plan_get_info": [vp, ctypes.POINTER(MtPlanInfo)],
             "fsdp_mt_plan_destroy": [vp],
             "fsdp_mt_reduce_sqnorm": [vp, vp, vp],
@@ -269,6 +272,18 @@ def fsdp_mt_step_clipped_capturable(plan, hp, step_dev, grad_scale, stream=None)
                                                   _stream(stream)))
 
 
+def fsdp_mt_step_amax_capturable(plan, hp, step_dev, amax_out, stream=None):
+    h = _hparams(hp, 1)
+    _check(lib().fsdp_mt_step_amax_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(amax_out),
+                                               _stream(stream)))
+
+
+def fsdp_mt_step_fp8_capturable(plan, hp, step_dev, scale_in, amax_out, stream=None):
+    h = _hparams(hp, 1)
+    _check(lib().fsdp_mt_step_fp8_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(scale_in),
+                                              _ptr(amax_out), _stream(stream)))
+
+
 def fsdp_mt_step_amax(plan, hp, step, amax_out, stream=None):
     h = _hparams(hp, step)
     _check(lib().fsdp_mt_step_amax(plan, ctypes.byref(h), _ptr(amax_out), _stream(stream)))
@@ -319,6 +334,12 @@ class MtPlan:
 
     def step_clipped_capturable(self, hp, step_dev, grad_scale, stream=None):
         fsdp_mt_step_clipped_capturable(self.handle, hp, step_dev, grad_scale, stream)
+
+    def step_amax_capturable(self, hp, step_dev, amax_out, stream=None):
+        fsdp_mt_step_amax_capturable(self.handle, hp, step_dev, amax_out, stream)
+
+    def step_fp8_capturable(self, hp, step_dev, scale_in, amax_out, stream=None):
+        fsdp_mt_step_fp8_capturable(self.handle, hp, step_dev, scale_in, amax_out, stream)
 
     def info(self):
         return fsdp_mt_plan_get_info(self.handle)

@@ -1114,10 +1114,12 @@ __global__ __launch_bounds__(kBlock) void mt_scaled_step_kernel(const TensorDesc
 
 // The fused step that also records, per workgroup, the largest |p'| (as
 // fp32 bits, in the workgroup's slot) for the fp8 copy's per-tensor scale.
-template <int NS, bool BF16, bool GENERAL, int POL>
+template <int NS, bool BF16, bool GENERAL, int POL, bool DEVC>
 __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* __restrict__ tensors,
                                                               const ChunkDesc* __restrict__ chunks,
-                                                              StepConsts c, uint32_t* tile_amax) {
+                                                              StepConsts c_arg, uint32_t* tile_amax,
+                                                              const StepConsts* cdev) {
+    const StepConsts c = step_consts<DEVC>(c_arg, cdev);
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         fused_tile<NS, BF16, true, false, GENERAL, POL>(T, b, e, c, &am);
@@ -1129,11 +1131,12 @@ __global__ __launch_bounds__(kBlock) void mt_step_amax_kernel(const TensorDesc* 
 // The fused step that also writes the fp8 codes of p' with a per-tensor scale
 // given in advance (scale_in[index], e.g. from the previous step's amax) and
 // records this step's per-workgroup largest |p'|, all in the one pass.
-template <int NS, bool BF16, bool GENERAL, int POL>
+template <int NS, bool BF16, bool GENERAL, int POL, bool DEVC>
 __global__ __launch_bounds__(kBlock) void mt_step_fp8_kernel(const TensorDesc* __restrict__ tensors,
                                                              const ChunkDesc* __restrict__ chunks,
-                                                             StepConsts c, const float* scale_in,
-                                                             uint32_t* tile_amax) {
+                                                             StepConsts c_arg, const float* scale_in,
+                                                             uint32_t* tile_amax, const StepConsts* cdev) {
+    const StepConsts c = step_consts<DEVC>(c_arg, cdev);
     uint32_t am = 0;
     for_my_tile(tensors, chunks, [&](const TensorDesc& T, int64_t b, int64_t e) {
         const float scale = ld(scale_in + T.index);
@@ -1405,48 +1408,58 @@ ReduceStoreKernel pick_reduce_store(int dtype, int n, bool sq, bool general, int
     });
 }
 
-using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, uint32_t*);
+using AmaxKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, uint32_t*, const StepConsts*);
 
-template <bool BF16, bool GENERAL, int POL>
+template <bool BF16, bool GENERAL, int POL, bool DEVC>
 AmaxKernel pick_amax(int n) {
     switch (n) {
-        case 1: return mt_step_amax_kernel<1, BF16, GENERAL, POL>;
-        case 2: return mt_step_amax_kernel<2, BF16, GENERAL, POL>;
-        case 4: return mt_step_amax_kernel<4, BF16, GENERAL, POL>;
-        case 8: return mt_step_amax_kernel<8, BF16, GENERAL, POL>;
-        default: return mt_step_amax_kernel<0, BF16, GENERAL, POL>;
+        case 1: return mt_step_amax_kernel<1, BF16, GENERAL, POL, DEVC>;
+        case 2: return mt_step_amax_kernel<2, BF16, GENERAL, POL, DEVC>;
+        case 4: return mt_step_amax_kernel<4, BF16, GENERAL, POL, DEVC>;
+        case 8: return mt_step_amax_kernel<8, BF16, GENERAL, POL, DEVC>;
+        default: return mt_step_amax_kernel<0, BF16, GENERAL, POL, DEVC>;
     }
 }
 
-AmaxKernel pick_amax(int dtype, int n, bool general, int pol) {
+template <int POL, bool DEVC>
+AmaxKernel pick_amax(int dtype, int n, bool general) {
+    if (dtype == FSDP_DT_BF16)
+        return general ? pick_amax<true, true, POL, DEVC>(n) : pick_amax<true, false, POL, DEVC>(n);
+    return general ? pick_amax<false, true, POL, DEVC>(n) : pick_amax<false, false, POL, DEVC>(n);
+}
+
+AmaxKernel pick_amax(int dtype, int n, bool general, int pol, bool devc) {
     return by_policy(pol, [&](auto P) {
         constexpr int kPol = decltype(P)::value;
-        if (dtype == FSDP_DT_BF16)
-            return general ? pick_amax<true, true, kPol>(n) : pick_amax<true, false, kPol>(n);
-        return general ? pick_amax<false, true, kPol>(n) : pick_amax<false, false, kPol>(n);
+        return devc ? pick_amax<kPol, true>(dtype, n, general) : pick_amax<kPol, false>(dtype, n, general);
     });
 }
 
 using Fp8StepKernel = void (*)(const TensorDesc*, const ChunkDesc*, StepConsts, const float*,
-                               uint32_t*);
+                               uint32_t*, const StepConsts*);
 
-template <bool BF16, bool GENERAL, int POL>
+template <bool BF16, bool GENERAL, int POL, bool DEVC>
 Fp8StepKernel pick_fp8_step(int n) {
     switch (n) {
-        case 1: return mt_step_fp8_kernel<1, BF16, GENERAL, POL>;
-        case 2: return mt_step_fp8_kernel<2, BF16, GENERAL, POL>;
-        case 4: return mt_step_fp8_kernel<4, BF16, GENERAL, POL>;
-        case 8: return mt_step_fp8_kernel<8, BF16, GENERAL, POL>;
-        default: return mt_step_fp8_kernel<0, BF16, GENERAL, POL>;
+        case 1: return mt_step_fp8_kernel<1, BF16, GENERAL, POL, DEVC>;
+        case 2: return mt_step_fp8_kernel<2, BF16, GENERAL, POL, DEVC>;
+        case 4: return mt_step_fp8_kernel<4, BF16, GENERAL, POL, DEVC>;
+        case 8: return mt_step_fp8_kernel<8, BF16, GENERAL, POL, DEVC>;
+        default: return mt_step_fp8_kernel<0, BF16, GENERAL, POL, DEVC>;
     }
 }
 
-Fp8StepKernel pick_fp8_step(int dtype, int n, bool general, int pol) {
+template <int POL, bool DEVC>
+Fp8StepKernel pick_fp8_step(int dtype, int n, bool general) {
+    if (dtype == FSDP_DT_BF16)
+        return general ? pick_fp8_step<true, true, POL, DEVC>(n) : pick_fp8_step<true, false, POL, DEVC>(n);
+    return general ? pick_fp8_step<false, true, POL, DEVC>(n) : pick_fp8_step<false, false, POL, DEVC>(n);
+}
+
+Fp8StepKernel pick_fp8_step(int dtype, int n, bool general, int pol, bool devc) {
     return by_policy(pol, [&](auto P) {
         constexpr int kPol = decltype(P)::value;
-        if (dtype == FSDP_DT_BF16)
-            return general ? pick_fp8_step<true, true, kPol>(n) : pick_fp8_step<true, false, kPol>(n);
-        return general ? pick_fp8_step<false, true, kPol>(n) : pick_fp8_step<false, false, kPol>(n);
+        return devc ? pick_fp8_step<kPol, true>(dtype, n, general) : pick_fp8_step<kPol, false>(dtype, n, general);
     });
 }
 
@@ -2443,32 +2456,58 @@ extern "C" int32_t fsdp_mt_step_clipped_capturable(fsdp_mt_plan* plan, const fsd
     return mt_step_clipped_impl(plan, hp, true, step_dev, grad_scale, stream, "fsdp_mt_step_clipped_capturable");
 }
 
-extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                     float* amax_out, hipStream_t stream) {
-    const char* who = "fsdp_mt_step_amax";
+// Two device buffers of a call on one plan may not overlap each other.
+static int32_t check_disjoint(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes,
+                              const char* who, const char* what) {
+    if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return FSDP_OK;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    if (x < y + static_cast<uintptr_t>(b_bytes) && y < x + static_cast<uintptr_t>(a_bytes))
+        return fail(FSDP_E_ALIAS, "%s: %s", who, what);
+    return FSDP_OK;
+}
+
+static int32_t mt_step_amax_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bool capturable,
+                                 int64_t* step_dev, float* amax_out, hipStream_t stream, const char* who) {
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
-    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    if ((st = capturable ? check_step_dev(plan, hp, step_dev, who) : check_hparams(hp)) != FSDP_OK) return st;
     if (!plan->any_fp8) return fail(FSDP_E_ARG, "%s: the plan has no fp8 outputs", who);
     if (!amax_out) return fail(FSDP_E_ARG, "%s: null amax_out", who);
     if (!aligned(amax_out, 4)) return fail(FSDP_E_ALIGN, "%s: amax_out misaligned", who);
     if ((st = check_extra(plan, amax_out, 4 * plan->n_tensors, true, who, "amax_out")) != FSDP_OK)
         return st;
+    if ((st = check_disjoint(step_dev, 8, amax_out, 4 * plan->n_tensors, who,
+                             "step_dev overlaps amax_out")) != FSDP_OK)
+        return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    StepConsts c;
+    const StepConsts* cdev;
+    if ((st = queue_step_consts(plan, hp, capturable ? step_dev : nullptr, stream, &c, &cdev, who)) != FSDP_OK)
+        return st;
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
-        const StepConsts c = make_consts(hp, plan->n_slices);
         const AmaxKernel k = pick_amax(plan->slice_dtype, plan->n_slices, plan->any_general,
-                                       write_policy(plan_slice_read(plan) + 12, 12 + plan_copy_write(plan)));
+                                       write_policy(plan_slice_read(plan) + 12, 12 + plan_copy_write(plan)),
+                                       cdev != nullptr);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(step_bytes(plan), RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
-                           plan->d_chunks, c, plan->d_tile_amax);
+                           plan->d_chunks, c, plan->d_tile_amax, cdev);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
     plan_launch(plan, true, shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)),
                 dim3(kAmaxBlock), 0, stream, static_cast<const ShardTiles*>(plan->d_shard_tiles),
                 static_cast<const uint32_t*>(plan->d_tile_amax), plan->n_blocks / kXcds, amax_out);
     return launch_status(who);
+}
+
+extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                     float* amax_out, hipStream_t stream) {
+    return mt_step_amax_impl(plan, hp, false, nullptr, amax_out, stream, "fsdp_mt_step_amax");
+}
+
+extern "C" int32_t fsdp_mt_step_amax_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                                int64_t* step_dev, float* amax_out, hipStream_t stream) {
+    return mt_step_amax_impl(plan, hp, true, step_dev, amax_out, stream, "fsdp_mt_step_amax_capturable");
 }
 
 static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_ranks,
@@ -2507,12 +2546,12 @@ static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int
     return launch_status(who);
 }
 
-static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                const float* scale_in, float* amax_out, hipStream_t stream) {
-    const char* who = "fsdp_mt_step_fp8";
+static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bool capturable,
+                                int64_t* step_dev, const float* scale_in, float* amax_out,
+                                hipStream_t stream, const char* who) {
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
-    if ((st = check_hparams(hp)) != FSDP_OK) return st;
+    if ((st = capturable ? check_step_dev(plan, hp, step_dev, who) : check_hparams(hp)) != FSDP_OK) return st;
     if (!plan->all_fp8) return fail(FSDP_E_ARG, "%s: every shard of the plan needs an fp8 output", who);
     if (plan->n_tensors > 0 && (!scale_in || !amax_out))
         return fail(FSDP_E_ARG, "%s: null scale_in or amax_out", who);
@@ -2526,16 +2565,25 @@ static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if ((st = check_extra(plan, scale_in, 4 * plan->n_tensors, false, who, "scale_in")) != FSDP_OK ||
         (st = check_extra(plan, amax_out, 4 * plan->n_tensors, true, who, "amax_out")) != FSDP_OK)
         return st;
+    if ((st = check_disjoint(step_dev, 8, amax_out, 4 * plan->n_tensors, who,
+                             "step_dev overlaps amax_out")) != FSDP_OK ||
+        (st = check_disjoint(step_dev, 8, scale_in, 4 * plan->n_tensors, who,
+                             "step_dev overlaps scale_in")) != FSDP_OK)
+        return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
+    StepConsts c;
+    const StepConsts* cdev;
+    if ((st = queue_step_consts(plan, hp, capturable ? step_dev : nullptr, stream, &c, &cdev, who)) != FSDP_OK)
+        return st;
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
-        const StepConsts c = make_consts(hp, plan->n_slices);
         const Fp8StepKernel k =
             pick_fp8_step(plan->slice_dtype, plan->n_slices, plan->any_general,
-                          write_policy(plan_slice_read(plan) + 12, 12 + plan_copy_write(plan) + plan->any_fp8));
+                          write_policy(plan_slice_read(plan) + 12, 12 + plan_copy_write(plan) + plan->any_fp8),
+                          cdev != nullptr);
         hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(plan->n_blocks)), dim3(kBlock),
                            lds_reserve(step_bytes(plan) + 1, RS_INFLIGHT_KB_FP8), stream, plan->d_tensors,
-                           plan->d_chunks, c, scale_in, plan->d_tile_amax);
+                           plan->d_chunks, c, scale_in, plan->d_tile_amax, cdev);
         if ((st = launch_status(who)) != FSDP_OK) return st;
     }
     plan_launch(plan, true, shard_amax_kernel, dim3(static_cast<uint32_t>(plan->n_tensors)),
@@ -2724,7 +2772,16 @@ extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks,
 extern "C" int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                                     const float* scale_in, float* amax_out, hipStream_t stream) {
     return fsdp::guarded("fsdp_mt_step_fp8", [&] {
-        return mt_step_fp8_impl(plan, hp, scale_in, amax_out, stream);
+        return mt_step_fp8_impl(plan, hp, false, nullptr, scale_in, amax_out, stream, "fsdp_mt_step_fp8");
+    });
+}
+
+extern "C" int32_t fsdp_mt_step_fp8_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
+                                               int64_t* step_dev, const float* scale_in, float* amax_out,
+                                               hipStream_t stream) {
+    return fsdp::guarded("fsdp_mt_step_fp8_capturable", [&] {
+        return mt_step_fp8_impl(plan, hp, true, step_dev, scale_in, amax_out, stream,
+                                "fsdp_mt_step_fp8_capturable");
     });
 }
 

@@ -5,6 +5,9 @@ int64 count and step at the new count, deriving the count's scalars on the
 device with the host's operations.  So:
   * eager calls equal fsdp_mt_step / fsdp_mt_step_clipped at t = 1, 2, ...
     bit for bit (one-range and chunk-table plans, both store policies);
+  * the fp8 forms (fsdp_mt_step_amax_capturable, fsdp_mt_step_fp8_capturable)
+    replayed from captured graphs equal the fixed-count fp8 calls, codes,
+    maxima and scales included;
   * one captured HIP graph, replayed with eager work and synchronisations
     between replays, steps through t = 1, 2, ... and equals the eager
     fixed-count calls at each t bit for bit, the count ending at the number
@@ -138,6 +141,50 @@ def test_clipped_graph_replays_advance_the_count(gpu):
     b.close()
 
 
+def _same_fp8(a, b, what):
+    _same(a, b, what)
+    assert torch.equal(a.fp8, b.fp8), f"{what}: fp8 codes differ"
+
+
+def test_fp8_graph_replays_advance_the_count(gpu):
+    """Dynamic scaling (step with amax, then the codes) and delayed scaling
+    (one pass with the previous step's scales), each captured once."""
+    w, a, b = _pair(3, gpu, bf16_out=False, fp8_out=True)
+    a.make_plan(with_grad_out=False, with_bf16=False)
+    b.make_plan(with_grad_out=False, with_bf16=False)
+    n = len(a.segments)
+    mk = lambda: torch.zeros(n, dtype=torch.float32, device=gpu)
+    amax_a, scale_a, amax_b, scale_b = mk(), mk(), mk(), mk()
+    count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    torch.cuda.synchronize()
+    g_dyn = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_dyn):
+        b.plan.step_amax_capturable(w.hparams, count, amax_b)
+        b.plan.cast_fp8(amax_b, 1, scale_b)
+    g_del = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_del):
+        b.plan.step_fp8_capturable(w.hparams, count, scale_b, amax_b)
+    torch.cuda.synchronize()
+    assert int(count.item()) == 0
+    for t in range(1, STEPS + 1):
+        a.load_grads(t)
+        b.load_grads(t)
+        if t % 2:
+            a.plan.step_amax(w.hparams, t, amax_a)
+            a.plan.cast_fp8(amax_a, 1, scale_a)
+            g_dyn.replay()
+        else:
+            a.plan.step_fp8(w.hparams, t, scale_a, amax_a)
+            g_del.replay()
+        torch.cuda.synchronize()
+        _same_fp8(a, b, f"fp8 replay {t}")
+        assert torch.equal(amax_a, amax_b) and torch.equal(scale_a, scale_b)
+        assert int(count.item()) == t
+    del g_dyn, g_del
+    a.close()
+    b.close()
+
+
 def test_far_counts_agree_with_the_host(gpu):
     """Counts where beta2^t is far from 1 and where it has vanished: the
     device-derived scalars step exactly as the host's."""
@@ -182,6 +229,9 @@ def test_empty_plan_and_refusals(gpu):
         B.fsdp_mt_step_capturable(st.plan.handle, w.hparams, st.exp_avg.data_ptr())
     with pytest.raises(B.FsdpError, match="FSDP_E_ALIAS"):
         B.fsdp_mt_step_clipped_capturable(st.plan.handle, w.hparams, coef.data_ptr(), coef.data_ptr())
+    amax = torch.zeros(len(st.segments), dtype=torch.float32, device=gpu)
+    with pytest.raises(B.FsdpError, match="FSDP_E_ARG"):
+        st.plan.step_amax_capturable(w.hparams, None, amax)   # (the plan has no fp8 copy either)
     bad = dict(w.hparams, lr=-1.0)
     with pytest.raises(B.FsdpError, match="FSDP_E_ARG"):
         st.plan.step_capturable(bad, count)
