@@ -3,7 +3,9 @@ __graft_entry__.build()) allocates with the HIP runtime, runs one fused
 multi-tensor step through the C ABI and writes its inputs and outputs.  No
 PyTorch is involved in the step.  The outputs must match the oracle to the
 parity bar and the kernel's stated fp32 sequence bit for bit, with +0 in the
-padding whatever the inputs hold there."""
+padding whatever the inputs hold there.  tests/c/graph_from_c captures
+fsdp_mt_step_capturable in a HIP graph from C and checks every replay
+against fixed-count eager steps bit for bit (it reports the result itself)."""
 
 import os
 import subprocess
@@ -55,3 +57,11 @@ def test_step_from_plain_c(gpu, tmp_path):
         for nm, got, want in (("p", p1, rp), ("m", m1, rm), ("v", v1, rv)):
             assert np.array_equal(got[:va].view(np.uint32), want.view(np.uint32)), f"C shard {i} {nm}"
     assert pos == len(raw)
+
+
+def test_graph_from_plain_c(gpu):
+    exe = os.path.join(ROOT, "tests", "c", "graph_from_c")
+    assert os.path.exists(exe), "tests/c/graph_from_c is missing: run __graft_entry__.build() first"
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "graph_from_c: ok" in r.stdout
