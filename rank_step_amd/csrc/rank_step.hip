@@ -63,8 +63,16 @@ namespace {
 #ifndef RS_NT_OUT
 #define RS_NT_OUT 1
 #endif
+// State loads (master, moments, a no_sync accumulator): non-temporal since
+// the stores write through, with which the 7B shard's step runs 1.6 % faster
+// (5.28 against 5.37 ms), the 70B shard's 1.0 %, the small workloads 1.5-2.7 %.
 #ifndef RS_NT_STATE_LD
-#define RS_NT_STATE_LD 0
+#define RS_NT_STATE_LD 1
+#endif
+// The synchronised accumulation's load of the running sum it adds to: an
+// ordinary load (2.94 ms per micro-batch on the 7B shard, 3.01 non-temporal).
+#ifndef RS_NT_ACC_LD
+#define RS_NT_ACC_LD 0
 #endif
 #ifndef RS_NT_STATE_ST
 #define RS_NT_STATE_ST 0
@@ -866,7 +874,7 @@ __device__ __forceinline__ double reduce_store_range(const TensorDesc& T, int64_
     for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         f32x4* go = reinterpret_cast<f32x4*>(T.grad_out + e);
         f32x4 old = {0.f, 0.f, 0.f, 0.f};
-        if (acc) old = ld_state(go);
+        if (acc) old = ld_s<RS_NT_ACC_LD>(go);
         float g[kGroup];
         reduce_group<NS, BF16, TABLE, GEN>(T, e, g, c);
         if (acc) {
