@@ -848,14 +848,15 @@ __device__ __forceinline__ void fused_range(const TensorDesc& T, int64_t begin, 
 
 // Reduce only: grad_out = mean of the slices on [begin, end); GEN: the
 // slices may start at any element alignment.
-template <int NS, bool BF16, bool GEN = false>
+template <int NS, bool BF16, bool GEN = false, int POL = kStPlain>
 __device__ __forceinline__ void reduce_range(const TensorDesc& T, int64_t begin, int64_t end,
                                              const StepConsts& c) {
     const int64_t vend = vector_end(T, begin, end);
     for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         float g[kGroup];
         reduce_group<NS, BF16, false, GEN>(T, e, g, c);
-        st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
+        if constexpr (POL != kStPlain) st_state_pol<POL>(T.grad_out + e, f32x4{g[0], g[1], g[2], g[3]});
+        else st_out(reinterpret_cast<f32x4*>(T.grad_out + e), f32x4{g[0], g[1], g[2], g[3]});
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
         st(T.grad_out + k, k < T.valid ? reduce_elem<BF16>(T, k, c) : 0.0f);
@@ -972,12 +973,13 @@ __device__ __forceinline__ void fp8_range(const TensorDesc& T, int64_t begin, in
 
 // Cast only: out_bf16 = RNE(param) on [begin, end); GEN: the copy may start
 // at any element alignment.
-template <bool GEN = false>
+template <bool GEN = false, int POL = kStPlain>
 __device__ __forceinline__ void cast_range(const TensorDesc& T, int64_t begin, int64_t end) {
     const int64_t vend = vector_end(T, begin, end);
     for (int64_t e = begin + threadIdx.x * kGroup; e < vend; e += kTile) {
         const f32x4 a = ld_s<RS_NT_CAST_LD>(reinterpret_cast<const f32x4*>(T.param + e));
         if constexpr (GEN) store_bf16_any(T.out_bf16 + e, pack_bf16(a), misalign(T.out_bf16, 8));
+        else if constexpr (POL != kStPlain) st_bf16_wt(T.out_bf16 + e, pack_bf16(a));
         else st_out(reinterpret_cast<u32x2*>(T.out_bf16 + e), pack_bf16(a));
     }
     for (int64_t k = vend + threadIdx.x; k < end; k += kBlock)
@@ -1277,23 +1279,23 @@ __global__ __launch_bounds__(kBlock) void step_count_kernel(int64_t* step_dev, S
 // Single-shard kernels: workgroup b covers elements [b*kTile, (b+1)*kTile).
 // GEN: the slices (the gradient, for AdamW alone) or the bf16 copy start off
 // a vector boundary, the fp32 buffers on it.
-template <int NS, bool BF16, bool GEN = false>
+template <int NS, bool BF16, bool GEN, int POL>
 __global__ __launch_bounds__(kBlock) void fused_single_kernel(TensorDesc T, StepConsts c) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
-    fused_range<NS, BF16, false, false, false, GEN>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel),
-                                                   c);
+    fused_range<NS, BF16, false, false, false, GEN, false, POL>(
+        T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
 }
 
-template <int NS, bool BF16, bool GEN = false>
+template <int NS, bool BF16, bool GEN, int POL>
 __global__ __launch_bounds__(kBlock) void reduce_single_kernel(TensorDesc T, StepConsts c) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
-    reduce_range<NS, BF16, GEN>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
+    reduce_range<NS, BF16, GEN, POL>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel), c);
 }
 
-template <bool GEN = false>
+template <bool GEN, int POL>
 __global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
-    cast_range<GEN>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel));
+    cast_range<GEN, POL>(T, begin, std::min<int64_t>(begin + kTile, T.shard_numel));
 }
 
 // Reduce one shard into grad_out and write each workgroup's sum of squares to
@@ -1492,20 +1494,23 @@ ScaledStepKernel pick_scaled_step(bool general, int pol, bool devc) {
     });
 }
 
-template <bool BF16, bool GEN>
+template <bool BF16, bool GEN, int POL>
 ReduceKernel pick_reduce(int n) {
     switch (n) {
-        case 1: return reduce_single_kernel<1, BF16, GEN>;
-        case 2: return reduce_single_kernel<2, BF16, GEN>;
-        case 4: return reduce_single_kernel<4, BF16, GEN>;
-        case 8: return reduce_single_kernel<8, BF16, GEN>;
-        default: return reduce_single_kernel<0, BF16, GEN>;
+        case 1: return reduce_single_kernel<1, BF16, GEN, POL>;
+        case 2: return reduce_single_kernel<2, BF16, GEN, POL>;
+        case 4: return reduce_single_kernel<4, BF16, GEN, POL>;
+        case 8: return reduce_single_kernel<8, BF16, GEN, POL>;
+        default: return reduce_single_kernel<0, BF16, GEN, POL>;
     }
 }
 
-ReduceKernel pick_reduce(int dtype, int n, bool gen) {
-    if (dtype == FSDP_DT_BF16) return gen ? pick_reduce<true, true>(n) : pick_reduce<true, false>(n);
-    return gen ? pick_reduce<false, true>(n) : pick_reduce<false, false>(n);
+ReduceKernel pick_reduce(int dtype, int n, bool gen, int pol) {
+    return by_policy(pol, [&](auto P) {
+        constexpr int kPol = decltype(P)::value;
+        if (dtype == FSDP_DT_BF16) return gen ? pick_reduce<true, true, kPol>(n) : pick_reduce<true, false, kPol>(n);
+        return gen ? pick_reduce<false, true, kPol>(n) : pick_reduce<false, false, kPol>(n);
+    });
 }
 
 using SqnormSingleKernel = void (*)(TensorDesc, StepConsts, double*);
@@ -1936,7 +1941,8 @@ static int32_t reduce_grad_shard_impl(float* grad_shard_out, const void* grad_sl
     const bool gen = T.vec_ok && !slices_vec_ok(grad_slices, slice_dtype, slice_stride, n_slices);
     const StepConsts c = make_consts(nullptr, n_slices);
     if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
-    const ReduceKernel k = pick_reduce(slice_dtype, n_slices, gen);
+    const ReduceKernel k =
+        pick_reduce(slice_dtype, n_slices, gen, write_policy(dtype_bytes(slice_dtype) * n_slices, 4));
     hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(tiles_for(shard_numel))), dim3(kBlock),
                        lds_reserve(dtype_bytes(slice_dtype) * inflight_slices(n_slices, slice_dtype) + 4),
                        stream, T, c);
@@ -1978,7 +1984,11 @@ static int32_t adamw_shard_step_impl(float* param_fp32, float* exp_avg, float* e
     const bool gen = T.vec_ok && !aligned(grad_shard, kF32Vec);
     const StepConsts c = make_consts(hp, 1);
     if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
-    const ReduceKernel k = gen ? fused_single_kernel<1, false, true> : fused_single_kernel<1, false, false>;
+    // 4 bytes of gradient and 12 of state read, 12 written
+    const ReduceKernel k = by_policy(write_policy(16, 12), [&](auto P) -> ReduceKernel {
+        constexpr int kPol = decltype(P)::value;
+        return gen ? fused_single_kernel<1, false, true, kPol> : fused_single_kernel<1, false, false, kPol>;
+    });
     hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
                        dim3(kBlock), lds_reserve(4 + 24), stream, T, c);
     return launch_status(who);
@@ -2008,8 +2018,13 @@ static int32_t cast_unshard_bf16_impl(uint16_t* unshard_bf16_out, const float* p
     T.vec_ok = aligned(param_fp32, kF32Vec);
     const bool gen = T.vec_ok && !aligned(unshard_bf16_out, kBf16Vec);
     if ((st = check_grid(tiles_for(shard_numel), who)) != FSDP_OK) return st;
-    hipLaunchKernelGGL(gen ? cast_single_kernel<true> : cast_single_kernel<false>,
-                       dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
+    // 4 bytes read per 2 written: write-through
+    using CastKernel = void (*)(TensorDesc);
+    const CastKernel k = by_policy(write_policy(4, 2), [&](auto P) -> CastKernel {
+        constexpr int kPol = decltype(P)::value;
+        return gen ? cast_single_kernel<true, kPol> : cast_single_kernel<false, kPol>;
+    });
+    hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(tiles_for(shard_numel))),
                        dim3(kBlock), lds_reserve(4 + 2), stream, T);
     return launch_status(who);
 }
