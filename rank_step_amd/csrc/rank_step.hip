@@ -1303,12 +1303,12 @@ __global__ __launch_bounds__(kBlock) void cast_single_kernel(TensorDesc T) {
 // plan holding this one shard launches it: workgroup b covers elements
 // [b*kTile, (b+1)*kTile), the same tile as the plan's tile b % 8 of entry
 // b / 8, and the workgroups past the shard's end store a zero partial.
-template <int NS, bool BF16, bool GEN = false>
+template <int NS, bool BF16, bool GEN, int POL>
 __global__ __launch_bounds__(kBlock) void reduce_sqnorm_single_kernel(TensorDesc T, StepConsts c,
                                                                       double* partials) {
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * kTile;
     const int64_t end = std::max(begin, std::min<int64_t>(begin + kTile, T.shard_numel));
-    const double sq = reduce_store_range<NS, BF16, true, false, GEN>(T, begin, end, c, false);
+    const double sq = reduce_store_range<NS, BF16, true, false, GEN, POL>(T, begin, end, c, false);
     const double total = wave_sum(sq);
     if (threadIdx.x == 0) st(partials + xcd_slot(blockIdx.x, gridDim.x), total);
 }
@@ -1515,20 +1515,24 @@ ReduceKernel pick_reduce(int dtype, int n, bool gen, int pol) {
 
 using SqnormSingleKernel = void (*)(TensorDesc, StepConsts, double*);
 
-template <bool BF16, bool GEN>
+template <bool BF16, bool GEN, int POL>
 SqnormSingleKernel pick_sqnorm_single(int n) {
     switch (n) {
-        case 1: return reduce_sqnorm_single_kernel<1, BF16, GEN>;
-        case 2: return reduce_sqnorm_single_kernel<2, BF16, GEN>;
-        case 4: return reduce_sqnorm_single_kernel<4, BF16, GEN>;
-        case 8: return reduce_sqnorm_single_kernel<8, BF16, GEN>;
-        default: return reduce_sqnorm_single_kernel<0, BF16, GEN>;
+        case 1: return reduce_sqnorm_single_kernel<1, BF16, GEN, POL>;
+        case 2: return reduce_sqnorm_single_kernel<2, BF16, GEN, POL>;
+        case 4: return reduce_sqnorm_single_kernel<4, BF16, GEN, POL>;
+        case 8: return reduce_sqnorm_single_kernel<8, BF16, GEN, POL>;
+        default: return reduce_sqnorm_single_kernel<0, BF16, GEN, POL>;
     }
 }
 
-SqnormSingleKernel pick_sqnorm_single(int dtype, int n, bool gen) {
-    if (dtype == FSDP_DT_BF16) return gen ? pick_sqnorm_single<true, true>(n) : pick_sqnorm_single<true, false>(n);
-    return gen ? pick_sqnorm_single<false, true>(n) : pick_sqnorm_single<false, false>(n);
+SqnormSingleKernel pick_sqnorm_single(int dtype, int n, bool gen, int pol) {
+    return by_policy(pol, [&](auto P) {
+        constexpr int kPol = decltype(P)::value;
+        if (dtype == FSDP_DT_BF16)
+            return gen ? pick_sqnorm_single<true, true, kPol>(n) : pick_sqnorm_single<true, false, kPol>(n);
+        return gen ? pick_sqnorm_single<false, true, kPol>(n) : pick_sqnorm_single<false, false, kPol>(n);
+    });
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -2717,7 +2721,9 @@ extern "C" int32_t fsdp_reduce_sqnorm_noalloc(float* grad_shard_out, double* sqn
     const StepConsts c = make_consts(nullptr, n_slices);
     const int64_t n = (shard_numel + kChunk - 1) / kChunk * kTilesPerChunk;
     const int64_t in_flight = dtype_bytes(slice_dtype) * inflight_slices(n_slices, slice_dtype);
-    hipLaunchKernelGGL(pick_sqnorm_single(slice_dtype, n_slices, gen), dim3(static_cast<uint32_t>(n)),
+    hipLaunchKernelGGL(pick_sqnorm_single(slice_dtype, n_slices, gen,
+                                          write_policy(dtype_bytes(slice_dtype) * n_slices, 4)),
+                       dim3(static_cast<uint32_t>(n)),
                        dim3(kBlock), lds_reserve(in_flight + 4), stream, T, c, partials);
     if ((st = launch_status(who)) != FSDP_OK) return st;
     // the same two fixed-order stages as a plan's: n partials -> up to
