@@ -151,10 +151,13 @@ namespace {
 #ifndef RS_RUN_STEP
 #define RS_RUN_STEP 1
 #endif
-// Budget of that one-range step under write-through stores: its waves stream
-// from their first instructions, so fewer resident waves keep the bytes in
-// flight (one Llama-7B block at N = 8: 162.5-163.0 us at 75 KB, 165.0 at
-// 100; the 128 MiB flat unit: 55.2 against 55.7).
+// Budget of that one-range step under write-through stores, for the slice
+// counts compiled in: its waves stream from their first instructions, so
+// fewer resident waves keep the bytes in flight (one Llama-7B block at N = 8:
+// 162.5-163.0 us at 75 KB, 165.0 at 100; the 128 MiB flat unit: 55.2 against
+// 55.7).  Batched slice counts keep the general budget: at 75 KB, N = 5, 16
+// and 32 bf16 slices lost 12-14 % (5.45, 5.66, 5.31 against 6.23, 6.29,
+// 6.06 TB/s).
 #ifndef RS_INFLIGHT_KB_RUN
 #define RS_INFLIGHT_KB_RUN 75
 #endif
@@ -2318,7 +2321,13 @@ static int32_t mt_step_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bo
                                                                   : RS_INFLIGHT_KB;
     if (plan->has_run) {
         const RunKernel k = pick_run(plan->slice_dtype, plan->n_slices, plan->store_pol, cdev != nullptr);
-        const int64_t run_budget = plan->store_pol == kStWriteThrough ? RS_INFLIGHT_KB_RUN : budget;
+        // the smaller budget where a tile's slice loads are all in flight at
+        // once (N compiled in); batched slice counts make several round trips
+        // per wave and keep the general one
+        const int32_t n = plan->n_slices;
+        const bool one_batch = n == 1 || n == 2 || n == 4 || n == 8;
+        const int64_t run_budget =
+            plan->store_pol == kStWriteThrough && one_batch ? RS_INFLIGHT_KB_RUN : budget;
         plan_launch(plan, true, k, dim3(static_cast<uint32_t>(tiles_for(plan->run.shard_numel))),
                     dim3(kBlock), lds_reserve(step_bytes(plan), run_budget), stream, plan->run, c, cdev);
         return launch_status(who);
