@@ -11,10 +11,11 @@
 // wave64 and covers one 256-element tile: each lane moves 4 consecutive
 // elements per access (one 16-byte load per fp32 array, one 8-byte load per
 // bf16 slice), and every load of the tile is issued before its first use.
-// Gradient slices and the low-precision copies are touched once and use
-// non-temporal accesses.  The fused step writes the updated state and the
-// bf16 copy through to memory, so that a launch does not end with dirty lines
-// in L2 for its release to write back.  The vector path needs a shard's fp32 buffers
+// Gradient slices, the low-precision copies and the state loads are touched
+// once and use non-temporal accesses.  Every streaming pass writes its
+// stores through to memory (plain or non-temporal write-through, by its mix
+// of bytes), so that a launch does not end with dirty lines in L2 for its
+// release to write back.  The vector path needs a shard's fp32 buffers
 // 16-byte aligned; its slices and copies may start at any element (shifted
 // loads, stores in narrower pieces), and a plan splits a shard whose fp32
 // buffers all start off a boundary into a short head and an aligned rest.
