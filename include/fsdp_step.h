@@ -29,7 +29,9 @@
  *     frees them (a plan allocates only its own tables, from the
  *     stream-ordered allocator, see fsdp_mt_plan_create).
  *   - Work is queued on the caller's stream (NULL = the null stream) and is
- *     asynchronous; no call synchronises the host except fsdp_mt_plan_create.
+ *     asynchronous; no call synchronises the host except fsdp_mt_plan_create
+ *     (one upload) and fsdp_mt_plan_destroy (which waits for the plan's own
+ *     last launch, and for nothing else).
  *   - Sizes and offsets are in elements unless a name says bytes.
  *   - Padding: positions [valid, shard_numel) of every buffer the call writes
  *     are set to +0.0 (all-zero bits); inputs are never read there.  NaN and
@@ -321,12 +323,14 @@ typedef struct {
  * may overlap each other), builds the chunk-descriptor table and uploads it
  * to device memory the plan owns on the current device.  When every
  * non-empty shard has a grad_shard_out the plan also owns one fp64 partial
- * sum per workgroup for fsdp_mt_reduce_sqnorm.  Synchronises
+ * sum per workgroup for fsdp_mt_reduce_sqnorm, and every non-empty plan a
+ * 48-byte slot for the scalars of the _capturable calls.  Synchronises
  * `stream` once.  The caller keeps every referenced buffer alive and in
  * place while the plan exists.  n_tensors may be 0 (an empty plan).
  * The plan keeps the byte ranges of its shards' buffers: the further device
  * buffers that the calls on it take (grad_scale, scale_in, amax_ranks as
- * inputs; sqnorm_out, amax_out, scale_out as outputs) are checked against
+ * inputs; sqnorm_out, amax_out, scale_out and the step_dev of the
+ * _capturable calls as outputs) are checked against
  * them.  An input may overlap only the read-only gradient slices, an output
  * no buffer of the plan (else FSDP_E_ALIAS, before any work is queued).
  * Errors: as the single-shard calls; FSDP_E_CAPACITY if one launch cannot
