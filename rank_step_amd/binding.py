@@ -27,7 +27,7 @@ DTYPES = {"f32": 0, "bf16": 1}
 LAYOUTS = {"flat": 0, "shard0": 1, "owner": 2}
 
 # Every function the header declares; the CPU tests check each is exported.
-EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_reduce_grad_shard",
+EXPORTS = ("fsdp_last_error", "fsdp_shard_layout", "fsdp_rank_buffer_layout", "fsdp_reduce_grad_shard",
            "fsdp_adamw_shard_step", "fsdp_cast_unshard_bf16", "fsdp_mt_plan_create",
            "fsdp_mt_step", "fsdp_mt_step_capturable", "fsdp_mt_step_clipped_capturable",
            "fsdp_mt_step_amax_capturable", "fsdp_mt_step_fp8_capturable",
@@ -63,6 +63,13 @@ class LayoutSummary(ctypes.Structure):
                                               "pad_numel", "bytes_param", "bytes_grad",
                                               "bytes_optim", "bytes_master",
                                               "bytes_grad_unsharded")]
+
+
+class RankBuffers(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("total_bytes", "region_align", "slice_stride",
+                                              "param_offset", "exp_avg_offset", "exp_avg_sq_offset",
+                                              "slices_offset", "bf16_offset", "grad_out_offset",
+                                              "fp8_offset")]
 
 
 class AdamWHparams(ctypes.Structure):
@@ -109,6 +116,7 @@ def lib():
         sig = {
             "fsdp_shard_layout": [i32, i32, i32, ctypes.POINTER(TensorShape), i32, i32,
                                   ctypes.POINTER(ShardView), ctypes.POINTER(LayoutSummary)],
+            "fsdp_rank_buffer_layout": [ctypes.c_int64, i32, i32, i32, i32, i32, ctypes.POINTER(RankBuffers)],
             "fsdp_reduce_grad_shard": [vp, vp, i32, i64, i32, i64, i64, vp],
             "fsdp_adamw_shard_step": [vp, vp, vp, vp, i64, i64, ctypes.POINTER(AdamWHparams), vp],
             "fsdp_cast_unshard_bf16": [vp, vp, i64, i64, vp],
@@ -171,6 +179,17 @@ def _hparams(hp, step):
 
 
 # ---------------------------------------------------------------- entry points
+
+def fsdp_rank_buffer_layout(shard_numel, n_slices, slice_dtype, bf16_slots=1, grad_out=False,
+                            fp8_out=False):
+    """Placement of one rank's step buffers in one allocation, as a dict of
+    ints named as in the header (offsets in bytes, -1 for absent buffers)."""
+    r = RankBuffers()
+    _check(lib().fsdp_rank_buffer_layout(int(shard_numel), int(n_slices), _dtype(slice_dtype),
+                                         int(bf16_slots), int(bool(grad_out)), int(bool(fp8_out)),
+                                         ctypes.byref(r)))
+    return {f: getattr(r, f) for f, _ in RankBuffers._fields_}
+
 
 def fsdp_shard_layout(mode, world_size, rank, shapes, has_master):
     """``shapes``: (numel, dim0, dtype) triples.  Returns (views, summary) as

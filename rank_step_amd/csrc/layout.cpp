@@ -217,3 +217,71 @@ extern "C" int32_t fsdp_shard_layout(int32_t mode, int32_t world_size, int32_t r
                             summary_out);
     });
 }
+
+namespace {
+
+constexpr int64_t kRegionAlign = int64_t(2) << 20;  // every region's start
+constexpr int64_t kRowLine = 64;                    // slice rows start on these element multiples
+constexpr int64_t kRowPad = 256;                    // elements between one row's shard and the next row
+
+int32_t rank_buffer_layout(int64_t S, int32_t n_slices, int32_t slice_dtype, int32_t bf16_slots,
+                           int32_t grad_out, int32_t fp8_out, fsdp_rank_buffers* out) {
+    const char* who = "fsdp_rank_buffer_layout";
+    if (!out) return fail(FSDP_E_ARG, "%s: null out", who);
+    if (S < 0) return fail(FSDP_E_ARG, "%s: shard_numel %lld < 0", who, static_cast<long long>(S));
+    if (slice_dtype != FSDP_DT_F32 && slice_dtype != FSDP_DT_BF16)
+        return fail(FSDP_E_DTYPE, "%s: unknown slice dtype %d", who, slice_dtype);
+    if (n_slices < 1 || n_slices > 1024)
+        return fail(FSDP_E_ARG, "%s: n_slices %d outside [1, 1024]", who, n_slices);
+    if (bf16_slots < 0) return fail(FSDP_E_ARG, "%s: bf16_slots %d < 0", who, bf16_slots);
+    if ((grad_out != 0 && grad_out != 1) || (fp8_out != 0 && fp8_out != 1))
+        return fail(FSDP_E_ARG, "%s: grad_out and fp8_out must be 0 or 1", who);
+    const int64_t es = slice_dtype == FSDP_DT_F32 ? 4 : 2;
+    fsdp_rank_buffers r{};
+    r.region_align = kRegionAlign;
+    int64_t stride = S;
+    if (n_slices > 1) {
+        int64_t up;
+        if (!fsdp::add_i64(S, kRowLine - 1, &up) || !fsdp::add_i64(up / kRowLine * kRowLine, kRowPad, &stride))
+            return fail(FSDP_E_ARG, "%s: sizes overflow int64", who);
+    }
+    r.slice_stride = stride;
+    // each present region: start at the next boundary, then advance by its bytes
+    int64_t end = 0;
+    bool ok = true;
+    auto place = [&](int64_t elems, int64_t esize, bool present) -> int64_t {
+        if (!present || !ok) return -1;
+        int64_t start, bytes;
+        if (!fsdp::add_i64(end, kRegionAlign - 1, &start) || !fsdp::mul_i64(elems, esize, &bytes)) {
+            ok = false;
+            return -1;
+        }
+        start = start / kRegionAlign * kRegionAlign;
+        if (!fsdp::add_i64(start, bytes, &end)) ok = false;
+        return start;
+    };
+    int64_t slice_elems = 0, bf16_elems = 0;
+    if (!fsdp::mul_i64(stride, n_slices, &slice_elems) || !fsdp::mul_i64(S, bf16_slots, &bf16_elems))
+        return fail(FSDP_E_ARG, "%s: sizes overflow int64", who);
+    r.param_offset = place(S, 4, true);
+    r.exp_avg_offset = place(S, 4, true);
+    r.exp_avg_sq_offset = place(S, 4, true);
+    r.slices_offset = place(slice_elems, es, true);
+    r.bf16_offset = place(bf16_elems, 2, bf16_slots > 0);
+    r.grad_out_offset = place(S, 4, grad_out != 0);
+    r.fp8_offset = place(S, 1, fp8_out != 0);
+    if (!ok) return fail(FSDP_E_ARG, "%s: sizes overflow int64", who);
+    r.total_bytes = end;
+    *out = r;
+    return FSDP_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t fsdp_rank_buffer_layout(int64_t shard_numel, int32_t n_slices, int32_t slice_dtype,
+                                           int32_t bf16_slots, int32_t grad_out, int32_t fp8_out,
+                                           fsdp_rank_buffers* out) {
+    return fsdp::guarded("fsdp_rank_buffer_layout", [&] {
+        return rank_buffer_layout(shard_numel, n_slices, slice_dtype, bf16_slots, grad_out, fp8_out, out);
+    });
+}

@@ -1,14 +1,16 @@
 """One rank's optimizer state of a workload, resident in HBM, and its plan.
 
-Sizes come from the library's own ``fsdp_shard_layout``; torch only allocates
-the memory.  Layout of the buffers: one device allocation per rank, carved
-into regions that each start on a 2 MiB boundary (the order below):
+Sizes come from the library's own ``fsdp_shard_layout`` and the placement of
+the buffers from its ``fsdp_rank_buffer_layout``; torch only allocates the
+memory.  Layout of the buffers: one device allocation per rank, carved into
+regions that each start on a 2 MiB boundary (the order below):
 
 * ``master``, ``exp_avg``, ``exp_avg_sq``: fp32 ``[S_total]``, the rank's
   local shards of every parameter packed in registration order (FLAT: the one
   flat shard), each shard at its ``view_offset``;
 * ``slices``: ``[N, S_total]`` in the slice dtype, rows ``slice_stride`` =
-  S_total + 256 elements apart -- slice q is the q-th incoming gradient
+  S_total rounded up to 64, plus 256, elements apart (S_total when N is 1) --
+  slice q is the q-th incoming gradient
   buffer of this rank's shard, i.e. the rank's chunk of rank q's full
   gradient -- so the slice stride of every shard is ``slice_stride``;
 * ``ag``: bf16 all-gather input.  With ``ag_full`` it is the packed
@@ -33,8 +35,6 @@ from . import binding
 from .workloads import grad_slices, init_master, init_seed, shapes_of
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
-REGION_ALIGN = 2 << 20      # every region starts on a 2 MiB boundary of the rank's allocation
-SLICE_PAD = 256             # elements between the end of one slice row and the next
 
 
 class RankState:
@@ -57,22 +57,21 @@ class RankState:
                     for v, p in zip(views, w.params) if v["shard_numel"] > 0]
         self.segments = segs
         sdt = _DT[w.slice_dtype]
-        self.slice_stride = total + SLICE_PAD if w.n_slices > 1 else total
-        n_ag = (total * w.world_size if ag_full else total) if bf16_out else 0
-        regions = [("master", torch.float32, total), ("exp_avg", torch.float32, total),
-                   ("exp_avg_sq", torch.float32, total),
-                   ("slices", sdt, w.n_slices * self.slice_stride), ("ag", torch.bfloat16, n_ag),
-                   ("grad_out", torch.float32, total if grad_out else 0),
-                   ("fp8", torch.uint8, total if fp8_out else 0)]
-        offs, end = {}, 0
-        for name, dt, n in regions:
-            end = (end + REGION_ALIGN - 1) // REGION_ALIGN * REGION_ALIGN
-            offs[name] = end
-            end += n * torch.empty(0, dtype=dt).element_size()
-        self._mem = torch.empty(max(end, 1), dtype=torch.uint8, device=device)
+        slots = (w.world_size if ag_full else 1) if bf16_out else 0
+        lay = binding.fsdp_rank_buffer_layout(total, w.n_slices, w.slice_dtype, slots, grad_out, fp8_out)
+        self.buffer_layout = lay
+        self.slice_stride = lay["slice_stride"]
+        n_ag = total * slots
+        offs = {"master": lay["param_offset"], "exp_avg": lay["exp_avg_offset"],
+                "exp_avg_sq": lay["exp_avg_sq_offset"], "slices": lay["slices_offset"],
+                "ag": lay["bf16_offset"], "grad_out": lay["grad_out_offset"], "fp8": lay["fp8_offset"]}
+        ra = lay["region_align"]
+        size = max(1, (lay["total_bytes"] + ra - 1) // ra * ra)   # a whole number of regions
+        self._mem = torch.empty(size, dtype=torch.uint8, device=device)
 
         def region(name, dt, n):
             es = torch.empty(0, dtype=dt).element_size()
+            assert offs[name] >= 0, name
             return self._mem[offs[name]:offs[name] + n * es].view(dt)
 
         self.master = region("master", torch.float32, total)
