@@ -379,7 +379,12 @@ typedef struct {
  * no buffer of the plan (else FSDP_E_ALIAS, before any work is queued).
  * Errors: as the single-shard calls; FSDP_E_CAPACITY if one launch cannot
  * hold the plan's workgroups (checked before any table is built); FSDP_E_HIP
- * if the upload fails. */
+ * if the upload fails.
+ * One plan steps with one set of hyperparameters.  Shards that need others
+ * (torch's parameter groups, e.g. no weight decay on norms and biases) go in
+ * a plan of their own, one step call per plan.  With the _capturable calls
+ * each such plan takes its own step count: every call advances the count it
+ * is given, so plans sharing one count would advance it once per plan. */
 int32_t fsdp_mt_plan_create(fsdp_mt_plan** plan_out, const fsdp_mt_tensor* tensors,
                             int32_t n_tensors, int32_t n_slices, int32_t slice_dtype,
                             hipStream_t stream);
