@@ -232,8 +232,9 @@ int32_t fsdp_rank_buffer_layout(int64_t shard_numel, int32_t n_slices, int32_t s
  * replayed at step 1000 steps 3.7x too far, with 1/sqrt(1 - beta2^3) = 18.3
  * where 1.0 is due), and nothing reports it.  To step a graph through
  * t = 1, 2, ..., capture the _capturable forms of the step calls, which read
- * the count from device memory (fsdp_mt_step_capturable and the clipped and
- * fp8 forms), or make the calls eagerly. */
+ * the count (and, if asked, the learning rate) from device memory
+ * (fsdp_mt_step_capturable and the clipped and fp8 forms), or make the calls
+ * eagerly. */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
     int64_t step;
@@ -372,10 +373,10 @@ typedef struct {
  * `stream` once.  The caller keeps every referenced buffer alive and in
  * place while the plan exists.  n_tensors may be 0 (an empty plan).
  * The plan keeps the byte ranges of its shards' buffers: the further device
- * buffers that the calls on it take (grad_scale, scale_in, amax_ranks as
- * inputs; sqnorm_out, amax_out, scale_out and the step_dev of the
- * _capturable calls as outputs) are checked against
- * them.  An input may overlap only the read-only gradient slices, an output
+ * buffers that the calls on it take (grad_scale, scale_in, amax_ranks and
+ * the lr_dev of the _capturable calls as inputs; sqnorm_out, amax_out,
+ * scale_out and their step_dev as outputs) are checked against them.  An
+ * input may overlap only the read-only gradient slices, an output
  * no buffer of the plan (else FSDP_E_ALIAS, before any work is queued).
  * Errors: as the single-shard calls; FSDP_E_CAPACITY if one launch cannot
  * hold the plan's workgroups (checked before any table is built); FSDP_E_HIP
@@ -412,16 +413,26 @@ int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, hipStream
  * a one-lane launch derives t's scalars on the device, with the host's
  * operations (so the results are bit-identical to fsdp_mt_step with
  * hp->step = t), into a slot the plan owns, and the step launch reads them
- * there.  hp->step is ignored; lr, betas, eps and weight_decay are taken at
- * the call (a captured graph keeps them).  Two launches, no allocation, no
- * host synchronisation; an empty plan advances the count only.  The step
- * waits for the one-lane launch: about 6 us more per step than fsdp_mt_step
- * (measured on MI355X), a share only small steps notice.  step_dev
- * must not overlap the plan's buffers (FSDP_E_ALIAS); null is FSDP_E_ARG,
- * misaligned FSDP_E_ALIGN.  Calls on one plan must not overlap (they share
- * the slot). */
+ * there.  hp->step is ignored; betas, eps and weight_decay are taken at the
+ * call (a captured graph keeps them).
+ *   lr_dev  NULL: the learning rate is hp->lr, taken at the call.  Else a
+ *           device double [1] read by the one-lane launch, in stream order,
+ *           in place of hp->lr (which must still be valid): a learning-rate
+ *           schedule for a replayed graph, whose caller writes the step's
+ *           rate there before each replay.  The decay factor 1 - lr*wd and
+ *           lr/(1 - beta1^t) are then derived from it on the device, so the
+ *           results are bit-identical to fsdp_mt_step with hp->lr = *lr_dev.
+ *           Finite and >= 0, not checked on the device.  8-byte aligned
+ *           (FSDP_E_ALIGN); it may overlap only the plan's read-only
+ *           gradient slices and not step_dev (FSDP_E_ALIAS).
+ * Two launches, no allocation, no host synchronisation; an empty plan
+ * advances the count only (and does not read lr_dev).  The step waits for
+ * the one-lane launch: about 6 us more per step than fsdp_mt_step (measured
+ * on MI355X), a share only small steps notice.  step_dev must not overlap
+ * the plan's buffers (FSDP_E_ALIAS); null is FSDP_E_ARG, misaligned
+ * FSDP_E_ALIGN.  Calls on one plan must not overlap (they share the slot). */
 int32_t fsdp_mt_step_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                int64_t* step_dev, hipStream_t stream);
+                                int64_t* step_dev, const double* lr_dev, hipStream_t stream);
 
 /* ------------------------------------------------------------------ clipping */
 
@@ -466,12 +477,13 @@ int32_t fsdp_clip_coef(float* coef_out, double* norm_out, const double* sqnorms,
 int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                              const float* grad_scale, hipStream_t stream);
 
-/* fsdp_mt_step_clipped with the step count in device memory, as
- * fsdp_mt_step_capturable: advances *step_dev, then the scaled update at the
- * new count.  step_dev must not overlap grad_scale either. */
+/* fsdp_mt_step_clipped with the step count (and optionally the learning
+ * rate) in device memory, as fsdp_mt_step_capturable: advances *step_dev,
+ * then the scaled update at the new count.  step_dev must not overlap
+ * grad_scale either. */
 int32_t fsdp_mt_step_clipped_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                        int64_t* step_dev, const float* grad_scale,
-                                        hipStream_t stream);
+                                        int64_t* step_dev, const double* lr_dev,
+                                        const float* grad_scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------ gradient accumulation */
 
@@ -536,11 +548,12 @@ int32_t fsdp_grad_accumulate(float* acc, const void* micro, int32_t micro_dtype,
 int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, float* amax_out,
                           hipStream_t stream);
 
-/* fsdp_mt_step_amax with the step count in device memory, as
- * fsdp_mt_step_capturable: advances *step_dev, then steps at the new count.
- * step_dev must not overlap amax_out either. */
+/* fsdp_mt_step_amax with the step count (and optionally the learning rate)
+ * in device memory, as fsdp_mt_step_capturable: advances *step_dev, then
+ * steps at the new count.  Neither step_dev nor lr_dev may overlap amax_out. */
 int32_t fsdp_mt_step_amax_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                     int64_t* step_dev, float* amax_out, hipStream_t stream);
+                                     int64_t* step_dev, const double* lr_dev, float* amax_out,
+                                     hipStream_t stream);
 
 /* Write every shard's fp8 codes from its updated fp32 parameter.  The amax
  * of shard i is the maximum over r of amax_ranks[r * n_tensors + i] (device
@@ -569,12 +582,13 @@ int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_
 int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, const float* scale_in,
                          float* amax_out, hipStream_t stream);
 
-/* fsdp_mt_step_fp8 with the step count in device memory, as
- * fsdp_mt_step_capturable: advances *step_dev, then steps at the new count.
- * step_dev must not overlap scale_in or amax_out either. */
+/* fsdp_mt_step_fp8 with the step count (and optionally the learning rate)
+ * in device memory, as fsdp_mt_step_capturable: advances *step_dev, then
+ * steps at the new count.  step_dev must not overlap scale_in or amax_out
+ * either, nor lr_dev amax_out. */
 int32_t fsdp_mt_step_fp8_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                    int64_t* step_dev, const float* scale_in, float* amax_out,
-                                    hipStream_t stream);
+                                    int64_t* step_dev, const double* lr_dev, const float* scale_in,
+                                    float* amax_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------ no device allocation */
 

@@ -122,10 +122,10 @@ def lib():
             "fsdp_cast_unshard_bf16": [vp, vp, i64, i64, vp],
             "fsdp_mt_plan_create": [ctypes.POINTER(vp), ctypes.POINTER(MtTensor), i32, i32, i32, vp],
             "fsdp_mt_step": [vp, ctypes.POINTER(AdamWHparams), vp],
-            "fsdp_mt_step_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp],
-            "fsdp_mt_step_clipped_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp],
-            "fsdp_mt_step_amax_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp],
-            "fsdp_mt_step_fp8_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp, vp],
+            "fsdp_mt_step_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp],
+            "fsdp_mt_step_clipped_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp, vp],
+            "fsdp_mt_step_amax_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp, vp],
+            "fsdp_mt_step_fp8_capturable": [vp, ctypes.POINTER(AdamWHparams), vp, vp, vp, vp, vp],
             "fsdp_mt_plan_get_info": [vp, ctypes.POINTER(MtPlanInfo)],
             "fsdp_mt_plan_destroy": [vp],
             "fsdp_mt_reduce_sqnorm": [vp, vp, vp],
@@ -279,28 +279,30 @@ def fsdp_mt_step_clipped(plan, hp, step, grad_scale, stream=None):
     _check(lib().fsdp_mt_step_clipped(plan, ctypes.byref(h), _ptr(grad_scale), _stream(stream)))
 
 
-def fsdp_mt_step_capturable(plan, hp, step_dev, stream=None):
-    """``step_dev``: device int64 [1], the steps taken so far (advanced by one)."""
+def fsdp_mt_step_capturable(plan, hp, step_dev, stream=None, lr_dev=None):
+    """``step_dev``: device int64 [1], the steps taken so far (advanced by one);
+    ``lr_dev``: None (hp's lr) or a device float64 [1] read in its place."""
     h = _hparams(hp, 1)
-    _check(lib().fsdp_mt_step_capturable(plan, ctypes.byref(h), _ptr(step_dev), _stream(stream)))
+    _check(lib().fsdp_mt_step_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(lr_dev),
+                                         _stream(stream)))
 
 
-def fsdp_mt_step_clipped_capturable(plan, hp, step_dev, grad_scale, stream=None):
+def fsdp_mt_step_clipped_capturable(plan, hp, step_dev, grad_scale, stream=None, lr_dev=None):
     h = _hparams(hp, 1)
-    _check(lib().fsdp_mt_step_clipped_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(grad_scale),
-                                                  _stream(stream)))
+    _check(lib().fsdp_mt_step_clipped_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(lr_dev),
+                                                 _ptr(grad_scale), _stream(stream)))
 
 
-def fsdp_mt_step_amax_capturable(plan, hp, step_dev, amax_out, stream=None):
+def fsdp_mt_step_amax_capturable(plan, hp, step_dev, amax_out, stream=None, lr_dev=None):
     h = _hparams(hp, 1)
-    _check(lib().fsdp_mt_step_amax_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(amax_out),
-                                               _stream(stream)))
-
-
-def fsdp_mt_step_fp8_capturable(plan, hp, step_dev, scale_in, amax_out, stream=None):
-    h = _hparams(hp, 1)
-    _check(lib().fsdp_mt_step_fp8_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(scale_in),
+    _check(lib().fsdp_mt_step_amax_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(lr_dev),
                                               _ptr(amax_out), _stream(stream)))
+
+
+def fsdp_mt_step_fp8_capturable(plan, hp, step_dev, scale_in, amax_out, stream=None, lr_dev=None):
+    h = _hparams(hp, 1)
+    _check(lib().fsdp_mt_step_fp8_capturable(plan, ctypes.byref(h), _ptr(step_dev), _ptr(lr_dev),
+                                             _ptr(scale_in), _ptr(amax_out), _stream(stream)))
 
 
 def fsdp_mt_step_amax(plan, hp, step, amax_out, stream=None):
@@ -348,17 +350,17 @@ class MtPlan:
     def step(self, hp, step, stream=None):
         fsdp_mt_step(self.handle, hp, step, stream)
 
-    def step_capturable(self, hp, step_dev, stream=None):
-        fsdp_mt_step_capturable(self.handle, hp, step_dev, stream)
+    def step_capturable(self, hp, step_dev, stream=None, lr_dev=None):
+        fsdp_mt_step_capturable(self.handle, hp, step_dev, stream, lr_dev)
 
-    def step_clipped_capturable(self, hp, step_dev, grad_scale, stream=None):
-        fsdp_mt_step_clipped_capturable(self.handle, hp, step_dev, grad_scale, stream)
+    def step_clipped_capturable(self, hp, step_dev, grad_scale, stream=None, lr_dev=None):
+        fsdp_mt_step_clipped_capturable(self.handle, hp, step_dev, grad_scale, stream, lr_dev)
 
-    def step_amax_capturable(self, hp, step_dev, amax_out, stream=None):
-        fsdp_mt_step_amax_capturable(self.handle, hp, step_dev, amax_out, stream)
+    def step_amax_capturable(self, hp, step_dev, amax_out, stream=None, lr_dev=None):
+        fsdp_mt_step_amax_capturable(self.handle, hp, step_dev, amax_out, stream, lr_dev)
 
-    def step_fp8_capturable(self, hp, step_dev, scale_in, amax_out, stream=None):
-        fsdp_mt_step_fp8_capturable(self.handle, hp, step_dev, scale_in, amax_out, stream)
+    def step_fp8_capturable(self, hp, step_dev, scale_in, amax_out, stream=None, lr_dev=None):
+        fsdp_mt_step_fp8_capturable(self.handle, hp, step_dev, scale_in, amax_out, stream, lr_dev)
 
     def info(self):
         return fsdp_mt_plan_get_info(self.handle)

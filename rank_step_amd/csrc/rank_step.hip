@@ -261,11 +261,13 @@ __host__ __device__ inline double pow_steps(double b, int64_t t) {
     return r;
 }
 
-// The step-count-dependent scalars of step t: lr / (1 - beta1^t) and
-// 1 / sqrt(1 - beta2^t), in double (correctly rounded division and square
-// root on the host and on the device alike), each rounded once to fp32.
-__host__ __device__ inline void count_scalars(StepConsts& c, double lr, double beta1, double beta2,
-                                              int64_t t) {
+// The scalars that depend on the step count t or on the learning rate:
+// 1 - lr*wd, lr / (1 - beta1^t) and 1 / sqrt(1 - beta2^t), in double
+// (correctly rounded division and square root on the host and on the device
+// alike), each rounded once to fp32.
+__host__ __device__ inline void count_scalars(StepConsts& c, double lr, double wd, double beta1,
+                                              double beta2, int64_t t) {
+    c.decay = static_cast<float>(1.0 - lr * wd);
     const double bc1 = 1.0 - pow_steps(beta1, t);
     const double bc2 = 1.0 - pow_steps(beta2, t);
     c.step_size = static_cast<float>(lr / bc1);
@@ -1263,16 +1265,19 @@ __global__ void clip_coef_kernel(float* coef_out, double* norm_out, const double
 }
 
 // A step whose count lives in device memory: advance *step_dev by one and
-// derive that step's count-dependent scalars into *out (when out is not
-// null), the others coming from the host in `c`.  One lane does it all, with
-// vector memory accesses.
-__global__ __launch_bounds__(kBlock) void step_count_kernel(int64_t* step_dev, StepConsts c, double lr,
+// derive that step's count- and learning-rate-dependent scalars into *out
+// (when out is not null), the learning rate from *lr_dev when that is not
+// null, the other scalars coming from the host in `c`.  One lane does it all,
+// with vector memory accesses.
+__global__ __launch_bounds__(kBlock) void step_count_kernel(int64_t* step_dev, const double* lr_dev,
+                                                            StepConsts c, double lr, double wd,
                                                             double beta1, double beta2, StepConsts* out) {
     if (threadIdx.x != 0) return;
     const int64_t t = ld(step_dev) + 1;
     st(step_dev, t);
     if (!out) return;
-    count_scalars(c, lr, beta1, beta2, t);
+    if (lr_dev) lr = ld(lr_dev);
+    count_scalars(c, lr, wd, beta1, beta2, t);
     static_assert(sizeof(StepConsts) % 4 == 0, "the scalars are stored as 32-bit words");
     uint32_t w[sizeof(StepConsts) / 4];
     __builtin_memcpy(w, &c, sizeof c);
@@ -1561,12 +1566,11 @@ int32_t check_hparams(const fsdp_adamw_hparams* hp) {
 StepConsts make_consts(const fsdp_adamw_hparams* hp, int32_t n) {
     StepConsts c{};
     if (hp) {
-        c.decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
         c.beta1 = static_cast<float>(hp->beta1);
         c.omb1 = static_cast<float>(1.0 - hp->beta1);
         c.beta2 = static_cast<float>(hp->beta2);
         c.omb2 = static_cast<float>(1.0 - hp->beta2);
-        count_scalars(c, hp->lr, hp->beta1, hp->beta2, hp->step);
+        count_scalars(c, hp->lr, hp->weight_decay, hp->beta1, hp->beta2, hp->step);
         c.eps = static_cast<float>(hp->eps);
     }
     c.n = n;
@@ -2279,23 +2283,36 @@ static int32_t mt_plan_create_impl(fsdp_mt_plan** plan_out, const fsdp_mt_tensor
 // A step's scalars for a plan launch: from hp on the host, or, with a device
 // step count, advance the count and derive them on the device (a one-lane
 // launch queued first) into the plan's slot, which *cdev then names.  hp's
-// own step is not used then.
+// own step is not used then, nor hp's lr when lr_dev is given.
 static int32_t queue_step_consts(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, int64_t* step_dev,
-                          hipStream_t stream, StepConsts* c, const StepConsts** cdev, const char* who) {
+                                 const double* lr_dev, hipStream_t stream, StepConsts* c,
+                                 const StepConsts** cdev, const char* who) {
     *cdev = nullptr;
     *c = make_consts(hp, plan->n_slices);
     if (!step_dev) return FSDP_OK;
-    hipLaunchKernelGGL(step_count_kernel, dim3(1), dim3(kBlock), 0, stream, step_dev, *c, hp->lr,
-                       hp->beta1, hp->beta2, plan->n_chunks > 0 ? plan->d_consts : nullptr);
+    hipLaunchKernelGGL(step_count_kernel, dim3(1), dim3(kBlock), 0, stream, step_dev, lr_dev, *c, hp->lr,
+                       hp->weight_decay, hp->beta1, hp->beta2,
+                       plan->n_chunks > 0 ? plan->d_consts : nullptr);
     *cdev = plan->d_consts;
     return launch_status(who);
 }
 
+// Two device buffers of a call on one plan may not overlap each other.
+static int32_t check_disjoint(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes,
+                              const char* who, const char* what) {
+    if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return FSDP_OK;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    if (x < y + static_cast<uintptr_t>(b_bytes) && y < x + static_cast<uintptr_t>(a_bytes))
+        return fail(FSDP_E_ALIAS, "%s: %s", who, what);
+    return FSDP_OK;
+}
+
 // The hyperparameter and step-count checks of the calls that take a device
-// step count: hp as for a call (its step aside), and step_dev a device int64
-// that is no buffer of the plan's.
+// step count: hp as for a call (its step aside), step_dev a device int64
+// that is no buffer of the plan's, and lr_dev (optional) a device double that
+// may lie only in the plan's read-only slices and not on step_dev.
 static int32_t check_step_dev(const fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, const int64_t* step_dev,
-                       const char* who) {
+                              const double* lr_dev, const char* who) {
     if (!hp) return fail(FSDP_E_ARG, "%s: null hyperparameters", who);
     fsdp_adamw_hparams h = *hp;
     h.step = 1;
@@ -2303,19 +2320,24 @@ static int32_t check_step_dev(const fsdp_mt_plan* plan, const fsdp_adamw_hparams
     if ((st = check_hparams(&h)) != FSDP_OK) return st;
     if (!step_dev) return fail(FSDP_E_ARG, "%s: null step_dev", who);
     if (!aligned(step_dev, 8)) return fail(FSDP_E_ALIGN, "%s: step_dev not 8-byte aligned", who);
-    return check_extra(plan, step_dev, 8, true, who, "step_dev");
+    if (!aligned(lr_dev, 8)) return fail(FSDP_E_ALIGN, "%s: lr_dev not 8-byte aligned", who);
+    if ((st = check_extra(plan, step_dev, 8, true, who, "step_dev")) != FSDP_OK ||
+        (st = check_extra(plan, lr_dev, 8, false, who, "lr_dev")) != FSDP_OK)
+        return st;
+    return check_disjoint(step_dev, 8, lr_dev, 8, who, "step_dev overlaps lr_dev");
 }
 
 // capturable: the count comes from step_dev (which must then be given).
 static int32_t mt_step_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bool capturable,
-                            int64_t* step_dev, hipStream_t stream, const char* who) {
+                            int64_t* step_dev, const double* lr_dev, hipStream_t stream, const char* who) {
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
-    if ((st = capturable ? check_step_dev(plan, hp, step_dev, who) : check_hparams(hp)) != FSDP_OK) return st;
+    if ((st = capturable ? check_step_dev(plan, hp, step_dev, lr_dev, who) : check_hparams(hp)) != FSDP_OK)
+        return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     StepConsts c;
     const StepConsts* cdev;
-    if ((st = queue_step_consts(plan, hp, step_dev, stream, &c, &cdev, who)) != FSDP_OK) return st;
+    if ((st = queue_step_consts(plan, hp, step_dev, lr_dev, stream, &c, &cdev, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const int64_t budget = plan->store_pol == kStWriteThrough     ? RS_INFLIGHT_KB_WT
                            : plan->store_pol == kStNtWriteThrough ? RS_INFLIGHT_KB_NTWT
@@ -2343,12 +2365,12 @@ static int32_t mt_step_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bo
 
 extern "C" int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                                 hipStream_t stream) {
-    return mt_step_impl(plan, hp, false, nullptr, stream, "fsdp_mt_step");
+    return mt_step_impl(plan, hp, false, nullptr, nullptr, stream, "fsdp_mt_step");
 }
 
 extern "C" int32_t fsdp_mt_step_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                           int64_t* step_dev, hipStream_t stream) {
-    return mt_step_impl(plan, hp, true, step_dev, stream, "fsdp_mt_step_capturable");
+                                           int64_t* step_dev, const double* lr_dev, hipStream_t stream) {
+    return mt_step_impl(plan, hp, true, step_dev, lr_dev, stream, "fsdp_mt_step_capturable");
 }
 
 extern "C" int32_t fsdp_mt_reduce_accumulate(fsdp_mt_plan* plan, int32_t accumulate,
@@ -2454,25 +2476,23 @@ static int32_t clip_coef_impl(float* coef_out, double* norm_out, const double* s
 }
 
 static int32_t mt_step_clipped_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bool capturable,
-                                    int64_t* step_dev, const float* grad_scale, hipStream_t stream,
-                                    const char* who) {
+                                    int64_t* step_dev, const double* lr_dev, const float* grad_scale,
+                                    hipStream_t stream, const char* who) {
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
-    if ((st = capturable ? check_step_dev(plan, hp, step_dev, who) : check_hparams(hp)) != FSDP_OK) return st;
+    if ((st = capturable ? check_step_dev(plan, hp, step_dev, lr_dev, who) : check_hparams(hp)) != FSDP_OK)
+        return st;
     if (!grad_scale) return fail(FSDP_E_ARG, "%s: null grad_scale", who);
     if (!aligned(grad_scale, 4)) return fail(FSDP_E_ALIGN, "%s: grad_scale misaligned", who);
     if (!plan->all_grad_out)
         return fail(FSDP_E_ARG, "%s: every shard of the plan needs a grad_shard_out", who);
     if ((st = check_extra(plan, grad_scale, 4, false, who, "grad_scale")) != FSDP_OK) return st;
-    if (step_dev) {
-        const uintptr_t a = reinterpret_cast<uintptr_t>(step_dev), b = reinterpret_cast<uintptr_t>(grad_scale);
-        if (a < b + 4 && b < a + 8)
-            return fail(FSDP_E_ALIAS, "%s: step_dev overlaps grad_scale", who);
-    }
+    if ((st = check_disjoint(step_dev, 8, grad_scale, 4, who, "step_dev overlaps grad_scale")) != FSDP_OK)
+        return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     StepConsts c;
     const StepConsts* cdev;
-    if ((st = queue_step_consts(plan, hp, step_dev, stream, &c, &cdev, who)) != FSDP_OK) return st;
+    if ((st = queue_step_consts(plan, hp, step_dev, lr_dev, stream, &c, &cdev, who)) != FSDP_OK) return st;
     if (plan->n_chunks == 0) return FSDP_OK;
     const ScaledStepKernel k =
         pick_scaled_step(plan->any_general, write_policy(4 + 12, 12 + 2 * plan->any_bf16), cdev != nullptr);
@@ -2484,42 +2504,39 @@ static int32_t mt_step_clipped_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams
 
 extern "C" int32_t fsdp_mt_step_clipped(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                                         const float* grad_scale, hipStream_t stream) {
-    return mt_step_clipped_impl(plan, hp, false, nullptr, grad_scale, stream, "fsdp_mt_step_clipped");
+    return mt_step_clipped_impl(plan, hp, false, nullptr, nullptr, grad_scale, stream,
+                                "fsdp_mt_step_clipped");
 }
 
 extern "C" int32_t fsdp_mt_step_clipped_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                                   int64_t* step_dev, const float* grad_scale,
-                                                   hipStream_t stream) {
-    return mt_step_clipped_impl(plan, hp, true, step_dev, grad_scale, stream, "fsdp_mt_step_clipped_capturable");
-}
-
-// Two device buffers of a call on one plan may not overlap each other.
-static int32_t check_disjoint(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes,
-                              const char* who, const char* what) {
-    if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return FSDP_OK;
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    if (x < y + static_cast<uintptr_t>(b_bytes) && y < x + static_cast<uintptr_t>(a_bytes))
-        return fail(FSDP_E_ALIAS, "%s: %s", who, what);
-    return FSDP_OK;
+                                                   int64_t* step_dev, const double* lr_dev,
+                                                   const float* grad_scale, hipStream_t stream) {
+    return mt_step_clipped_impl(plan, hp, true, step_dev, lr_dev, grad_scale, stream,
+                                "fsdp_mt_step_clipped_capturable");
 }
 
 static int32_t mt_step_amax_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bool capturable,
-                                 int64_t* step_dev, float* amax_out, hipStream_t stream, const char* who) {
+                                 int64_t* step_dev, const double* lr_dev, float* amax_out, hipStream_t stream,
+                                 const char* who) {
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
-    if ((st = capturable ? check_step_dev(plan, hp, step_dev, who) : check_hparams(hp)) != FSDP_OK) return st;
+    if ((st = capturable ? check_step_dev(plan, hp, step_dev, lr_dev, who) : check_hparams(hp)) != FSDP_OK)
+        return st;
     if (!plan->any_fp8) return fail(FSDP_E_ARG, "%s: the plan has no fp8 outputs", who);
     if (!amax_out) return fail(FSDP_E_ARG, "%s: null amax_out", who);
     if (!aligned(amax_out, 4)) return fail(FSDP_E_ALIGN, "%s: amax_out misaligned", who);
     if ((st = check_extra(plan, amax_out, 4 * plan->n_tensors, true, who, "amax_out")) != FSDP_OK)
         return st;
     if ((st = check_disjoint(step_dev, 8, amax_out, 4 * plan->n_tensors, who,
-                             "step_dev overlaps amax_out")) != FSDP_OK)
+                             "step_dev overlaps amax_out")) != FSDP_OK ||
+        (st = check_disjoint(lr_dev, 8, amax_out, 4 * plan->n_tensors, who,
+                             "lr_dev overlaps amax_out")) != FSDP_OK)
         return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     StepConsts c;
     const StepConsts* cdev;
-    if ((st = queue_step_consts(plan, hp, capturable ? step_dev : nullptr, stream, &c, &cdev, who)) != FSDP_OK)
+    if ((st = queue_step_consts(plan, hp, capturable ? step_dev : nullptr, lr_dev, stream, &c, &cdev, who)) !=
+        FSDP_OK)
         return st;
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
@@ -2539,12 +2556,14 @@ static int32_t mt_step_amax_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* h
 
 extern "C" int32_t fsdp_mt_step_amax(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                                      float* amax_out, hipStream_t stream) {
-    return mt_step_amax_impl(plan, hp, false, nullptr, amax_out, stream, "fsdp_mt_step_amax");
+    return mt_step_amax_impl(plan, hp, false, nullptr, nullptr, amax_out, stream, "fsdp_mt_step_amax");
 }
 
 extern "C" int32_t fsdp_mt_step_amax_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                                int64_t* step_dev, float* amax_out, hipStream_t stream) {
-    return mt_step_amax_impl(plan, hp, true, step_dev, amax_out, stream, "fsdp_mt_step_amax_capturable");
+                                                int64_t* step_dev, const double* lr_dev, float* amax_out,
+                                                hipStream_t stream) {
+    return mt_step_amax_impl(plan, hp, true, step_dev, lr_dev, amax_out, stream,
+                             "fsdp_mt_step_amax_capturable");
 }
 
 static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int32_t n_ranks,
@@ -2584,11 +2603,12 @@ static int32_t mt_cast_fp8_impl(fsdp_mt_plan* plan, const float* amax_ranks, int
 }
 
 static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, bool capturable,
-                                int64_t* step_dev, const float* scale_in, float* amax_out,
+                                int64_t* step_dev, const double* lr_dev, const float* scale_in, float* amax_out,
                                 hipStream_t stream, const char* who) {
     if (!plan) return fail(FSDP_E_ARG, "%s: null plan", who);
     int32_t st;
-    if ((st = capturable ? check_step_dev(plan, hp, step_dev, who) : check_hparams(hp)) != FSDP_OK) return st;
+    if ((st = capturable ? check_step_dev(plan, hp, step_dev, lr_dev, who) : check_hparams(hp)) != FSDP_OK)
+        return st;
     if (!plan->all_fp8) return fail(FSDP_E_ARG, "%s: every shard of the plan needs an fp8 output", who);
     if (plan->n_tensors > 0 && (!scale_in || !amax_out))
         return fail(FSDP_E_ARG, "%s: null scale_in or amax_out", who);
@@ -2605,12 +2625,15 @@ static int32_t mt_step_fp8_impl(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp
     if ((st = check_disjoint(step_dev, 8, amax_out, 4 * plan->n_tensors, who,
                              "step_dev overlaps amax_out")) != FSDP_OK ||
         (st = check_disjoint(step_dev, 8, scale_in, 4 * plan->n_tensors, who,
-                             "step_dev overlaps scale_in")) != FSDP_OK)
+                             "step_dev overlaps scale_in")) != FSDP_OK ||
+        (st = check_disjoint(lr_dev, 8, amax_out, 4 * plan->n_tensors, who,
+                             "lr_dev overlaps amax_out")) != FSDP_OK)
         return st;
     if ((st = check_plan_device(plan, who)) != FSDP_OK) return st;
     StepConsts c;
     const StepConsts* cdev;
-    if ((st = queue_step_consts(plan, hp, capturable ? step_dev : nullptr, stream, &c, &cdev, who)) != FSDP_OK)
+    if ((st = queue_step_consts(plan, hp, capturable ? step_dev : nullptr, lr_dev, stream, &c, &cdev, who)) !=
+        FSDP_OK)
         return st;
     if (plan->n_tensors == 0) return FSDP_OK;
     if (plan->n_chunks > 0) {
@@ -2811,15 +2834,16 @@ extern "C" int32_t fsdp_mt_cast_fp8(fsdp_mt_plan* plan, const float* amax_ranks,
 extern "C" int32_t fsdp_mt_step_fp8(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
                                     const float* scale_in, float* amax_out, hipStream_t stream) {
     return fsdp::guarded("fsdp_mt_step_fp8", [&] {
-        return mt_step_fp8_impl(plan, hp, false, nullptr, scale_in, amax_out, stream, "fsdp_mt_step_fp8");
+        return mt_step_fp8_impl(plan, hp, false, nullptr, nullptr, scale_in, amax_out, stream,
+                                "fsdp_mt_step_fp8");
     });
 }
 
 extern "C" int32_t fsdp_mt_step_fp8_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
-                                               int64_t* step_dev, const float* scale_in, float* amax_out,
-                                               hipStream_t stream) {
+                                               int64_t* step_dev, const double* lr_dev, const float* scale_in,
+                                               float* amax_out, hipStream_t stream) {
     return fsdp::guarded("fsdp_mt_step_fp8_capturable", [&] {
-        return mt_step_fp8_impl(plan, hp, true, step_dev, scale_in, amax_out, stream,
+        return mt_step_fp8_impl(plan, hp, true, step_dev, lr_dev, scale_in, amax_out, stream,
                                 "fsdp_mt_step_fp8_capturable");
     });
 }

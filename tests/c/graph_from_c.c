@@ -3,10 +3,12 @@
  * copies of the same three shards (one with padding, 8 bf16 gradient slices
  * each, shared read-only) are stepped side by side: copy A by fsdp_mt_step
  * at t = 1, 2, 3, 4, copy B by replays of one HIP graph that captured
- * fsdp_mt_step_capturable once.  After every replay the two copies' state and
- * bf16 outputs must be equal bit for bit and the device count must equal the
- * replays made.  Prints "graph_from_c: ok" and exits 0, else prints what
- * differs and exits 1. */
+ * fsdp_mt_step_capturable once.  The learning rate follows a schedule
+ * (linear warmup, then decay): A passes each step's rate in its hparams, B
+ * reads it from a device double that the host writes before each replay.
+ * After every replay the two copies' state and bf16 outputs must be equal
+ * bit for bit and the device count must equal the replays made.  Prints
+ * "graph_from_c: ok" and exits 0, else prints what differs and exits 1. */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -112,23 +114,28 @@ int main(void) {
     FSDP_OK_OR_FAIL(fsdp_mt_plan_create(&plan_a, t[0], NSHARDS, NS, FSDP_DT_BF16, stream));
     FSDP_OK_OR_FAIL(fsdp_mt_plan_create(&plan_b, t[1], NSHARDS, NS, FSDP_DT_BF16, stream));
     int64_t* d_count;
+    double* d_lr;
     HIP_OK(hipMalloc((void**)&d_count, 8));
     HIP_OK(hipMemset(d_count, 0, 8));
+    HIP_OK(hipMalloc((void**)&d_lr, 8));
     HIP_OK(hipDeviceSynchronize());
 
-    /* capture one capturable step */
+    /* capture one capturable step, its learning rate read from d_lr */
     fsdp_adamw_hparams hp = {1e-3, 0.9, 0.999, 1e-8, 0.01, 1};
+    const double schedule[REPLAYS] = {2.5e-4, 5e-4, 1e-3, 7.5e-4};
     hipGraph_t graph;
     hipGraphExec_t exec;
     HIP_OK(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
-    FSDP_OK_OR_FAIL(fsdp_mt_step_capturable(plan_b, &hp, d_count, stream));
+    FSDP_OK_OR_FAIL(fsdp_mt_step_capturable(plan_b, &hp, d_count, d_lr, stream));
     HIP_OK(hipStreamEndCapture(stream, &graph));
     HIP_OK(hipGraphInstantiate(&exec, graph, NULL, NULL, 0));
 
     int bad = 0;
     for (int r = 1; r <= REPLAYS && !bad; ++r) {
         hp.step = r;
+        hp.lr = schedule[r - 1];
         FSDP_OK_OR_FAIL(fsdp_mt_step(plan_a, &hp, stream));
+        HIP_OK(hipMemcpyAsync(d_lr, &schedule[r - 1], 8, hipMemcpyHostToDevice, stream));
         HIP_OK(hipGraphLaunch(exec, stream));
         HIP_OK(hipStreamSynchronize(stream));
         int64_t count = -1;
@@ -164,6 +171,7 @@ int main(void) {
         }
     }
     (void)hipFree(d_count);
+    (void)hipFree(d_lr);
     free(h1);
     free(h2);
     if (bad) return 1;

@@ -2,7 +2,8 @@
 
 fsdp_mt_step_capturable and fsdp_mt_step_clipped_capturable advance a device
 int64 count and step at the new count, deriving the count's scalars on the
-device with the host's operations.  So:
+device with the host's operations; given a device learning rate they derive
+the rate's scalars from it the same way.  So:
   * eager calls equal fsdp_mt_step / fsdp_mt_step_clipped at t = 1, 2, ...
     bit for bit (one-range and chunk-table plans, both store policies);
   * the fp8 forms (fsdp_mt_step_amax_capturable, fsdp_mt_step_fp8_capturable)
@@ -12,6 +13,10 @@ device with the host's operations.  So:
     between replays, steps through t = 1, 2, ... and equals the eager
     fixed-count calls at each t bit for bit, the count ending at the number
     of replays;
+  * with the learning rate in device memory, written before each replay, the
+    replays follow a schedule (warmup, then decay) and equal the eager calls
+    at each step's rate bit for bit: the fused step on one-range and
+    chunk-table plans, the clipped step and both fp8 forms;
   * counts far out (t up to 10^6, where the bias corrections are 1) still
     agree with the host's scalars;
   * an empty plan advances the count only; bad arguments are refused before
@@ -110,7 +115,54 @@ def test_graph_replays_advance_the_count(table, gpu):
     b.close()
 
 
+# a learning-rate schedule: linear warmup over two steps, then decay
+SCHEDULE = [5e-4, 1e-3, 8e-4, 6.4e-4, 5.12e-4]
+
+
+def _lr(t):
+    return SCHEDULE[t - 1]
+
+
+@pytest.mark.parametrize("table", [False, True])
+def test_graph_replays_follow_a_device_learning_rate(table, gpu):
+    w, a, b = _pair(3, gpu, bf16_out=True)
+    if table:
+        _table_order_plan(a, with_grad_out=False, with_fp8=False)
+        _table_order_plan(b, with_grad_out=False, with_fp8=False)
+    else:
+        a.make_plan(with_grad_out=False)
+        b.make_plan(with_grad_out=False)
+    count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    lr = torch.zeros(1, dtype=torch.float64, device=gpu)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.plan.step_capturable(w.hparams, count, lr_dev=lr)
+    torch.cuda.synchronize()
+    for t in range(1, len(SCHEDULE) + 1):
+        a.load_grads(t)
+        b.load_grads(t)
+        a.plan.step(dict(w.hparams, lr=_lr(t)), t)
+        lr.fill_(_lr(t))
+        g.replay()
+        torch.cuda.synchronize()
+        _same(a, b, f"lr replay {t}")
+        assert int(count.item()) == t
+    # the same rate from the device and from the host: the eager forms agree too
+    a.load_grads(9)
+    b.load_grads(9)
+    lr.fill_(3e-4)
+    a.plan.step(dict(w.hparams, lr=3e-4), len(SCHEDULE) + 1)
+    b.plan.step_capturable(w.hparams, count, lr_dev=lr)
+    torch.cuda.synchronize()
+    _same(a, b, "eager, device rate")
+    del g
+    a.close()
+    b.close()
+
+
 def test_clipped_graph_replays_advance_the_count(gpu):
+    """With the learning rate in device memory as well."""
     w, a, b = _pair(3, gpu, bf16_out=True, grad_out=True)
     a.make_plan()
     b.make_plan()
@@ -118,19 +170,21 @@ def test_clipped_graph_replays_advance_the_count(gpu):
     sq_a, coef_a, norm_a = mk(1, torch.float64), mk(1, torch.float32), mk(1, torch.float64)
     sq_b, coef_b, norm_b = mk(1, torch.float64), mk(1, torch.float32), mk(1, torch.float64)
     count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    lr = mk(1, torch.float64)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         b.plan.reduce_sqnorm(sq_b)
         B.fsdp_clip_coef(coef_b, norm_b, sq_b, 1, 0.05)
-        b.plan.step_clipped_capturable(w.hparams, count, coef_b)
+        b.plan.step_clipped_capturable(w.hparams, count, coef_b, lr_dev=lr)
     torch.cuda.synchronize()
     for t in range(1, STEPS + 1):
         a.load_grads(t)
         b.load_grads(t)
         a.plan.reduce_sqnorm(sq_a)
         B.fsdp_clip_coef(coef_a, norm_a, sq_a, 1, 0.05)
-        a.plan.step_clipped(w.hparams, t, coef_a)
+        a.plan.step_clipped(dict(w.hparams, lr=_lr(t)), t, coef_a)
+        lr.fill_(_lr(t))
         g.replay()
         torch.cuda.synchronize()
         _same(a, b, f"clipped replay {t}")
@@ -148,7 +202,8 @@ def _same_fp8(a, b, what):
 
 def test_fp8_graph_replays_advance_the_count(gpu):
     """Dynamic scaling (step with amax, then the codes) and delayed scaling
-    (one pass with the previous step's scales), each captured once."""
+    (one pass with the previous step's scales), each captured once; the
+    learning rate in device memory."""
     w, a, b = _pair(3, gpu, bf16_out=False, fp8_out=True)
     a.make_plan(with_grad_out=False, with_bf16=False)
     b.make_plan(with_grad_out=False, with_bf16=False)
@@ -156,25 +211,28 @@ def test_fp8_graph_replays_advance_the_count(gpu):
     mk = lambda: torch.zeros(n, dtype=torch.float32, device=gpu)
     amax_a, scale_a, amax_b, scale_b = mk(), mk(), mk(), mk()
     count = torch.zeros(1, dtype=torch.int64, device=gpu)
+    lr = torch.zeros(1, dtype=torch.float64, device=gpu)
     torch.cuda.synchronize()
     g_dyn = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_dyn):
-        b.plan.step_amax_capturable(w.hparams, count, amax_b)
+        b.plan.step_amax_capturable(w.hparams, count, amax_b, lr_dev=lr)
         b.plan.cast_fp8(amax_b, 1, scale_b)
     g_del = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_del):
-        b.plan.step_fp8_capturable(w.hparams, count, scale_b, amax_b)
+        b.plan.step_fp8_capturable(w.hparams, count, scale_b, amax_b, lr_dev=lr)
     torch.cuda.synchronize()
     assert int(count.item()) == 0
     for t in range(1, STEPS + 1):
         a.load_grads(t)
         b.load_grads(t)
+        hp_t = dict(w.hparams, lr=_lr(t))
+        lr.fill_(_lr(t))
         if t % 2:
-            a.plan.step_amax(w.hparams, t, amax_a)
+            a.plan.step_amax(hp_t, t, amax_a)
             a.plan.cast_fp8(amax_a, 1, scale_a)
             g_dyn.replay()
         else:
-            a.plan.step_fp8(w.hparams, t, scale_a, amax_a)
+            a.plan.step_fp8(hp_t, t, scale_a, amax_a)
             g_del.replay()
         torch.cuda.synchronize()
         _same_fp8(a, b, f"fp8 replay {t}")
@@ -229,6 +287,19 @@ def test_empty_plan_and_refusals(gpu):
         B.fsdp_mt_step_capturable(st.plan.handle, w.hparams, st.exp_avg.data_ptr())
     with pytest.raises(B.FsdpError, match="FSDP_E_ALIAS"):
         B.fsdp_mt_step_clipped_capturable(st.plan.handle, w.hparams, coef.data_ptr(), coef.data_ptr())
+    # the device learning rate: 8-byte aligned, no written buffer of the plan,
+    # not on the count
+    lr_buf = torch.zeros(4, dtype=torch.float64, device=gpu)
+    with pytest.raises(B.FsdpError, match="FSDP_E_ALIGN"):
+        st.plan.step_capturable(w.hparams, count, lr_dev=lr_buf.view(torch.int32)[1:].data_ptr())
+    with pytest.raises(B.FsdpError, match="FSDP_E_ALIAS"):
+        st.plan.step_capturable(w.hparams, count, lr_dev=st.exp_avg.data_ptr())
+    with pytest.raises(B.FsdpError, match="FSDP_E_ALIAS"):
+        st.plan.step_capturable(w.hparams, count, lr_dev=st.ag_slot.data_ptr())
+    with pytest.raises(B.FsdpError, match="FSDP_E_ALIAS"):
+        st.plan.step_capturable(w.hparams, count, lr_dev=count.data_ptr())
+    with pytest.raises(B.FsdpError, match="FSDP_E_ALIAS"):
+        st.plan.step_clipped_capturable(w.hparams, count, coef, lr_dev=st.grad_out.data_ptr())
     amax = torch.zeros(len(st.segments), dtype=torch.float32, device=gpu)
     with pytest.raises(B.FsdpError, match="FSDP_E_ARG"):
         st.plan.step_amax_capturable(w.hparams, None, amax)   # (the plan has no fp8 copy either)
