@@ -115,8 +115,10 @@ def test_graph_replays_advance_the_count(table, gpu):
     b.close()
 
 
-# a learning-rate schedule: linear warmup over two steps, then decay
-SCHEDULE = [5e-4, 1e-3, 8e-4, 6.4e-4, 5.12e-4]
+# a learning-rate schedule: linear warmup over two steps, then decay, and a
+# last step at rate 0 (the fused-step test only), where the parameters must
+# not move at all while the moments still do
+SCHEDULE = [5e-4, 1e-3, 8e-4, 6.4e-4, 5.12e-4, 0.0]
 
 
 def _lr(t):
@@ -142,12 +144,16 @@ def test_graph_replays_follow_a_device_learning_rate(table, gpu):
     for t in range(1, len(SCHEDULE) + 1):
         a.load_grads(t)
         b.load_grads(t)
+        before = (b.master.clone(), b.exp_avg.clone())
         a.plan.step(dict(w.hparams, lr=_lr(t)), t)
         lr.fill_(_lr(t))
         g.replay()
         torch.cuda.synchronize()
         _same(a, b, f"lr replay {t}")
         assert int(count.item()) == t
+        if _lr(t) == 0.0:
+            assert torch.equal(_bits(b.master), _bits(before[0])), "rate 0 moved the parameters"
+            assert not torch.equal(_bits(b.exp_avg), _bits(before[1]))
     # the same rate from the device and from the host: the eager forms agree too
     a.load_grads(9)
     b.load_grads(9)
