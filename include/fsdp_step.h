@@ -427,8 +427,9 @@ int32_t fsdp_mt_step(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp, hipStream
  *           gradient slices and not step_dev (FSDP_E_ALIAS).
  * Two launches, no allocation, no host synchronisation; an empty plan
  * advances the count only (and does not read lr_dev).  The step waits for
- * the one-lane launch: about 6 us more per step than fsdp_mt_step (measured
- * on MI355X), a share only small steps notice.  step_dev must not overlap
+ * the one-lane launch: about 6 us more per step than fsdp_mt_step, and about
+ * 5 us more per replay of a one-step graph (measured on MI355X, with or
+ * without lr_dev), a share only small steps notice.  step_dev must not overlap
  * the plan's buffers (FSDP_E_ALIAS); null is FSDP_E_ARG, misaligned
  * FSDP_E_ALIGN.  Calls on one plan must not overlap (they share the slot). */
 int32_t fsdp_mt_step_capturable(fsdp_mt_plan* plan, const fsdp_adamw_hparams* hp,
