@@ -78,7 +78,7 @@ def measured_traffic(workload, launches_numel):
 
 def host_cores():
     """Cores this process may use: the affinity mask, bounded by the cgroup's
-    CPU quota where one is set (a one-GPU machine grants 16)."""
+    CPU quota where one is set (a host may show more cores than its quota)."""
     n = len(os.sched_getaffinity(0))
     try:
         with open("/sys/fs/cgroup/cpu.max") as f:
@@ -508,7 +508,7 @@ def time_fused(w, dev, stream, args, keep=False, **state_kw):
     t = 0
     # warm-up: W steps, at least one on every copy, and at least SETTLE_S of
     # steps, so that a GPU that was idle has reached its working clocks (a
-    # box's first few hundred milliseconds of work can run several % slower)
+    # GPU's first few hundred milliseconds of work can run several % slower)
     n_warm = max(args.warmup, n_copies) if n_copies > 1 else args.warmup
     w0 = time.perf_counter()
     i = 0

@@ -173,8 +173,8 @@ def _free_check(st, idx_t, ref, ffl, name):
 
 
 def _host_threads():
-    """Worker threads for the host-side checks: the machine's CPU share (at most
-    16 on a one-GPU machine), whatever the affinity mask shows."""
+    """Worker threads for the host-side checks: at most 16, the CPU share a
+    host grants one GPU's process, whatever the affinity mask shows."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
